@@ -1,0 +1,217 @@
+/*
+ * l3.h -- C ABI of the MI355X (gfx950) Large Lookup Layer (L^3) forward pass.
+ *
+ * The layer ("L^3: Large Lookup Layers", Tseng & De Sa, ICML 2026; the layer
+ * equation on the papernotes.org page, section 整体框架, and on the
+ * kimjy99.github.io page, section "Method") maps a hidden state x (d_in) and
+ * a token ID t to
+ *
+ *     L3(x, t) = W_mix [ LN( W_up( V_t^T softmax(K_t x) ) ) ; x ]    (d_out)
+ *
+ * where K_t (d_t x d_in) and V_t (d_t x d_emb) are the d_t rows of the
+ * concatenated tables W_K (v x d_in) and W_V (v x d_emb) that the token ID
+ * selects statically (kimjy99.github.io page, section "2. Efficient Training
+ * and Inference": the per-token key and value matrices concatenated into one
+ * table each).  Row ranges come from the allocation D = (d_t), 1 <= d_t <= k,
+ * sum d_t = v (papernotes.org page, section 关键设计 item 2), given here as
+ * CSR offsets: token t owns rows [off[t], off[t+1]).
+ *
+ * Shape readings (the pages print inconsistent shapes): W_up is d_up x d_emb;
+ * W_mix is d_out x (d_up + d_in) with columns [0, d_up) acting on the
+ * LayerNorm output and [d_up, d_up + d_in) on x.  No biases, no softmax
+ * temperature.  LayerNorm normalises the d_up features of one token with the
+ * biased variance, then applies gamma and beta (fp32, d_up each) with the
+ * plan's eps.  Token IDs are 0-based.
+ *
+ * Conventions for every call:
+ *  - Matrices are dense, row-major, contiguous.  Row j of W_K / W_V is
+ *    embedding j.  W_up and W_mix use the (out x in) layout.
+ *  - Float tensors (x, W_K, W_V, W_up, W_mix, out) are all fp32 or all bf16
+ *    (plan dtype); gamma and beta are always fp32; accumulation is fp32.
+ *  - "dev" pointers are HIP device memory (or host memory the device can
+ *    read, where stated); "host" pointers are ordinary host memory.  The
+ *    caller owns every buffer it passes; the library owns only what it
+ *    creates (plans, staging objects) and frees it in the matching destroy.
+ *  - `stream` is a hipStream_t (NULL = the null stream), `event` a hipEvent_t.
+ *    Calls only enqueue work on the stream; they do not synchronise, except
+ *    l3_status (documented below).
+ *  - Errors found on the host (bad arguments, offsets, sizes, capacities)
+ *    are returned before anything is enqueued.  Token IDs outside
+ *    [0, vocab) found on the device set a flag in the workspace; the output
+ *    rows of those tokens are unspecified and l3_status reports the flag.
+ *  - n = 0 is a no-op returning L3_OK.
+ *  - Plans are immutable after creation and may be shared across threads and
+ *    streams; a workspace serves one call at a time.
+ */
+#ifndef L3_H
+#define L3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct l3_plan_s *l3_plan_t;
+typedef struct l3_staging_s *l3_staging_t;
+
+enum {
+    L3_OK = 0,
+    L3_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum        */
+    L3_ERR_BAD_OFFSETS = -2, /* off[0] != 0, d_t < 1, d_t > k, off[vocab]!=v */
+    L3_ERR_TOKEN_RANGE = -3, /* a token ID outside [0, vocab)                */
+    L3_ERR_UNSUPPORTED = -4, /* dims this build does not handle              */
+    L3_ERR_CAPACITY = -5,    /* n or rows above what a buffer was sized for  */
+    L3_ERR_NOMEM = -6,       /* host or device allocation failed             */
+    L3_ERR_HIP = -7          /* a HIP runtime call failed                    */
+};
+
+enum { L3_F32 = 0, L3_BF16 = 1 };
+
+typedef struct {
+    int64_t d_in, d_emb, d_up, d_out;
+    int32_t dtype;  /* L3_F32 or L3_BF16 */
+    float ln_eps;   /* LayerNorm epsilon (e.g. 1e-5) */
+} l3_dims_t;
+
+/* Text of a status code (static storage). */
+const char *l3_strerror(int status);
+
+/*
+ * l3_plan -- validate an allocation and upload its CSR offsets.
+ * offsets: host, vocab + 1 int64 entries; off[0] = 0, 1 <= off[t+1]-off[t] <= k,
+ *          off[vocab] = v (the allocation bounds of the pages: every token gets
+ *          at least one and at most k embeddings, budget v = sum d_t).
+ * dims:    host; bf16 needs d_in, d_emb, d_up, d_out multiples of 64 and
+ *          d_in, d_up <= 8192, d_emb <= 1024; fp32 takes any positive dims.
+ * plan:    out; the handle owns a device copy of the offsets (allocated on the
+ *          current HIP device).  Errors: INVALID_ARG, BAD_OFFSETS, UNSUPPORTED,
+ *          NOMEM, HIP.
+ */
+int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k,
+            const l3_dims_t *dims, l3_plan_t *plan);
+
+/* Frees a plan (NULL is accepted). */
+int l3_plan_destroy(l3_plan_t plan);
+
+/* Plan facts: vocab, v, k and the largest d_t (any pointer may be NULL). */
+int l3_plan_info(l3_plan_t plan, int64_t *vocab, int64_t *v, int32_t *k,
+                 int32_t *max_d);
+
+/* Bytes of device workspace l3_forward / l3_route need for up to n_max tokens
+ * (0 on a bad argument).  The workspace is caller-allocated device memory,
+ * 256-byte aligned; its contents need no initialisation. */
+size_t l3_workspace_size(l3_plan_t plan, int64_t n_max);
+
+/*
+ * l3_forward -- out = L3(x, token_ids) for n tokens.
+ * x:         dev [n x d_in]        token_ids: dev int32 [n]
+ * W_K:       dev [v x d_in]        W_V:       dev [v x d_emb]
+ * W_up:      dev [d_up x d_emb]    ln_gamma, ln_beta: dev fp32 [d_up]
+ * W_mix:     dev [d_out x (d_up + d_in)]
+ * out:       dev [n x d_out], rows in the input token order.
+ * workspace: dev, >= l3_workspace_size(plan, n) bytes (workspace_bytes).
+ * The batch is sorted by token ID so each distinct ID's K_t / V_t rows are
+ * read once per call (the pages' batch sort: sciencestack.ai page, Fig. 3
+ * caption); the result does not depend on the batch order.
+ * Errors: INVALID_ARG, CAPACITY (workspace too small), HIP.
+ */
+int l3_forward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t n,
+               const void *W_K, const void *W_V, const void *W_up,
+               const float *ln_gamma, const float *ln_beta, const void *W_mix,
+               void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * l3_route -- the batch sort alone (what l3_forward does first).
+ * Sorting is stable: tokens with equal IDs keep their batch order.  IDs outside
+ * [0, vocab) sort as the key `vocab` after every valid ID and set the flag.
+ * Outputs (dev int32, caller-allocated; any may be NULL to skip):
+ *   perm[n]        sorted position -> batch index
+ *   sorted_ids[n]  keys in sorted order
+ *   inv_perm[n]    batch index -> sorted position
+ *   uniq[n]        the m distinct keys, ascending (first m entries written)
+ *   counts[n]      tokens per distinct key (first m entries)
+ *   seg_start[n+1] start of each key's block (first m+1 entries, last = n)
+ *   num_segments   dev int32 scalar: m
+ * Errors: INVALID_ARG, CAPACITY, HIP.
+ */
+int l3_route(l3_plan_t plan, const int32_t *token_ids, int64_t n, void *workspace,
+             size_t workspace_bytes, void *stream, int32_t *perm, int32_t *sorted_ids,
+             int32_t *inv_perm, int32_t *uniq, int32_t *counts, int32_t *seg_start,
+             int32_t *num_segments);
+
+/*
+ * l3_status -- synchronises `stream`, then reports the device-side flag of the
+ * last l3_forward / l3_route that used `workspace`: L3_ERR_TOKEN_RANGE if an ID
+ * was outside [0, vocab), else L3_OK (or L3_ERR_HIP).
+ */
+int l3_status(void *workspace, void *stream);
+
+/*
+ * Decode path: the tables live in pinned host memory; only the rows of the
+ * tokens being decoded cross to the device, copied on a side stream while the
+ * main stream runs earlier layers (the pages' offloaded inference:
+ * sciencestack.ai page, Fig. 4 caption; papernotes.org page, section 关键设计
+ * item 3).
+ *
+ * l3_staging_create -- device staging for up to max_rows table rows and
+ * max_tokens tokens per step (rows: K and V of the distinct IDs of one step).
+ * Allocates device memory (owned by the staging object) on the current device.
+ */
+int l3_staging_create(l3_plan_t plan, int64_t max_rows, int64_t max_tokens,
+                      l3_staging_t *staging);
+int l3_staging_destroy(l3_staging_t staging);
+
+/*
+ * l3_prefetch -- enqueue the copy of the K / V rows that `token_ids_host` need.
+ * token_ids_host: host int32 [n] (the IDs just sampled).
+ * W_K_host, W_V_host: the full tables in pinned host memory (hipHostMalloc),
+ *          same dtype and layout as the device tables of l3_forward.
+ * The distinct IDs are found on the host; each one's K rows and V rows (each
+ * contiguous) are copied with hipMemcpyAsync on `side_stream`, followed by the
+ * compact offsets and the remapped IDs; `ready_event` (may be NULL) is
+ * recorded on `side_stream` after the last copy.  The caller orders the
+ * staged forward after it (hipStreamWaitEvent).  The host arrays are read
+ * before the call returns (token_ids_host may be reused at once); the pinned
+ * tables must stay valid until the copies finish.
+ * Errors: INVALID_ARG, TOKEN_RANGE (an ID outside [0, vocab); nothing is
+ * enqueued), CAPACITY (more than max_tokens tokens or max_rows rows), HIP.
+ */
+int l3_prefetch(l3_plan_t plan, const int32_t *token_ids_host, int64_t n,
+                const void *W_K_host, const void *W_V_host, l3_staging_t staging,
+                void *side_stream, void *ready_event);
+
+/*
+ * l3_forward_staged -- l3_forward over the rows the last l3_prefetch staged,
+ * for the same n tokens in the same order.  workspace: >= l3_workspace_size
+ * (plan, n) bytes.  Errors: INVALID_ARG, CAPACITY, HIP.
+ */
+int l3_forward_staged(l3_staging_t staging, const void *x, int64_t n, const void *W_up,
+                      const float *ln_gamma, const float *ln_beta, const void *W_mix,
+                      void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dense bf16 GEMM on the library's MFMA kernel: C[M x N] = A[M x K] * B[N x K]^T
+ * (both operands k-contiguous, torch Linear layout), fp32 accumulate, bf16 out.
+ * Used as the decode workload's stand-in for the layers before L^3.
+ * K must be a multiple of 64.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                 void *stream);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, l3_forward records a
+ * pair of HIP events on its stream around each of its kernel stages and
+ * accumulates their elapsed time; l3_profile_read synchronises those events.
+ * Stages: 0 route (sort + blocks + work lists), 1 gather-attention,
+ * 2 W_up GEMM, 3 W_mix GEMM.  Not thread-safe; for benchmarking only.
+ */
+int l3_profile_enable(int enable);
+int l3_profile_read(double *ms_total, int64_t *launches, int max_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* L3_H */

@@ -1,0 +1,503 @@
+// Host side of the C ABI declared in include/l3.h: plan validation, workspace
+// layout, launch sequencing, the decode-time prefetch, and stage timing.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "l3_internal.h"
+
+using namespace l3;
+
+struct l3_plan_s {
+    int64_t vocab = 0, v = 0;
+    int32_t k = 0, max_d = 0;
+    Dims dims{};
+    int64_t *d_off = nullptr;   // device CSR offsets (vocab + 1)
+    std::vector<int64_t> h_off; // host copy, used by the prefetch path
+    bool owns_off = true;
+};
+
+struct l3_staging_s {
+    l3_plan_t plan = nullptr;
+    int64_t max_rows = 0, max_tokens = 0;
+    void *d_K = nullptr, *d_V = nullptr;
+    int64_t *d_off = nullptr;   // compact CSR over the distinct IDs of one step
+    int32_t *d_ids = nullptr;   // the step's IDs remapped to [0, m)
+    int64_t *h_off = nullptr;   // pinned host mirrors of the two arrays above
+    int32_t *h_ids = nullptr;
+    hipEvent_t small_done = nullptr;  // last copy out of h_off / h_ids
+    bool small_pending = false;
+    int64_t n = 0, m = 0, rows = 0, max_d = 0;
+};
+
+namespace {
+
+size_t esize(int dtype) { return dtype == L3_BF16 ? 2 : 4; }
+
+// ---- stage timing (benchmark aid)
+struct Prof {
+    bool on = false;
+    struct Pair { hipEvent_t a, b; int stage; };
+    std::vector<Pair> pending;
+    std::vector<hipEvent_t> pool;
+    double ms[8] = {};
+    int64_t launches[8] = {};
+} g_prof;
+
+hipEvent_t prof_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct StageTimer {
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    int stage;
+    StageTimer(int st, hipStream_t str) : s(str), stage(st) {
+        if (g_prof.on && (a = prof_event())) (void)hipEventRecord(a, s);
+    }
+    ~StageTimer() {
+        if (!a) return;
+        hipEvent_t b = prof_event();
+        if (!b) return;
+        (void)hipEventRecord(b, s);
+        g_prof.pending.push_back({a, b, stage});
+    }
+};
+
+int validate_dims(const l3_dims_t *d) {
+    if (!d) return L3_ERR_INVALID_ARG;
+    if (d->d_in <= 0 || d->d_emb <= 0 || d->d_up <= 0 || d->d_out <= 0) return L3_ERR_INVALID_ARG;
+    if (d->dtype != L3_F32 && d->dtype != L3_BF16) return L3_ERR_INVALID_ARG;
+    if (!(d->ln_eps >= 0.f)) return L3_ERR_INVALID_ARG;
+    if (d->dtype == L3_BF16) {
+        if (d->d_in % 64 || d->d_up % 64 || d->d_out % 64) return L3_ERR_UNSUPPORTED;
+        if (d->d_in > 4096) return L3_ERR_UNSUPPORTED;
+        if (d->d_emb != 64 && d->d_emb != 128 && d->d_emb != 256 && d->d_emb != 512)
+            return L3_ERR_UNSUPPORTED;
+    }
+    return L3_OK;
+}
+
+int check_offsets(const int64_t *off, int64_t vocab, int64_t v, int32_t k, int32_t *max_d) {
+    if (off[0] != 0) return L3_ERR_BAD_OFFSETS;
+    int64_t mx = 0;
+    for (int64_t t = 0; t < vocab; ++t) {
+        const int64_t d = off[t + 1] - off[t];
+        if (d < 1 || d > k) return L3_ERR_BAD_OFFSETS;
+        mx = std::max(mx, d);
+    }
+    if (off[vocab] != v) return L3_ERR_BAD_OFFSETS;
+    *max_d = (int32_t)mx;
+    return L3_OK;
+}
+
+// One forward over any CSR/table view (the full tables, or a staging's compact copy).
+int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                 const void *WV, const void *W_up, const float *gamma, const float *beta,
+                 const void *W_mix, void *out, void *ws, size_t ws_bytes, hipStream_t s) {
+    const Dims &D = P.dims;
+    const WsLayout L = ws_layout(D, n, P.max_d);
+    if (ws_bytes < L.total) return L3_ERR_CAPACITY;
+    RouteBufs b{};
+    b.hdr = ws_ptr<int32_t>(ws, L.hdr);
+    b.keys_a = ws_ptr<int32_t>(ws, L.keys_a);
+    b.vals_a = ws_ptr<int32_t>(ws, L.vals_a);
+    b.keys_b = ws_ptr<int32_t>(ws, L.keys_b);
+    b.vals_b = ws_ptr<int32_t>(ws, L.vals_b);
+    b.rank = ws_ptr<int32_t>(ws, L.rank);
+    b.hist = ws_ptr<int32_t>(ws, L.hist);
+    b.tile_cnt = ws_ptr<int32_t>(ws, L.tile_cnt);
+    b.inv_perm = ws_ptr<int32_t>(ws, L.inv_perm);
+    b.uniq = ws_ptr<int32_t>(ws, L.uniq);
+    b.counts = ws_ptr<int32_t>(ws, L.counts);
+    b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
+    int2 *light = ws_ptr<int2>(ws, L.light);
+    int2 *heavy = ws_ptr<int2>(ws, L.heavy);
+    void *o = ws_ptr<char>(ws, L.o);
+    void *h = ws_ptr<char>(ws, L.h);
+    float *lnp = ws_ptr<float>(ws, L.lnp);
+
+    const int light_tok = attn_light_tokens(D.d_in, D.dtype);
+    const int heavy_min = attn_heavy_min_tokens(D.d_in, D.d_emb, D.dtype, P.max_d);
+    {
+        StageTimer tm(0, s);
+        L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
+        L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));
+        L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, light_tok, light, heavy, s));
+    }
+    {
+        StageTimer tm(1, s);
+        AttnArgs a{};
+        a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
+        a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
+        a.light = light; a.heavy = heavy;
+        a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
+        a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;
+        L3_HIP_TRY(launch_attn(a, D.dtype, 1, s));
+    }
+    if (D.dtype == L3_BF16) {
+        {
+            StageTimer tm(2, s);
+            L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h, n,
+                                        D.d_up, D.d_emb, lnp, s));
+        }
+        {
+            StageTimer tm(3, s);
+            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, lnp, gamma, beta,
+                                            D.eps, (const uint16_t *)W_mix, (uint16_t *)out, n,
+                                            D.d_up, D.d_in, D.d_out, s));
+        }
+    } else {
+        {
+            StageTimer tm(2, s);
+            L3_HIP_TRY(launch_gemm_f32((const float *)o, (const float *)W_up, (float *)h, n, D.d_up,
+                                       D.d_emb, s));
+        }
+        {
+            StageTimer tm(3, s);
+            L3_HIP_TRY(launch_gemm_mix_f32((const float *)h, (const float *)x, lnp, gamma, beta, D.eps,
+                                           (const float *)W_mix, (float *)out, n, D.d_up, D.d_in,
+                                           D.d_out, s));
+        }
+    }
+    return L3_OK;
+}
+
+}  // namespace
+
+namespace l3 {
+
+WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
+    WsLayout L{};
+    const int64_t n = std::max<int64_t>(n_max, 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    L.ntiles = (n + kSortTile - 1) / kSortTile;
+    L.hdr = take(HDR_WORDS * 4);
+    L.keys_a = take(n * 4);
+    L.vals_a = take(n * 4);
+    L.keys_b = take(n * 4);
+    L.vals_b = take(n * 4);
+    L.rank = take(n * 4);
+    L.hist = take((size_t)kRadix * L.ntiles * 4);
+    L.tile_cnt = take(L.ntiles * 4);
+    L.inv_perm = take(n * 4);
+    L.uniq = take(n * 4);
+    L.counts = take(n * 4);
+    L.seg_start = take((n + 1) * 4);
+    L.light = take(n * 8);
+    L.heavy = take(n * 8);
+    L.scores = take(d.dtype == L3_F32 ? (size_t)n * std::max(max_d, 1) * 4 : 0);
+    const size_t es = esize(d.dtype);
+    L.o = take((size_t)n * d.d_emb * es);
+    L.h = take((size_t)n * d.d_up * es);
+    const int64_t np = (d.d_up + kLnPart - 1) / kLnPart;
+    L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace l3
+
+extern "C" {
+
+const char *l3_strerror(int status) {
+    switch (status) {
+        case L3_OK: return "ok";
+        case L3_ERR_INVALID_ARG: return "invalid argument";
+        case L3_ERR_BAD_OFFSETS: return "bad offsets: need off[0]=0, 1<=d_t<=k, off[vocab]=v";
+        case L3_ERR_TOKEN_RANGE: return "token id outside [0, vocab)";
+        case L3_ERR_UNSUPPORTED: return "unsupported dimensions";
+        case L3_ERR_CAPACITY: return "capacity exceeded (workspace or staging too small)";
+        case L3_ERR_NOMEM: return "out of memory";
+        case L3_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k, const l3_dims_t *dims,
+            l3_plan_t *plan) {
+    if (!plan) return L3_ERR_INVALID_ARG;
+    *plan = nullptr;
+    if (!offsets || vocab <= 0 || v <= 0 || k < 1) return L3_ERR_INVALID_ARG;
+    if (vocab >= (1ll << 30) || v >= (1ll << 31)) return L3_ERR_UNSUPPORTED;
+    int rc = validate_dims(dims);
+    if (rc) return rc;
+    int32_t max_d = 0;
+    rc = check_offsets(offsets, vocab, v, k, &max_d);
+    if (rc) return rc;
+    l3_plan_s *p = new (std::nothrow) l3_plan_s();
+    if (!p) return L3_ERR_NOMEM;
+    p->vocab = vocab;
+    p->v = v;
+    p->k = k;
+    p->max_d = max_d;
+    p->dims = Dims{dims->d_in, dims->d_emb, dims->d_up, dims->d_out, dims->dtype, dims->ln_eps};
+    try {
+        p->h_off.assign(offsets, offsets + vocab + 1);
+    } catch (...) {
+        delete p;
+        return L3_ERR_NOMEM;
+    }
+    const size_t bytes = (size_t)(vocab + 1) * sizeof(int64_t);
+    if (hipMalloc(&p->d_off, bytes) != hipSuccess) {
+        delete p;
+        return L3_ERR_HIP;
+    }
+    if (hipMemcpy(p->d_off, offsets, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(p->d_off);
+        delete p;
+        return L3_ERR_HIP;
+    }
+    *plan = p;
+    return L3_OK;
+}
+
+int l3_plan_destroy(l3_plan_t p) {
+    if (!p) return L3_OK;
+    if (p->owns_off && p->d_off) (void)hipFree(p->d_off);
+    delete p;
+    return L3_OK;
+}
+
+int l3_plan_info(l3_plan_t p, int64_t *vocab, int64_t *v, int32_t *k, int32_t *max_d) {
+    if (!p) return L3_ERR_INVALID_ARG;
+    if (vocab) *vocab = p->vocab;
+    if (v) *v = p->v;
+    if (k) *k = p->k;
+    if (max_d) *max_d = p->max_d;
+    return L3_OK;
+}
+
+size_t l3_workspace_size(l3_plan_t p, int64_t n_max) {
+    if (!p || n_max < 0) return 0;
+    return ws_layout(p->dims, n_max, p->max_d).total;
+}
+
+int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
+               const void *WV, const void *W_up, const float *gamma, const float *beta,
+               const void *W_mix, void *out, void *ws, size_t ws_bytes, void *stream) {
+    if (!p || n < 0) return L3_ERR_INVALID_ARG;
+    if (n == 0) return L3_OK;
+    if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
+    if (!x || !ids || !WK || !WV || !W_up || !gamma || !beta || !W_mix || !out || !ws)
+        return L3_ERR_INVALID_ARG;
+    return forward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, out, ws, ws_bytes,
+                        (hipStream_t)stream);
+}
+
+int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_bytes, void *stream,
+             int32_t *perm, int32_t *sorted_ids, int32_t *inv_perm, int32_t *uniq, int32_t *counts,
+             int32_t *seg_start, int32_t *num_segments) {
+    if (!p || n < 0 || !ws) return L3_ERR_INVALID_ARG;
+    if (n == 0) return L3_OK;
+    if (!ids) return L3_ERR_INVALID_ARG;
+    if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const WsLayout L = ws_layout(p->dims, n, p->max_d);
+    if (ws_bytes < L.total) return L3_ERR_CAPACITY;
+    RouteBufs b{};
+    b.hdr = ws_ptr<int32_t>(ws, L.hdr);
+    b.keys_a = ws_ptr<int32_t>(ws, L.keys_a);
+    b.vals_a = ws_ptr<int32_t>(ws, L.vals_a);
+    b.keys_b = ws_ptr<int32_t>(ws, L.keys_b);
+    b.vals_b = ws_ptr<int32_t>(ws, L.vals_b);
+    b.rank = ws_ptr<int32_t>(ws, L.rank);
+    b.hist = ws_ptr<int32_t>(ws, L.hist);
+    b.tile_cnt = ws_ptr<int32_t>(ws, L.tile_cnt);
+    b.inv_perm = ws_ptr<int32_t>(ws, L.inv_perm);
+    b.uniq = ws_ptr<int32_t>(ws, L.uniq);
+    b.counts = ws_ptr<int32_t>(ws, L.counts);
+    b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
+    L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
+    L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
+    L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, 1, ws_ptr<int2>(ws, L.light),
+                               ws_ptr<int2>(ws, L.heavy), s));
+    const size_t nb = (size_t)n * 4;
+    auto cp = [&](int32_t *dst, const int32_t *src, size_t bytes) -> hipError_t {
+        return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;
+    };
+    L3_HIP_TRY(cp(perm, b.perm, nb));
+    L3_HIP_TRY(cp(sorted_ids, b.sorted_ids, nb));
+    L3_HIP_TRY(cp(inv_perm, b.inv_perm, nb));
+    L3_HIP_TRY(cp(uniq, b.uniq, nb));
+    L3_HIP_TRY(cp(counts, b.counts, nb));
+    L3_HIP_TRY(cp(seg_start, b.seg_start, nb + 4));
+    L3_HIP_TRY(cp(num_segments, b.hdr + HDR_NSEG, 4));
+    return L3_OK;
+}
+
+int l3_status(void *ws, void *stream) {
+    if (!ws) return L3_ERR_INVALID_ARG;
+    L3_HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    int32_t flag = 0;
+    L3_HIP_TRY(hipMemcpy(&flag, ws_ptr<int32_t>(ws, 0) + HDR_ERR, 4, hipMemcpyDeviceToHost));
+    return flag ? L3_ERR_TOKEN_RANGE : L3_OK;
+}
+
+int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                 void *stream) {
+    if (!A || !B || !C || M < 0 || N < 0 || K <= 0) return L3_ERR_INVALID_ARG;
+    if (K % 64 || N % 64) return L3_ERR_UNSUPPORTED;
+    L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)A, (const uint16_t *)B, (uint16_t *)C, M, N, K,
+                                nullptr, (hipStream_t)stream));
+    return L3_OK;
+}
+
+// ---------------------------------------------------------------- decode staging
+
+int l3_staging_create(l3_plan_t p, int64_t max_rows, int64_t max_tokens, l3_staging_t *out) {
+    if (!p || !out || max_rows <= 0 || max_tokens <= 0) return L3_ERR_INVALID_ARG;
+    *out = nullptr;
+    l3_staging_s *st = new (std::nothrow) l3_staging_s();
+    if (!st) return L3_ERR_NOMEM;
+    st->plan = p;
+    st->max_rows = max_rows;
+    st->max_tokens = max_tokens;
+    const size_t es = esize(p->dims.dtype);
+    bool ok = hipMalloc(&st->d_K, max_rows * p->dims.d_in * es) == hipSuccess &&
+              hipMalloc(&st->d_V, max_rows * p->dims.d_emb * es) == hipSuccess &&
+              hipMalloc(&st->d_off, (max_tokens + 1) * sizeof(int64_t)) == hipSuccess &&
+              hipMalloc(&st->d_ids, max_tokens * sizeof(int32_t)) == hipSuccess &&
+              hipHostMalloc(&st->h_off, (max_tokens + 1) * sizeof(int64_t), 0) == hipSuccess &&
+              hipHostMalloc(&st->h_ids, max_tokens * sizeof(int32_t), 0) == hipSuccess &&
+              hipEventCreateWithFlags(&st->small_done, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        l3_staging_destroy(st);
+        return L3_ERR_HIP;
+    }
+    *out = st;
+    return L3_OK;
+}
+
+int l3_staging_destroy(l3_staging_t st) {
+    if (!st) return L3_OK;
+    if (st->small_pending && st->small_done) (void)hipEventSynchronize(st->small_done);
+    if (st->d_K) (void)hipFree(st->d_K);
+    if (st->d_V) (void)hipFree(st->d_V);
+    if (st->d_off) (void)hipFree(st->d_off);
+    if (st->d_ids) (void)hipFree(st->d_ids);
+    if (st->h_off) (void)hipHostFree(st->h_off);
+    if (st->h_ids) (void)hipHostFree(st->h_ids);
+    if (st->small_done) (void)hipEventDestroy(st->small_done);
+    delete st;
+    return L3_OK;
+}
+
+int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
+                const void *WV_host, l3_staging_t st, void *side_stream, void *ready_event) {
+    if (!p || !st || st->plan != p || n < 0 || !WK_host || !WV_host) return L3_ERR_INVALID_ARG;
+    if (n > 0 && !ids) return L3_ERR_INVALID_ARG;
+    if (n > st->max_tokens) return L3_ERR_CAPACITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= p->vocab) return L3_ERR_TOKEN_RANGE;
+    std::vector<int32_t> u(ids, ids + n);
+    std::sort(u.begin(), u.end());
+    u.erase(std::unique(u.begin(), u.end()), u.end());
+    const int64_t m = (int64_t)u.size();
+    int64_t rows = 0, max_d = 0;
+    for (int32_t t : u) {
+        const int64_t d = p->h_off[t + 1] - p->h_off[t];
+        rows += d;
+        max_d = std::max(max_d, d);
+    }
+    if (rows > st->max_rows) return L3_ERR_CAPACITY;
+    hipStream_t s = (hipStream_t)side_stream;
+    // the pinned mirrors may still feed the previous step's copies
+    if (st->small_pending) L3_HIP_TRY(hipEventSynchronize(st->small_done));
+    st->small_pending = false;
+    st->h_off[0] = 0;
+    for (int64_t i = 0; i < m; ++i) st->h_off[i + 1] = st->h_off[i] + (p->h_off[u[i] + 1] - p->h_off[u[i]]);
+    for (int64_t i = 0; i < n; ++i)
+        st->h_ids[i] = (int32_t)(std::lower_bound(u.begin(), u.end(), ids[i]) - u.begin());
+    const size_t es = esize(p->dims.dtype);
+    const size_t rk = p->dims.d_in * es, rv = p->dims.d_emb * es;
+    // one copy per run of consecutive IDs (their rows are adjacent in both layouts)
+    for (int64_t i = 0; i < m;) {
+        int64_t j = i + 1;
+        while (j < m && u[j] == u[j - 1] + 1) ++j;
+        const int64_t src = p->h_off[u[i]];
+        const int64_t len = p->h_off[u[j - 1] + 1] - src;
+        const int64_t dst = st->h_off[i];
+        L3_HIP_TRY(hipMemcpyAsync((char *)st->d_K + dst * rk, (const char *)WK_host + src * rk, len * rk,
+                                  hipMemcpyHostToDevice, s));
+        L3_HIP_TRY(hipMemcpyAsync((char *)st->d_V + dst * rv, (const char *)WV_host + src * rv, len * rv,
+                                  hipMemcpyHostToDevice, s));
+        i = j;
+    }
+    if (n > 0) {
+        L3_HIP_TRY(hipMemcpyAsync(st->d_off, st->h_off, (m + 1) * sizeof(int64_t), hipMemcpyHostToDevice, s));
+        L3_HIP_TRY(hipMemcpyAsync(st->d_ids, st->h_ids, n * sizeof(int32_t), hipMemcpyHostToDevice, s));
+        L3_HIP_TRY(hipEventRecord(st->small_done, s));
+        st->small_pending = true;
+    }
+    if (ready_event) L3_HIP_TRY(hipEventRecord((hipEvent_t)ready_event, s));
+    st->n = n;
+    st->m = m;
+    st->rows = rows;
+    st->max_d = max_d;
+    return L3_OK;
+}
+
+int l3_forward_staged(l3_staging_t st, const void *x, int64_t n, const void *W_up,
+                      const float *gamma, const float *beta, const void *W_mix, void *out, void *ws,
+                      size_t ws_bytes, void *stream) {
+    if (!st || n < 0) return L3_ERR_INVALID_ARG;
+    if (n != st->n) return L3_ERR_INVALID_ARG;
+    if (n == 0) return L3_OK;
+    if (!x || !W_up || !gamma || !beta || !W_mix || !out || !ws) return L3_ERR_INVALID_ARG;
+    // a plan view over the compact CSR; workspace sizing uses the full plan's max_d
+    l3_plan_s view;
+    view.vocab = st->m;
+    view.v = st->rows;
+    view.k = st->plan->k;
+    view.max_d = st->plan->max_d;
+    view.dims = st->plan->dims;
+    view.d_off = st->d_off;
+    view.owns_off = false;
+    return forward_impl(view, x, st->d_ids, n, st->d_K, st->d_V, W_up, gamma, beta, W_mix, out, ws,
+                        ws_bytes, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- stage timing
+
+int l3_profile_enable(int enable) {
+    g_prof.on = enable != 0;
+    if (g_prof.on) {
+        std::memset(g_prof.ms, 0, sizeof(g_prof.ms));
+        std::memset(g_prof.launches, 0, sizeof(g_prof.launches));
+    }
+    return L3_OK;
+}
+
+int l3_profile_read(double *ms_total, int64_t *launches, int max_stages) {
+    for (auto &pr : g_prof.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pr.b) != hipSuccess) return L3_ERR_HIP;
+        if (hipEventElapsedTime(&ms, pr.a, pr.b) != hipSuccess) return L3_ERR_HIP;
+        g_prof.ms[pr.stage] += ms;
+        g_prof.launches[pr.stage] += 1;
+        g_prof.pool.push_back(pr.a);
+        g_prof.pool.push_back(pr.b);
+    }
+    g_prof.pending.clear();
+    for (int i = 0; i < max_stages && i < 8; ++i) {
+        if (ms_total) ms_total[i] = g_prof.ms[i];
+        if (launches) launches[i] = g_prof.launches[i];
+    }
+    return L3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Internal declarations of the L^3 forward library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/l3.h"
+
+#define L3_HIP_TRY(expr)                                   \
+    do {                                                   \
+        hipError_t e_ = (expr);                            \
+        if (e_ != hipSuccess) return L3_ERR_HIP;           \
+    } while (0)
+
+namespace l3 {
+
+constexpr int kSortTile = 2048;    // keys ranked per workgroup and pass
+constexpr int kRadixBits = 9;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kLnPart = 128;       // LayerNorm partial statistics cover 128 features
+constexpr int kHeavyMaxD = 512;    // MFMA gather-attention keeps all d_t <= 512 scores on chip
+constexpr int kHeavyTile = 64;     // tokens per MFMA gather-attention work item
+
+// Workspace header (int32 words), zeroed at the start of every call.
+enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_WORDS = 64 };
+
+struct Dims {
+    int64_t d_in, d_emb, d_up, d_out;
+    int dtype;
+    float eps;
+};
+
+// Byte offsets of the workspace regions for n_max tokens.
+struct WsLayout {
+    size_t hdr, keys_a, vals_a, keys_b, vals_b, rank, hist, tile_cnt;
+    size_t inv_perm, uniq, counts, seg_start, light, heavy;
+    size_t scores;  // fp32 path only: n x max_d
+    size_t o, h, lnp;
+    size_t total;
+    int64_t ntiles;
+};
+
+WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d);
+
+template <typename T>
+inline T *ws_ptr(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+// Route outputs inside (or outside) the workspace.
+struct RouteBufs {
+    int32_t *hdr;
+    int32_t *keys_a, *vals_a, *keys_b, *vals_b, *rank, *hist, *tile_cnt;
+    int32_t *sorted_ids;  // final keys
+    int32_t *perm;        // final values
+    int32_t *inv_perm, *uniq, *counts, *seg_start;
+};
+
+// ---- launchers (all enqueue on `s`; return hipError_t of the last launch)
+hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s);
+hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs &b, int64_t ntiles,
+                        hipStream_t s);
+// Work lists for the gather-attention kernels (reads the route outputs).
+hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
+                           int heavy_min_tokens, int light_tokens, int2 *light, int2 *heavy,
+                           hipStream_t s);
+
+struct AttnArgs {
+    const void *x, *WK, *WV;
+    const int64_t *off;
+    const int32_t *uniq, *seg_start, *perm, *hdr;
+    const int2 *light, *heavy;
+    int64_t n, d_in, d_emb, vocab;
+    void *o;
+    float *scores;  // fp32 path scratch
+    int32_t max_d;
+};
+int attn_light_tokens(int64_t d_in, int dtype);   // tokens per light work item
+int attn_heavy_min_tokens(int64_t d_in, int64_t d_emb, int dtype, int32_t max_d);  // INT32_MAX = none
+hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t s);
+
+// out[M x N] = A[M x K] B[N x K]^T, bf16 in / bf16 out, fp32 accumulate.
+// Optional LayerNorm partial statistics of the stored (bf16-rounded) rows of C
+// (ln_out [M x ceil(N/128) x 2] = per 128-column chunk (mean, M2)).
+hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N,
+                            int64_t K, float *ln_out, hipStream_t s);
+// out = [LN(h) ; x] W_mix^T: columns k < d_up of the A operand are LN(h) built from
+// the partial statistics, the rest are x.
+hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *lnp,
+                                const float *gamma, const float *beta, float eps,
+                                const uint16_t *W_mix, uint16_t *out, int64_t M, int64_t d_up,
+                                int64_t d_in, int64_t d_out, hipStream_t s);
+// fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
+// separate per-row statistics pass.
+hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
+hipError_t launch_gemm_mix_f32(const float *h, const float *x, float *stats, const float *gamma,
+                               const float *beta, float eps, const float *W_mix, float *out,
+                               int64_t M, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
+
+}  // namespace l3

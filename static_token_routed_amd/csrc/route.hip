@@ -1,0 +1,320 @@
+// Batch sort by token ID and the per-ID blocks ("L^3: Large Lookup Layers":
+// sciencestack.ai page, Fig. 3 caption -- the layer mixes channels only, so the
+// batch may be sorted by token ID, giving one contiguous block per ID, and the
+// sort undone afterwards; kimjy99.github.io page, section "2. Efficient
+// Training and Inference" -- sorted, the "allowed tokens" mask is block
+// diagonal).
+//
+// Stable LSD radix sort of the keys (token ID, or `vocab` for an ID outside
+// [0, vocab)) in 9-bit digits.  Per pass:
+//   k_sort_rank    each workgroup ranks 2048 keys: every wave takes 512
+//                  consecutive keys, 64 at a time in batch order; lanes with the
+//                  same digit find each other with 9 ballots, the lowest lane
+//                  reserves their places with one LDS atomic, so ranks are
+//                  stable; writes the tile's digit histogram (digit-major).
+//   k_scan         exclusive scan of the digit-major histogram.
+//   k_sort_scatter position = scanned histogram + rank.
+// Blocks: head flags of the sorted keys, counted per tile, scanned, written.
+// Nothing is read back to the host: counts stay on the device.
+#include "l3_internal.h"
+
+namespace l3 {
+namespace {
+
+__device__ inline int key_of(int32_t id, int32_t vocab) {
+    return (id >= 0 && id < vocab) ? id : vocab;
+}
+
+__global__ __launch_bounds__(256) void k_zero_i32(int32_t *p, int64_t count) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
+// Ranks the keys of one 2048-key tile for the digit at `shift`.
+__global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ keys, int n,
+                                                   int shift, int from_ids, int vocab,
+                                                   int32_t *__restrict__ rank,
+                                                   int32_t *__restrict__ hist, int ntiles,
+                                                   int32_t *__restrict__ err) {
+    __shared__ uint32_t cnt[4][kRadix];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int tile = blockIdx.x;
+    for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+
+    const int base = tile * kSortTile + w * (kSortTile / 4);
+    uint32_t dig[8], rk[8];
+    int bad = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int idx = base + r * 64 + lane;
+        const bool valid = idx < n;
+        int key = 0;
+        if (valid) {
+            key = keys[idx];
+            if (from_ids) {
+                const int k2 = key_of(key, vocab);
+                bad |= (k2 != key);
+                key = k2;
+            }
+        }
+        const uint32_t d = ((uint32_t)key >> shift) & (kRadix - 1);
+        uint64_t mask = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            const uint32_t bit = (d >> b) & 1u;
+            const uint64_t bb = __ballot(bit);
+            mask &= bit ? bb : ~bb;
+        }
+        const int leader = valid ? (__ffsll((unsigned long long)mask) - 1) : lane;
+        const uint32_t below = (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        uint32_t old = 0;
+        if (valid && lane == leader) old = atomicAdd(&cnt[w][d], (uint32_t)__popcll(mask));
+        old = __shfl(old, leader);
+        dig[r] = d;
+        rk[r] = old + below;
+    }
+    if (from_ids) {
+        if (__ballot(bad) != 0ull && lane == 0) atomicOr(err, 1);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < kRadix; d += 256) {
+        uint32_t run = 0;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const uint32_t c = cnt[ww][d];
+            cnt[ww][d] = run;
+            run += c;
+        }
+        hist[(int64_t)d * ntiles + tile] = (int32_t)run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int idx = base + r * 64 + lane;
+        if (idx < n) rank[idx] = (int32_t)(cnt[w][dig[r]] + rk[r]);
+    }
+}
+
+// Exclusive scan of `len` int32 in place by one 1024-thread workgroup; the total is
+// written to *total when total != nullptr.
+__global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ data, int len,
+                                               int32_t *__restrict__ total) {
+    __shared__ int32_t part[1024];
+    __shared__ int32_t wsum[16];
+    const int t = threadIdx.x;
+    const int per = (len + 1023) / 1024;
+    const int beg = min(t * per, len), end = min(beg + per, len);
+    int32_t s = 0;
+    for (int i = beg; i < end; ++i) s += data[i];
+    // inclusive scan of s over the workgroup
+    const int lane = t & 63, w = t >> 6;
+    int32_t v = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    if (w == 0) {
+        int32_t x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int32_t u = __shfl_up(x, o);
+            if (lane >= o) x += u;
+        }
+        if (lane < 16) wsum[lane] = x;
+    }
+    __syncthreads();
+    const int32_t incl = v + (w > 0 ? wsum[w - 1] : 0);
+    part[t] = incl - s;
+    if (t == 1023 && total) *total = incl;
+    int32_t run = part[t];
+    for (int i = beg; i < end; ++i) {
+        const int32_t x = data[i];
+        data[i] = run;
+        run += x;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict__ keys_in,
+                                                      const int32_t *__restrict__ vals_in, int n,
+                                                      int shift, int from_ids, int vocab,
+                                                      const int32_t *__restrict__ hist, int ntiles,
+                                                      const int32_t *__restrict__ rank,
+                                                      int32_t *__restrict__ keys_out,
+                                                      int32_t *__restrict__ vals_out) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    int key = keys_in[idx];
+    if (from_ids) key = key_of(key, vocab);
+    const uint32_t d = ((uint32_t)key >> shift) & (kRadix - 1);
+    const int pos = hist[(int64_t)d * ntiles + idx / kSortTile] + rank[idx];
+    if ((unsigned)pos >= (unsigned)n) return;  // cannot happen for a consistent ranking
+    keys_out[pos] = key;
+    vals_out[pos] = from_ids ? idx : vals_in[idx];
+}
+
+// Per 2048-key tile: number of block heads; also the inverse permutation.
+__global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ sk,
+                                                   const int32_t *__restrict__ perm, int n,
+                                                   int32_t *__restrict__ tile_cnt,
+                                                   int32_t *__restrict__ inv_perm) {
+    __shared__ int32_t wsum[4];
+    const int base = blockIdx.x * kSortTile;
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int s = base + r * 256 + threadIdx.x;
+        if (s < n) {
+            c += (s == 0 || sk[s] != sk[s - 1]);
+            const int i = perm[s];
+            if ((unsigned)i < (unsigned)n) inv_perm[i] = s;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// Writes uniq[] and seg_start[] of the heads in one tile (8 consecutive keys per thread).
+__global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ sk, int n,
+                                                   const int32_t *__restrict__ tile_off,
+                                                   const int32_t *__restrict__ nseg,
+                                                   int32_t *__restrict__ uniq,
+                                                   int32_t *__restrict__ seg_start) {
+    __shared__ int32_t wsum[4];
+    const int base = blockIdx.x * kSortTile + threadIdx.x * 8;
+    int flags = 0, c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int s = base + i;
+        const int f = (s < n) && (s == 0 || sk[s] != sk[s - 1]);
+        flags |= f << i;
+        c += f;
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int v = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int pre = 0;
+    for (int ww = 0; ww < w; ++ww) pre += wsum[ww];
+    int j = tile_off[blockIdx.x] + pre + v - c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if ((flags & (1 << i)) && j < n) {
+            uniq[j] = sk[base + i];
+            seg_start[j] = base + i;
+            ++j;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) seg_start[min(*nseg, n)] = n;
+}
+
+// One thread per block (segment): its size, and its work items appended to the light
+// or heavy list (one wave-aggregated atomic per list; item order does not affect
+// results, only scheduling).
+__global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ uniq,
+                                                  const int32_t *__restrict__ seg_start,
+                                                  int32_t *__restrict__ counts,
+                                                  const int64_t *__restrict__ off, int vocab,
+                                                  int heavy_min, int light_tok,
+                                                  int2 *__restrict__ light,
+                                                  int2 *__restrict__ heavy,
+                                                  int32_t *__restrict__ hdr) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int m = hdr[HDR_NSEG];
+    const int lane = threadIdx.x & 63;
+    int nl = 0, nh = 0, S = 0;
+    if (j < m) {
+        S = seg_start[j + 1] - seg_start[j];
+        counts[j] = S;
+        const int t = uniq[j];
+        const int d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
+        if (t < vocab && S >= heavy_min && d <= kHeavyMaxD)
+            nh = (S + kHeavyTile - 1) / kHeavyTile;
+        else
+            nl = (S + light_tok - 1) / light_tok;
+    }
+    // wave-inclusive scans of nl and nh
+    int sl = nl, sh = nh;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int a = __shfl_up(sl, o), b = __shfl_up(sh, o);
+        if (lane >= o) { sl += a; sh += b; }
+    }
+    int bl = 0, bh = 0;
+    if (lane == 63) {
+        if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
+        if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
+    }
+    bl = __shfl(bl, 63) + sl - nl;
+    bh = __shfl(bh, 63) + sh - nh;
+    for (int q = 0; q < nl; ++q) light[bl + q] = make_int2(j, q * light_tok);
+    for (int q = 0; q < nh; ++q) heavy[bh + q] = make_int2(j, q * kHeavyTile);
+}
+
+inline int blocks_for(int64_t n, int per) { return (int)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_i32, dim3(blocks_for(count, 256)), dim3(256), 0, s, p, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBufs &b, int64_t ntiles,
+                        hipStream_t s) {
+    const int n = (int)n64;
+    int bits = 1;
+    while ((1ll << bits) <= vocab) ++bits;  // keys lie in [0, vocab]
+    const int passes = (bits + kRadixBits - 1) / kRadixBits;
+    const int32_t *kin = ids;
+    const int32_t *vin = nullptr;
+    int32_t *kout = b.keys_a, *vout = b.vals_a;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = p * kRadixBits;
+        const int from_ids = p == 0;
+        hipLaunchKernelGGL(k_sort_rank, dim3((unsigned)ntiles), dim3(256), 0, s, kin, n, shift,
+                           from_ids, (int)vocab, b.rank, b.hist, (int)ntiles, b.hdr + HDR_ERR);
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, b.hist, (int)(kRadix * ntiles),
+                           (int32_t *)nullptr);
+        hipLaunchKernelGGL(k_sort_scatter, dim3(blocks_for(n, 256)), dim3(256), 0, s, kin,
+                           vin ? vin : kin, n, shift, from_ids, (int)vocab, b.hist, (int)ntiles,
+                           b.rank, kout, vout);
+        kin = kout;
+        vin = vout;
+        kout = (kout == b.keys_a) ? b.keys_b : b.keys_a;
+        vout = (vout == b.vals_a) ? b.vals_b : b.vals_a;
+    }
+    b.sorted_ids = const_cast<int32_t *>(kin);
+    b.perm = const_cast<int32_t *>(vin);
+    hipLaunchKernelGGL(k_seg_heads, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, b.perm,
+                       n, b.tile_cnt, b.inv_perm);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, b.tile_cnt, (int)ntiles,
+                       b.hdr + HDR_NSEG);
+    hipLaunchKernelGGL(k_seg_write, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, n,
+                       b.tile_cnt, b.hdr + HDR_NSEG, b.uniq, b.seg_start);
+    return hipGetLastError();
+}
+
+hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
+                           int heavy_min_tokens, int light_tokens, int2 *light, int2 *heavy,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(k_worklist, dim3(blocks_for(n, 256)), dim3(256), 0, s, b.uniq, b.seg_start,
+                       b.counts, off, (int)vocab, heavy_min_tokens, light_tokens, light, heavy,
+                       b.hdr);
+    return hipGetLastError();
+}
+
+}  // namespace l3

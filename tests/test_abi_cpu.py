@@ -1,0 +1,77 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/l3.h
+declares, and rejects bad arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "l3.h")
+
+l3 = pytest.importorskip("static_token_routed_amd", reason="libl3.so not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z][\w \*]*?\b(l3_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for must in ("l3_plan", "l3_forward", "l3_prefetch", "l3_route", "l3_status",
+                 "l3_workspace_size", "l3_forward_staged"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(l3.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared()) == set(l3.EXPORTS)
+
+
+def test_strerror_texts():
+    for c in range(-7, 1):
+        assert l3.l3_strerror(c)
+    assert "unknown" in l3.l3_strerror(-99)
+
+
+def _plan(off, v, k, dims=(64, 64, 64, 64), dtype="bf16", eps=1e-5):
+    return l3.l3_plan(np.asarray(off, np.int64), len(off) - 1, v, k, *dims, dtype, eps)
+
+
+@pytest.mark.parametrize("off,v,k,code", [
+    ([0, 2, 2, 5], 5, 4, l3.L3_ERR_BAD_OFFSETS),    # d_t = 0
+    ([0, 2, 7, 9], 9, 4, l3.L3_ERR_BAD_OFFSETS),    # d_t > k
+    ([1, 2, 3, 5], 5, 4, l3.L3_ERR_BAD_OFFSETS),    # off[0] != 0
+    ([0, 2, 3, 5], 6, 4, l3.L3_ERR_BAD_OFFSETS),    # off[vocab] != v
+    ([0, 2, 3, 5], 5, 0, l3.L3_ERR_INVALID_ARG),    # k < 1
+])
+def test_plan_rejects_bad_offsets(off, v, k, code):
+    with pytest.raises(l3.L3Error) as e:
+        _plan(off, v, k)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("dims,dtype,code", [
+    ((100, 64, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),   # d_in not a multiple of 64
+    ((64, 96, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),    # d_emb not a supported width
+    ((8192, 64, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),  # d_in above 4096
+    ((64, 64, 64, -1), "bf16", l3.L3_ERR_INVALID_ARG),
+])
+def test_plan_rejects_bad_dims(dims, dtype, code):
+    with pytest.raises(l3.L3Error) as e:
+        _plan([0, 2, 3, 5], 5, 4, dims, dtype)
+    assert e.value.code == code
+
+
+def test_null_and_size_checks():
+    assert l3._lib.l3_plan(None, 3, 5, 4, None, None) == l3.L3_ERR_INVALID_ARG
+    assert l3._lib.l3_forward(None, None, None, 1, *([None] * 8), 0, None) == l3.L3_ERR_INVALID_ARG
+    assert l3._lib.l3_workspace_size(None, 10) == 0
+    assert l3._lib.l3_plan_destroy(None) == l3.L3_OK
+    assert l3._lib.l3_staging_destroy(None) == l3.L3_OK
+    assert l3._lib.l3_gemm_bf16(None, None, None, 1, 64, 64, None) == l3.L3_ERR_INVALID_ARG
