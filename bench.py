@@ -1,0 +1,210 @@
+"""Benchmark of the L^3 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload paper_bf16]
+
+One step = one l3_forward over the whole batch (route, gather-attention, W_up,
+W_mix) with every input already resident in HBM.  Prints one JSON line:
+tokens/s over K timed steps, the roofline of the dominant kernel (algorithmic
+bytes or FLOPs per launch over its HIP-event duration, measured inside the
+library on the launch stream), all stage rooflines, and the fp64 oracle timed
+on a bounded token sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16 MFMA
+STAGES = ["route", "gather_attention", "w_up_gemm", "w_mix_gemm"]
+KERNEL_SOURCES = {"gather_attention": "attn.hip", "w_up_gemm": "gemm.hip",
+                  "w_mix_gemm": "gemm.hip", "route": "route.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="paper_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the oracle timing on the host")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    return ap.parse_args()
+
+
+def src_hash(name: str) -> str:
+    p = os.path.join(ROOT, "static_token_routed_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"{stage}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != src_hash(KERNEL_SOURCES[stage]):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import static_token_routed_amd as l3
+
+    cfg = synth.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    off = synth.offsets(cfg)
+    ids = synth.token_ids(cfg)
+    x, WK, WV = synth.hidden(cfg), synth.table(cfg, "W_K"), synth.table(cfg, "W_V")
+    Wup, Wmix = synth.dense(cfg, "W_up"), synth.dense(cfg, "W_mix")
+    g, b = synth.ln_params(cfg)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    dx, dWK, dWV, dWup, dWmix = dev(x), dev(WK), dev(WV), dev(Wup), dev(Wmix)
+    dids = torch.from_numpy(ids).cuda()
+    dg, db = torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda()
+    print(f"[bench] {cfg.name}: inputs generated and uploaded in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    plan = l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16", cfg.ln_eps)
+    n = cfg.n
+    out = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+    ws = plan.workspace(n)
+
+    def step():
+        l3.l3_forward(plan.handle, dx, dids, n, dWK, dWV, dWup, dg, db, dWmix, out, ws, ws.numel())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert plan.status() == l3.L3_OK
+
+    l3.l3_profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stage_ms, launches = l3.l3_profile_read(len(STAGES))
+    l3.l3_profile_enable(False)
+    print(f"[bench] {args.steps} steps in {elapsed:.4f}s", file=sys.stderr, flush=True)
+
+    # algorithmic work per launch
+    u = np.unique(ids)
+    d = off[u + 1] - off[u]
+    R = int(d.sum())
+    kv_bytes = R * (cfg.d_in + cfg.d_emb) * 2
+    up_flops = 2.0 * n * cfg.d_up * cfg.d_emb
+    mix_flops = 2.0 * n * cfg.d_out * (cfg.d_up + cfg.d_in)
+    avg = {s: stage_ms[i] / max(1, launches[i]) for i, s in enumerate(STAGES)}
+    kernels = {
+        "gather_attention": {"bound": "hbm", "achieved": kv_bytes / (avg["gather_attention"] * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "work_per_launch": f"{kv_bytes} B of distinct K/V rows ({R} rows x "
+                                                f"{(cfg.d_in + cfg.d_emb) * 2} B)"},
+        "w_up_gemm": {"bound": "mfma", "achieved": up_flops / (avg["w_up_gemm"] * 1e-3) / 1e12,
+                      "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                      "work_per_launch": f"{up_flops:.4g} FLOP"},
+        "w_mix_gemm": {"bound": "mfma", "achieved": mix_flops / (avg["w_mix_gemm"] * 1e-3) / 1e12,
+                       "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                       "work_per_launch": f"{mix_flops:.4g} FLOP"},
+    }
+    for k_, v_ in kernels.items():
+        v_["frac"] = v_["achieved"] / v_["peak"]
+        v_["ms"] = avg[k_]
+        v_["traffic"] = traffic_from_profiles(k_, cfg.name)
+    dominant = max(kernels, key=lambda s: avg[s])
+    roof = {k_: kernels[dominant][k_] for k_ in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dominant
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, args.cpu_seconds)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    line = {
+        "metric": "L3 fwd tokens/s; K/V gather GB/s vs HBM peak; MFMA util (v=710K, d_in=2048)",
+        "value": n * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Zipf token IDs, Zipf-shaped allocation, N(0, 1/sqrt(fan_in)) weights)",
+        "config": {"workload": f"{cfg.name}: vocab {cfg.vocab}, v {cfg.v}, k {cfg.k}, d_in {cfg.d_in}, "
+                               f"d_emb {cfg.d_emb}, d_up {cfg.d_up}, d_out {cfg.d_out}, "
+                               f"{n} tokens, token IDs Zipf({cfg.ids_s})",
+                   "global_batch": n, "distinct_ids": int(len(u)), "distinct_rows": R},
+        "roofline": roof,
+        "kernels": kernels,
+        "stage_ms": {s: avg[s] for s in STAGES},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
+def cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, seconds):
+    """The fp64 oracle as it stands, on a seeded sample of the batch's tokens,
+    grown until about `seconds` of wall time; tokens/s over the timed chunks."""
+    import oracle
+
+    f32 = lambda a: synth_f32(a)
+    nt = max(1, min(16, len(os.sched_getaffinity(0))))
+    rng = np.random.default_rng(123)
+    order = rng.permutation(len(ids))
+    Wup64, Wmix64 = f32(Wup).astype(np.float64), f32(Wmix).astype(np.float64)
+    done, spent, chunk = 0, 0.0, 64
+    while spent < seconds and done < len(ids):
+        rows = order[done:done + chunk]
+        u, inv = np.unique(ids[rows], return_inverse=True)
+        dd = off[u + 1] - off[u]
+        coff = np.concatenate([[0], np.cumsum(dd)]).astype(np.int64)
+        sel = np.concatenate([np.arange(off[t], off[t + 1]) for t in u])
+        xs, wk, wv = f32(x[rows]), f32(WK[sel]), f32(WV[sel])
+        t = time.perf_counter()
+        oracle.forward(coff, cfg.k, xs, inv.astype(np.int32), wk, wv, Wup64, g, b, Wmix64,
+                       eps=cfg.ln_eps, nthreads=nt)
+        spent += time.perf_counter() - t
+        done += len(rows)
+        chunk = min(chunk * 2, 1024)
+    return {"value": done / spent, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"{done} tokens drawn (seeded) from the {cfg.name} batch, tables cut to "
+                      f"their rows; {spent:.1f}s of oracle time on {nt} threads"}
+
+
+def synth_f32(a):
+    import synth
+    return synth.as_f32(a, "bf16")
+
+
+if __name__ == "__main__":
+    main()
