@@ -13,23 +13,16 @@
 // d_t rows is an online (running max / running sum) fp32 softmax, so any d_t
 // streams through registers.  The result row goes to the token's original
 // batch position, which undoes the sort in the store.
+#include "cdna4.h"
 #include "l3_internal.h"
 
 namespace l3 {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ inline uint32_t f2bf(float f) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
-}
-__device__ inline uint32_t pack2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
 
 __device__ inline float wave_sum(float v) {
 #pragma unroll
@@ -273,6 +266,269 @@ __global__ __launch_bounds__(256) void k_attn_f32(F32Args a) {
     }
 }
 
+// ---------------------------------------------------------------- MFMA path
+//
+// Blocks with many tokens, or with many rows (d_t), run on the matrix cores.
+// One workgroup takes one ID and up to 64 of its tokens; wavefront w owns tokens
+// [16w, 16w + 16).
+//   scores  S^T (d_t x 16 tokens) = K_t x^T with v_mfma_f32_16x16x32_bf16.  K
+//           tiles (128 rows x 64 columns) and the gathered x tiles (64 tokens x
+//           64 columns) stream through a 3-stage LDS ring filled by asynchronous
+//           global->LDS copies; all d_t <= 512 scores stay in the accumulators,
+//           so the softmax is exact (one max, one sum) and no accumulator is
+//           rescaled.
+//   values  O^T (d_emb x 16 tokens) = V_t^T P^T, the same MFMA, over 32-row
+//           stages of V copied row-major into the ring and read transposed with
+//           ds_read_b64_tr_b16.
+// The MFMA reduction index k maps to rows as k = 8*(lane/16) + j  <->  row
+// 4*(lane/16) + j for j < 4, 16 + 4*(lane/16) + (j - 4) for j >= 4: exactly the
+// rows whose scores that lane holds in two consecutive 16-row accumulators, so
+// P never moves between lanes.  Work items of one ID are consecutive in the
+// list; each XCD takes a contiguous eighth of the list, so the tiles of one ID
+// mostly share that XCD's L2.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+struct HeavyArgs {
+    const uint16_t *x, *WK, *WV;
+    const int64_t *off;
+    const int32_t *uniq, *seg_start, *perm, *hdr;
+    const int2 *items;
+    int64_t d_in;
+    uint16_t *o;
+};
+
+constexpr int QK_RB = 128;                          // K rows per scores stage
+constexpr int QK_KC = 64;                           // d_in columns per scores stage
+constexpr int QK_NS = 4;                            // ring depth
+constexpr int QK_KBYTES = QK_RB * QK_KC * 2;        // 16 KB
+constexpr int QK_XBYTES = kHeavyTile * QK_KC * 2;   // 8 KB
+constexpr int QK_STAGE = QK_KBYTES + QK_XBYTES;
+constexpr int RING_BYTES = QK_NS * QK_STAGE;        // 96 KB
+constexpr int QK_LOADS = (QK_KBYTES + QK_XBYTES) / 1024 / 4;  // copies per wave and stage (6)
+constexpr int PV_ROWS = 32;
+
+template <int N>
+__device__ inline void wait_upto(int later_stages_issued) {
+    // wait until at most N * later_stages_issued copies of this wave are in flight
+    if (later_stages_issued >= 3) wait_vmcnt<3 * N>();
+    else if (later_stages_issued == 2) wait_vmcnt<2 * N>();
+    else if (later_stages_issued == 1) wait_vmcnt<N>();
+    else wait_vmcnt<0>();
+}
+
+// One work item with NRB 128-row blocks of K_t (d_t <= 128 * NRB).  Every score and
+// value MFMA of the item runs unconditionally: rows past d_t are copies of row
+// d_t - 1 whose scores are masked to -inf, so they weigh nothing.
+template <int VEB, int NRB>
+__device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *ring, uint32_t ring0,
+                                          int sb, int tq, int ntok, int64_t r0, int d) {
+    constexpr int DE = VEB * 16;
+    constexpr int NPASS = VEB > 16 ? 2 : 1;                  // values passes over halves of d_emb
+    constexpr int VEBH = VEB / NPASS;
+    constexpr int DEH = VEBH * 16;                           // d_emb columns per pass
+    constexpr int CPR = DEH / 8;                             // 16-byte chunks per (half) V row
+    constexpr int V_STAGE = PV_ROWS * DEH * 2;               // bytes per values stage
+    constexpr int PV_NS = RING_BYTES / V_STAGE >= 4 ? 4 : RING_BYTES / V_STAGE;  // values ring depth
+    constexpr int V_LOADS = V_STAGE / 1024 / 4;              // copies per wave and values stage
+    constexpr int RPC = 1024 / (DEH * 2);                    // V rows per 1 KB copy
+    constexpr int NB = 8 * NRB;                              // 16-row score blocks
+    constexpr int NPV = 4 * NRB;                             // 32-row values stages
+    static_assert(V_LOADS >= 1 && PV_NS * V_STAGE <= RING_BYTES, "values stage");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int l16 = lane & 15, kg = lane >> 4, cph = lane & 7;
+    const int64_t d_in = a.d_in;
+    const int nkc = (int)(d_in / QK_KC);
+    const int nqk = nkc * NRB;
+    const bool active = 16 * w < ntok;
+
+    // x rows (tokens) this lane copies: tile rows 8 * (2w + i) + lane / 8
+    int64_t xoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tr = 8 * (2 * w + i) + (lane >> 3);
+        xoff[i] = (int64_t)a.perm[sb + tq + min(tr, ntok - 1)] * d_in;
+    }
+    auto issue_qk = [&](int s) {
+        const int c = s / NRB, rb = s - c * NRB;
+        const uint32_t base = ring0 + (uint32_t)((s % QK_NS) * QK_STAGE);
+        const int64_t col = (int64_t)c * QK_KC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * w + i;
+            const int row = 8 * q + (lane >> 3);
+            const int64_t grow = r0 + min(rb * QK_RB + row, d - 1);
+            async_ld16(a.WK + grow * d_in + col + (cph ^ (row & 7)) * 8, base + q * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 2 * w + i;
+            const int row = 8 * q + (lane >> 3);
+            async_ld16(a.x + xoff[i] + col + (cph ^ (row & 7)) * 8, base + QK_KBYTES + q * 1024);
+        }
+    };
+
+    f32x4_t Sc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) Sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < QK_NS - 1 && i < nqk; ++i) issue_qk(i);
+    for (int c = 0; c < nkc; ++c) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int s = c * NRB + rb;
+            wait_upto<QK_LOADS>(min(QK_NS - 2, nqk - 1 - s));
+            lds_barrier();
+            if (s + QK_NS - 1 < nqk) issue_qk(s + QK_NS - 1);
+            if (active) {
+                const uint16_t *kt = reinterpret_cast<const uint16_t *>(ring + (s % QK_NS) * QK_STAGE);
+                const uint16_t *xt = kt + QK_KBYTES / 2;
+#pragma unroll
+                for (int kk = 0; kk < QK_KC / 32; ++kk) {
+                    const int ch = kk * 4 + kg;
+                    const int xr = 16 * w + l16;
+                    const bf16x8_t B = *reinterpret_cast<const bf16x8_t *>(&xt[xr * QK_KC + ((ch ^ (xr & 7)) * 8)]);
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) {
+                        const int kr = 16 * b + l16;
+                        const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(&kt[kr * QK_KC + ((ch ^ (kr & 7)) * 8)]);
+                        Sc[rb * 8 + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, Sc[rb * 8 + b], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // exact softmax over the d_t rows (lane: token l16, rows 16b + 4kg + i)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = (16 * b + 4 * kg + i < d) ? Sc[b][i] : -INFINITY;
+            Sc[b][i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float lsum = 0.f;
+    uint4 Pk[NPV];
+#pragma unroll
+    for (int g = 0; g < NPV; ++g) {
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = __expf(Sc[2 * g][i] - mx);
+            pr[4 + i] = __expf(Sc[2 * g + 1][i] - mx);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lsum += pr[i];
+        Pk[g] = make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]), pack2(pr[6], pr[7]));
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    const float inv = 1.f / lsum;
+    const int qi = 16 * w + l16;
+    const int tok = qi < ntok ? a.perm[sb + tq + qi] : 0;
+
+    // values stages: rows [32g, 32g + 32) of V_t and columns [hp*DEH, (hp+1)*DEH),
+    // copied row-major; chunk p of a row holds global chunk p ^ swz(row) so the
+    // transposed reads spread over the banks
+    auto swz = [](int row) { return (2 * (row & 7)) & (CPR - 1); };
+#pragma unroll
+    for (int hp = 0; hp < NPASS; ++hp) {
+        auto issue_pv = [&](int g) {
+            const uint32_t base = ring0 + (uint32_t)((g % PV_NS) * V_STAGE);
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int q = V_LOADS * w + i;
+                const int row = q * RPC + lane / CPR;
+                const int64_t grow = r0 + min(PV_ROWS * g + row, d - 1);
+                async_ld16(a.WV + grow * DE + hp * DEH + ((lane % CPR) ^ swz(row)) * 8, base + q * 1024);
+            }
+        };
+        lds_barrier();  // every wave is done with the previous stages in the ring
+#pragma unroll
+        for (int i = 0; i < PV_NS - 1 && i < NPV; ++i) issue_pv(i);
+        f32x4_t O[VEBH];
+#pragma unroll
+        for (int e = 0; e < VEBH; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NPV; ++g) {
+            wait_upto<V_LOADS>(min(PV_NS - 2, NPV - 1 - g));
+            lds_barrier();
+            if (g + PV_NS - 1 < NPV) issue_pv(g + PV_NS - 1);
+            if (active) {
+                const uint16_t *vt = reinterpret_cast<const uint16_t *>(ring + (g % PV_NS) * V_STAGE);
+                const bf16x8_t P = __builtin_bit_cast(bf16x8_t, Pk[g]);
+                const int ra = 4 * kg + (l16 >> 2), rbw = ra + 16;
+#pragma unroll
+                for (int eb = 0; eb < VEBH; ++eb) {
+                    const int col = eb * 16 + 4 * (l16 & 3);
+                    const int chk = col >> 3, half = col & 7;
+                    const uint16_t *pa = vt + ra * DEH + ((chk ^ swz(ra)) * 8) + half;
+                    const uint16_t *pb = vt + rbw * DEH + ((chk ^ swz(rbw)) * 8) + half;
+                    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t *)(pa));
+                    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t *)(pb));
+                    const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+                    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
+                    O[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P, O[eb], 0, 0, 0);
+                }
+            }
+        }
+        if (active && qi < ntok) {
+            uint16_t *orow = a.o + (int64_t)tok * DE + hp * DEH + 4 * kg;
+#pragma unroll
+            for (int eb = 0; eb < VEBH; ++eb) {
+                const uint2 u = make_uint2(pack2(O[eb][0] * inv, O[eb][1] * inv),
+                                           pack2(O[eb][2] * inv, O[eb][3] * inv));
+                *reinterpret_cast<uint2 *>(orow + eb * 16) = u;
+            }
+        }
+    }
+    lds_barrier();  // the next item's copies reuse the ring
+}
+
+template <int VEB>  // d_emb / 16
+__global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[RING_BYTES];
+    const uint32_t ring0 = lds_addr(ring);
+    const int nitems = a.hdr[HDR_NHEAVY];
+    // XCD-aware order: XCD x (= blockIdx % 8) walks the x-th eighth of the list
+    const int nbx = gridDim.x >> 3, lb = blockIdx.x >> 3;
+    const int per = (nitems + 7) >> 3;
+    const int ibeg = (blockIdx.x & 7) * per, iend = min(nitems, ibeg + per);
+    for (int it = ibeg + lb; it < iend; it += nbx) {
+        const int2 item = a.items[it];
+        const int j = item.x, tq = item.y;
+        const int sb = a.seg_start[j];
+        const int S = a.seg_start[j + 1] - sb;
+        const int ntok = min(kHeavyTile, S - tq);
+        const int id = a.uniq[j];
+        const int64_t r0 = a.off[id];
+        const int d = (int)(a.off[id + 1] - r0);
+        switch ((d + QK_RB - 1) / QK_RB) {
+            case 1: mfma_item<VEB, 1>(a, ring, ring0, sb, tq, ntok, r0, d); break;
+            case 2: mfma_item<VEB, 2>(a, ring, ring0, sb, tq, ntok, r0, d); break;
+            case 3: mfma_item<VEB, 3>(a, ring, ring0, sb, tq, ntok, r0, d); break;
+            default: mfma_item<VEB, 4>(a, ring, ring0, sb, tq, ntok, r0, d); break;
+        }
+    }
+}
+
+constexpr int kHeavyBlocks = 256;   // one per CU, a multiple of 8 (XCD order)
+
+hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
+    switch (d_emb) {
+        case 64: hipLaunchKernelGGL((k_attn_mfma<4>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 128: hipLaunchKernelGGL((k_attn_mfma<8>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 256: hipLaunchKernelGGL((k_attn_mfma<16>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 512: hipLaunchKernelGGL((k_attn_mfma<32>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 constexpr int kAttnBlocks = 2048;
 
 template <int NCI>
@@ -296,10 +552,11 @@ int attn_light_tokens(int64_t d_in, int dtype) {
     return light_tokens_for<8>();
 }
 
-int attn_heavy_min_tokens(int64_t, int64_t, int, int32_t) { return INT32_MAX; }
+int attn_heavy_min_tokens(int64_t, int64_t, int dtype, int32_t) {
+    return dtype == L3_BF16 ? kHeavyMinTokens : INT32_MAX;
+}
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t s) {
-    (void)use_heavy;
     if (dtype == L3_F32) {
         F32Args fa{(const float *)a.x, (const float *)a.WK, (const float *)a.WV, a.off, a.uniq,
                    a.seg_start, a.perm, a.hdr, a.light, a.d_in, a.d_emb, (int32_t)a.vocab,
@@ -310,6 +567,12 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t 
     LightArgs la{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
                  a.uniq, a.seg_start, a.perm, a.hdr, a.light, a.d_in, a.d_emb, (int32_t)a.vocab,
                  (uint16_t *)a.o};
+    if (use_heavy) {
+        HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
+                     a.uniq, a.seg_start, a.perm, a.hdr, a.heavy, a.d_in, (uint16_t *)a.o};
+        const hipError_t e = launch_heavy(ha, a.d_emb, s);
+        if (e != hipSuccess) return e;
+    }
     const int64_t nci = (a.d_in + 511) / 512;
     if (nci <= 1) return launch_light_nci<1>(la, a.d_emb, s);
     if (nci <= 2) return launch_light_nci<2>(la, a.d_emb, s);

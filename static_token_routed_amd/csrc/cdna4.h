@@ -1,0 +1,56 @@
+// Small gfx950 (CDNA4) device helpers shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace l3 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ inline uint32_t f2bf(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ inline uint32_t pack2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// not for its outstanding global loads (HIP's __syncthreads also drains those,
+// which would cap every prefetch at one barrier).  The empty asm statements
+// keep the compiler from moving memory operations across it.
+__device__ inline void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// LDS byte offset of a __shared__ object.
+template <typename T>
+__device__ inline uint32_t lds_addr(T *p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void *)p);
+}
+
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane l's
+// 16 bytes land at lds_base + 16 * l; lds_base must be uniform across the wave.
+// Completion is tracked by vmcnt only; callers wait with wait_vmcnt<N>() before
+// a barrier.  Written as asm so the compiler does not treat later LDS reads as
+// depending on every copy still in flight.
+__device__ inline void async_ld16(const void *gptr, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(m0v), "v"(gptr)
+                     : "memory");
+}
+
+// s_waitcnt vmcnt(N) (N <= 63), other counters untouched.
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+}  // namespace l3

@@ -7,58 +7,50 @@
 //
 // Kernel shape (gfx950): 256 threads = 4 wavefronts in 2 x 2, each owning a
 // 128 x 128 block of a 256 x 256 output tile as 4 x 4 v_mfma_f32_32x32x16_bf16
-// accumulators (256 fp32 per lane).  K advances 64 at a time through two LDS
-// stages (A and B tiles, 32 KB each, double-buffered: 128 KB); each 16-byte
-// chunk of a 128-byte LDS row is XOR-swizzled by the row index so the
-// fragment reads of 32 consecutive rows spread over the banks.  The MFMA takes
-// the B tile as its first operand, so each lane ends up holding 4 consecutive
-// output columns of one row: the epilogue stores 8-byte row segments directly.
+// accumulators (256 fp32 per lane).  K advances 64 at a time.  Both operand
+// tiles (256 x 64 bf16 each) go global -> LDS by asynchronous 16-byte copies
+// (no register staging) into a double buffer: the copies of stage s+1 are in
+// flight while stage s is multiplied, and barriers wait for LDS traffic only.
+// Each 16-byte chunk of a 128-byte LDS row is XOR-swizzled by the row index
+// (the swizzle is applied to the source address, since a copy lands at a fixed
+// lane-linear LDS slot) so fragment reads of 32 consecutive rows spread over the
+// banks.  The MFMA takes the B tile as its first operand, so each lane holds 4
+// consecutive output columns of one row: the epilogue stores 8-byte segments.
 // Tiles are numbered so that the workgroups the dispatcher sends to one XCD
 // (workgroup id mod 8) form a contiguous, grouped block of tiles, sharing A
 // rows and B columns in that XCD's L2.
 //
-// Fused work:
-//  * W_up epilogue: per output row and 128-column chunk, the mean and the sum
-//    of squared deviations (M2) of the bf16-rounded h values (LayerNorm
-//    partial statistics).
-//  * W_mix prologue: the A operand is built while staging: columns k < d_up
-//    are LN(h) = (h - mean) * rstd * gamma + beta, with mean and variance
-//    merged from the partials (Chan's pairwise update), columns k >= d_up are
-//    x -- the concat [LN(h) ; x] never exists in memory.
+// LayerNorm and the concat [LN(h) ; x] are fused into the W_mix operand path:
+// the A tiles of the first d_up columns are h, copied raw into LDS; each 8-value
+// A fragment read from LDS becomes (h - mean) * rstd * gamma + beta before it
+// enters the MFMA (mean and rstd per row, from the W_up epilogue's partial
+// statistics -- per row and 128-column chunk, the mean and the sum of squared
+// deviations of the stored bf16 values -- merged with Chan's pairwise update;
+// gamma and beta slices travel with each stage as one more async copy).  The
+// remaining columns are x.  The concatenated operand never exists in memory.
+#include <type_traits>
+
+#include "cdna4.h"
 #include "l3_internal.h"
 
 namespace l3 {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int GROUP_M = 8;
 
 struct GemmP {
-    const uint16_t *A;   // M x lda, columns [0, K1)
-    const uint16_t *A2;  // M x lda2, supplies columns [K1, K) (may be null if K1 == K)
-    const uint16_t *B;   // N x K
-    uint16_t *C;         // M x N
-    int64_t lda, lda2, K1;
+    const uint16_t *A, *A2;  // A columns [0, K1) from A (row stride lda), [K1, K) from A2 (lda2)
+    const uint16_t *B;       // N x K, row stride ldb
+    uint16_t *C;             // M x N, row stride N
+    int64_t lda, lda2, ldb, K1;
     int64_t M, N, K;
-    // LayerNorm input statistics (W_mix prologue)
-    const float *lnp;  // [M x npart x 2]
-    const float *gamma, *beta;
-    float eps;
-    int npart;
-    int64_t ln_width;  // number of normalised features (= K1)
-    // LayerNorm output partials (W_up epilogue)
-    float *ln_out;  // [M x npart_out x 2]
+    const float *row_stats;  // [M x 2] (mean, rstd) of the A rows in [0, K1)  (LN_IN)
+    const float *gamma, *beta;  // [K1]                                         (LN_IN)
+    float *ln_out;           // [M x npart_out x 2] partial statistics of the stored rows
     int npart_out;
     int tiles_m, tiles_n;
 };
-
-__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ inline uint32_t f2bf(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
-__device__ inline uint32_t pack2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
 
 // tile id -> (tm, tn): XCD-contiguous, then grouped by GROUP_M tile rows.
 __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
@@ -77,9 +69,9 @@ __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
 
 template <bool LN_IN, bool LN_OUT>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
-    __shared__ float s_mean[LN_IN ? BM : 1], s_rstd[LN_IN ? BM : 1];
+    __shared__ __attribute__((aligned(1024))) uint16_t As[2][BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[2][BN * BK];
+    __shared__ __attribute__((aligned(16))) float GB[2][2 * BK];  // gamma, beta of the stage
 
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -87,79 +79,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int wm = w >> 1, wn = w & 1;
 
-    if constexpr (LN_IN) {
-        const int64_t row = m0 + t;
-        float mean = 0.f, rstd = 0.f;
-        if (row < p.M) {
-            const float *pp = p.lnp + row * p.npart * 2;
-            float cnt = 0.f, mu = 0.f, m2 = 0.f;
-            for (int i = 0; i < p.npart; ++i) {
-                const float nb = (float)min<int64_t>(kLnPart, p.ln_width - (int64_t)i * kLnPart);
-                const float mb = pp[2 * i], m2b = pp[2 * i + 1];
-                const float nn = cnt + nb;
-                const float delta = mb - mu;
-                mu += delta * (nb / nn);
-                m2 += m2b + delta * delta * (cnt * nb / nn);
-                cnt = nn;
-            }
-            mean = mu;
-            rstd = 1.f / sqrtf(m2 / cnt + p.eps);
-        }
-        s_mean[t] = mean;
-        s_rstd[t] = rstd;
-        __syncthreads();
-    }
-
-    // loader mapping: 16-byte chunk c of rows rb + 32 i
-    const int lc = t & 7, lr = t >> 3;
-    uint4 ra[8], rb[8];
-
-    auto load_stage = [&](int64_t k0) {
+    // Copy mapping: wave w issues 8 copies per operand and stage; copy q covers tile
+    // rows [8q, 8q + 8) (1 KB of LDS).  Lane l fills physical chunk l % 8 of row
+    // 8q + l / 8 with global chunk (l % 8) ^ (row & 7).  Rows past M (N) are clamped:
+    // they only feed accumulators that are never stored.
+    const int crow = lane >> 3, cphys = lane & 7;
+    const uint32_t a_lds0 = lds_addr(&As[0][0]), b_lds0 = lds_addr(&Bs[0][0]);
+    const uint32_t gb_lds0 = lds_addr(&GB[0][0]);
+    auto issue = [&](int64_t k0, int buf) {
         const bool first = k0 < p.K1;
+        const uint16_t *abase = first ? p.A + k0 : p.A2 + (k0 - p.K1);
+        const int64_t lda = first ? p.lda : p.lda2;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int64_t row = m0 + lr + 32 * i;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row < p.M) {
-                const uint16_t *src = first ? p.A + row * p.lda + k0 + lc * 8
-                                            : p.A2 + row * p.lda2 + (k0 - p.K1) + lc * 8;
-                v = *reinterpret_cast<const uint4 *>(src);
-            }
-            ra[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t col = n0 + lr + 32 * i;
-            rb[i] = col < p.N ? *reinterpret_cast<const uint4 *>(p.B + col * p.K + k0 + lc * 8)
-                              : make_uint4(0, 0, 0, 0);
+            const int q = w * 8 + i;
+            const int row = q * 8 + crow;
+            const int gch = cphys ^ (row & 7);
+            const int64_t ar = min<int64_t>(m0 + row, p.M - 1);
+            const int64_t br = min<int64_t>(n0 + row, p.N - 1);
+            const uint32_t off = (uint32_t)(buf * BM * BK * 2 + q * 1024);
+            async_ld16(abase + ar * lda + gch * 8, a_lds0 + off);
+            async_ld16(p.B + br * p.ldb + k0 + gch * 8, b_lds0 + off);
         }
         if constexpr (LN_IN) {
-            if (first) {
-                const int64_t k = k0 + lc * 8;
-                const float4 g0 = *reinterpret_cast<const float4 *>(p.gamma + k);
-                const float4 g1 = *reinterpret_cast<const float4 *>(p.gamma + k + 4);
-                const float4 b0 = *reinterpret_cast<const float4 *>(p.beta + k);
-                const float4 b1 = *reinterpret_cast<const float4 *>(p.beta + k + 4);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float mu = s_mean[lr + 32 * i], rs = s_rstd[lr + 32 * i];
-                    uint4 v = ra[i];
-                    v.x = pack2((bf_lo(v.x) - mu) * rs * g0.x + b0.x, (bf_hi(v.x) - mu) * rs * g0.y + b0.y);
-                    v.y = pack2((bf_lo(v.y) - mu) * rs * g0.z + b0.z, (bf_hi(v.y) - mu) * rs * g0.w + b0.w);
-                    v.z = pack2((bf_lo(v.z) - mu) * rs * g1.x + b1.x, (bf_hi(v.z) - mu) * rs * g1.y + b1.y);
-                    v.w = pack2((bf_lo(v.w) - mu) * rs * g1.z + b1.z, (bf_hi(v.w) - mu) * rs * g1.w + b1.w);
-                    ra[i] = v;
-                }
+            // gamma[k0, k0+64) and beta[k0, k0+64): 32 lanes x 16 B of wave 0
+            if (first && w == 0) {
+                const float *src = lane < 16 ? p.gamma + k0 + lane * 4 : p.beta + k0 + (lane - 16) * 4;
+                if (lane < 32) async_ld16(src, gb_lds0 + buf * 2 * BK * 4);
             }
-        }
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = lr + 32 * i;
-            const int pc = lc ^ (r & 7);
-            *reinterpret_cast<uint4 *>(&As[buf][r * BK + pc * 8]) = ra[i];
-            *reinterpret_cast<uint4 *>(&Bs[buf][r * BK + pc * 8]) = rb[i];
         }
     };
 
@@ -171,13 +118,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nst = (int)(p.K / BK);
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nst) load_stage((int64_t)(st + 1) * BK);
+    // LayerNorm statistics of the lane's 4 A rows (LN_IN)
+    float mu[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (LN_IN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = min<int64_t>(m0 + wm * 128 + i * 32 + (lane & 31), p.M - 1);
+            mu[i] = p.row_stats[2 * m];
+            rs[i] = p.row_stats[2 * m + 1];
+        }
+    }
+
+    auto compute = [&](int buf, auto ln_tag) {
+        constexpr bool LN = decltype(ln_tag)::value;
         const uint16_t *as = As[buf];
         const uint16_t *bs = Bs[buf];
 #pragma unroll
@@ -188,6 +141,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
             for (int i = 0; i < 4; ++i) {
                 const int r = wm * 128 + i * 32 + (lane & 31);
                 fa[i] = *reinterpret_cast<const bf16x8_t *>(&as[r * BK + ((ch ^ (r & 7)) * 8)]);
+            }
+            if constexpr (LN) {
+                // y = (h - mean) * rstd * gamma + beta on the lane's 8 columns
+                const float4 g0 = *reinterpret_cast<const float4 *>(&GB[buf][ch * 8]);
+                const float4 g1 = *reinterpret_cast<const float4 *>(&GB[buf][ch * 8 + 4]);
+                const float4 b0 = *reinterpret_cast<const float4 *>(&GB[buf][BK + ch * 8]);
+                const float4 b1 = *reinterpret_cast<const float4 *>(&GB[buf][BK + ch * 8 + 4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint4 u = __builtin_bit_cast(uint4, fa[i]);
+                    const float m_ = mu[i], r_ = rs[i];
+                    u.x = pack2((bf_lo(u.x) - m_) * r_ * g0.x + b0.x, (bf_hi(u.x) - m_) * r_ * g0.y + b0.y);
+                    u.y = pack2((bf_lo(u.y) - m_) * r_ * g0.z + b0.z, (bf_hi(u.y) - m_) * r_ * g0.w + b0.w);
+                    u.z = pack2((bf_lo(u.z) - m_) * r_ * g1.x + b1.x, (bf_hi(u.z) - m_) * r_ * g1.y + b1.y);
+                    u.w = pack2((bf_lo(u.w) - m_) * r_ * g1.z + b1.z, (bf_hi(u.w) - m_) * r_ * g1.w + b1.w);
+                    fa[i] = __builtin_bit_cast(bf16x8_t, u);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -200,8 +170,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
         }
-        if (st + 1 < nst) store_stage(buf ^ 1);
-        __syncthreads();
+    };
+    // one pipelined stage: wait for its copies, start the next stage's, multiply
+    const int nst = (int)(p.K / BK);
+    const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages whose A operand is normalised
+    issue(0, 0);
+    for (int st = 0; st < nst1; ++st) {
+        wait_vmcnt<0>();  // this stage's copies (the only ones in flight) have landed
+        lds_barrier();    // ... for every wave; and everyone is done with the other buffer
+        if (st + 1 < nst) issue((int64_t)(st + 1) * BK, (st + 1) & 1);
+        compute(st & 1, std::true_type{});
+    }
+    for (int st = nst1; st < nst; ++st) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (st + 1 < nst) issue((int64_t)(st + 1) * BK, (st + 1) & 1);
+        compute(st & 1, std::false_type{});
     }
 
     // Epilogue.  acc[i][j] element e of lane l: output row m = m0 + wm*128 + i*32 + (l&31),
@@ -216,8 +200,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t n = nbase + j * 32 + 8 * g + 4 * (lane >> 5);
-                const uint32_t lo = pack2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                const uint32_t hi = pack2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                const uint32_t lo = pack2(v0, v1), hi = pack2(v2, v3);
                 if (m < p.M && n < p.N)
                     *reinterpret_cast<uint2 *>(p.C + m * p.N + n) = make_uint2(lo, hi);
                 if constexpr (LN_OUT) {
@@ -256,6 +241,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
             }
         }
     }
+}
+
+// Row statistics of h from the W_up epilogue's partials: one thread per row,
+// Chan's pairwise merge of (count, mean, M2), then rstd = 1 / sqrt(M2/width + eps).
+__global__ __launch_bounds__(256) void k_ln_finalize(const float *__restrict__ lnp, int64_t M,
+                                                     int npart, int64_t width, float eps,
+                                                     float *__restrict__ stats) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= M) return;
+    const float *pp = lnp + row * npart * 2;
+    float cnt = 0.f, mu = 0.f, m2 = 0.f;
+    for (int i = 0; i < npart; ++i) {
+        const float nb = (float)min<int64_t>(kLnPart, width - (int64_t)i * kLnPart);
+        const float mb = pp[2 * i], m2b = pp[2 * i + 1];
+        const float nn = cnt + nb;
+        const float delta = mb - mu;
+        mu += delta * (nb / nn);
+        m2 += m2b + delta * delta * (cnt * nb / nn);
+        cnt = nn;
+    }
+    stats[2 * row] = mu;
+    stats[2 * row + 1] = 1.f / sqrtf(m2 / cnt + eps);
 }
 
 // ---------------------------------------------------------------- fp32 (any dims)
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(256) void k_ln_stats_f32(const float *__restrict__ 
 
 GemmP make_plain(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N, int64_t K) {
     GemmP p{};
-    p.A = A; p.A2 = nullptr; p.B = B; p.C = C;
-    p.lda = K; p.lda2 = 0; p.K1 = K;
+    p.A = A; p.A2 = A; p.B = B; p.C = C;
+    p.lda = K; p.lda2 = K; p.ldb = K; p.K1 = K;
     p.M = M; p.N = N; p.K = K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
@@ -361,22 +368,27 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *lnp,
-                                const float *gamma, const float *beta, float eps,
-                                const uint16_t *W_mix, uint16_t *out, int64_t M, int64_t d_up,
-                                int64_t d_in, int64_t d_out, hipStream_t s) {
+hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float eps, float *stats,
+                              hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_ln_finalize, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, lnp, M,
+                       (int)((d_up + kLnPart - 1) / kLnPart), d_up, eps, stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
+                                const float *gamma, const float *beta, const uint16_t *W_mix,
+                                uint16_t *out, int64_t M, int64_t d_up, int64_t d_in, int64_t d_out,
+                                hipStream_t s) {
     if (M <= 0) return hipSuccess;
     GemmP p = make_plain(h, W_mix, out, M, d_out, d_up + d_in);
     p.lda = d_up;
     p.A2 = x;
     p.lda2 = d_in;
     p.K1 = d_up;
-    p.lnp = lnp;
+    p.row_stats = stats;
     p.gamma = gamma;
     p.beta = beta;
-    p.eps = eps;
-    p.npart = (int)((d_up + kLnPart - 1) / kLnPart);
-    p.ln_width = d_up;
     hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
     return hipGetLastError();
 }

@@ -144,6 +144,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         L3_HIP_TRY(launch_attn(a, D.dtype, 1, s));
     }
     if (D.dtype == L3_BF16) {
+        float *stats = ws_ptr<float>(ws, L.stats);
         {
             StageTimer tm(2, s);
             L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h, n,
@@ -151,9 +152,10 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         }
         {
             StageTimer tm(3, s);
-            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, lnp, gamma, beta,
-                                            D.eps, (const uint16_t *)W_mix, (uint16_t *)out, n,
-                                            D.d_up, D.d_in, D.d_out, s));
+            L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
+            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, stats, gamma, beta,
+                                            (const uint16_t *)W_mix, (uint16_t *)out, n, D.d_up, D.d_in,
+                                            D.d_out, s));
         }
     } else {
         {
@@ -205,6 +207,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.h = take((size_t)n * d.d_up * es);
     const int64_t np = (d.d_up + kLnPart - 1) / kLnPart;
     L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
+    L.stats = take((size_t)n * 2 * 4);
     L.total = off;
     return L;
 }

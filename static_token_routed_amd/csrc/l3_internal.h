@@ -21,6 +21,8 @@ constexpr int kRadix = 1 << kRadixBits;
 constexpr int kLnPart = 128;       // LayerNorm partial statistics cover 128 features
 constexpr int kHeavyMaxD = 512;    // MFMA gather-attention keeps all d_t <= 512 scores on chip
 constexpr int kHeavyTile = 64;     // tokens per MFMA gather-attention work item
+constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
+constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
 
 // Workspace header (int32 words), zeroed at the start of every call.
 enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_WORDS = 64 };
@@ -37,6 +39,7 @@ struct WsLayout {
     size_t inv_perm, uniq, counts, seg_start, light, heavy;
     size_t scores;  // fp32 path only: n x max_d
     size_t o, h, lnp;
+    size_t stats;  // LayerNorm row statistics (mean, rstd)
     size_t total;
     int64_t ntiles;
 };
@@ -83,12 +86,14 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t 
 // (ln_out [M x ceil(N/128) x 2] = per 128-column chunk (mean, M2)).
 hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N,
                             int64_t K, float *ln_out, hipStream_t s);
-// out = [LN(h) ; x] W_mix^T: columns k < d_up of the A operand are LN(h) built from
-// the partial statistics, the rest are x.
-hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *lnp,
-                                const float *gamma, const float *beta, float eps,
-                                const uint16_t *W_mix, uint16_t *out, int64_t M, int64_t d_up,
-                                int64_t d_in, int64_t d_out, hipStream_t s);
+// stats [M x 2] = (mean, 1/sqrt(var + eps)) per row from the W_up partials.
+hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float eps, float *stats,
+                              hipStream_t s);
+// out = W_mix [LN(h) ; x] with LN applied to the A fragments of the first d_up columns.
+hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
+                                const float *gamma, const float *beta, const uint16_t *W_mix,
+                                uint16_t *out, int64_t M, int64_t d_up, int64_t d_in, int64_t d_out,
+                                hipStream_t s);
 // fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
 // separate per-row statistics pass.
 hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,

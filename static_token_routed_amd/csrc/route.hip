@@ -240,7 +240,10 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
         counts[j] = S;
         const int t = uniq[j];
         const int d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
-        if (t < vocab && S >= heavy_min && d <= kHeavyMaxD)
+        // the MFMA path takes blocks with many tokens or many rows (long row chains
+        // stall the wavefront-per-item path), up to kHeavyMaxD rows
+        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows) &&
+            d <= kHeavyMaxD)
             nh = (S + kHeavyTile - 1) / kHeavyTile;
         else
             nl = (S + light_tok - 1) / light_tok;
