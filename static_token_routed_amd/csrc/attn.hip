@@ -292,28 +292,27 @@ struct HeavyArgs {
     const uint16_t *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
+    int32_t *queue;  // 8 per-XCD work counters (zeroed with the header)
     const int2 *items;
     int64_t d_in;
     uint16_t *o;
 };
 
-constexpr int QK_RB = 128;                          // K rows per scores stage
-constexpr int QK_KC = 64;                           // d_in columns per scores stage
-constexpr int QK_NS = 4;                            // ring depth
-constexpr int QK_KBYTES = QK_RB * QK_KC * 2;        // 16 KB
-constexpr int QK_XBYTES = kHeavyTile * QK_KC * 2;   // 8 KB
-constexpr int QK_STAGE = QK_KBYTES + QK_XBYTES;
-constexpr int RING_BYTES = QK_NS * QK_STAGE;        // 96 KB
-constexpr int QK_LOADS = (QK_KBYTES + QK_XBYTES) / 1024 / 4;  // copies per wave and stage (6)
-constexpr int PV_ROWS = 32;
+constexpr int QK_RB = 128;                           // K rows per row block
+constexpr int QK_KC = 64;                            // d_in columns per scores stage
+constexpr int QK_XBYTES = kHeavyTile * QK_KC * 2;    // gathered x tile per stage (8 KB)
+constexpr int RING_BYTES = 144 * 1024;
+constexpr int PV_ROWS = 64;                          // V rows per values stage
+constexpr int QCHUNK = 4;                            // items per round-robin chunk of the XCD queues
 
-template <int N>
-__device__ inline void wait_upto(int later_stages_issued) {
-    // wait until at most N * later_stages_issued copies of this wave are in flight
-    if (later_stages_issued >= 3) wait_vmcnt<3 * N>();
-    else if (later_stages_issued == 2) wait_vmcnt<2 * N>();
-    else if (later_stages_issued == 1) wait_vmcnt<N>();
-    else wait_vmcnt<0>();
+// wait until at most N * later copies of this wave are in flight (later <= MAXL)
+template <int N, int MAXL>
+__device__ inline void wait_upto(int later) {
+    if constexpr (MAXL >= 4) { if (later >= 4) { wait_vmcnt<4 * N>(); return; } }
+    if constexpr (MAXL >= 3) { if (later == 3) { wait_vmcnt<3 * N>(); return; } }
+    if constexpr (MAXL >= 2) { if (later == 2) { wait_vmcnt<2 * N>(); return; } }
+    if constexpr (MAXL >= 1) { if (later == 1) { wait_vmcnt<N>(); return; } }
+    wait_vmcnt<0>();
 }
 
 // One work item with NRB 128-row blocks of K_t (d_t <= 128 * NRB).  Every score and
@@ -327,18 +326,22 @@ __device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *rin
     constexpr int VEBH = VEB / NPASS;
     constexpr int DEH = VEBH * 16;                           // d_emb columns per pass
     constexpr int CPR = DEH / 8;                             // 16-byte chunks per (half) V row
+    constexpr int KBYTES = NRB * QK_RB * QK_KC * 2;          // K tile per scores stage
+    constexpr int QSTAGE = KBYTES + QK_XBYTES;
+    constexpr int QNS = RING_BYTES / QSTAGE >= 6 ? 6 : RING_BYTES / QSTAGE;  // scores ring depth
+    constexpr int QLOADS = QSTAGE / 1024 / 4;                // copies per wave and scores stage
+    constexpr int KCOPIES = KBYTES / 1024 / 4;               // ... of which K
     constexpr int V_STAGE = PV_ROWS * DEH * 2;               // bytes per values stage
-    constexpr int PV_NS = RING_BYTES / V_STAGE >= 4 ? 4 : RING_BYTES / V_STAGE;  // values ring depth
+    constexpr int VNS = RING_BYTES / V_STAGE >= 6 ? 6 : RING_BYTES / V_STAGE;  // values ring depth
     constexpr int V_LOADS = V_STAGE / 1024 / 4;              // copies per wave and values stage
     constexpr int RPC = 1024 / (DEH * 2);                    // V rows per 1 KB copy
     constexpr int NB = 8 * NRB;                              // 16-row score blocks
-    constexpr int NPV = 4 * NRB;                             // 32-row values stages
-    static_assert(V_LOADS >= 1 && PV_NS * V_STAGE <= RING_BYTES, "values stage");
+    constexpr int NPV = (QK_RB / PV_ROWS) * NRB;             // values stages
+    static_assert(QNS >= 2 && VNS >= 2 && V_LOADS >= 1, "ring");
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int l16 = lane & 15, kg = lane >> 4, cph = lane & 7;
     const int64_t d_in = a.d_in;
     const int nkc = (int)(d_in / QK_KC);
-    const int nqk = nkc * NRB;
     const bool active = 16 * w < ntok;
 
     // x rows (tokens) this lane copies: tile rows 8 * (2w + i) + lane / 8
@@ -348,50 +351,49 @@ __device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *rin
         const int tr = 8 * (2 * w + i) + (lane >> 3);
         xoff[i] = (int64_t)a.perm[sb + tq + min(tr, ntok - 1)] * d_in;
     }
-    auto issue_qk = [&](int s) {
-        const int c = s / NRB, rb = s - c * NRB;
-        const uint32_t base = ring0 + (uint32_t)((s % QK_NS) * QK_STAGE);
+    // stage c: K[all rows][64c, 64c + 64) and x[tokens][same columns]; copy q of
+    // the K tile covers tile rows [8q, 8q + 8)
+    auto issue_qk = [&](int c) {
+        const uint32_t base = ring0 + (uint32_t)((c % QNS) * QSTAGE);
         const int64_t col = (int64_t)c * QK_KC;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 4 * w + i;
+        for (int i = 0; i < KCOPIES; ++i) {
+            const int q = KCOPIES * w + i;
             const int row = 8 * q + (lane >> 3);
-            const int64_t grow = r0 + min(rb * QK_RB + row, d - 1);
+            const int64_t grow = r0 + min(row, d - 1);
             async_ld16(a.WK + grow * d_in + col + (cph ^ (row & 7)) * 8, base + q * 1024);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int q = 2 * w + i;
             const int row = 8 * q + (lane >> 3);
-            async_ld16(a.x + xoff[i] + col + (cph ^ (row & 7)) * 8, base + QK_KBYTES + q * 1024);
+            async_ld16(a.x + xoff[i] + col + (cph ^ (row & 7)) * 8, base + KBYTES + q * 1024);
         }
     };
 
     f32x4_t Sc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) Sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < QK_NS - 1 && i < nqk; ++i) issue_qk(i);
+    for (int i = 0; i < QNS - 1 && i < nkc; ++i) issue_qk(i);
     for (int c = 0; c < nkc; ++c) {
+        wait_upto<QLOADS, QNS - 2>(min(QNS - 2, nkc - 1 - c));
+        lds_barrier();
+        if (c + QNS - 1 < nkc) issue_qk(c + QNS - 1);
+        if (active) {
+            const uint16_t *kt = reinterpret_cast<const uint16_t *>(ring + (c % QNS) * QSTAGE);
+            const uint16_t *xt = kt + KBYTES / 2;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const int s = c * NRB + rb;
-            wait_upto<QK_LOADS>(min(QK_NS - 2, nqk - 1 - s));
-            lds_barrier();
-            if (s + QK_NS - 1 < nqk) issue_qk(s + QK_NS - 1);
-            if (active) {
-                const uint16_t *kt = reinterpret_cast<const uint16_t *>(ring + (s % QK_NS) * QK_STAGE);
-                const uint16_t *xt = kt + QK_KBYTES / 2;
+            for (int kk = 0; kk < QK_KC / 32; ++kk) {
+                const int ch = kk * 4 + kg;
+                const int xr = 16 * w + l16;
+                const bf16x8_t B = *reinterpret_cast<const bf16x8_t *>(&xt[xr * QK_KC + ((ch ^ (xr & 7)) * 8)]);
 #pragma unroll
-                for (int kk = 0; kk < QK_KC / 32; ++kk) {
-                    const int ch = kk * 4 + kg;
-                    const int xr = 16 * w + l16;
-                    const bf16x8_t B = *reinterpret_cast<const bf16x8_t *>(&xt[xr * QK_KC + ((ch ^ (xr & 7)) * 8)]);
-#pragma unroll
-                    for (int b = 0; b < 8; ++b) {
-                        const int kr = 16 * b + l16;
-                        const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(&kt[kr * QK_KC + ((ch ^ (kr & 7)) * 8)]);
-                        Sc[rb * 8 + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, Sc[rb * 8 + b], 0, 0, 0);
-                    }
+                for (int b = 0; b < NB; ++b) {
+                    const int kr = 16 * b + l16;
+                    const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(&kt[kr * QK_KC + ((ch ^ (kr & 7)) * 8)]);
+                    Sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, Sc[b], 0, 0, 0);
+                    // keep operand reads within a 128-row block (bounds live registers)
+                    if ((b & 7) == 7) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -410,9 +412,9 @@ __device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *rin
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     float lsum = 0.f;
-    uint4 Pk[NPV];
+    uint4 Pk[NB / 2];
 #pragma unroll
-    for (int g = 0; g < NPV; ++g) {
+    for (int g = 0; g < NB / 2; ++g) {
         float pr[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -429,50 +431,59 @@ __device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *rin
     const int qi = 16 * w + l16;
     const int tok = qi < ntok ? a.perm[sb + tq + qi] : 0;
 
-    // values stages: rows [32g, 32g + 32) of V_t and columns [hp*DEH, (hp+1)*DEH),
-    // copied row-major; chunk p of a row holds global chunk p ^ swz(row) so the
-    // transposed reads spread over the banks
-    auto swz = [](int row) { return (2 * (row & 7)) & (CPR - 1); };
+    // values stages: rows [64g, 64g + 64) of V_t and columns [hp*DEH, (hp+1)*DEH).
+    // A stage is stored as 1 KB blocks of 16 rows x 64 bytes (4 chunks): block
+    // (cg, rg) holds chunks [4cg, 4cg + 4) of rows [16rg, 16rg + 16), row-major.  One
+    // async copy fills one block (4 lanes per 64-byte row segment).  A transposed
+    // read by 16 lanes touches 4 rows x 4 column quads: 32 distinct banks.
+    constexpr int NRG = PV_ROWS / 16;  // row groups per stage
+    static_assert((CPR / 4) * NRG == V_STAGE / 1024, "values blocks");
+    // lane part of the transposed-read address (bytes): row 4kg + l16/4 of a row
+    // group, column quad l16 % 4 (two per 16-byte chunk)
+    const uint32_t tr_lane = (4 * kg + (l16 >> 2)) * 64 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
 #pragma unroll
     for (int hp = 0; hp < NPASS; ++hp) {
         auto issue_pv = [&](int g) {
-            const uint32_t base = ring0 + (uint32_t)((g % PV_NS) * V_STAGE);
+            const uint32_t base = ring0 + (uint32_t)((g % VNS) * V_STAGE);
 #pragma unroll
             for (int i = 0; i < V_LOADS; ++i) {
                 const int q = V_LOADS * w + i;
-                const int row = q * RPC + lane / CPR;
+                const int cg = q / NRG, rg = q % NRG;
+                const int row = rg * 16 + (lane >> 2);
                 const int64_t grow = r0 + min(PV_ROWS * g + row, d - 1);
-                async_ld16(a.WV + grow * DE + hp * DEH + ((lane % CPR) ^ swz(row)) * 8, base + q * 1024);
+                async_ld16(a.WV + grow * DE + hp * DEH + (cg * 4 + (lane & 3)) * 8, base + q * 1024);
             }
         };
         lds_barrier();  // every wave is done with the previous stages in the ring
 #pragma unroll
-        for (int i = 0; i < PV_NS - 1 && i < NPV; ++i) issue_pv(i);
+        for (int i = 0; i < VNS - 1 && i < NPV; ++i) issue_pv(i);
         f32x4_t O[VEBH];
 #pragma unroll
         for (int e = 0; e < VEBH; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NPV; ++g) {
-            wait_upto<V_LOADS>(min(PV_NS - 2, NPV - 1 - g));
+            wait_upto<V_LOADS, VNS - 2>(min(VNS - 2, NPV - 1 - g));
             lds_barrier();
-            if (g + PV_NS - 1 < NPV) issue_pv(g + PV_NS - 1);
+            if (g + VNS - 1 < NPV) issue_pv(g + VNS - 1);
             if (active) {
-                const uint16_t *vt = reinterpret_cast<const uint16_t *>(ring + (g % PV_NS) * V_STAGE);
-                const bf16x8_t P = __builtin_bit_cast(bf16x8_t, Pk[g]);
-                const int ra = 4 * kg + (l16 >> 2), rbw = ra + 16;
 #pragma unroll
-                for (int eb = 0; eb < VEBH; ++eb) {
-                    const int col = eb * 16 + 4 * (l16 & 3);
-                    const int chk = col >> 3, half = col & 7;
-                    const uint16_t *pa = vt + ra * DEH + ((chk ^ swz(ra)) * 8) + half;
-                    const uint16_t *pb = vt + rbw * DEH + ((chk ^ swz(rbw)) * 8) + half;
-                    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4_t *)(pa));
-                    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4_t *)(pb));
-                    const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
-                    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
-                    O[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P, O[eb], 0, 0, 0);
+                for (int ks = 0; ks < PV_ROWS / 32; ++ks) {
+                    const unsigned char *vt = ring + (g % VNS) * V_STAGE + tr_lane;
+                    const bf16x8_t P = __builtin_bit_cast(bf16x8_t, Pk[g * (PV_ROWS / 32) + ks]);
+#pragma unroll
+                    for (int eb = 0; eb < VEBH; ++eb) {
+                        // rows 32ks + 4kg + e (first read) and 32ks + 16 + 4kg + e (second):
+                        // row groups 2ks and 2ks + 1; chunks 2eb, 2eb + 1 (block eb / 2)
+                        const int blk_a = (eb >> 1) * NRG + 2 * ks, blk_b = blk_a + 1;
+                        const int cofs = (eb & 1) * 32;
+                        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4_t *)(vt + blk_a * 1024 + cofs));
+                        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4_t *)(vt + blk_b * 1024 + cofs));
+                        const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
+                        O[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P, O[eb], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -492,13 +503,23 @@ __device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *rin
 template <int VEB>  // d_emb / 16
 __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char ring[RING_BYTES];
+    __shared__ int s_item;
     const uint32_t ring0 = lds_addr(ring);
     const int nitems = a.hdr[HDR_NHEAVY];
-    // XCD-aware order: XCD x (= blockIdx % 8) walks the x-th eighth of the list
-    const int nbx = gridDim.x >> 3, lb = blockIdx.x >> 3;
-    const int per = (nitems + 7) >> 3;
-    const int ibeg = (blockIdx.x & 7) * per, iend = min(nitems, ibeg + per);
-    for (int it = ibeg + lb; it < iend; it += nbx) {
+    // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
+    // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
+    // items from its own counter, in order.  Consecutive items (tiles of one ID)
+    // share an XCD's L2; every XCD gets a similar mix of large and small IDs.
+    const int xcd = blockIdx.x & 7;
+    for (;;) {
+        if (threadIdx.x == 0) {
+            const int n = atomicAdd(&a.queue[xcd], 1);
+            const int it = ((n / QCHUNK) * 8 + xcd) * QCHUNK + n % QCHUNK;
+            s_item = it < nitems ? it : -1;
+        }
+        lds_barrier();
+        const int it = s_item;
+        if (it < 0) break;
         const int2 item = a.items[it];
         const int j = item.x, tq = item.y;
         const int sb = a.seg_start[j];
@@ -569,7 +590,7 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t 
                  (uint16_t *)a.o};
     if (use_heavy) {
         HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
-                     a.uniq, a.seg_start, a.perm, a.hdr, a.heavy, a.d_in, (uint16_t *)a.o};
+                     a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.d_in, (uint16_t *)a.o};
         const hipError_t e = launch_heavy(ha, a.d_emb, s);
         if (e != hipSuccess) return e;
     }

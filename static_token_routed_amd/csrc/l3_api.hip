@@ -138,6 +138,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         AttnArgs a{};
         a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
         a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
+        a.queue = b.hdr + HDR_QUEUE;
         a.light = light; a.heavy = heavy;
         a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
         a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;

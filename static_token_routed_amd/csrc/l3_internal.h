@@ -25,7 +25,7 @@ constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use 
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
 
 // Workspace header (int32 words), zeroed at the start of every call.
-enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_WORDS = 64 };
+enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_QUEUE = 8, HDR_WORDS = 64 };
 
 struct Dims {
     int64_t d_in, d_emb, d_up, d_out;
@@ -71,6 +71,7 @@ struct AttnArgs {
     const void *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
+    int32_t *queue;  // per-XCD work counters of the MFMA path (in the header)
     const int2 *light, *heavy;
     int64_t n, d_in, d_emb, vocab;
     void *o;
