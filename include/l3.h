@@ -39,6 +39,9 @@
  *    are returned before anything is enqueued.  Token IDs outside
  *    [0, vocab) found on the device set a flag in the workspace; the output
  *    rows of those tokens are unspecified and l3_status reports the flag.
+ *  - Device tensors and the workspace are at least 16-byte aligned (kernels
+ *    use 16-byte vector accesses), token ID arrays 4-byte aligned; a
+ *    misaligned pointer is rejected with L3_ERR_INVALID_ARG.
  *  - n = 0 is a no-op returning L3_OK.
  *  - Plans are immutable after creation and may be shared across threads and
  *    streams; a workspace serves one call at a time.
@@ -83,8 +86,8 @@ const char *l3_strerror(int status);
  * offsets: host, vocab + 1 int64 entries; off[0] = 0, 1 <= off[t+1]-off[t] <= k,
  *          off[vocab] = v (the allocation bounds of the pages: every token gets
  *          at least one and at most k embeddings, budget v = sum d_t).
- * dims:    host; bf16 needs d_in, d_emb, d_up, d_out multiples of 64 and
- *          d_in, d_up <= 8192, d_emb <= 1024; fp32 takes any positive dims.
+ * dims:    host; bf16 needs d_in, d_up, d_out multiples of 64, d_in <= 4096
+ *          and d_emb one of 64, 128, 256, 512; fp32 takes any positive dims.
  * plan:    out; the handle owns a device copy of the offsets (allocated on the
  *          current HIP device).  Errors: INVALID_ARG, BAD_OFFSETS, UNSUPPORTED,
  *          NOMEM, HIP.
@@ -195,7 +198,8 @@ int l3_forward_staged(l3_staging_t staging, const void *x, int64_t n, const void
  * Dense bf16 GEMM on the library's MFMA kernel: C[M x N] = A[M x K] * B[N x K]^T
  * (both operands k-contiguous, torch Linear layout), fp32 accumulate, bf16 out.
  * Used as the decode workload's stand-in for the layers before L^3.
- * K must be a multiple of 64.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ * K and N must be multiples of 64.  Errors: INVALID_ARG (also a pointer not
+ * 16-byte aligned), UNSUPPORTED, HIP.
  */
 int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                  void *stream);

@@ -5,9 +5,10 @@
 //   out = W_mix [LN(h) ; x]  (W_mix: d_out x (d_up + d_in))
 // as bf16 MFMA GEMMs C[M x N] = A[M x K] B[N x K]^T with fp32 accumulation.
 //
-// Kernel shape (gfx950): 256 threads = 4 wavefronts in 2 x 2, each owning a
-// 128 x 128 block of a 256 x 256 output tile as 4 x 4 v_mfma_f32_32x32x16_bf16
-// accumulators (256 fp32 per lane).  K advances 64 at a time.  Both operand
+// Kernel shape (gfx950): 512 threads = 8 wavefronts in 2 x 4, each owning a
+// 128 x 64 block of a 256 x 256 output tile as 4 x 2 v_mfma_f32_32x32x16_bf16
+// accumulators (128 fp32 per lane), so two wavefronts share each SIMD and one's
+// MFMAs cover the other's LDS reads.  K advances 64 at a time.  Both operand
 // tiles (256 x 64 bf16 each) go global -> LDS by asynchronous 16-byte copies
 // (no register staging) into a double buffer: the copies of stage s+1 are in
 // flight while stage s is multiplied, and barriers wait for LDS traffic only.
@@ -20,14 +21,14 @@
 // (workgroup id mod 8) form a contiguous, grouped block of tiles, sharing A
 // rows and B columns in that XCD's L2.
 //
-// LayerNorm and the concat [LN(h) ; x] are fused into the W_mix operand path:
-// the A tiles of the first d_up columns are h, copied raw into LDS; each 8-value
-// A fragment read from LDS becomes (h - mean) * rstd * gamma + beta before it
-// enters the MFMA (mean and rstd per row, from the W_up epilogue's partial
-// statistics -- per row and 128-column chunk, the mean and the sum of squared
-// deviations of the stored bf16 values -- merged with Chan's pairwise update;
-// gamma and beta slices travel with each stage as one more async copy).  The
-// remaining columns are x.  The concatenated operand never exists in memory.
+// LayerNorm and the concat [LN(h) ; x] are fused into the W_mix operand path.
+// For the first d_up columns the A tile is h, loaded into registers one stage
+// ahead, turned into (h - mean) * rstd * gamma + beta (each element once per
+// workgroup) and written into the swizzled LDS layout; mean and rstd per row
+// come from the W_up epilogue's partial statistics (per row and 64-column
+// chunk, the mean and the sum of squared deviations of the stored bf16 values),
+// merged with Chan's pairwise update.  The remaining columns are x, copied
+// asynchronously like B.  The concatenated operand never exists in memory.
 #include <type_traits>
 
 #include "cdna4.h"
@@ -68,140 +69,156 @@ __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
 }
 
 template <bool LN_IN, bool LN_OUT>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmP p) {
     __shared__ __attribute__((aligned(1024))) uint16_t As[2][BM * BK];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[2][BN * BK];
-    __shared__ __attribute__((aligned(16))) float GB[2][2 * BK];  // gamma, beta of the stage
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 2, wn = w & 3;
 
-    // Copy mapping: wave w issues 8 copies per operand and stage; copy q covers tile
+    // Copy mapping: wave w issues 4 copies per operand and stage; copy q covers tile
     // rows [8q, 8q + 8) (1 KB of LDS).  Lane l fills physical chunk l % 8 of row
     // 8q + l / 8 with global chunk (l % 8) ^ (row & 7).  Rows past M (N) are clamped:
     // they only feed accumulators that are never stored.
     const int crow = lane >> 3, cphys = lane & 7;
     const uint32_t a_lds0 = lds_addr(&As[0][0]), b_lds0 = lds_addr(&Bs[0][0]);
-    const uint32_t gb_lds0 = lds_addr(&GB[0][0]);
-    auto issue = [&](int64_t k0, int buf) {
+    auto issue = [&](int64_t k0, int buf, bool a_async) {
         const bool first = k0 < p.K1;
         const uint16_t *abase = first ? p.A + k0 : p.A2 + (k0 - p.K1);
         const int64_t lda = first ? p.lda : p.lda2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = w * 8 + i;
+        for (int i = 0; i < 4; ++i) {
+            const int q = w * 4 + i;
             const int row = q * 8 + crow;
             const int gch = cphys ^ (row & 7);
             const int64_t ar = min<int64_t>(m0 + row, p.M - 1);
             const int64_t br = min<int64_t>(n0 + row, p.N - 1);
             const uint32_t off = (uint32_t)(buf * BM * BK * 2 + q * 1024);
-            async_ld16(abase + ar * lda + gch * 8, a_lds0 + off);
+            if (a_async) async_ld16(abase + ar * lda + gch * 8, a_lds0 + off);
             async_ld16(p.B + br * p.ldb + k0 + gch * 8, b_lds0 + off);
-        }
-        if constexpr (LN_IN) {
-            // gamma[k0, k0+64) and beta[k0, k0+64): 32 lanes x 16 B of wave 0
-            if (first && w == 0) {
-                const float *src = lane < 16 ? p.gamma + k0 + lane * 4 : p.beta + k0 + (lane - 16) * 4;
-                if (lane < 32) async_ld16(src, gb_lds0 + buf * 2 * BK * 4);
-            }
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // LayerNorm statistics of the lane's 4 A rows (LN_IN)
+    // LayerNorm staging (LN_IN): thread t owns chunk t % 8 of tile rows t / 8 + 64 i
+    const int sc = t & 7, sr = t >> 3;
     float mu[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (LN_IN) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t m = min<int64_t>(m0 + wm * 128 + i * 32 + (lane & 31), p.M - 1);
+            const int64_t m = min<int64_t>(m0 + sr + 64 * i, p.M - 1);
             mu[i] = p.row_stats[2 * m];
             rs[i] = p.row_stats[2 * m + 1];
         }
     }
+    uint4 hreg[4];
+    float4 gam0, gam1, bet0, bet1;
+    auto load_h = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = min<int64_t>(m0 + sr + 64 * i, p.M - 1);
+            hreg[i] = *reinterpret_cast<const uint4 *>(p.A + m * p.lda + k0 + sc * 8);
+        }
+        gam0 = *reinterpret_cast<const float4 *>(p.gamma + k0 + sc * 8);
+        gam1 = *reinterpret_cast<const float4 *>(p.gamma + k0 + sc * 8 + 4);
+        bet0 = *reinterpret_cast<const float4 *>(p.beta + k0 + sc * 8);
+        bet1 = *reinterpret_cast<const float4 *>(p.beta + k0 + sc * 8 + 4);
+    };
+    auto store_h = [&](int buf) {  // y = (h - mean) * rstd * gamma + beta, into the swizzled tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = sr + 64 * i;
+            uint4 u = hreg[i];
+            const float m_ = mu[i], r_ = rs[i];
+            u.x = pack2((bf_lo(u.x) - m_) * r_ * gam0.x + bet0.x, (bf_hi(u.x) - m_) * r_ * gam0.y + bet0.y);
+            u.y = pack2((bf_lo(u.y) - m_) * r_ * gam0.z + bet0.z, (bf_hi(u.y) - m_) * r_ * gam0.w + bet0.w);
+            u.z = pack2((bf_lo(u.z) - m_) * r_ * gam1.x + bet1.x, (bf_hi(u.z) - m_) * r_ * gam1.y + bet1.y);
+            u.w = pack2((bf_lo(u.w) - m_) * r_ * gam1.z + bet1.z, (bf_hi(u.w) - m_) * r_ * gam1.w + bet1.w);
+            *reinterpret_cast<uint4 *>(&As[buf][r * BK + ((sc ^ (r & 7)) * 8)]) = u;
+        }
+    };
 
-    auto compute = [&](int buf, auto ln_tag) {
-        constexpr bool LN = decltype(ln_tag)::value;
+    // Fragments of k-substep kk (16 columns): A rows wm*128 + i*32 + lane%32 and B rows
+    // wn*64 + j*32 + lane%32, 8 columns each (chunk 2kk + lane/32 of the 128-byte row).
+    auto load_frags = [&](int buf, int kk, bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
         const uint16_t *as = As[buf];
         const uint16_t *bs = Bs[buf];
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + (lane & 31);
+            fa[i] = *reinterpret_cast<const bf16x8_t *>(&as[r * BK + ((ch ^ (r & 7)) * 8)]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wn * 64 + j * 32 + (lane & 31);
+            fb[j] = *reinterpret_cast<const bf16x8_t *>(&bs[r * BK + ((ch ^ (r & 7)) * 8)]);
+        }
+    };
+    auto compute = [&](int buf) {
+        bf16x8_t fa[2][4], fb[2][2];
+        load_frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int ch = kk * 2 + (lane >> 5);
-            bf16x8_t fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 128 + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8_t *>(&as[r * BK + ((ch ^ (r & 7)) * 8)]);
-            }
-            if constexpr (LN) {
-                // y = (h - mean) * rstd * gamma + beta on the lane's 8 columns
-                const float4 g0 = *reinterpret_cast<const float4 *>(&GB[buf][ch * 8]);
-                const float4 g1 = *reinterpret_cast<const float4 *>(&GB[buf][ch * 8 + 4]);
-                const float4 b0 = *reinterpret_cast<const float4 *>(&GB[buf][BK + ch * 8]);
-                const float4 b1 = *reinterpret_cast<const float4 *>(&GB[buf][BK + ch * 8 + 4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint4 u = __builtin_bit_cast(uint4, fa[i]);
-                    const float m_ = mu[i], r_ = rs[i];
-                    u.x = pack2((bf_lo(u.x) - m_) * r_ * g0.x + b0.x, (bf_hi(u.x) - m_) * r_ * g0.y + b0.y);
-                    u.y = pack2((bf_lo(u.y) - m_) * r_ * g0.z + b0.z, (bf_hi(u.y) - m_) * r_ * g0.w + b0.w);
-                    u.z = pack2((bf_lo(u.z) - m_) * r_ * g1.x + b1.x, (bf_hi(u.z) - m_) * r_ * g1.y + b1.y);
-                    u.w = pack2((bf_lo(u.w) - m_) * r_ * g1.z + b1.z, (bf_hi(u.w) - m_) * r_ * g1.w + b1.w);
-                    fa[i] = __builtin_bit_cast(bf16x8_t, u);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn * 128 + j * 32 + (lane & 31);
-                fb[j] = *reinterpret_cast<const bf16x8_t *>(&bs[r * BK + ((ch ^ (r & 7)) * 8)]);
-            }
+            const int cur = kk & 1;
+            // the next substep's fragments are read while this substep's MFMAs run
+            if (kk < 3) load_frags(buf, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
         }
     };
-    // one pipelined stage: wait for its copies, start the next stage's, multiply
+    // Pipelined stages: wait for this stage's copies (the only loads in flight), start
+    // the next stage's, multiply; an h stage is staged through registers and written
+    // (normalised) into the other buffer after the multiply.
     const int nst = (int)(p.K / BK);
-    const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages whose A operand is normalised
-    issue(0, 0);
-    for (int st = 0; st < nst1; ++st) {
-        wait_vmcnt<0>();  // this stage's copies (the only ones in flight) have landed
-        lds_barrier();    // ... for every wave; and everyone is done with the other buffer
-        if (st + 1 < nst) issue((int64_t)(st + 1) * BK, (st + 1) & 1);
-        compute(st & 1, std::true_type{});
+    const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages whose A operand is normalised h
+    if (0 < nst1) {
+        load_h(0);
+        issue(0, 0, false);
+        store_h(0);
+    } else {
+        issue(0, 0, true);
     }
-    for (int st = nst1; st < nst; ++st) {
+    for (int st = 0; st < nst; ++st) {
         wait_vmcnt<0>();
         lds_barrier();
-        if (st + 1 < nst) issue((int64_t)(st + 1) * BK, (st + 1) & 1);
-        compute(st & 1, std::false_type{});
+        const bool next = st + 1 < nst;
+        const bool next_h = st + 1 < nst1;
+        if (next) {
+            if (next_h) load_h((int64_t)(st + 1) * BK);
+            issue((int64_t)(st + 1) * BK, (st + 1) & 1, !next_h);
+        }
+        compute(st & 1);
+        if (next_h) store_h((st + 1) & 1);
     }
 
     // Epilogue.  acc[i][j] element e of lane l: output row m = m0 + wm*128 + i*32 + (l&31),
-    // column n = n0 + wn*128 + j*32 + 8*(e/4) + 4*(l/32) + (e%4).
-    const int64_t nbase = n0 + wn * 128;
+    // column n = n0 + wn*64 + j*32 + 8*(e/4) + 4*(l/32) + (e%4).
+    const int64_t nbase = n0 + wn * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
-        float hv[4][16];
+        float hv[2][16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t n = nbase + j * 32 + 8 * g + 4 * (lane >> 5);
-                float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
                 const uint32_t lo = pack2(v0, v1), hi = pack2(v2, v3);
                 if (m < p.M && n < p.N)
                     *reinterpret_cast<uint2 *>(p.C + m * p.N + n) = make_uint2(lo, hi);
@@ -214,18 +231,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
                 }
             }
         if constexpr (LN_OUT) {
+            // partial statistics of this row over the wavefront's 64 columns
             const int64_t width = min<int64_t>(kLnPart, p.N - nbase);
             if (width > 0) {
                 float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) s += hv[j][e];
                 s += __shfl_xor(s, 32);
                 const float mean = s / (float)width;
                 float q = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int64_t n = nbase + j * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
@@ -361,9 +379,9 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     if (ln_out) {
         p.ln_out = ln_out;
         p.npart_out = (int)((N + kLnPart - 1) / kLnPart);
-        hipLaunchKernelGGL((k_gemm_bf16<false, true>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((k_gemm_bf16<false, true>), grid, dim3(512), 0, s, p);
     } else {
-        hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(512), 0, s, p);
     }
     return hipGetLastError();
 }
@@ -389,7 +407,7 @@ hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const floa
     p.row_stats = stats;
     p.gamma = gamma;
     p.beta = beta;
-    hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 

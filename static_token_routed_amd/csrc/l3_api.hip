@@ -2,6 +2,7 @@
 // layout, launch sequencing, the decode-time prefetch, and stage timing.
 #include <algorithm>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -84,6 +85,13 @@ int validate_dims(const l3_dims_t *d) {
             return L3_ERR_UNSUPPORTED;
     }
     return L3_OK;
+}
+
+// Device arrays are read and written with 16-byte vector accesses.
+bool aligned16(std::initializer_list<const void *> ps) {
+    for (const void *q : ps)
+        if (reinterpret_cast<uintptr_t>(q) & 15) return false;
+    return true;
 }
 
 int check_offsets(const int64_t *off, int64_t vocab, int64_t v, int32_t k, int32_t *max_d) {
@@ -298,6 +306,8 @@ int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const 
     if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
     if (!x || !ids || !WK || !WV || !W_up || !gamma || !beta || !W_mix || !out || !ws)
         return L3_ERR_INVALID_ARG;
+    if (!aligned16({x, WK, WV, W_up, gamma, beta, W_mix, out, ws})) return L3_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(ids) & 3) return L3_ERR_INVALID_ARG;
     return forward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, out, ws, ws_bytes,
                         (hipStream_t)stream);
 }
@@ -355,6 +365,7 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
                  void *stream) {
     if (!A || !B || !C || M < 0 || N < 0 || K <= 0) return L3_ERR_INVALID_ARG;
     if (K % 64 || N % 64) return L3_ERR_UNSUPPORTED;
+    if (!aligned16({A, B, C})) return L3_ERR_INVALID_ARG;
     L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)A, (const uint16_t *)B, (uint16_t *)C, M, N, K,
                                 nullptr, (hipStream_t)stream));
     return L3_OK;
@@ -462,6 +473,7 @@ int l3_forward_staged(l3_staging_t st, const void *x, int64_t n, const void *W_u
     if (n != st->n) return L3_ERR_INVALID_ARG;
     if (n == 0) return L3_OK;
     if (!x || !W_up || !gamma || !beta || !W_mix || !out || !ws) return L3_ERR_INVALID_ARG;
+    if (!aligned16({x, W_up, gamma, beta, W_mix, out, ws})) return L3_ERR_INVALID_ARG;
     // a plan view over the compact CSR; workspace sizing uses the full plan's max_d
     l3_plan_s view;
     view.vocab = st->m;

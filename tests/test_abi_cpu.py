@@ -75,3 +75,13 @@ def test_null_and_size_checks():
     assert l3._lib.l3_plan_destroy(None) == l3.L3_OK
     assert l3._lib.l3_staging_destroy(None) == l3.L3_OK
     assert l3._lib.l3_gemm_bf16(None, None, None, 1, 64, 64, None) == l3.L3_ERR_INVALID_ARG
+
+
+def test_gemm_shape_and_alignment_checks():
+    # rejected on the host: the pointers are never dereferenced
+    g = l3._lib.l3_gemm_bf16
+    a, b, c = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    assert g(a, b, c, 64, 64, 96, None) == l3.L3_ERR_UNSUPPORTED   # K not a multiple of 64
+    assert g(a, b, c, 64, 96, 64, None) == l3.L3_ERR_UNSUPPORTED   # N not a multiple of 64
+    assert g(ctypes.c_void_p(0x1008), b, c, 64, 64, 64, None) == l3.L3_ERR_INVALID_ARG
+    assert g(a, b, ctypes.c_void_p(0x3002), 64, 64, 64, None) == l3.L3_ERR_INVALID_ARG
