@@ -39,6 +39,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the oracle timing on the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB (5 times) and exit: the "
+                         "reference kernel that scales the HBM byte counters")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                           "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE of this "
+                         "benchmark and of --copy-probe) into profiles/<stage>_<workload>_"
+                         "counters.json, then exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size the copy probe ran with")
     return ap.parse_args()
 
 
@@ -59,14 +68,103 @@ def traffic_from_profiles(stage: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def copy_probe(mib: int):
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[copy-probe] 5 copies of {mib} MiB done", file=sys.stderr, flush=True)
+
+
+# kernel name prefix -> stage of one forward
+STAGE_OF_KERNEL = [("k_attn", "gather_attention"), ("k_gemm_bf16<false, true>", "w_up_gemm"),
+                   ("k_gemm_bf16<true, false>", "w_mix_gemm"), ("k_ln_finalize", "w_mix_gemm"),
+                   ("k_sort", "route"), ("k_scan", "route"), ("k_seg", "route"),
+                   ("k_worklist", "route"), ("k_zero_i32", "route")]
+
+
+def read_counter_csv(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "")
+            name = name[5:] if name.startswith("void ") else name
+            name = name.split("(")[0]
+            per.setdefault(name, []).append(float(r["Counter_Value"]))
+    return per
+
+
+def ingest_counters(args):
+    """HBM bytes per launch of each stage: mean per dispatch of FETCH_SIZE and
+    WRITE_SIZE (KiB), each scaled by bytes / counter of the plain copy kernel."""
+    fetch = read_counter_csv(args.ingest_counters[0], "FETCH_SIZE")
+    write = read_counter_csv(args.ingest_counters[1], "WRITE_SIZE")
+    cfetch = read_counter_csv(args.ingest_counters[2], "FETCH_SIZE")
+    cwrite = read_counter_csv(args.ingest_counters[3], "WRITE_SIZE")
+    copy_bytes = args.copy_mib << 20
+
+    def copy_factor(per):
+        k = max(per, key=lambda n: np.mean(per[n]))  # the copy kernel: largest reading
+        return copy_bytes / (np.median(per[k]) * 1024.0), k
+
+    ff, fk = copy_factor(cfetch)
+    wf, wk = copy_factor(cwrite)
+    stages = {}
+    for name in fetch:
+        st = next((s for p, s in STAGE_OF_KERNEL if name.startswith(p)), None)
+        if st is None:
+            continue
+        d = stages.setdefault(st, {"kernels": {}, "fetch_kib": 0.0, "write_kib": 0.0})
+        # per forward: dispatches of a kernel per forward = calls / forwards
+        d["kernels"][name] = {"fetch_kib_per_dispatch": float(np.mean(fetch[name])),
+                              "write_kib_per_dispatch": float(np.mean(write.get(name, [0.0]))),
+                              "dispatches": len(fetch[name])}
+    forwards = max(len(fetch[n]) for n in fetch if n.startswith("k_attn"))
+    for st, d in stages.items():
+        for name, kd in d["kernels"].items():
+            per_fwd = kd["dispatches"] / forwards
+            d["fetch_kib"] += kd["fetch_kib_per_dispatch"] * per_fwd
+            d["write_kib"] += kd["write_kib_per_dispatch"] * per_fwd
+        out = {
+            "stage": st, "workload": args.workload,
+            "source_sha256_16": src_hash(KERNEL_SOURCES[st]),
+            "fetch_kib_per_launch": d["fetch_kib"], "write_kib_per_launch": d["write_kib"],
+            "copy_probe": {"bytes": copy_bytes, "fetch_kernel": fk, "write_kernel": wk,
+                           "fetch_factor": ff, "write_factor": wf},
+            "hbm_read_bytes_per_launch": d["fetch_kib"] * 1024.0 * ff,
+            "hbm_write_bytes_per_launch": d["write_kib"] * 1024.0 * wf,
+            "kernels": d["kernels"],
+            "forwards_profiled": forwards,
+            "commands": [" ".join(sys.argv)],
+        }
+        out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+        path = os.path.join(ROOT, "profiles", f"{st}_{args.workload}_counters.json")
+        json.dump(out, open(path, "w"), indent=1)
+        print(f"{path}: {out['hbm_bytes_per_launch'] / 1e9:.3f} GB per launch")
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import synth
     import static_token_routed_amd as l3

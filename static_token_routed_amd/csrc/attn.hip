@@ -13,6 +13,8 @@
 // d_t rows is an online (running max / running sum) fp32 softmax, so any d_t
 // streams through registers.  The result row goes to the token's original
 // batch position, which undoes the sort in the store.
+#include <type_traits>
+
 #include "cdna4.h"
 #include "l3_internal.h"
 
@@ -269,23 +271,27 @@ __global__ __launch_bounds__(256) void k_attn_f32(F32Args a) {
 // ---------------------------------------------------------------- MFMA path
 //
 // Blocks with many tokens, or with many rows (d_t), run on the matrix cores.
-// One workgroup takes one ID and up to 64 of its tokens; wavefront w owns tokens
-// [16w, 16w + 16).
-//   scores  S^T (d_t x 16 tokens) = K_t x^T with v_mfma_f32_16x16x32_bf16.  K
-//           tiles (128 rows x 64 columns) and the gathered x tiles (64 tokens x
-//           64 columns) stream through a 3-stage LDS ring filled by asynchronous
-//           global->LDS copies; all d_t <= 512 scores stay in the accumulators,
-//           so the softmax is exact (one max, one sum) and no accumulator is
-//           rescaled.
-//   values  O^T (d_emb x 16 tokens) = V_t^T P^T, the same MFMA, over 32-row
-//           stages of V copied row-major into the ring and read transposed with
-//           ds_read_b64_tr_b16.
-// The MFMA reduction index k maps to rows as k = 8*(lane/16) + j  <->  row
-// 4*(lane/16) + j for j < 4, 16 + 4*(lane/16) + (j - 4) for j >= 4: exactly the
-// rows whose scores that lane holds in two consecutive 16-row accumulators, so
-// P never moves between lanes.  Work items of one ID are consecutive in the
-// list; each XCD takes a contiguous eighth of the list, so the tiles of one ID
-// mostly share that XCD's L2.
+// One workgroup takes one ID and up to 32 of its tokens.  Its 4 wavefronts form
+// 2 token groups (16 tokens each) x 2 column halves: wavefront (tg, ch) keeps
+// x[token][ch half of d_in] of its 16 tokens in registers as MFMA operands and
+// produces the ch half of their d_emb outputs.  K_t and V_t stream once, in
+// 128-row groups, through a ring of 16 KB LDS stages filled by asynchronous
+// global->LDS copies (1 KB contiguous row pieces):
+//   scores  partial S^T (16 rows x 16 tokens) over the wavefront's d_in half,
+//           v_mfma_f32_16x16x32_bf16, from K stages of 16 rows x 512 columns;
+//           the two halves of a token group swap partials through LDS once per
+//           group, so both hold the full scores.
+//   softmax running max and sum per token, updated once per group (its scores
+//           are all in registers); rows past d_t are masked.
+//   values  O^T (d_emb half x 16 tokens) += V_t^T P^T, the same MFMA, from V
+//           stages of 16 KB (rows x up to 256 columns, row-major) read
+//           transposed with ds_read_b64_tr_b16.
+// The K and V stages of all groups form one sequence that the copies run ahead
+// of by kSlots - 1 stages, so the softmax and the switch between K and V do not
+// drain the ring.  The MFMA reduction index k maps to rows as
+// k = 8*(lane/16) + j  <->  row 4*(lane/16) + j for j < 4, 16 + 4*(lane/16) +
+// (j - 4) for j >= 4: exactly the rows whose scores that lane holds in two
+// consecutive 16-row accumulators, so P never moves between lanes.
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 struct HeavyArgs {
@@ -298,256 +304,325 @@ struct HeavyArgs {
     uint16_t *o;
 };
 
-constexpr int QK_RB = 128;                           // K rows per row block
-constexpr int QK_KC = 64;                            // d_in columns per scores stage
-constexpr int QK_XBYTES = kHeavyTile * QK_KC * 2;    // gathered x tile per stage (8 KB)
-constexpr int RING_BYTES = 144 * 1024;
-constexpr int PV_ROWS = 64;                          // V rows per values stage
-constexpr int QCHUNK = 4;                            // items per round-robin chunk of the XCD queues
+constexpr int kSlot = 16384;       // bytes per ring stage
+constexpr int kSlots = 8;          // ring depth
+constexpr int kXchg = 4 * 64 * 32 * 4;  // score partials of the 4 wavefronts (32 KB)
+constexpr int kGroup = 128;        // rows per softmax group
+constexpr int kKCols = 512;        // d_in columns per K stage
+constexpr int QCHUNK = 4;          // items per round-robin chunk of the XCD queues
+static_assert(kHeavyTile == 32, "two 16-token groups per item");
 
-// wait until at most N * later copies of this wave are in flight (later <= MAXL)
+// s_waitcnt vmcnt(N * later) for a runtime later in [0, MAXL]
 template <int N, int MAXL>
-__device__ inline void wait_upto(int later) {
-    if constexpr (MAXL >= 4) { if (later >= 4) { wait_vmcnt<4 * N>(); return; } }
-    if constexpr (MAXL >= 3) { if (later == 3) { wait_vmcnt<3 * N>(); return; } }
-    if constexpr (MAXL >= 2) { if (later == 2) { wait_vmcnt<2 * N>(); return; } }
-    if constexpr (MAXL >= 1) { if (later == 1) { wait_vmcnt<N>(); return; } }
-    wait_vmcnt<0>();
+__device__ inline void wait_stages(int later) {
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) { wait_vmcnt<N * MAXL>(); return; }
+        wait_stages<N, MAXL - 1>(later);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 
-// One work item with NRB 128-row blocks of K_t (d_t <= 128 * NRB).  Every score and
-// value MFMA of the item runs unconditionally: rows past d_t are copies of row
-// d_t - 1 whose scores are masked to -inf, so they weigh nothing.
-template <int VEB, int NRB>
-__device__ __forceinline__ void mfma_item(const HeavyArgs &a, unsigned char *ring, uint32_t ring0,
-                                          int sb, int tq, int ntok, int64_t r0, int d) {
-    constexpr int DE = VEB * 16;
-    constexpr int NPASS = VEB > 16 ? 2 : 1;                  // values passes over halves of d_emb
-    constexpr int VEBH = VEB / NPASS;
-    constexpr int DEH = VEBH * 16;                           // d_emb columns per pass
-    constexpr int CPR = DEH / 8;                             // 16-byte chunks per (half) V row
-    constexpr int KBYTES = NRB * QK_RB * QK_KC * 2;          // K tile per scores stage
-    constexpr int QSTAGE = KBYTES + QK_XBYTES;
-    constexpr int QNS = RING_BYTES / QSTAGE >= 6 ? 6 : RING_BYTES / QSTAGE;  // scores ring depth
-    constexpr int QLOADS = QSTAGE / 1024 / 4;                // copies per wave and scores stage
-    constexpr int KCOPIES = KBYTES / 1024 / 4;               // ... of which K
-    constexpr int V_STAGE = PV_ROWS * DEH * 2;               // bytes per values stage
-    constexpr int VNS = RING_BYTES / V_STAGE >= 6 ? 6 : RING_BYTES / V_STAGE;  // values ring depth
-    constexpr int V_LOADS = V_STAGE / 1024 / 4;              // copies per wave and values stage
-    constexpr int RPC = 1024 / (DEH * 2);                    // V rows per 1 KB copy
-    constexpr int NB = 8 * NRB;                              // 16-row score blocks
-    constexpr int NPV = (QK_RB / PV_ROWS) * NRB;             // values stages
-    static_assert(QNS >= 2 && VNS >= 2 && V_LOADS >= 1, "ring");
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int l16 = lane & 15, kg = lane >> 4, cph = lane & 7;
-    const int64_t d_in = a.d_in;
-    const int nkc = (int)(d_in / QK_KC);
-    const bool active = 16 * w < ntok;
-
-    // x rows (tokens) this lane copies: tile rows 8 * (2w + i) + lane / 8
-    int64_t xoff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tr = 8 * (2 * w + i) + (lane >> 3);
-        xoff[i] = (int64_t)a.perm[sb + tq + min(tr, ntok - 1)] * d_in;
-    }
-    // stage c: K[all rows][64c, 64c + 64) and x[tokens][same columns]; copy q of
-    // the K tile covers tile rows [8q, 8q + 8)
-    auto issue_qk = [&](int c) {
-        const uint32_t base = ring0 + (uint32_t)((c % QNS) * QSTAGE);
-        const int64_t col = (int64_t)c * QK_KC;
-#pragma unroll
-        for (int i = 0; i < KCOPIES; ++i) {
-            const int q = KCOPIES * w + i;
-            const int row = 8 * q + (lane >> 3);
-            const int64_t grow = r0 + min(row, d - 1);
-            async_ld16(a.WK + grow * d_in + col + (cph ^ (row & 7)) * 8, base + q * 1024);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * w + i;
-            const int row = 8 * q + (lane >> 3);
-            async_ld16(a.x + xoff[i] + col + (cph ^ (row & 7)) * 8, base + KBYTES + q * 1024);
-        }
-    };
-
-    f32x4_t Sc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) Sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < QNS - 1 && i < nkc; ++i) issue_qk(i);
-    for (int c = 0; c < nkc; ++c) {
-        wait_upto<QLOADS, QNS - 2>(min(QNS - 2, nkc - 1 - c));
-        lds_barrier();
-        if (c + QNS - 1 < nkc) issue_qk(c + QNS - 1);
-        if (active) {
-            const uint16_t *kt = reinterpret_cast<const uint16_t *>(ring + (c % QNS) * QSTAGE);
-            const uint16_t *xt = kt + KBYTES / 2;
-#pragma unroll
-            for (int kk = 0; kk < QK_KC / 32; ++kk) {
-                const int ch = kk * 4 + kg;
-                const int xr = 16 * w + l16;
-                const bf16x8_t B = *reinterpret_cast<const bf16x8_t *>(&xt[xr * QK_KC + ((ch ^ (xr & 7)) * 8)]);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int kr = 16 * b + l16;
-                    const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(&kt[kr * QK_KC + ((ch ^ (kr & 7)) * 8)]);
-                    Sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, Sc[b], 0, 0, 0);
-                    // keep operand reads within a 128-row block (bounds live registers)
-                    if ((b & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-    }
-
-    // exact softmax over the d_t rows (lane: token l16, rows 16b + 4kg + i)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v = (16 * b + 4 * kg + i < d) ? Sc[b][i] : -INFINITY;
-            Sc[b][i] = v;
-            mx = fmaxf(mx, v);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float lsum = 0.f;
-    uint4 Pk[NB / 2];
-#pragma unroll
-    for (int g = 0; g < NB / 2; ++g) {
-        float pr[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = __expf(Sc[2 * g][i] - mx);
-            pr[4 + i] = __expf(Sc[2 * g + 1][i] - mx);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lsum += pr[i];
-        Pk[g] = make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]), pack2(pr[6], pr[7]));
-    }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const float inv = 1.f / lsum;
-    const int qi = 16 * w + l16;
-    const int tok = qi < ntok ? a.perm[sb + tq + qi] : 0;
-
-    // values stages: rows [64g, 64g + 64) of V_t and columns [hp*DEH, (hp+1)*DEH).
-    // A stage is stored as 1 KB blocks of 16 rows x 64 bytes (4 chunks): block
-    // (cg, rg) holds chunks [4cg, 4cg + 4) of rows [16rg, 16rg + 16), row-major.  One
-    // async copy fills one block (4 lanes per 64-byte row segment).  A transposed
-    // read by 16 lanes touches 4 rows x 4 column quads: 32 distinct banks.
-    constexpr int NRG = PV_ROWS / 16;  // row groups per stage
-    static_assert((CPR / 4) * NRG == V_STAGE / 1024, "values blocks");
-    // lane part of the transposed-read address (bytes): row 4kg + l16/4 of a row
-    // group, column quad l16 % 4 (two per 16-byte chunk)
-    const uint32_t tr_lane = (4 * kg + (l16 >> 2)) * 64 + ((l16 & 3) >> 1) * 16 + (l16 & 1) * 8;
-#pragma unroll
-    for (int hp = 0; hp < NPASS; ++hp) {
-        auto issue_pv = [&](int g) {
-            const uint32_t base = ring0 + (uint32_t)((g % VNS) * V_STAGE);
-#pragma unroll
-            for (int i = 0; i < V_LOADS; ++i) {
-                const int q = V_LOADS * w + i;
-                const int cg = q / NRG, rg = q % NRG;
-                const int row = rg * 16 + (lane >> 2);
-                const int64_t grow = r0 + min(PV_ROWS * g + row, d - 1);
-                async_ld16(a.WV + grow * DE + hp * DEH + (cg * 4 + (lane & 3)) * 8, base + q * 1024);
-            }
-        };
-        lds_barrier();  // every wave is done with the previous stages in the ring
-#pragma unroll
-        for (int i = 0; i < VNS - 1 && i < NPV; ++i) issue_pv(i);
-        f32x4_t O[VEBH];
-#pragma unroll
-        for (int e = 0; e < VEBH; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < NPV; ++g) {
-            wait_upto<V_LOADS, VNS - 2>(min(VNS - 2, NPV - 1 - g));
-            lds_barrier();
-            if (g + VNS - 1 < NPV) issue_pv(g + VNS - 1);
-            if (active) {
-#pragma unroll
-                for (int ks = 0; ks < PV_ROWS / 32; ++ks) {
-                    const unsigned char *vt = ring + (g % VNS) * V_STAGE + tr_lane;
-                    const bf16x8_t P = __builtin_bit_cast(bf16x8_t, Pk[g * (PV_ROWS / 32) + ks]);
-#pragma unroll
-                    for (int eb = 0; eb < VEBH; ++eb) {
-                        // rows 32ks + 4kg + e (first read) and 32ks + 16 + 4kg + e (second):
-                        // row groups 2ks and 2ks + 1; chunks 2eb, 2eb + 1 (block eb / 2)
-                        const int blk_a = (eb >> 1) * NRG + 2 * ks, blk_b = blk_a + 1;
-                        const int cofs = (eb & 1) * 32;
-                        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4_t *)(vt + blk_a * 1024 + cofs));
-                        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4_t *)(vt + blk_b * 1024 + cofs));
-                        const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
-                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
-                        O[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, P, O[eb], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (active && qi < ntok) {
-            uint16_t *orow = a.o + (int64_t)tok * DE + hp * DEH + 4 * kg;
-#pragma unroll
-            for (int eb = 0; eb < VEBH; ++eb) {
-                const uint2 u = make_uint2(pack2(O[eb][0] * inv, O[eb][1] * inv),
-                                           pack2(O[eb][2] * inv, O[eb][3] * inv));
-                *reinterpret_cast<uint2 *>(orow + eb * 16) = u;
-            }
-        }
-    }
-    lds_barrier();  // the next item's copies reuse the ring
-}
-
-template <int VEB>  // d_emb / 16
+// XQ: x fragments (32 columns each) per lane, d_in = 64 XQ.  Each K stage's 512
+// columns (16 fragments; fewer when d_in < 512) are split in two halves of HW
+// fragments: half ch holds fragments [ch HW, ch HW + HW) of every stage, so all 4
+// wavefronts work on every stage.  DE: d_emb.
+template <int XQ, int DE>
 __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[RING_BYTES];
-    __shared__ int s_item;
+    constexpr int DEV = DE < 256 ? DE : 256;  // d_emb columns per V stage
+    constexpr int NVH = DE / DEV;             // V stages per row block (column parts)
+    constexpr int RV = kSlot / 2 / DEV;       // V rows per stage (32, 64 or 128)
+    constexpr int VPG = kGroup / RV;          // V row blocks per full group
+    constexpr int OB = DE / 32;               // 16-column output blocks per wavefront
+    constexpr int CPR = DEV / 8;              // 16-byte chunks per V stage row
+    constexpr int RPC = 64 / CPR;             // V rows per 1 KB copy
+    constexpr int64_t d_in = 64 * XQ;
+    constexpr int nq = (int)((d_in + kKCols - 1) / kKCols);  // K stages per 16-row block
+    constexpr int HW = XQ < 8 ? XQ : 8;       // fragments per wavefront and K stage
+    static_assert(CPR >= 8 && RV % 32 == 0 && (NVH == 1 || OB == 2 * (DEV / 32)), "V stage shape");
+    static_assert(HW % 2 == 0 && XQ % HW == 0, "K stage split");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * kSlot];
+    __shared__ __attribute__((aligned(16))) float xchg[kXchg / 4];
+    int *const s_item = reinterpret_cast<int *>(xchg);  // free between items
     const uint32_t ring0 = lds_addr(ring);
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) from here on
+    const int tg = w & 1, ch = w >> 1;
+    const int l16 = lane & 15, kg = lane >> 4;
     const int nitems = a.hdr[HDR_NHEAVY];
     // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
     // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
-    // items from its own counter, in order.  Consecutive items (tiles of one ID)
-    // share an XCD's L2; every XCD gets a similar mix of large and small IDs.
+    // items from its own counter, in order.
     const int xcd = blockIdx.x & 7;
+
+    // LDS read addresses as per-lane bases plus compile-time offsets.
+    // K stage: row r at 1024 r, logical 16-byte chunk c at physical chunk c ^ (r & 7).
+    // Fragment step kk reads row l16, chunk 4kk + kg: (4kk + kg) ^ (l16 & 7) =
+    // 4 (kk ^ b) + cq with b = bit 2 of l16, cq = (kg ^ l16) & 3; kk ^ b is kk + b for
+    // even kk and (kk - 1) + (1 - b) for odd kk.  Half ch starts at step ch HW.
+    const int kb2 = (l16 >> 2) & 1, kcq = (kg ^ l16) & 3;
+    const uint32_t k_even = l16 * 1024 + 16 * kcq + 64 * kb2 + 64 * HW * ch;
+    const uint32_t k_odd = l16 * 1024 + 16 * kcq + 64 * (1 - kb2) + 64 * HW * ch;
+    // V stage: row r at 2 DEV r, chunk c at physical chunk c ^ 2 (r & 3).  A transposed
+    // read for output block E (16 columns) takes row 4kg + l16/4 (+ 32kb, + 16) and
+    // column quad l16 % 4: chunk 2E + h, h = (l16 & 3) / 2, byte (l16 & 1) * 8; with
+    // r3 = (l16 / 4) & 3 the physical chunk is 2 (E ^ r3) + h.  Blocks E = eb0 + 4m + n
+    // (eb0 a multiple of 4, or OB <= 2) sit at vbase[n] + 128 m.
+    const int eb0 = NVH == 1 ? ch * OB : 0;
+    const int r3 = (l16 >> 2) & 3;
+    uint32_t vbase[OB < 4 ? OB : 4];
+#pragma unroll
+    for (int n = 0; n < (OB < 4 ? OB : 4); ++n)
+        vbase[n] = (4 * kg + (l16 >> 2)) * (2 * DEV) + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1) +
+                   32 * ((eb0 + n) ^ r3);
+
     for (;;) {
-        if (threadIdx.x == 0) {
+        if (t == 0) {
             const int n = atomicAdd(&a.queue[xcd], 1);
             const int it = ((n / QCHUNK) * 8 + xcd) * QCHUNK + n % QCHUNK;
-            s_item = it < nitems ? it : -1;
+            *s_item = it < nitems ? it : -1;
         }
         lds_barrier();
-        const int it = s_item;
+        const int it = *s_item;
         if (it < 0) break;
         const int2 item = a.items[it];
         const int j = item.x, tq = item.y;
         const int sb = a.seg_start[j];
-        const int S = a.seg_start[j + 1] - sb;
-        const int ntok = min(kHeavyTile, S - tq);
+        const int ntok = min(kHeavyTile, a.seg_start[j + 1] - sb - tq);
         const int id = a.uniq[j];
         const int64_t r0 = a.off[id];
         const int d = (int)(a.off[id + 1] - r0);
-        switch ((d + QK_RB - 1) / QK_RB) {
-            case 1: mfma_item<VEB, 1>(a, ring, ring0, sb, tq, ntok, r0, d); break;
-            case 2: mfma_item<VEB, 2>(a, ring, ring0, sb, tq, ntok, r0, d); break;
-            case 3: mfma_item<VEB, 3>(a, ring, ring0, sb, tq, ntok, r0, d); break;
-            default: mfma_item<VEB, 4>(a, ring, ring0, sb, tq, ntok, r0, d); break;
+        const bool active = 16 * tg < ntok;
+        const int qi = 16 * tg + l16;
+        const int tok = a.perm[sb + tq + min(qi, ntok - 1)];
+
+        // x fragments: xr[f] = x[tok][32 kc + 8kg, +8) with kc = 16 (f / HW) + ch HW + f % HW
+        bf16x8_t xr[XQ];
+        if (active) {
+            const uint16_t *xp = a.x + (int64_t)tok * d_in + 32 * HW * ch + 8 * kg;
+#pragma unroll
+            for (int f = 0; f < XQ; ++f)
+                xr[f] = *reinterpret_cast<const bf16x8_t *>(xp + 32 * (16 * (f / HW) + f % HW));
+            // Take delivery of x here, before any copy of this item is in flight: the
+            // compiler's own wait for these loads would otherwise be repeated in every
+            // group and drain the copy ring (it does not count the asynchronous copies).
+#pragma unroll
+            for (int f = 0; f < XQ; ++f) __asm__ volatile("" ::"v"(xr[f]));
         }
+
+        // stage sequence: per group, nrb * nq K stages (16-row block major), then
+        // ceil(rows / RV) * NVH V stages (row block major).  The copy side walks it
+        // with a cursor (rows before the group, phase, block, part).
+        const int ng = (d + kGroup - 1) / kGroup;
+        const int rows_last = d - kGroup * (ng - 1);
+        const int NS = (ng - 1) * (8 * nq + VPG * NVH) + ((rows_last + 15) / 16) * nq +
+                       ((rows_last + RV - 1) / RV) * NVH;
+        int c_gr = 0, c_v = 0, c_b = 0, c_p = 0;
+        auto issue = [&](int st) {
+            const uint32_t base = ring0 + (uint32_t)((st % kSlots) * kSlot);
+            const int rows_g = min(kGroup, d - c_gr);
+            if (!c_v) {
+                // K rows [gr + 16b, +16), columns [512p, +512): copy c = row of the block;
+                // lane l fills chunk l of the 1 KB row with global chunk l ^ (row & 7)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int row = 4 * w + c;
+                    const int64_t grow = r0 + min(c_gr + 16 * c_b + row, d - 1);
+                    int64_t col = (int64_t)kKCols * c_p + 8 * (lane ^ (row & 7));
+                    if (col >= d_in) col = 0;  // past d_in: filler, never read
+                    async_ld16(a.WK + grow * d_in + col, base + row * 1024);
+                }
+                if (++c_p == nq) {
+                    c_p = 0;
+                    if (16 * ++c_b >= rows_g) { c_b = 0; c_v = 1; }
+                }
+            } else {
+                // V rows [gr + RV b, +RV), columns [DEV p, +DEV): copy cp holds rows
+                // [RPC cp, +RPC); chunk c of row r holds global chunk c ^ 2(r & 3)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int cp = 4 * w + c;
+                    const int row = cp * RPC + lane / CPR;
+                    const int64_t grow = r0 + min(c_gr + RV * c_b + row, d - 1);
+                    const int cc = (lane % CPR) ^ (2 * (row & 3));
+                    async_ld16(a.WV + grow * DE + DEV * c_p + 8 * cc, base + cp * 1024);
+                }
+                if (++c_p == NVH) {
+                    c_p = 0;
+                    if (RV * ++c_b >= rows_g) { c_b = 0; c_v = 0; c_gr += kGroup; }
+                }
+            }
+        };
+        int st = 0;
+        for (int i = 0; i < kSlots - 1 && i < NS; ++i) issue(i);
+        // wait for stage st, then refill the slot every wave has finished with
+        auto next_stage = [&]() -> uint32_t {
+            wait_stages<4, kSlots - 2>(min(kSlots - 2, NS - 1 - st));
+            lds_barrier();
+            if (st + kSlots - 1 < NS) issue(st + kSlots - 1);
+            const uint32_t p = (uint32_t)((st % kSlots) * kSlot);
+            ++st;
+            return p;
+        };
+        auto lds16 = [&](uint32_t byte) {
+            return *reinterpret_cast<const bf16x8_t *>(ring + byte);
+        };
+
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x4_t O[OB];
+#pragma unroll
+        for (int e = 0; e < OB; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        f32x4_t *const xw = reinterpret_cast<f32x4_t *>(xchg) + w * 8 * 64 + lane;
+        const f32x4_t *const xo = reinterpret_cast<const f32x4_t *>(xchg) + (w ^ 2) * 8 * 64 + lane;
+        for (int g = 0; g < ng; ++g) {
+            const int rows_g = g == ng - 1 ? rows_last : kGroup;
+            const int nrb = (rows_g + 15) / 16;
+            // scores of one 16-row block per iteration (two accumulator chains, even and
+            // odd fragment steps); the partial goes to this wavefront's exchange slot
+            for (int rb = 0; rb < nrb; ++rb) {
+                f32x4_t S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < nq; ++q) {
+                    const uint32_t kt = next_stage();
+                    if (active) {
+                        bf16x8_t A[HW];
+#pragma unroll
+                        for (int i = 0; i < HW; ++i)
+                            A[i] = lds16(kt + ((i & 1) ? k_odd + 64 * (i - 1) : k_even + 64 * i));
+#pragma unroll
+                        for (int i = 0; i < HW; i += 2) {
+                            S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], xr[q * HW + i], S0, 0, 0, 0);
+                            S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i + 1], xr[q * HW + i + 1], S1, 0, 0, 0);
+                        }
+                    }
+                }
+                xw[rb * 64] = S0 + S1;
+            }
+
+            // full scores: own partial plus the other column half's (row blocks past
+            // the group's rows are masked below, whatever their slots hold)
+            lds_barrier();
+            f32x4_t Sc[8];
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) Sc[rb] = xw[rb * 64] + xo[rb * 64];
+
+            // online softmax: lane holds rows 128g + 16rb + 4kg + i of token l16
+            float gm = -INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = (16 * rb + 4 * kg + i < rows_g) ? Sc[rb][i] : -INFINITY;
+                    Sc[rb][i] = v;
+                    gm = fmaxf(gm, v);
+                }
+            gm = fmaxf(gm, __shfl_xor(gm, 16));
+            gm = fmaxf(gm, __shfl_xor(gm, 32));
+            const float mn = fmaxf(m_run, gm);
+            const float al = __expf(m_run - mn);
+            m_run = mn;
+#pragma unroll
+            for (int e = 0; e < OB; ++e) O[e] *= al;
+            float ls = 0.f;
+            uint4 Pk[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float pr[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = __expf(Sc[2 * p][i] - mn);
+                    pr[4 + i] = __expf(Sc[2 * p + 1][i] - mn);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ls += pr[i];
+                Pk[p] = make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]),
+                                   pack2(pr[6], pr[7]));
+            }
+            ls += __shfl_xor(ls, 16);
+            ls += __shfl_xor(ls, 32);
+            l_run = fmaf(l_run, al, ls);
+
+            // values: V stage (vr, vh) holds rows [RV vr, +RV) of the group, row-major.
+            // With two V stages per row block (d_emb 512) half ch takes stage vh = ch
+            // whole; otherwise it takes blocks [ch OB, +OB) of each.
+            const int nvr = (rows_g + RV - 1) / RV;
+            for (int vr = 0; vr < nvr; ++vr) {
+#pragma unroll
+                for (int vh = 0; vh < NVH; ++vh) {
+                    const uint32_t vt = next_stage();
+                    if (active && (NVH == 1 || vh == ch)) {
+#pragma unroll
+                        for (int kb = 0; kb < RV / 32; ++kb) {
+                            // P of rows [32 (vr RV/32 + kb), +32) of the group
+                            uint4 pk = Pk[kb];
+                            if constexpr (RV / 32 < 4) {
+#pragma unroll
+                                for (int p = 1; p < 4 * 32 / RV; ++p)
+                                    if (vr == p) pk = Pk[p * (RV / 32) + kb];
+                            }
+                            const bf16x8_t P = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+                            for (int e = 0; e < OB; ++e) {
+                                // rows 32kb + 4kg + l16/4 (first read) and 16 rows further (second)
+                                const uint32_t pa = vt + vbase[e & 3] + 128 * (e >> 2) + 64 * DEV * kb;
+                                const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) i16x4_t *)(ring + pa));
+                                const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) i16x4_t *)(ring + pa + 32 * DEV));
+                                const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+                                const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
+                                O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, P, O[e], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        if (active && qi < ntok) {
+            const float inv = 1.f / l_run;
+            uint16_t *orow = a.o + (int64_t)tok * DE + 16 * OB * ch + 4 * kg;
+#pragma unroll
+            for (int e = 0; e < OB; ++e) {
+                const uint2 u = make_uint2(pack2(O[e][0] * inv, O[e][1] * inv),
+                                           pack2(O[e][2] * inv, O[e][3] * inv));
+                *reinterpret_cast<uint2 *>(orow + e * 16) = u;
+            }
+        }
+        lds_barrier();  // the next item's copies reuse the ring and s_item
     }
 }
 
 constexpr int kHeavyBlocks = 256;   // one per CU, a multiple of 8 (XCD order)
 
-hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
+template <int XQ>
+hipError_t launch_heavy_xq(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
     switch (d_emb) {
-        case 64: hipLaunchKernelGGL((k_attn_mfma<4>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
-        case 128: hipLaunchKernelGGL((k_attn_mfma<8>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
-        case 256: hipLaunchKernelGGL((k_attn_mfma<16>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
-        case 512: hipLaunchKernelGGL((k_attn_mfma<32>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 64: hipLaunchKernelGGL((k_attn_mfma<XQ, 64>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 128: hipLaunchKernelGGL((k_attn_mfma<XQ, 128>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 256: hipLaunchKernelGGL((k_attn_mfma<XQ, 256>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
+        case 512: hipLaunchKernelGGL((k_attn_mfma<XQ, 512>), dim3(kHeavyBlocks), dim3(256), 0, s, ha); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// d_in widths the MFMA path is built for (each token's x row is held in registers)
+bool heavy_d_in(int64_t d_in) {
+    return d_in == 128 || d_in == 256 || d_in == 512 || d_in == 1024 || d_in == 2048;
+}
+
+hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
+    switch (ha.d_in) {
+        case 128: return launch_heavy_xq<2>(ha, d_emb, s);
+        case 256: return launch_heavy_xq<4>(ha, d_emb, s);
+        case 512: return launch_heavy_xq<8>(ha, d_emb, s);
+        case 1024: return launch_heavy_xq<16>(ha, d_emb, s);
+        case 2048: return launch_heavy_xq<32>(ha, d_emb, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 constexpr int kAttnBlocks = 2048;
@@ -573,8 +648,8 @@ int attn_light_tokens(int64_t d_in, int dtype) {
     return light_tokens_for<8>();
 }
 
-int attn_heavy_min_tokens(int64_t, int64_t, int dtype, int32_t) {
-    return dtype == L3_BF16 ? kHeavyMinTokens : INT32_MAX;
+int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
+    return dtype == L3_BF16 && heavy_d_in(d_in) ? kHeavyMinTokens : INT32_MAX;
 }
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t s) {

@@ -150,7 +150,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         a.light = light; a.heavy = heavy;
         a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
         a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;
-        L3_HIP_TRY(launch_attn(a, D.dtype, 1, s));
+        L3_HIP_TRY(launch_attn(a, D.dtype, heavy_min != INT32_MAX, s));
     }
     if (D.dtype == L3_BF16) {
         float *stats = ws_ptr<float>(ws, L.stats);

@@ -19,8 +19,7 @@ constexpr int kSortTile = 2048;    // keys ranked per workgroup and pass
 constexpr int kRadixBits = 9;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 features
-constexpr int kHeavyMaxD = 512;    // MFMA gather-attention keeps all d_t <= 512 scores on chip
-constexpr int kHeavyTile = 64;     // tokens per MFMA gather-attention work item
+constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
 

@@ -241,9 +241,8 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
         const int t = uniq[j];
         const int d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
         // the MFMA path takes blocks with many tokens or many rows (long row chains
-        // stall the wavefront-per-item path), up to kHeavyMaxD rows
-        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows) &&
-            d <= kHeavyMaxD)
+        // stall the wavefront-per-item path)
+        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows))
             nh = (S + kHeavyTile - 1) / kHeavyTile;
         else
             nl = (S + light_tok - 1) / light_tok;

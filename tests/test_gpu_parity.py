@@ -85,6 +85,11 @@ SMALL_BF16 = [
     ("d2048_e512", 600, 96, 2048, 512, 512, 256, 1500, 20000),
     ("d4096_e512", 400, 64, 4096, 512, 256, 256, 700, 9000),
     ("ragged_e64", 50, 200, 192, 64, 128, 64, 513, 3000),
+    # MFMA path over several 128-row softmax groups, a partial last group, and
+    # blocks longer than 512 rows, for each V stage shape (d_emb 64 / 256 / 512)
+    ("groups_d128_e64", 80, 300, 128, 64, 128, 128, 800, 8000),
+    ("groups_d256_e256_k700", 60, 700, 256, 256, 256, 128, 600, 12000),
+    ("groups_d1024_e512", 100, 260, 1024, 512, 256, 256, 700, 9000),
 ]
 
 
