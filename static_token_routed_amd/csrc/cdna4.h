@@ -46,6 +46,21 @@ __device__ inline void async_ld16(const void *gptr, uint32_t lds_base) {
                      : "memory");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base plus a 32-bit per-lane
+// byte offset (the scalar-base form of the instruction).
+__device__ inline void async_ld16_sb(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: widen through uint32_t so the low half is not sign-extended
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0v), "v"(voff), "s"(sb)
+                     : "memory");
+}
+
 // s_waitcnt vmcnt(N) (N <= 63), other counters untouched.
 template <int N>
 __device__ inline void wait_vmcnt() {

@@ -5,30 +5,32 @@
 //   out = W_mix [LN(h) ; x]  (W_mix: d_out x (d_up + d_in))
 // as bf16 MFMA GEMMs C[M x N] = A[M x K] B[N x K]^T with fp32 accumulation.
 //
-// Kernel shape (gfx950): 512 threads = 8 wavefronts in 2 x 4, each owning a
-// 128 x 64 block of a 256 x 256 output tile as 4 x 2 v_mfma_f32_32x32x16_bf16
-// accumulators (128 fp32 per lane), so two wavefronts share each SIMD and one's
-// MFMAs cover the other's LDS reads.  K advances 64 at a time.  Both operand
-// tiles (256 x 64 bf16 each) go global -> LDS by asynchronous 16-byte copies
-// (no register staging) into a double buffer: the copies of stage s+1 are in
-// flight while stage s is multiplied, and barriers wait for LDS traffic only.
-// Each 16-byte chunk of a 128-byte LDS row is XOR-swizzled by the row index
-// (the swizzle is applied to the source address, since a copy lands at a fixed
-// lane-linear LDS slot) so fragment reads of 32 consecutive rows spread over the
-// banks.  The MFMA takes the B tile as its first operand, so each lane holds 4
-// consecutive output columns of one row: the epilogue stores 8-byte segments.
-// Tiles are numbered so that the workgroups the dispatcher sends to one XCD
-// (workgroup id mod 8) form a contiguous, grouped block of tiles, sharing A
-// rows and B columns in that XCD's L2.
+// Kernel shape (gfx950): 256 threads = 4 wavefronts in 2 x 2, each owning a
+// 128 x 128 block of a 256 x 256 output tile as 8 x 8 v_mfma_f32_16x16x32_bf16
+// accumulators (256 fp32 per lane, in AGPRs): 64 MFMAs per 16 fragment reads.
+// K advances 64 columns per stage through two LDS buffers filled by
+// asynchronous global -> LDS copies (no register staging); the copies of stage
+// s + 1 are issued between stage s's MFMAs, and barriers wait for LDS traffic
+// only.  LDS rows are 128 bytes (64 bf16); 16-byte chunk c of row r sits at
+// physical chunk c ^ (r & 7) (applied to the copy's source address, since a
+// copy lands at a fixed lane-linear slot), so the 16 rows a fragment read
+// touches fall on distinct banks.  The MFMA takes the B tile as its first
+// operand, so each lane holds 4 consecutive output columns of one row: the
+// epilogue stores 8-byte segments.  Tiles are numbered so that the workgroups
+// the dispatcher sends to one XCD (workgroup id mod 8) form a contiguous,
+// grouped block of tiles, sharing A rows and B columns in that XCD's L2.
 //
-// LayerNorm and the concat [LN(h) ; x] are fused into the W_mix operand path.
-// For the first d_up columns the A tile is h, loaded into registers one stage
-// ahead, turned into (h - mean) * rstd * gamma + beta (each element once per
-// workgroup) and written into the swizzled LDS layout; mean and rstd per row
-// come from the W_up epilogue's partial statistics (per row and 64-column
+// LayerNorm and the concat [LN(h) ; x] are folded into the W_mix GEMM.  With
+// W_mix = [W1 | W2] (columns acting on LN(h) and on x), LN(h) = (h - mean) * rstd
+// * gamma + beta per row, W1' = W1 diag(gamma), c1 = W1' 1 and c2 = W1 beta:
+//   W_mix [LN(h) ; x] = rstd * (W1' h - mean * c1) + c2 + W2 x.
+// A small kernel forms W1' (bf16), c1 and c2 from W_mix, gamma and beta; the GEMM
+// then runs over [h | x] against [W1' | W2], rescales its accumulators once,
+// when the h columns are done, and adds c2 in the epilogue.  mean and rstd per
+// row come from the W_up epilogue's partial statistics (per row and 64-column
 // chunk, the mean and the sum of squared deviations of the stored bf16 values),
-// merged with Chan's pairwise update.  The remaining columns are x, copied
-// asynchronously like B.  The concatenated operand never exists in memory.
+// merged with Chan's pairwise update.  The concatenated operand never exists in
+// memory and the inner loop carries no LayerNorm arithmetic.
 #include <type_traits>
 
 #include "cdna4.h"
@@ -38,16 +40,18 @@ namespace l3 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int TILE = BM * BK * 2;          // bytes of one operand tile of a stage
+constexpr int SLOT = 2 * TILE;             // one stage (double-buffered)
 constexpr int GROUP_M = 8;
 
 struct GemmP {
     const uint16_t *A, *A2;  // A columns [0, K1) from A (row stride lda), [K1, K) from A2 (lda2)
-    const uint16_t *B;       // N x K, row stride ldb
+    const uint16_t *B, *B2;  // B columns [0, K1) from B (ldb), [K1, K) from B2 (ldb2)
     uint16_t *C;             // M x N, row stride N
-    int64_t lda, lda2, ldb, K1;
+    int64_t lda, lda2, ldb, ldb2, K1;
     int64_t M, N, K;
     const float *row_stats;  // [M x 2] (mean, rstd) of the A rows in [0, K1)  (LN_IN)
-    const float *gamma, *beta;  // [K1]                                         (LN_IN)
+    const float *c1, *c2;    // [N] LayerNorm fold terms                         (LN_IN)
     float *ln_out;           // [M x npart_out x 2] partial statistics of the stored rows
     int npart_out;
     int tiles_m, tiles_n;
@@ -69,190 +73,190 @@ __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
 }
 
 template <bool LN_IN, bool LN_OUT>
-__global__ __launch_bounds__(512, 1) void k_gemm_bf16(GemmP p) {
-    __shared__ __attribute__((aligned(1024))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Bs[2][BN * BK];
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * SLOT];
+    // LN_IN: (mean, rstd) of the tile's rows; c1, c2 of its columns
+    __shared__ float2 rowst[LN_IN ? BM : 1];
+    __shared__ float2 colc[LN_IN ? BN : 1];
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w >> 2, wn = w & 3;
-
-    // Copy mapping: wave w issues 4 copies per operand and stage; copy q covers tile
-    // rows [8q, 8q + 8) (1 KB of LDS).  Lane l fills physical chunk l % 8 of row
-    // 8q + l / 8 with global chunk (l % 8) ^ (row & 7).  Rows past M (N) are clamped:
-    // they only feed accumulators that are never stored.
-    const int crow = lane >> 3, cphys = lane & 7;
-    const uint32_t a_lds0 = lds_addr(&As[0][0]), b_lds0 = lds_addr(&Bs[0][0]);
-    auto issue = [&](int64_t k0, int buf, bool a_async) {
-        const bool first = k0 < p.K1;
-        const uint16_t *abase = first ? p.A + k0 : p.A2 + (k0 - p.K1);
-        const int64_t lda = first ? p.lda : p.lda2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = w * 4 + i;
-            const int row = q * 8 + crow;
-            const int gch = cphys ^ (row & 7);
-            const int64_t ar = min<int64_t>(m0 + row, p.M - 1);
-            const int64_t br = min<int64_t>(n0 + row, p.N - 1);
-            const uint32_t off = (uint32_t)(buf * BM * BK * 2 + q * 1024);
-            if (a_async) async_ld16(abase + ar * lda + gch * 8, a_lds0 + off);
-            async_ld16(p.B + br * p.ldb + k0 + gch * 8, b_lds0 + off);
-        }
-    };
-
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    // LayerNorm staging (LN_IN): thread t owns chunk t % 8 of tile rows t / 8 + 64 i
-    const int sc = t & 7, sr = t >> 3;
-    float mu[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (LN_IN) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t m = min<int64_t>(m0 + sr + 64 * i, p.M - 1);
-            mu[i] = p.row_stats[2 * m];
-            rs[i] = p.row_stats[2 * m + 1];
-        }
-    }
-    uint4 hreg[4];
-    float4 gam0, gam1, bet0, bet1;
-    auto load_h = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t m = min<int64_t>(m0 + sr + 64 * i, p.M - 1);
-            hreg[i] = *reinterpret_cast<const uint4 *>(p.A + m * p.lda + k0 + sc * 8);
-        }
-        gam0 = *reinterpret_cast<const float4 *>(p.gamma + k0 + sc * 8);
-        gam1 = *reinterpret_cast<const float4 *>(p.gamma + k0 + sc * 8 + 4);
-        bet0 = *reinterpret_cast<const float4 *>(p.beta + k0 + sc * 8);
-        bet1 = *reinterpret_cast<const float4 *>(p.beta + k0 + sc * 8 + 4);
-    };
-    auto store_h = [&](int buf) {  // y = (h - mean) * rstd * gamma + beta, into the swizzled tile
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = sr + 64 * i;
-            uint4 u = hreg[i];
-            const float m_ = mu[i], r_ = rs[i];
-            u.x = pack2((bf_lo(u.x) - m_) * r_ * gam0.x + bet0.x, (bf_hi(u.x) - m_) * r_ * gam0.y + bet0.y);
-            u.y = pack2((bf_lo(u.y) - m_) * r_ * gam0.z + bet0.z, (bf_hi(u.y) - m_) * r_ * gam0.w + bet0.w);
-            u.z = pack2((bf_lo(u.z) - m_) * r_ * gam1.x + bet1.x, (bf_hi(u.z) - m_) * r_ * gam1.y + bet1.y);
-            u.w = pack2((bf_lo(u.w) - m_) * r_ * gam1.z + bet1.z, (bf_hi(u.w) - m_) * r_ * gam1.w + bet1.w);
-            *reinterpret_cast<uint4 *>(&As[buf][r * BK + ((sc ^ (r & 7)) * 8)]) = u;
-        }
-    };
-
-    // Fragments of k-substep kk (16 columns): A rows wm*128 + i*32 + lane%32 and B rows
-    // wn*64 + j*32 + lane%32, 8 columns each (chunk 2kk + lane/32 of the 128-byte row).
-    auto load_frags = [&](int buf, int kk, bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
-        const uint16_t *as = As[buf];
-        const uint16_t *bs = Bs[buf];
-        const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + i * 32 + (lane & 31);
-            fa[i] = *reinterpret_cast<const bf16x8_t *>(&as[r * BK + ((ch ^ (r & 7)) * 8)]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = wn * 64 + j * 32 + (lane & 31);
-            fb[j] = *reinterpret_cast<const bf16x8_t *>(&bs[r * BK + ((ch ^ (r & 7)) * 8)]);
-        }
-    };
-    auto compute = [&](int buf) {
-        bf16x8_t fa[2][4], fb[2][2];
-        load_frags(buf, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1;
-            // the next substep's fragments are read while this substep's MFMAs run
-            if (kk < 3) load_frags(buf, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-        }
-    };
-    // Pipelined stages: wait for this stage's copies (the only loads in flight), start
-    // the next stage's, multiply; an h stage is staged through registers and written
-    // (normalised) into the other buffer after the multiply.
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const uint32_t ring0 = lds_addr(ring);
     const int nst = (int)(p.K / BK);
-    const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages whose A operand is normalised h
-    if (0 < nst1) {
-        load_h(0);
-        issue(0, 0, false);
-        store_h(0);
-    } else {
-        issue(0, 0, true);
+    const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages over the h columns
+
+    // Copies: 32 per operand and stage, 1 KB = 8 rows x 128 bytes each; wave w issues
+    // q = 8w + i.  Lane l fills row 8q + l/8, physical chunk l % 8, with global chunk
+    // (l % 8) ^ (l / 8) (= row & 7).  Rows past M (N) are clamped: they only feed
+    // accumulators that are never stored.  With LN_IN the columns [K1, K) come from
+    // A2 and B2, addressed as a wave-uniform tile base plus a 32-bit lane offset.
+    const int gch = (lane & 7) ^ (lane >> 3);
+    const uint16_t *srcA[8], *srcB[8];
+    uint32_t offA2[LN_IN ? 8 : 1], offB2[LN_IN ? 8 : 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (8 * w + i) + (lane >> 3);
+        const int64_t ra = min<int64_t>(m0 + row, p.M - 1), rb = min<int64_t>(n0 + row, p.N - 1);
+        srcA[i] = p.A + ra * p.lda + gch * 8;
+        srcB[i] = p.B + rb * p.ldb + gch * 8;
+        if constexpr (LN_IN) {
+            offA2[i] = (uint32_t)((ra - m0) * p.lda2 * 2 + gch * 16);
+            offB2[i] = (uint32_t)((rb - n0) * p.ldb2 * 2 + gch * 16);
+        }
     }
-    for (int st = 0; st < nst; ++st) {
+    const uint16_t *tileA2 = p.A2 + m0 * p.lda2 - p.K1, *tileB2 = p.B2 + n0 * p.ldb2 - p.K1;
+    // half h (copies 4h .. 4h + 3 of each operand) of stage st's copies
+    auto issue_half = [&](int st, int h) {
+        const int64_t k0 = (int64_t)st * BK;
+        const uint32_t base = ring0 + (uint32_t)((st & 1) * SLOT);
+        const bool first = !LN_IN || st < nst1;
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i) {
+            const uint32_t off = (uint32_t)((8 * w + i) * 1024);
+            if (first) {
+                async_ld16(srcA[i] + k0, base + off);
+                async_ld16(srcB[i] + k0, base + TILE + off);
+            } else if constexpr (LN_IN) {
+                async_ld16_sb(tileA2 + k0, offA2[i], base + off);
+                async_ld16_sb(tileB2 + k0, offB2[i], base + TILE + off);
+            }
+        }
+    };
+
+    f32x4_t acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment of 16-row block rb, 32-column step ks: row 16rb + (l & 15) of the wave's
+    // rows, logical chunk 4ks + l/16, at physical chunk (4ks + l/16) ^ (l & 7).
+    uint32_t fA[2], fB[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t c = 16 * ((4 * ks + (lane >> 4)) ^ (lane & 7));
+        fA[ks] = (uint32_t)(wm * 128 + (lane & 15)) * 128 + c;
+        fB[ks] = TILE + (uint32_t)(wn * 128 + (lane & 15)) * 128 + c;
+    }
+    auto load_frags = [&](int st, int ks, bf16x8_t (&fa)[8], bf16x8_t (&fb)[8]) {
+        const unsigned char *sb = ring + (st & 1) * SLOT;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            fa[r] = *reinterpret_cast<const bf16x8_t *>(sb + fA[ks] + 2048 * r);
+            fb[r] = *reinterpret_cast<const bf16x8_t *>(sb + fB[ks] + 2048 * r);
+        }
+    };
+
+    if constexpr (LN_IN) {
+        // written before any copy is in flight; the first barrier publishes them
+        const int64_t m = min<int64_t>(m0 + t, p.M - 1), n = min<int64_t>(n0 + t, p.N - 1);
+        rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
+        colc[t] = make_float2(p.c1[n], p.c2[n]);
+    }
+    // after the h columns: acc = rstd * (acc - mean * c1) per element
+    auto fold = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float2 st2 = rowst[wm * 128 + 16 * i + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&colc[wn * 128 + 16 * j + 4 * (lane >> 4)]);
+                const float4 c4b = *reinterpret_cast<const float4 *>(&colc[wn * 128 + 16 * j + 4 * (lane >> 4) + 2]);
+                acc[i][j][0] = st2.y * (acc[i][j][0] - st2.x * c4.x);
+                acc[i][j][1] = st2.y * (acc[i][j][1] - st2.x * c4.z);
+                acc[i][j][2] = st2.y * (acc[i][j][2] - st2.x * c4b.x);
+                acc[i][j][3] = st2.y * (acc[i][j][3] - st2.x * c4b.z);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one 16-row block at a time: few live VGPRs
+        }
+    };
+
+    // Double-buffered stages: wait for this stage's copies (the only global loads in
+    // flight), read the first 32-column step's fragments, then per step: read the
+    // next step's fragments, issue half of the next stage's copies, run the MFMAs
+    // (the scheduling barrier keeps the reads ahead of the MFMAs that hide them).
+    auto stage = [&](int st) {
         wait_vmcnt<0>();
         lds_barrier();
-        const bool next = st + 1 < nst;
-        const bool next_h = st + 1 < nst1;
-        if (next) {
-            if (next_h) load_h((int64_t)(st + 1) * BK);
-            issue((int64_t)(st + 1) * BK, (st + 1) & 1, !next_h);
+        bf16x8_t fa[2][8], fb[2][8];
+        load_frags(st, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 0) load_frags(st, 1, fa[1], fb[1]);
+            if (st + 1 < nst) issue_half(st + 1, ks);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        compute(st & 1);
-        if (next_h) store_h((st + 1) & 1);
-    }
+    };
+    issue_half(0, 0);
+    issue_half(0, 1);
+    // LN_IN: the h stages, the rescale, then the x stages (the copies of the first x
+    // stage are already in flight when the rescale runs)
+    for (int st = 0; st < nst1; ++st) stage(st);
+    if constexpr (LN_IN) fold();
+    for (int st = nst1; st < nst; ++st) stage(st);
 
-    // Epilogue.  acc[i][j] element e of lane l: output row m = m0 + wm*128 + i*32 + (l&31),
-    // column n = n0 + wn*64 + j*32 + 8*(e/4) + 4*(l/32) + (e%4).
-    const int64_t nbase = n0 + wn * 64;
+    // Epilogue.  acc[i][j] element e of lane l: row m0 + wm*128 + 16i + (l & 15),
+    // column n0 + wn*128 + 16j + 4(l/16) + e.
+    const int64_t nbase = n0 + wn * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
-        float hv[2][16];
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t n = nbase + j * 32 + 8 * g + 4 * (lane >> 5);
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                const uint32_t lo = pack2(v0, v1), hi = pack2(v2, v3);
-                if (m < p.M && n < p.N)
-                    *reinterpret_cast<uint2 *>(p.C + m * p.N + n) = make_uint2(lo, hi);
-                if constexpr (LN_OUT) {
-                    const bool ok = n < p.N;
-                    hv[j][4 * g + 0] = ok ? bf_lo(lo) : 0.f;
-                    hv[j][4 * g + 1] = ok ? bf_hi(lo) : 0.f;
-                    hv[j][4 * g + 2] = ok ? bf_lo(hi) : 0.f;
-                    hv[j][4 * g + 3] = ok ? bf_hi(hi) : 0.f;
-                }
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
+            if constexpr (LN_IN) {
+                const float2 *cc = &colc[wn * 128 + 16 * j + 4 * (lane >> 4)];
+                acc[i][j][0] += cc[0].y;
+                acc[i][j][1] += cc[1].y;
+                acc[i][j][2] += cc[2].y;
+                acc[i][j][3] += cc[3].y;
             }
+            if (m < p.M && n < p.N)
+                *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
+                    make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+        }
         if constexpr (LN_OUT) {
-            // partial statistics of this row over the wavefront's 64 columns
-            const int64_t width = min<int64_t>(kLnPart, p.N - nbase);
-            if (width > 0) {
-                float s = 0.f;
+            // partial statistics of this row's stored (bf16) values over each 64
+            // columns (4 blocks of 16)
+            auto stored = [&](int j, int e) {
+                const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
+                return n < p.N ? __uint_as_float(f2bf(acc[i][j][e]) << 16) : 0.f;
+            };
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int part = 0; part < 2; ++part) {
+                const int64_t c0 = nbase + 64 * part;
+                const int64_t width = min<int64_t>(kLnPart, p.N - c0);
+                if (width <= 0) continue;
+                float sum = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) s += hv[j][e];
-                s += __shfl_xor(s, 32);
-                const float mean = s / (float)width;
+                for (int j = 4 * part; j < 4 * part + 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum += stored(j, e);
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                const float mean = sum / (float)width;
                 float q = 0.f;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 4 * part; j < 4 * part + 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int64_t n = nbase + j * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-                        const float dv = hv[j][e] - mean;
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
+                        const float dv = stored(j, e) - mean;
                         q += n < p.N ? dv * dv : 0.f;
                     }
+                q += __shfl_xor(q, 16);
                 q += __shfl_xor(q, 32);
-                if (lane < 32 && m < p.M) {
-                    float *dst = p.ln_out + (m * p.npart_out + nbase / kLnPart) * 2;
+                if (lane < 16 && m < p.M) {
+                    float *dst = p.ln_out + (m * p.npart_out + c0 / kLnPart) * 2;
                     dst[0] = mean;
                     dst[1] = q;
                 }
@@ -359,10 +363,56 @@ __global__ __launch_bounds__(256) void k_ln_stats_f32(const float *__restrict__ 
     }
 }
 
+// LayerNorm fold terms of W_mix (one workgroup per output row n):
+// W1'[n][k] = bf16(W_mix[n][k] * gamma[k]) for k < d_up, c1[n] = sum_k W1'[n][k],
+// c2[n] = sum_k W_mix[n][k] * beta[k]  (fp32 sums).
+__global__ __launch_bounds__(256) void k_mix_fold(const uint16_t *__restrict__ W_mix,
+                                                  const float *__restrict__ gamma,
+                                                  const float *__restrict__ beta, int64_t d_up,
+                                                  int64_t ld, uint16_t *__restrict__ w1p,
+                                                  float *__restrict__ c1, float *__restrict__ c2) {
+    __shared__ float red[2][4];
+    const int64_t n = blockIdx.x;
+    const uint16_t *row = W_mix + n * ld;
+    float s1 = 0.f, s2 = 0.f;
+    for (int64_t k = 8 * threadIdx.x; k < d_up; k += 8 * 256) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(row + k);
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float w0 = bf_lo(uu[e]), w1 = bf_hi(uu[e]);
+            o[e] = pack2(w0 * gamma[k + 2 * e], w1 * gamma[k + 2 * e + 1]);
+            s1 += bf_lo(o[e]) + bf_hi(o[e]);
+            s2 = fmaf(w0, beta[k + 2 * e], s2);
+            s2 = fmaf(w1, beta[k + 2 * e + 1], s2);
+        }
+        *reinterpret_cast<uint4 *>(w1p + n * d_up + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        s1 += __shfl_xor(s1, o);
+        s2 += __shfl_xor(s2, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = s1;
+        red[1][threadIdx.x >> 6] = s2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        c1[n] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        c2[n] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    }
+}
+
+size_t mix_fold_w1p_bytes(int64_t d_up, int64_t d_out) {
+    return ((size_t)d_out * d_up * 2 + 255) & ~(size_t)255;
+}
+
 GemmP make_plain(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N, int64_t K) {
     GemmP p{};
-    p.A = A; p.A2 = A; p.B = B; p.C = C;
-    p.lda = K; p.lda2 = K; p.ldb = K; p.K1 = K;
+    p.A = A; p.A2 = A; p.B = B; p.B2 = B; p.C = C;
+    p.lda = K; p.lda2 = K; p.ldb = K; p.ldb2 = K; p.K1 = K;
     p.M = M; p.N = N; p.K = K;
     p.tiles_m = (int)((M + BM - 1) / BM);
     p.tiles_n = (int)((N + BN - 1) / BN);
@@ -379,9 +429,9 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     if (ln_out) {
         p.ln_out = ln_out;
         p.npart_out = (int)((N + kLnPart - 1) / kLnPart);
-        hipLaunchKernelGGL((k_gemm_bf16<false, true>), grid, dim3(512), 0, s, p);
+        hipLaunchKernelGGL((k_gemm_bf16<false, true>), grid, dim3(256), 0, s, p);
     } else {
-        hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(512), 0, s, p);
+        hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }
@@ -396,19 +446,31 @@ hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float e
 
 hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
                                 const float *gamma, const float *beta, const uint16_t *W_mix,
-                                uint16_t *out, int64_t M, int64_t d_up, int64_t d_in, int64_t d_out,
-                                hipStream_t s) {
+                                uint16_t *out, void *fold_ws, int64_t M, int64_t d_up, int64_t d_in,
+                                int64_t d_out, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    GemmP p = make_plain(h, W_mix, out, M, d_out, d_up + d_in);
+    uint16_t *w1p = static_cast<uint16_t *>(fold_ws);
+    float *c1 = reinterpret_cast<float *>(static_cast<char *>(fold_ws) + mix_fold_w1p_bytes(d_up, d_out));
+    float *c2 = c1 + d_out;
+    hipLaunchKernelGGL(k_mix_fold, dim3((unsigned)d_out), dim3(256), 0, s, W_mix, gamma, beta, d_up,
+                       d_up + d_in, w1p, c1, c2);
+    GemmP p = make_plain(h, w1p, out, M, d_out, d_up + d_in);
     p.lda = d_up;
+    p.ldb = d_up;
     p.A2 = x;
     p.lda2 = d_in;
+    p.B2 = W_mix + d_up;
+    p.ldb2 = d_up + d_in;
     p.K1 = d_up;
     p.row_stats = stats;
-    p.gamma = gamma;
-    p.beta = beta;
-    hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+    p.c1 = c1;
+    p.c2 = c2;
+    hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+size_t mix_fold_bytes(int64_t d_up, int64_t d_out) {
+    return mix_fold_w1p_bytes(d_up, d_out) + (size_t)d_out * 2 * 4;
 }
 
 hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,

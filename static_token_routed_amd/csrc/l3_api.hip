@@ -163,8 +163,8 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
             StageTimer tm(3, s);
             L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
             L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, stats, gamma, beta,
-                                            (const uint16_t *)W_mix, (uint16_t *)out, n, D.d_up, D.d_in,
-                                            D.d_out, s));
+                                            (const uint16_t *)W_mix, (uint16_t *)out,
+                                            ws_ptr<char>(ws, L.fold), n, D.d_up, D.d_in, D.d_out, s));
         }
     } else {
         {
@@ -217,6 +217,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     const int64_t np = (d.d_up + kLnPart - 1) / kLnPart;
     L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
     L.stats = take((size_t)n * 2 * 4);
+    L.fold = take(d.dtype == L3_BF16 ? mix_fold_bytes(d.d_up, d.d_out) : 0);
     L.total = off;
     return L;
 }

@@ -39,6 +39,7 @@ struct WsLayout {
     size_t scores;  // fp32 path only: n x max_d
     size_t o, h, lnp;
     size_t stats;  // LayerNorm row statistics (mean, rstd)
+    size_t fold;   // LayerNorm fold of W_mix (bf16 path)
     size_t total;
     int64_t ntiles;
 };
@@ -89,11 +90,13 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
 // stats [M x 2] = (mean, 1/sqrt(var + eps)) per row from the W_up partials.
 hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float eps, float *stats,
                               hipStream_t s);
-// out = W_mix [LN(h) ; x] with LN applied to the A fragments of the first d_up columns.
+// out = W_mix [LN(h) ; x] with LayerNorm folded into the h columns of W_mix;
+// fold_ws holds the folded weights and terms (mix_fold_bytes).
 hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
                                 const float *gamma, const float *beta, const uint16_t *W_mix,
-                                uint16_t *out, int64_t M, int64_t d_up, int64_t d_in, int64_t d_out,
-                                hipStream_t s);
+                                uint16_t *out, void *fold_ws, int64_t M, int64_t d_up, int64_t d_in,
+                                int64_t d_out, hipStream_t s);
+size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
 // fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
 // separate per-row statistics pass.
 hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,
