@@ -102,6 +102,12 @@ int l3_plan_destroy(l3_plan_t plan);
 int l3_plan_info(l3_plan_t plan, int64_t *vocab, int64_t *v, int32_t *k,
                  int32_t *max_d);
 
+/* Which distinct IDs of a batch the matrix-core gather-attention takes (the rest
+ * go one wavefront per item): those with at least *min_tokens tokens in the
+ * batch or at least *min_rows rows (d_t); both are INT32_MAX when the plan's
+ * dims have no matrix-core path.  Either pointer may be NULL. */
+int l3_worklist_rule(l3_plan_t plan, int32_t *min_tokens, int32_t *min_rows);
+
 /* Bytes of device workspace l3_forward / l3_route need for up to n_max tokens
  * (0 on a bad argument).  The workspace is caller-allocated device memory,
  * 256-byte aligned; its contents need no initialisation. */
@@ -208,8 +214,11 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
  * Per-kernel timing for measurement.  While enabled, l3_forward records a
  * pair of HIP events on its stream around each of its kernel stages and
  * accumulates their elapsed time; l3_profile_read synchronises those events.
- * Stages: 0 route (sort + blocks + work lists), 1 gather-attention,
- * 2 W_up GEMM, 3 W_mix GEMM.  Not thread-safe; for benchmarking only.
+ * Stages: 0 route (sort + blocks + work lists), 1 gather-attention on the
+ * matrix cores (heavy work list), 2 gather-attention, one wavefront per item
+ * (light work list), 3 W_up GEMM, 4 W_mix preparation (LayerNorm statistics and
+ * the LayerNorm fold of W_mix), 5 W_mix GEMM.  max_stages <= 8.  Not
+ * thread-safe; for benchmarking only.
  */
 int l3_profile_enable(int enable);
 int l3_profile_read(double *ms_total, int64_t *launches, int max_stages);

@@ -45,6 +45,7 @@ _SIG = {
     "l3_plan": (ctypes.c_int, [_P, _I64, _I64, _I32, ctypes.POINTER(l3_dims_t), ctypes.POINTER(_P)]),
     "l3_plan_destroy": (ctypes.c_int, [_P]),
     "l3_plan_info": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "l3_worklist_rule": (ctypes.c_int, [_P, _P, _P]),
     "l3_workspace_size": (_SZ, [_P, _I64]),
     "l3_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "l3_route": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -118,6 +119,14 @@ def l3_plan_info(plan: int) -> dict:
     return {"vocab": vocab.value, "v": v.value, "k": k.value, "max_d": mx.value}
 
 
+def l3_worklist_rule(plan) -> tuple[int, int]:
+    """(min_tokens, min_rows): blocks with at least this many tokens or rows run on
+    the matrix-core gather-attention (INT32_MAX: no such path for these dims)."""
+    mt, mr = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.l3_worklist_rule(plan, ctypes.byref(mt), ctypes.byref(mr)), "l3_worklist_rule")
+    return mt.value, mr.value
+
+
 def l3_workspace_size(plan: int, n_max: int) -> int:
     return int(_lib.l3_workspace_size(plan, n_max))
 
@@ -180,7 +189,7 @@ def l3_profile_enable(enable: bool) -> None:
     _check(_lib.l3_profile_enable(int(bool(enable))), "l3_profile_enable")
 
 
-def l3_profile_read(stages: int = 4) -> tuple[list, list]:
+def l3_profile_read(stages: int = 6) -> tuple[list, list]:
     ms = (ctypes.c_double * stages)()
     cnt = (ctypes.c_int64 * stages)()
     _check(_lib.l3_profile_read(ctypes.addressof(ms), ctypes.addressof(cnt), stages), "l3_profile_read")

@@ -652,7 +652,13 @@ int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
     return dtype == L3_BF16 && heavy_d_in(d_in) ? kHeavyMinTokens : INT32_MAX;
 }
 
-hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t s) {
+hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {
+    HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
+                 a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.d_in, (uint16_t *)a.o};
+    return launch_heavy(ha, a.d_emb, s);
+}
+
+hipError_t launch_attn_light(const AttnArgs &a, int dtype, hipStream_t s) {
     if (dtype == L3_F32) {
         F32Args fa{(const float *)a.x, (const float *)a.WK, (const float *)a.WV, a.off, a.uniq,
                    a.seg_start, a.perm, a.hdr, a.light, a.d_in, a.d_emb, (int32_t)a.vocab,
@@ -663,12 +669,6 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t 
     LightArgs la{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
                  a.uniq, a.seg_start, a.perm, a.hdr, a.light, a.d_in, a.d_emb, (int32_t)a.vocab,
                  (uint16_t *)a.o};
-    if (use_heavy) {
-        HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
-                     a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.d_in, (uint16_t *)a.o};
-        const hipError_t e = launch_heavy(ha, a.d_emb, s);
-        if (e != hipSuccess) return e;
-    }
     const int64_t nci = (a.d_in + 511) / 512;
     if (nci <= 1) return launch_light_nci<1>(la, a.d_emb, s);
     if (nci <= 2) return launch_light_nci<2>(la, a.d_emb, s);

@@ -444,16 +444,22 @@ hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float e
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
-                                const float *gamma, const float *beta, const uint16_t *W_mix,
-                                uint16_t *out, void *fold_ws, int64_t M, int64_t d_up, int64_t d_in,
-                                int64_t d_out, hipStream_t s) {
-    if (M <= 0) return hipSuccess;
+hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const float *beta,
+                           void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
     uint16_t *w1p = static_cast<uint16_t *>(fold_ws);
     float *c1 = reinterpret_cast<float *>(static_cast<char *>(fold_ws) + mix_fold_w1p_bytes(d_up, d_out));
-    float *c2 = c1 + d_out;
     hipLaunchKernelGGL(k_mix_fold, dim3((unsigned)d_out), dim3(256), 0, s, W_mix, gamma, beta, d_up,
-                       d_up + d_in, w1p, c1, c2);
+                       d_up + d_in, w1p, c1, c1 + d_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
+                                const uint16_t *W_mix, uint16_t *out, const void *fold_ws, int64_t M,
+                                int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const uint16_t *w1p = static_cast<const uint16_t *>(fold_ws);
+    const float *c1 = reinterpret_cast<const float *>(static_cast<const char *>(fold_ws) +
+                                                      mix_fold_w1p_bytes(d_up, d_out));
     GemmP p = make_plain(h, w1p, out, M, d_out, d_up + d_in);
     p.lda = d_up;
     p.ldb = d_up;
@@ -464,7 +470,7 @@ hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const floa
     p.K1 = d_up;
     p.row_stats = stats;
     p.c1 = c1;
-    p.c2 = c2;
+    p.c2 = c1 + d_out;
     hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
     return hipGetLastError();
 }

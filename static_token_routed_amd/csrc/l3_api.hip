@@ -142,7 +142,6 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, light_tok, light, heavy, s));
     }
     {
-        StageTimer tm(1, s);
         AttnArgs a{};
         a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
         a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
@@ -150,30 +149,43 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         a.light = light; a.heavy = heavy;
         a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
         a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;
-        L3_HIP_TRY(launch_attn(a, D.dtype, heavy_min != INT32_MAX, s));
+        if (heavy_min != INT32_MAX) {
+            StageTimer tm(1, s);
+            L3_HIP_TRY(launch_attn_heavy(a, s));
+        }
+        {
+            StageTimer tm(2, s);
+            L3_HIP_TRY(launch_attn_light(a, D.dtype, s));
+        }
     }
     if (D.dtype == L3_BF16) {
         float *stats = ws_ptr<float>(ws, L.stats);
+        void *fold = ws_ptr<char>(ws, L.fold);
         {
-            StageTimer tm(2, s);
+            StageTimer tm(3, s);
             L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h, n,
                                         D.d_up, D.d_emb, lnp, s));
         }
         {
-            StageTimer tm(3, s);
+            StageTimer tm(4, s);
             L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
-            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, stats, gamma, beta,
-                                            (const uint16_t *)W_mix, (uint16_t *)out,
-                                            ws_ptr<char>(ws, L.fold), n, D.d_up, D.d_in, D.d_out, s));
+            L3_HIP_TRY(launch_mix_fold((const uint16_t *)W_mix, gamma, beta, fold, D.d_up, D.d_in,
+                                       D.d_out, s));
+        }
+        {
+            StageTimer tm(5, s);
+            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, stats,
+                                            (const uint16_t *)W_mix, (uint16_t *)out, fold, n, D.d_up,
+                                            D.d_in, D.d_out, s));
         }
     } else {
         {
-            StageTimer tm(2, s);
+            StageTimer tm(3, s);
             L3_HIP_TRY(launch_gemm_f32((const float *)o, (const float *)W_up, (float *)h, n, D.d_up,
                                        D.d_emb, s));
         }
         {
-            StageTimer tm(3, s);
+            StageTimer tm(5, s);
             L3_HIP_TRY(launch_gemm_mix_f32((const float *)h, (const float *)x, lnp, gamma, beta, D.eps,
                                            (const float *)W_mix, (float *)out, n, D.d_up, D.d_in,
                                            D.d_out, s));
@@ -291,6 +303,14 @@ int l3_plan_info(l3_plan_t p, int64_t *vocab, int64_t *v, int32_t *k, int32_t *m
     if (v) *v = p->v;
     if (k) *k = p->k;
     if (max_d) *max_d = p->max_d;
+    return L3_OK;
+}
+
+int l3_worklist_rule(l3_plan_t p, int32_t *min_tokens, int32_t *min_rows) {
+    if (!p) return L3_ERR_INVALID_ARG;
+    const int hm = attn_heavy_min_tokens(p->dims.d_in, p->dims.d_emb, p->dims.dtype, p->max_d);
+    if (min_tokens) *min_tokens = hm;
+    if (min_rows) *min_rows = hm == INT32_MAX ? INT32_MAX : kHeavyMinRows;
     return L3_OK;
 }
 

@@ -80,7 +80,10 @@ struct AttnArgs {
 };
 int attn_light_tokens(int64_t d_in, int dtype);   // tokens per light work item
 int attn_heavy_min_tokens(int64_t d_in, int64_t d_emb, int dtype, int32_t max_d);  // INT32_MAX = none
-hipError_t launch_attn(const AttnArgs &a, int dtype, int use_heavy, hipStream_t s);
+// the MFMA kernel over the heavy work list (bf16, when attn_heavy_min_tokens allows it),
+// and the wavefront-per-item kernel over the light list (any dtype)
+hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_light(const AttnArgs &a, int dtype, hipStream_t s);
 
 // out[M x N] = A[M x K] B[N x K]^T, bf16 in / bf16 out, fp32 accumulate.
 // Optional LayerNorm partial statistics of the stored (bf16-rounded) rows of C
@@ -93,9 +96,11 @@ hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float e
 // out = W_mix [LN(h) ; x] with LayerNorm folded into the h columns of W_mix;
 // fold_ws holds the folded weights and terms (mix_fold_bytes).
 hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const float *stats,
-                                const float *gamma, const float *beta, const uint16_t *W_mix,
-                                uint16_t *out, void *fold_ws, int64_t M, int64_t d_up, int64_t d_in,
-                                int64_t d_out, hipStream_t s);
+                                const uint16_t *W_mix, uint16_t *out, const void *fold_ws, int64_t M,
+                                int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
+// the fold terms of W_mix (W1' = W1 diag(gamma), c1, c2) into fold_ws
+hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const float *beta,
+                           void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
 // fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
 // separate per-row statistics pass.
