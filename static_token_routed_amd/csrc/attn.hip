@@ -298,8 +298,9 @@ struct HeavyArgs {
     const uint16_t *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
-    int32_t *queue;  // 8 per-XCD work counters (zeroed with the header)
-    const int2 *items;
+    int32_t *queue;  // 8 per-XCD work counters, then the dense items' counter (zeroed with the header)
+    const int2 *items;   // streaming items (ID block, first token), 32 tokens
+    const int2 *dense;   // dense items, 128 tokens, d_t <= 512; taken before the others
     int64_t d_in;
     uint16_t *o;
 };
@@ -323,6 +324,174 @@ __device__ inline void wait_stages(int later) {
     }
 }
 
+// Dense work item: one ID with up to 64 tokens (kDenseTile) and d_t <= 512 rows, so
+// that the rows of the IDs that fill most of a batch are read once per 64 tokens
+// (instead of once per 32).  Wavefront w owns tokens [16w, 16w + 16) and all rows.
+// Scores: the d_in columns stream in 64-column stages (the K rows' chunk, 512 x 64,
+// and the gathered x rows' chunk, 64 x 64: 72 KB, double-buffered) into 32
+// accumulators of v_mfma_f32_16x16x32_bf16 per wavefront, so the softmax is exact.
+// Values: V rows stream in 64-row stages, read transposed, into DE/16 accumulators.
+template <int XQ, int DE>
+__device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *lds, uint32_t lds0,
+                                           int sb, int tq, int ntok, int64_t r0, int d, int w) {
+    constexpr int64_t d_in = 64 * XQ;
+    constexpr int NKC = XQ;                  // 64-column stages over d_in
+    constexpr int KT = 512 * 128;            // K chunk: 512 rows x 128 bytes
+    constexpr int SST = KT + 64 * 128;       // + x chunk: 64 tokens x 128 bytes (72 KB)
+    constexpr int VROWS = 64;                // V rows per values stage
+    constexpr int VST = VROWS * DE * 2;      // <= 64 KB
+    constexpr int VCP = VST / 1024 / 4;      // V copies per wavefront and stage
+    constexpr int RPC = 512 / DE;            // V rows per 1 KB copy
+    constexpr int CPR = DE / 8;              // 16-byte chunks per V row
+    constexpr int OE = DE / 16;              // 16-column output blocks
+    static_assert(VCP >= 1 && CPR >= 8 && VST <= SST && 2 * SST <= kSlots * kSlot + kXchg, "stages");
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int nvs = (d + VROWS - 1) / VROWS; // values stages
+
+    // every wavefront has read the item index before the LDS is overwritten
+    lds_barrier();
+
+    // Copies of a scores stage: K rows [8q, 8q + 8) for q = 16w + i (rows past d_t
+    // repeat row d_t - 1), x rows of tokens [8q, 8q + 8) for q = 2w + i; lane l fills
+    // chunk l % 8 of row 8q + l / 8 with global chunk (l % 8) ^ (l / 8).
+    const int gch = (lane & 7) ^ (lane >> 3);
+    uint32_t koff[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (16 * w + i) + (lane >> 3);
+        koff[i] = (uint32_t)(min(row, d - 1) * d_in * 2 + gch * 16);
+    }
+    const uint16_t *xsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tk = 8 * (2 * w + i) + (lane >> 3);
+        xsrc[i] = a.x + (int64_t)a.perm[sb + tq + min(tk, ntok - 1)] * d_in + gch * 8;
+    }
+    const uint16_t *kbase = a.WK + r0 * d_in;
+    auto issue_qk = [&](int c) {
+        const uint32_t base = lds0 + (uint32_t)((c & 1) * SST);
+        const int64_t col = (int64_t)c * 64;
+        const uint32_t kb = base + 16 * w * 1024, xb = base + KT + 2 * w * 1024;
+        static_for<16>([&](auto i) { async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb); });
+        static_for<2>([&](auto i) { async_ld16_o<i * 1024>(xsrc[i] + col, xb); });
+    };
+    // Copies of values stage g into slot (NKC + g) & 1: rows [64g, 64g + 64) (past d_t
+    // repeat row d_t - 1); copy q = VCP w + i holds rows [RPC q, +RPC); chunk c of
+    // row r holds global chunk c ^ 2 (r & 3).
+    auto issue_v = [&](int g) {
+        const uint32_t base = lds0 + (uint32_t)(((NKC + g) & 1) * SST) + VCP * w * 1024;
+        static_for<VCP>([&](auto i) {
+            const int q = VCP * w + i;
+            const int row = RPC * q + lane / CPR;
+            const int64_t grow = r0 + min(VROWS * g + row, d - 1);
+            const int cc = (lane % CPR) ^ (2 * (row & 3));
+            async_ld16_o<i * 1024>(a.WV + grow * DE + 8 * cc, base);
+        });
+    };
+
+    // fragment addresses: row (or token) 16b + (l & 15), chunk (4ks + l/16) ^ (l & 7)
+    uint32_t fofs[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) fofs[ks] = (uint32_t)l16 * 128 + 16 * ((4 * ks + kg) ^ (lane & 7));
+
+    f32x4_t S[32];
+#pragma unroll
+    for (int rb = 0; rb < 32; ++rb) S[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    issue_qk(0);
+    for (int c = 0; c < NKC; ++c) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (c + 1 < NKC) issue_qk(c + 1);
+        else issue_v(0);  // the first values stage overlaps the last scores stage and the softmax
+        const unsigned char *st = lds + (c & 1) * SST;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t xb = *reinterpret_cast<const bf16x8_t *>(st + KT + (16 * w) * 128 + fofs[ks]);
+            // all 32 row blocks: rows past d_t are copies of row d_t - 1, masked below
+#pragma unroll
+            for (int rb = 0; rb < 32; ++rb) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(st + rb * 2048 + fofs[ks]);
+                S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xb, S[rb], 0, 0, 0);
+            }
+        }
+    }
+
+    // exact softmax per token over its d_t rows: lane holds rows 16rb + 4kg + i of
+    // token 16w + l16 (scores are only read, never rewritten)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 32; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (16 * rb + 4 * kg + i < d) mx = fmaxf(mx, S[rb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    uint4 Pk[16];
+    float ls = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = (32 * p + 4 * kg + i < d) ? __expf(S[2 * p][i] - mx) : 0.f;
+            pr[4 + i] = (32 * p + 16 + 4 * kg + i < d) ? __expf(S[2 * p + 1][i] - mx) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ls += pr[i];
+        Pk[p] = make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]),
+                           pack2(pr[6], pr[7]));
+    }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    const float inv = 1.f / ls;
+
+    // values: O^T (DE x 16 tokens) += V^T P^T per 32-row block kb of each stage
+    const int r3 = (l16 >> 2) & 3;
+    uint32_t vbase[OE < 4 ? OE : 4];
+#pragma unroll
+    for (int n = 0; n < (OE < 4 ? OE : 4); ++n)
+        vbase[n] = (4 * kg + (l16 >> 2)) * (2 * DE) + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1) + 32 * (n ^ r3);
+    f32x4_t O[OE];
+#pragma unroll
+    for (int e = 0; e < OE; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < nvs; ++g) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (g + 1 < nvs) issue_v(g + 1);
+        const unsigned char *vt = lds + ((NKC + g) & 1) * SST;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // P of rows [64g + 32kb, +32): block p = 2g + kb
+            uint4 pk = Pk[kb];
+#pragma unroll
+            for (int gg = 1; gg < 8; ++gg)
+                if (g == gg) pk = Pk[2 * gg + kb];
+            const bf16x8_t P = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+            for (int e = 0; e < OE; ++e) {
+                const uint32_t pa = vbase[e & 3] + 128 * (e >> 2) + 64 * DE * kb;
+                const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt + pa));
+                const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt + pa + 32 * DE));
+                const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+                const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
+                O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, P, O[e], 0, 0, 0);
+            }
+        }
+    }
+    const int qi = 16 * w + l16;
+    if (qi < ntok) {
+        uint16_t *orow = a.o + (int64_t)a.perm[sb + tq + qi] * DE + 4 * kg;
+#pragma unroll
+        for (int e = 0; e < OE; ++e) {
+            const uint2 u = make_uint2(pack2(O[e][0] * inv, O[e][1] * inv), pack2(O[e][2] * inv, O[e][3] * inv));
+            *reinterpret_cast<uint2 *>(orow + e * 16) = u;
+        }
+    }
+}
+
 // XQ: x fragments (32 columns each) per lane, d_in = 64 XQ.  Each K stage's 512
 // columns (16 fragments; fewer when d_in < 512) are split in two halves of HW
 // fragments: half ch holds fragments [ch HW, ch HW + HW) of every stage, so all 4
@@ -342,14 +511,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     static_assert(CPR >= 8 && RV % 32 == 0 && (NVH == 1 || OB == 2 * (DEV / 32)), "V stage shape");
     static_assert(HW % 2 == 0 && XQ % HW == 0, "K stage split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * kSlot];
-    __shared__ __attribute__((aligned(16))) float xchg[kXchg / 4];
+    // one 160 KB allocation: the streaming ring, then the score exchange area; the
+    // dense path uses it as two 72 KB stages
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[kSlots * kSlot + kXchg];
+    unsigned char *const ring = lds_all;
+    float *const xchg = reinterpret_cast<float *>(lds_all + kSlots * kSlot);
     int *const s_item = reinterpret_cast<int *>(xchg);  // free between items
     const uint32_t ring0 = lds_addr(ring);
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) from here on
     const int tg = w & 1, ch = w >> 1;
     const int l16 = lane & 15, kg = lane >> 4;
+    const int ndense = a.hdr[HDR_NDENSE];
     const int nitems = a.hdr[HDR_NHEAVY];
     // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
     // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
@@ -377,6 +550,25 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         vbase[n] = (4 * kg + (l16 >> 2)) * (2 * DEV) + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1) +
                    32 * ((eb0 + n) ^ r3);
 
+    // dense items first (one shared counter), then the streaming items; the two loops
+    // keep the two paths' registers apart
+    for (;;) {
+        if (t == 0) {
+            const int n = atomicAdd(&a.queue[8], 1);
+            *s_item = n < ndense ? n : -1;
+        }
+        lds_barrier();
+        const int it = *s_item;
+        if (it < 0) break;
+        const int2 di = a.dense[it];
+        const int dsb = a.seg_start[di.x];
+        const int dn = min(kDenseTile, a.seg_start[di.x + 1] - dsb - di.y);
+        const int did = a.uniq[di.x];
+        const int64_t dr0 = a.off[did];
+        dense_item<XQ, DE>(a, ring, ring0, dsb, di.y, dn, dr0, (int)(a.off[did + 1] - dr0), w);
+        lds_barrier();  // the next item's copies reuse the LDS and its index slot
+    }
+    lds_barrier();  // every wavefront has read the last dense index before it is rewritten
     for (;;) {
         if (t == 0) {
             const int n = atomicAdd(&a.queue[xcd], 1);
@@ -425,14 +617,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
             if (!c_v) {
                 // K rows [gr + 16b, +16), columns [512p, +512): copy c = row of the block;
                 // lane l fills chunk l of the 1 KB row with global chunk l ^ (row & 7)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                static_for<4>([&](auto c) {
                     const int row = 4 * w + c;
                     const int64_t grow = r0 + min(c_gr + 16 * c_b + row, d - 1);
                     int64_t col = (int64_t)kKCols * c_p + 8 * (lane ^ (row & 7));
                     if (col >= d_in) col = 0;  // past d_in: filler, never read
-                    async_ld16(a.WK + grow * d_in + col, base + row * 1024);
-                }
+                    async_ld16_o<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
+                });
                 if (++c_p == nq) {
                     c_p = 0;
                     if (16 * ++c_b >= rows_g) { c_b = 0; c_v = 1; }
@@ -440,14 +631,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
             } else {
                 // V rows [gr + RV b, +RV), columns [DEV p, +DEV): copy cp holds rows
                 // [RPC cp, +RPC); chunk c of row r holds global chunk c ^ 2(r & 3)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                static_for<4>([&](auto c) {
                     const int cp = 4 * w + c;
                     const int row = cp * RPC + lane / CPR;
                     const int64_t grow = r0 + min(c_gr + RV * c_b + row, d - 1);
                     const int cc = (lane % CPR) ^ (2 * (row & 3));
-                    async_ld16(a.WV + grow * DE + DEV * c_p + 8 * cc, base + cp * 1024);
-                }
+                    async_ld16_o<c * 1024>(a.WV + grow * DE + DEV * c_p + 8 * cc, base + 4 * w * 1024);
+                });
                 if (++c_p == NVH) {
                     c_p = 0;
                     if (RV * ++c_b >= rows_g) { c_b = 0; c_v = 0; c_gr += kGroup; }
@@ -648,13 +838,18 @@ int attn_light_tokens(int64_t d_in, int dtype) {
     return light_tokens_for<8>();
 }
 
+int attn_dense_min_tokens(int64_t d_in, int64_t, int dtype) {
+    return dtype == L3_BF16 && heavy_d_in(d_in) ? kDenseMinTokens : INT32_MAX;
+}
+
 int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
     return dtype == L3_BF16 && heavy_d_in(d_in) ? kHeavyMinTokens : INT32_MAX;
 }
 
 hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {
     HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
-                 a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.d_in, (uint16_t *)a.o};
+                 a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.dense, a.d_in,
+                 (uint16_t *)a.o};
     return launch_heavy(ha, a.d_emb, s);
 }
 

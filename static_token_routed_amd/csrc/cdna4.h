@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace l3 {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -59,6 +61,40 @@ __device__ inline void async_ld16_sb(const void *sbase, uint32_t voff, uint32_t 
                      :
                      : "s"(m0v), "v"(voff), "s"(sb)
                      : "memory");
+}
+
+// Both copies with the LDS destination given as a wave-uniform base plus the
+// compile-time byte offset OFF (added to M0 inside the asm, so a run of copies
+// needs one scalar register for its destinations, not one per copy).
+template <uint32_t OFF>
+__device__ inline void async_ld16_o(const void *gptr, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    __asm__ volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(m0v), "v"(gptr), "i"(OFF)
+                     : "memory", "scc");
+}
+
+template <uint32_t OFF>
+__device__ inline void async_ld16_sbo(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    __asm__ volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0v), "v"(voff), "s"(sb), "i"(OFF)
+                     : "memory", "scc");
+}
+
+// compile-time loop: f(std::integral_constant<int, I>) for I in [0, N)
+template <int N, int I = 0, typename F>
+__device__ inline void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 // s_waitcnt vmcnt(N) (N <= 63), other counters untouched.

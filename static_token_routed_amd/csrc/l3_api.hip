@@ -129,24 +129,27 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
     int2 *light = ws_ptr<int2>(ws, L.light);
     int2 *heavy = ws_ptr<int2>(ws, L.heavy);
+    int2 *dense = ws_ptr<int2>(ws, L.dense);
     void *o = ws_ptr<char>(ws, L.o);
     void *h = ws_ptr<char>(ws, L.h);
     float *lnp = ws_ptr<float>(ws, L.lnp);
 
     const int light_tok = attn_light_tokens(D.d_in, D.dtype);
     const int heavy_min = attn_heavy_min_tokens(D.d_in, D.d_emb, D.dtype, P.max_d);
+    const int dense_min = attn_dense_min_tokens(D.d_in, D.d_emb, D.dtype);
     {
         StageTimer tm(0, s);
         L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
         L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));
-        L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, light_tok, light, heavy, s));
+        L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
+                                   heavy, dense, s));
     }
     {
         AttnArgs a{};
         a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
         a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
         a.queue = b.hdr + HDR_QUEUE;
-        a.light = light; a.heavy = heavy;
+        a.light = light; a.heavy = heavy; a.dense = dense;
         a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
         a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;
         if (heavy_min != INT32_MAX) {
@@ -222,6 +225,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.seg_start = take((n + 1) * 4);
     L.light = take(n * 8);
     L.heavy = take(n * 8);
+    L.dense = take(n * 8);
     L.scores = take(d.dtype == L3_F32 ? (size_t)n * std::max(max_d, 1) * 4 : 0);
     const size_t es = esize(d.dtype);
     L.o = take((size_t)n * d.d_emb * es);
@@ -358,8 +362,9 @@ int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_byt
     b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
     L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
     L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
-    L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, 1, ws_ptr<int2>(ws, L.light),
-                               ws_ptr<int2>(ws, L.heavy), s));
+    L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
+                               ws_ptr<int2>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
+                               ws_ptr<int2>(ws, L.dense), s));
     const size_t nb = (size_t)n * 4;
     auto cp = [&](int32_t *dst, const int32_t *src, size_t bytes) -> hipError_t {
         return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;

@@ -22,9 +22,13 @@ constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 feat
 constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
+constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
+constexpr int kDenseMinTokens = 48;  // blocks with at least this many tokens ...
+constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense items
 
 // Workspace header (int32 words), zeroed at the start of every call.
-enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_QUEUE = 8, HDR_WORDS = 64 };
+enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_QUEUE = 8,
+       HDR_WORDS = 64 };
 
 struct Dims {
     int64_t d_in, d_emb, d_up, d_out;
@@ -35,7 +39,7 @@ struct Dims {
 // Byte offsets of the workspace regions for n_max tokens.
 struct WsLayout {
     size_t hdr, keys_a, vals_a, keys_b, vals_b, rank, hist, tile_cnt;
-    size_t inv_perm, uniq, counts, seg_start, light, heavy;
+    size_t inv_perm, uniq, counts, seg_start, light, heavy, dense;
     size_t scores;  // fp32 path only: n x max_d
     size_t o, h, lnp;
     size_t stats;  // LayerNorm row statistics (mean, rstd)
@@ -63,16 +67,19 @@ hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s);
 hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs &b, int64_t ntiles,
                         hipStream_t s);
 // Work lists for the gather-attention kernels (reads the route outputs).
+// Blocks go to the dense list (>= dense_min_tokens tokens, d_t <= kDenseMaxD, items of
+// kDenseTile tokens), else the heavy list (>= heavy_min_tokens tokens or >= kHeavyMinRows
+// rows, items of kHeavyTile tokens), else the light list (items of light_tokens tokens).
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
-                           int heavy_min_tokens, int light_tokens, int2 *light, int2 *heavy,
-                           hipStream_t s);
+                           int heavy_min_tokens, int dense_min_tokens, int light_tokens,
+                           int2 *light, int2 *heavy, int2 *dense, hipStream_t s);
 
 struct AttnArgs {
     const void *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
     int32_t *queue;  // per-XCD work counters of the MFMA path (in the header)
-    const int2 *light, *heavy;
+    const int2 *light, *heavy, *dense;
     int64_t n, d_in, d_emb, vocab;
     void *o;
     float *scores;  // fp32 path scratch
@@ -80,6 +87,7 @@ struct AttnArgs {
 };
 int attn_light_tokens(int64_t d_in, int dtype);   // tokens per light work item
 int attn_heavy_min_tokens(int64_t d_in, int64_t d_emb, int dtype, int32_t max_d);  // INT32_MAX = none
+int attn_dense_min_tokens(int64_t d_in, int64_t d_emb, int dtype);                  // INT32_MAX = none
 // the MFMA kernel over the heavy work list (bf16, when attn_heavy_min_tokens allows it),
 // and the wavefront-per-item kernel over the light list (any dtype)
 hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s);

@@ -227,42 +227,51 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
                                                   const int32_t *__restrict__ seg_start,
                                                   int32_t *__restrict__ counts,
                                                   const int64_t *__restrict__ off, int vocab,
-                                                  int heavy_min, int light_tok,
+                                                  int heavy_min, int dense_min, int light_tok,
                                                   int2 *__restrict__ light,
                                                   int2 *__restrict__ heavy,
+                                                  int2 *__restrict__ dense,
                                                   int32_t *__restrict__ hdr) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int m = hdr[HDR_NSEG];
     const int lane = threadIdx.x & 63;
-    int nl = 0, nh = 0, S = 0;
+    int nl = 0, nh = 0, nd = 0, S = 0;
     if (j < m) {
         S = seg_start[j + 1] - seg_start[j];
         counts[j] = S;
         const int t = uniq[j];
         const int d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
-        // the MFMA path takes blocks with many tokens or many rows (long row chains
-        // stall the wavefront-per-item path)
-        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows))
-            nh = (S + kHeavyTile - 1) / kHeavyTile;
-        else
+        // the MFMA paths take blocks with many tokens or many rows (long row chains
+        // stall the wavefront-per-item path); long blocks of short enough rows are
+        // taken in 128-token dense items, the rest in 32-token streaming items
+        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows)) {
+            if (S >= dense_min && d <= kDenseMaxD)
+                nd = (S + kDenseTile - 1) / kDenseTile;
+            else
+                nh = (S + kHeavyTile - 1) / kHeavyTile;
+        } else {
             nl = (S + light_tok - 1) / light_tok;
+        }
     }
-    // wave-inclusive scans of nl and nh
-    int sl = nl, sh = nh;
+    // wave-inclusive scans of nl, nh and nd
+    int sl = nl, sh = nh, sd = nd;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(sl, o), b = __shfl_up(sh, o);
-        if (lane >= o) { sl += a; sh += b; }
+        const int a = __shfl_up(sl, o), b = __shfl_up(sh, o), c = __shfl_up(sd, o);
+        if (lane >= o) { sl += a; sh += b; sd += c; }
     }
-    int bl = 0, bh = 0;
+    int bl = 0, bh = 0, bd = 0;
     if (lane == 63) {
         if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
         if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
+        if (sd) bd = atomicAdd(&hdr[HDR_NDENSE], sd);
     }
     bl = __shfl(bl, 63) + sl - nl;
     bh = __shfl(bh, 63) + sh - nh;
+    bd = __shfl(bd, 63) + sd - nd;
     for (int q = 0; q < nl; ++q) light[bl + q] = make_int2(j, q * light_tok);
     for (int q = 0; q < nh; ++q) heavy[bh + q] = make_int2(j, q * kHeavyTile);
+    for (int q = 0; q < nd; ++q) dense[bd + q] = make_int2(j, q * kDenseTile);
 }
 
 inline int blocks_for(int64_t n, int per) { return (int)((n + per - 1) / per); }
@@ -311,11 +320,11 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
 }
 
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
-                           int heavy_min_tokens, int light_tokens, int2 *light, int2 *heavy,
-                           hipStream_t s) {
+                           int heavy_min_tokens, int dense_min_tokens, int light_tokens,
+                           int2 *light, int2 *heavy, int2 *dense, hipStream_t s) {
     hipLaunchKernelGGL(k_worklist, dim3(blocks_for(n, 256)), dim3(256), 0, s, b.uniq, b.seg_start,
-                       b.counts, off, (int)vocab, heavy_min_tokens, light_tokens, light, heavy,
-                       b.hdr);
+                       b.counts, off, (int)vocab, heavy_min_tokens, dense_min_tokens, light_tokens,
+                       light, heavy, dense, b.hdr);
     return hipGetLastError();
 }
 
