@@ -86,6 +86,7 @@ const char *l3_strerror(int status);
  * offsets: host, vocab + 1 int64 entries; off[0] = 0, 1 <= off[t+1]-off[t] <= k,
  *          off[vocab] = v (the allocation bounds of the pages: every token gets
  *          at least one and at most k embeddings, budget v = sum d_t).
+ *          v and vocab must be below 2^31 (UNSUPPORTED otherwise).
  * dims:    host; bf16 needs d_in, d_up, d_out multiples of 64, d_in <= 4096
  *          and d_emb one of 64, 128, 256, 512; fp32 takes any positive dims.
  * plan:    out; the handle owns a device copy of the offsets (allocated on the

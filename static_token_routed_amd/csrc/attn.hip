@@ -72,7 +72,7 @@ struct LightArgs {
     const uint16_t *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
-    const int2 *items;
+    const int4 *items;  // {first sorted position, tokens, first row, d_t (-1: ID out of range)}
     int64_t d_in, d_emb;
     int32_t vocab;
     uint16_t *o;
@@ -174,17 +174,15 @@ __global__ __launch_bounds__(256) void k_attn_light_bf16(LightArgs a) {
     const int nw = gridDim.x * 4;
     const int nitems = a.hdr[HDR_NLIGHT];
     for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += nw) {
-        const int2 item = a.items[it];
-        const int j = __builtin_amdgcn_readfirstlane(item.x);
-        const int c0 = __builtin_amdgcn_readfirstlane(item.y);
-        const int sb = a.seg_start[j];
-        const int S = a.seg_start[j + 1] - sb;
-        const int nt = min(TL, S - c0);
-        const int t = a.uniq[j];
+        const int4 item = a.items[it];
+        const int p0 = __builtin_amdgcn_readfirstlane(item.x);
+        const int nt = __builtin_amdgcn_readfirstlane(item.y);
+        const int64_t r0 = __builtin_amdgcn_readfirstlane(item.z);
+        const int d = __builtin_amdgcn_readfirstlane(item.w);
         int tok[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tok[q] = q < nt ? a.perm[sb + c0 + q] : 0;
-        if (t >= a.vocab) {  // ID out of range: the flag is set, the row is zeroed
+        for (int q = 0; q < 8; ++q) tok[q] = q < nt ? a.perm[p0 + q] : 0;
+        if (d < 0) {  // ID out of range: the flag is set, the row is zeroed
             for (int q = 0; q < nt; ++q) {
                 float z[VE];
 #pragma unroll
@@ -193,8 +191,6 @@ __global__ __launch_bounds__(256) void k_attn_light_bf16(LightArgs a) {
             }
             continue;
         }
-        const int64_t r0 = a.off[t];
-        const int64_t d = a.off[t + 1] - r0;
         switch (nt) {
             case 1: light_item<NCI, VE, 1>(a, tok, r0, d, lane); break;
             case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2>(a, tok, r0, d, lane); break;
@@ -215,7 +211,7 @@ struct F32Args {
     const float *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
-    const int2 *items;
+    const int4 *items;  // as LightArgs::items, one token each
     int64_t d_in, d_emb;
     int32_t vocab, max_d;
     float *o, *scores;
@@ -226,18 +222,15 @@ __global__ __launch_bounds__(256) void k_attn_f32(F32Args a) {
     const int nw = gridDim.x * 4;
     const int nitems = a.hdr[HDR_NLIGHT];
     for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += nw) {
-        const int2 item = a.items[it];
-        const int j = item.x;
-        const int sb = a.seg_start[j];
-        const int tok = a.perm[sb + item.y];
-        const int t = a.uniq[j];
+        const int4 item = a.items[it];
+        const int tok = a.perm[item.x];
         float *o = a.o + (int64_t)tok * a.d_emb;
-        if (t >= a.vocab) {
+        if (item.w < 0) {
             for (int64_t e = lane; e < a.d_emb; e += 64) o[e] = 0.f;
             continue;
         }
-        const int64_t r0 = a.off[t];
-        const int64_t d = a.off[t + 1] - r0;
+        const int64_t r0 = item.z;
+        const int64_t d = item.w;
         const float *x = a.x + (int64_t)tok * a.d_in;
         float *sc = a.scores + (int64_t)tok * a.max_d;
         float mx = -INFINITY;
@@ -373,7 +366,11 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
         const uint32_t base = lds0 + (uint32_t)((c & 1) * SST);
         const int64_t col = (int64_t)c * 64;
         const uint32_t kb = base + 16 * w * 1024, xb = base + KT + 2 * w * 1024;
-        static_for<16>([&](auto i) { async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb); });
+        // K row groups wholly past d_t are not copied: their (stale) scores are masked,
+        // and this path waits for all of its copies (vmcnt 0), whatever their number
+        static_for<16>([&](auto i) {
+            if (8 * (16 * w + i) < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
+        });
         static_for<2>([&](auto i) { async_ld16_o<i * 1024>(xsrc[i] + col, xb); });
     };
     // Copies of values stage g into slot (NKC + g) & 1: rows [64g, 64g + 64) (past d_t

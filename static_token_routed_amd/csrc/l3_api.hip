@@ -127,7 +127,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     b.uniq = ws_ptr<int32_t>(ws, L.uniq);
     b.counts = ws_ptr<int32_t>(ws, L.counts);
     b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
-    int2 *light = ws_ptr<int2>(ws, L.light);
+    int4 *light = ws_ptr<int4>(ws, L.light);
     int2 *heavy = ws_ptr<int2>(ws, L.heavy);
     int2 *dense = ws_ptr<int2>(ws, L.dense);
     void *o = ws_ptr<char>(ws, L.o);
@@ -223,7 +223,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.uniq = take(n * 4);
     L.counts = take(n * 4);
     L.seg_start = take((n + 1) * 4);
-    L.light = take(n * 8);
+    L.light = take(n * 16);
     L.heavy = take(n * 8);
     L.dense = take(n * 8);
     L.scores = take(d.dtype == L3_F32 ? (size_t)n * std::max(max_d, 1) * 4 : 0);
@@ -261,6 +261,7 @@ int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k, const l
     if (!plan) return L3_ERR_INVALID_ARG;
     *plan = nullptr;
     if (!offsets || vocab <= 0 || v <= 0 || k < 1) return L3_ERR_INVALID_ARG;
+    if (v >= (1ll << 31) || vocab >= (1ll << 31) - 1) return L3_ERR_UNSUPPORTED;  // 32-bit row and ID indices
     if (vocab >= (1ll << 30) || v >= (1ll << 31)) return L3_ERR_UNSUPPORTED;
     int rc = validate_dims(dims);
     if (rc) return rc;
@@ -363,7 +364,7 @@ int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_byt
     L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
     L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
     L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
-                               ws_ptr<int2>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
+                               ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
                                ws_ptr<int2>(ws, L.dense), s));
     const size_t nb = (size_t)n * 4;
     auto cp = [&](int32_t *dst, const int32_t *src, size_t bytes) -> hipError_t {

@@ -23,7 +23,7 @@ constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
-constexpr int kDenseMinTokens = 48;  // blocks with at least this many tokens ...
+constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...
 constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense items
 
 // Workspace header (int32 words), zeroed at the start of every call.
@@ -69,17 +69,19 @@ hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs 
 // Work lists for the gather-attention kernels (reads the route outputs).
 // Blocks go to the dense list (>= dense_min_tokens tokens, d_t <= kDenseMaxD, items of
 // kDenseTile tokens), else the heavy list (>= heavy_min_tokens tokens or >= kHeavyMinRows
-// rows, items of kHeavyTile tokens), else the light list (items of light_tokens tokens).
+// rows, items of kHeavyTile tokens), else the light list (items of light_tokens tokens,
+// written out as {first sorted position, tokens, first row, d_t (-1: ID out of range)}).
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
                            int heavy_min_tokens, int dense_min_tokens, int light_tokens,
-                           int2 *light, int2 *heavy, int2 *dense, hipStream_t s);
+                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s);
 
 struct AttnArgs {
     const void *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
     int32_t *queue;  // per-XCD work counters of the MFMA path (in the header)
-    const int2 *light, *heavy, *dense;
+    const int4 *light;
+    const int2 *heavy, *dense;
     int64_t n, d_in, d_emb, vocab;
     void *o;
     float *scores;  // fp32 path scratch

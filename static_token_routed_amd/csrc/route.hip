@@ -228,19 +228,21 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
                                                   int32_t *__restrict__ counts,
                                                   const int64_t *__restrict__ off, int vocab,
                                                   int heavy_min, int dense_min, int light_tok,
-                                                  int2 *__restrict__ light,
+                                                  int4 *__restrict__ light,
                                                   int2 *__restrict__ heavy,
                                                   int2 *__restrict__ dense,
                                                   int32_t *__restrict__ hdr) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int m = hdr[HDR_NSEG];
     const int lane = threadIdx.x & 63;
-    int nl = 0, nh = 0, nd = 0, S = 0;
+    int nl = 0, nh = 0, nd = 0, S = 0, sb = 0, r0 = 0, d = 0;
     if (j < m) {
-        S = seg_start[j + 1] - seg_start[j];
+        sb = seg_start[j];
+        S = seg_start[j + 1] - sb;
         counts[j] = S;
         const int t = uniq[j];
-        const int d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
+        d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
+        r0 = t < vocab ? (int)off[t] : 0;
         // the MFMA paths take blocks with many tokens or many rows (long row chains
         // stall the wavefront-per-item path); long blocks of short enough rows are
         // taken in 128-token dense items, the rest in 32-token streaming items
@@ -269,7 +271,10 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     bl = __shfl(bl, 63) + sl - nl;
     bh = __shfl(bh, 63) + sh - nh;
     bd = __shfl(bd, 63) + sd - nd;
-    for (int q = 0; q < nl; ++q) light[bl + q] = make_int2(j, q * light_tok);
+    // light items carry what the kernel needs, so it starts loading rows at once
+    for (int q = 0; q < nl; ++q)
+        light[bl + q] = make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), r0,
+                                  j < m && uniq[j] < vocab ? d : -1);
     for (int q = 0; q < nh; ++q) heavy[bh + q] = make_int2(j, q * kHeavyTile);
     for (int q = 0; q < nd; ++q) dense[bd + q] = make_int2(j, q * kDenseTile);
 }
@@ -321,7 +326,7 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
 
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
                            int heavy_min_tokens, int dense_min_tokens, int light_tokens,
-                           int2 *light, int2 *heavy, int2 *dense, hipStream_t s) {
+                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s) {
     hipLaunchKernelGGL(k_worklist, dim3(blocks_for(n, 256)), dim3(256), 0, s, b.uniq, b.seg_start,
                        b.counts, off, (int)vocab, heavy_min_tokens, dense_min_tokens, light_tokens,
                        light, heavy, dense, b.hdr);
