@@ -176,17 +176,21 @@ int l3_staging_destroy(l3_staging_t staging);
 /*
  * l3_prefetch -- enqueue the copy of the K / V rows that `token_ids_host` need.
  * token_ids_host: host int32 [n] (the IDs just sampled).
- * W_K_host, W_V_host: the full tables in pinned host memory (hipHostMalloc),
- *          same dtype and layout as the device tables of l3_forward.
- * The distinct IDs are found on the host; each one's K rows and V rows (each
- * contiguous) are copied with hipMemcpyAsync on `side_stream`, followed by the
- * compact offsets and the remapped IDs; `ready_event` (may be NULL) is
- * recorded on `side_stream` after the last copy.  The caller orders the
- * staged forward after it (hipStreamWaitEvent).  The host arrays are read
- * before the call returns (token_ids_host may be reused at once); the pinned
- * tables must stay valid until the copies finish.
- * Errors: INVALID_ARG, TOKEN_RANGE (an ID outside [0, vocab); nothing is
- * enqueued), CAPACITY (more than max_tokens tokens or max_rows rows), HIP.
+ * W_K_host, W_V_host: the full tables in pinned host memory (hipHostMalloc, or
+ *          torch's pin_memory), 16-byte aligned, same dtype and layout as the
+ *          device tables of l3_forward; read-only while the staging is in use.
+ * The distinct IDs are found on the host; their compact offsets, first table
+ * rows and the remapped IDs go to the device in one hipMemcpyAsync on
+ * `side_stream`, then one kernel on the same stream reads every row of those
+ * IDs through the tables' device mapping (over PCIe) into the staging buffers.
+ * `ready_event` (may be NULL) is recorded on `side_stream` after the kernel.
+ * The caller orders the staged forward after it (hipStreamWaitEvent), and the
+ * next prefetch into the same staging after that forward.  The host arrays are
+ * read before the call returns (token_ids_host may be reused at once); the
+ * pinned tables must stay valid until the kernel finishes.
+ * Errors: INVALID_ARG (also tables without a device mapping, e.g. pageable
+ * memory), TOKEN_RANGE (an ID outside [0, vocab); nothing is enqueued),
+ * CAPACITY (more than max_tokens tokens or max_rows rows), HIP.
  */
 int l3_prefetch(l3_plan_t plan, const int32_t *token_ids_host, int64_t n,
                 const void *W_K_host, const void *W_V_host, l3_staging_t staging,

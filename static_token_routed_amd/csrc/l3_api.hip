@@ -23,11 +23,13 @@ struct l3_staging_s {
     l3_plan_t plan = nullptr;
     int64_t max_rows = 0, max_tokens = 0;
     void *d_K = nullptr, *d_V = nullptr;
-    int64_t *d_off = nullptr;   // compact CSR over the distinct IDs of one step
-    int32_t *d_ids = nullptr;   // the step's IDs remapped to [0, m)
-    int64_t *h_off = nullptr;   // pinned host mirrors of the two arrays above
-    int32_t *h_ids = nullptr;
-    hipEvent_t small_done = nullptr;  // last copy out of h_off / h_ids
+    // one step's index arrays, packed as [coff (m+1) | src (m) | ids (n)]: the compact
+    // CSR over the step's distinct IDs, each ID's first table row, and the step's IDs
+    // remapped to [0, m); built on the host in h_meta (pinned), copied to d_meta
+    char *d_meta = nullptr, *h_meta = nullptr;
+    int64_t *d_off = nullptr;  // into d_meta, for the current step
+    int32_t *d_ids = nullptr;
+    hipEvent_t small_done = nullptr;  // last copy out of h_meta
     bool small_pending = false;
     int64_t n = 0, m = 0, rows = 0, max_d = 0;
 };
@@ -400,6 +402,10 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
 
 // ---------------------------------------------------------------- decode staging
 
+static size_t staging_meta_bytes(int64_t max_tokens) {
+    return (size_t)(2 * max_tokens + 1) * sizeof(int64_t) + (size_t)max_tokens * sizeof(int32_t);
+}
+
 int l3_staging_create(l3_plan_t p, int64_t max_rows, int64_t max_tokens, l3_staging_t *out) {
     if (!p || !out || max_rows <= 0 || max_tokens <= 0) return L3_ERR_INVALID_ARG;
     *out = nullptr;
@@ -409,12 +415,11 @@ int l3_staging_create(l3_plan_t p, int64_t max_rows, int64_t max_tokens, l3_stag
     st->max_rows = max_rows;
     st->max_tokens = max_tokens;
     const size_t es = esize(p->dims.dtype);
+    const size_t meta = staging_meta_bytes(max_tokens);
     bool ok = hipMalloc(&st->d_K, max_rows * p->dims.d_in * es) == hipSuccess &&
               hipMalloc(&st->d_V, max_rows * p->dims.d_emb * es) == hipSuccess &&
-              hipMalloc(&st->d_off, (max_tokens + 1) * sizeof(int64_t)) == hipSuccess &&
-              hipMalloc(&st->d_ids, max_tokens * sizeof(int32_t)) == hipSuccess &&
-              hipHostMalloc(&st->h_off, (max_tokens + 1) * sizeof(int64_t), 0) == hipSuccess &&
-              hipHostMalloc(&st->h_ids, max_tokens * sizeof(int32_t), 0) == hipSuccess &&
+              hipMalloc(&st->d_meta, meta) == hipSuccess &&
+              hipHostMalloc(&st->h_meta, meta, 0) == hipSuccess &&
               hipEventCreateWithFlags(&st->small_done, hipEventDisableTiming) == hipSuccess;
     if (!ok) {
         l3_staging_destroy(st);
@@ -429,10 +434,8 @@ int l3_staging_destroy(l3_staging_t st) {
     if (st->small_pending && st->small_done) (void)hipEventSynchronize(st->small_done);
     if (st->d_K) (void)hipFree(st->d_K);
     if (st->d_V) (void)hipFree(st->d_V);
-    if (st->d_off) (void)hipFree(st->d_off);
-    if (st->d_ids) (void)hipFree(st->d_ids);
-    if (st->h_off) (void)hipHostFree(st->h_off);
-    if (st->h_ids) (void)hipHostFree(st->h_ids);
+    if (st->d_meta) (void)hipFree(st->d_meta);
+    if (st->h_meta) (void)hipHostFree(st->h_meta);
     if (st->small_done) (void)hipEventDestroy(st->small_done);
     delete st;
     return L3_OK;
@@ -445,6 +448,15 @@ int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
     if (n > st->max_tokens) return L3_ERR_CAPACITY;
     for (int64_t i = 0; i < n; ++i)
         if (ids[i] < 0 || ids[i] >= p->vocab) return L3_ERR_TOKEN_RANGE;
+    // the kernel reads the tables through their device mapping: they must be
+    // pinned host memory (hipHostMalloc), 16-byte aligned
+    void *WK_dev = nullptr, *WV_dev = nullptr;
+    if (hipHostGetDevicePointer(&WK_dev, const_cast<void *>(WK_host), 0) != hipSuccess ||
+        hipHostGetDevicePointer(&WV_dev, const_cast<void *>(WV_host), 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return L3_ERR_INVALID_ARG;
+    }
+    if (!aligned16({WK_host, WV_host, WK_dev, WV_dev})) return L3_ERR_INVALID_ARG;
     std::vector<int32_t> u(ids, ids + n);
     std::sort(u.begin(), u.end());
     u.erase(std::unique(u.begin(), u.end()), u.end());
@@ -457,33 +469,30 @@ int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
     }
     if (rows > st->max_rows) return L3_ERR_CAPACITY;
     hipStream_t s = (hipStream_t)side_stream;
-    // the pinned mirrors may still feed the previous step's copies
+    // the pinned mirror may still feed the previous step's copy
     if (st->small_pending) L3_HIP_TRY(hipEventSynchronize(st->small_done));
     st->small_pending = false;
-    st->h_off[0] = 0;
-    for (int64_t i = 0; i < m; ++i) st->h_off[i + 1] = st->h_off[i] + (p->h_off[u[i] + 1] - p->h_off[u[i]]);
-    for (int64_t i = 0; i < n; ++i)
-        st->h_ids[i] = (int32_t)(std::lower_bound(u.begin(), u.end(), ids[i]) - u.begin());
-    const size_t es = esize(p->dims.dtype);
-    const size_t rk = p->dims.d_in * es, rv = p->dims.d_emb * es;
-    // one copy per run of consecutive IDs (their rows are adjacent in both layouts)
-    for (int64_t i = 0; i < m;) {
-        int64_t j = i + 1;
-        while (j < m && u[j] == u[j - 1] + 1) ++j;
-        const int64_t src = p->h_off[u[i]];
-        const int64_t len = p->h_off[u[j - 1] + 1] - src;
-        const int64_t dst = st->h_off[i];
-        L3_HIP_TRY(hipMemcpyAsync((char *)st->d_K + dst * rk, (const char *)WK_host + src * rk, len * rk,
-                                  hipMemcpyHostToDevice, s));
-        L3_HIP_TRY(hipMemcpyAsync((char *)st->d_V + dst * rv, (const char *)WV_host + src * rv, len * rv,
-                                  hipMemcpyHostToDevice, s));
-        i = j;
+    int64_t *h_coff = reinterpret_cast<int64_t *>(st->h_meta);
+    int64_t *h_src = h_coff + (m + 1);
+    int32_t *h_ids = reinterpret_cast<int32_t *>(h_src + m);
+    h_coff[0] = 0;
+    for (int64_t i = 0; i < m; ++i) {
+        h_coff[i + 1] = h_coff[i] + (p->h_off[u[i] + 1] - p->h_off[u[i]]);
+        h_src[i] = p->h_off[u[i]];
     }
+    for (int64_t i = 0; i < n; ++i)
+        h_ids[i] = (int32_t)(std::lower_bound(u.begin(), u.end(), ids[i]) - u.begin());
+    int64_t *d_coff = reinterpret_cast<int64_t *>(st->d_meta);
+    st->d_off = d_coff;
+    st->d_ids = reinterpret_cast<int32_t *>(d_coff + (2 * m + 1));
     if (n > 0) {
-        L3_HIP_TRY(hipMemcpyAsync(st->d_off, st->h_off, (m + 1) * sizeof(int64_t), hipMemcpyHostToDevice, s));
-        L3_HIP_TRY(hipMemcpyAsync(st->d_ids, st->h_ids, n * sizeof(int32_t), hipMemcpyHostToDevice, s));
+        const size_t bytes = (size_t)(2 * m + 1) * sizeof(int64_t) + (size_t)n * sizeof(int32_t);
+        L3_HIP_TRY(hipMemcpyAsync(st->d_meta, st->h_meta, bytes, hipMemcpyHostToDevice, s));
         L3_HIP_TRY(hipEventRecord(st->small_done, s));
         st->small_pending = true;
+        const size_t es = esize(p->dims.dtype);
+        L3_HIP_TRY(launch_stage_rows(d_coff, d_coff + (m + 1), m, rows, WK_dev, WV_dev, st->d_K,
+                                     st->d_V, p->dims.d_in * es, p->dims.d_emb * es, s));
     }
     if (ready_event) L3_HIP_TRY(hipEventRecord((hipEvent_t)ready_event, s));
     st->n = n;

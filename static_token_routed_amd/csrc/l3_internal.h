@@ -112,6 +112,12 @@ hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const floa
 hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const float *beta,
                            void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
+// Decode staging: destination row r of the compact tables belongs to compact ID i
+// with coff[i] <= r < coff[i+1] and comes from table row src[i] + (r - coff[i]);
+// WK_dev / WV_dev are the device mappings of the pinned host tables.
+hipError_t launch_stage_rows(const int64_t *coff, const int64_t *src, int64_t m, int64_t rows,
+                             const void *WK_dev, const void *WV_dev, void *dK, void *dV,
+                             int64_t row_k_bytes, int64_t row_v_bytes, hipStream_t s);
 // fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
 // separate per-row statistics pass.
 hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,

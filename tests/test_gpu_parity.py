@@ -220,31 +220,61 @@ def test_workspace_too_small(small_cfg_gpu):
     assert e.value.code == l3.L3_ERR_CAPACITY
 
 
-def test_decode_staged_equals_resident():
+DECODE_CASES = {
+    "decode_bf16": synth.CONFIGS["decode_bf16"],
+    # rows of 320 16-byte chunks: two rounds of the staging copy, K/V seam inside one
+    "wide_bf16": dataclasses.replace(
+        synth.small("wide", vocab=5000, k=256, d_in=2048, d_emb=512, d_up=512, d_out=512,
+                    n=64, v=60000, dtype="bf16", seed=3), ids_s=1.05),
+    "decode_f32": synth.small("dec32", vocab=3000, k=96, d_in=256, d_emb=128, d_up=256,
+                              d_out=256, n=64, v=40000, dtype="f32", seed=4),
+}
+
+
+def _pinned(a, dtype):
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(a)
+    return t.pin_memory()
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_decode_staged_equals_resident(name):
     """Pinned-host tables + prefetch of the step's rows + staged forward give the
     same bits as the forward over device-resident tables."""
-    cfg = synth.CONFIGS["decode_bf16"]
+    cfg = DECODE_CASES[name]
+    print(f"decode case {name}", flush=True)
     case = make_case(cfg, ln_random=True)
     g = Gpu(case)
-    WKh = torch.from_numpy(case.WK.view(np.int16)).view(torch.bfloat16).pin_memory()
-    WVh = torch.from_numpy(case.WV.view(np.int16)).view(torch.bfloat16).pin_memory()
+    WKh, WVh = _pinned(case.WK, cfg.dtype), _pinned(case.WV, cfg.dtype)
     st = l3.l3_staging_create(g.plan.handle, 64 * cfg.k, 64)
     side = torch.cuda.Stream()
     ev = torch.cuda.Event()
     ws = g.plan.workspace(64)
-    for step in range(4):
-        ids = synth.token_ids(cfg, n=64, step=step)
-        x = dev(synth.hidden(cfg, n=64, step=step), "bf16")
-        l3.l3_prefetch(g.plan.handle, ids, 64, WKh, WVh, st, side, ev)
+    for step in range(5):
+        n = (64, 64, 1, 37, 64)[step]
+        if step == 0:  # the case's own batch, also checked against the oracle
+            ids, x = np.ascontiguousarray(case.ids, dtype=np.int32), g.x
+        else:
+            ids = synth.token_ids(cfg, n=n, step=step)
+            x = dev(synth.hidden(cfg, n=n, step=step), cfg.dtype)
+        l3.l3_prefetch(g.plan.handle, ids, n, WKh, WVh, st, side, ev)
         torch.cuda.current_stream().wait_event(ev)
-        out = torch.empty((64, cfg.d_out), dtype=torch.bfloat16, device="cuda")
-        l3.l3_forward_staged(st, x, 64, g.Wup, g.gamma, g.beta, g.Wmix, out, ws, ws.numel())
+        out = torch.empty((n, cfg.d_out), dtype=x.dtype, device="cuda")
+        l3.l3_forward_staged(st, x, n, g.Wup, g.gamma, g.beta, g.Wmix, out, ws, ws.numel())
         ref = g.forward(x=x, ids=torch.from_numpy(ids).cuda())
         assert torch.equal(out, ref), f"step {step}"
+        if step == 0:
+            err = rowwise_err(to_np(out), oracle_out(case))
+            print(f"decode {name} staged vs oracle err {err:.2e}", flush=True)
+            assert err <= case.tol
     torch.cuda.synchronize()
     with pytest.raises(l3.L3Error) as e:
         l3.l3_prefetch(g.plan.handle, np.array([cfg.vocab], np.int32), 1, WKh, WVh, st, side, ev)
     assert e.value.code == l3.L3_ERR_TOKEN_RANGE
+    # tables in pageable host memory have no device mapping: refused, nothing enqueued
+    pageable = torch.from_numpy(np.ascontiguousarray(case.WK[:16]))
+    with pytest.raises(l3.L3Error) as e:
+        l3.l3_prefetch(g.plan.handle, np.array([0], np.int32), 1, pageable, WVh, st, side, ev)
+    assert e.value.code == l3.L3_ERR_INVALID_ARG
     l3.l3_staging_destroy(st)
     g.close()
 
