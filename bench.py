@@ -364,6 +364,8 @@ def decode_bench(args, cfg, torch, l3, synth):
     g, b = (torch.from_numpy(a).cuda() for a in synth.ln_params(cfg))
     pa, pb = (dev(a) for a in synth.pre_gemm_operands(cfg))
     pc = torch.empty((cfg.pre_m, cfg.pre_n), dtype=torch.bfloat16, device="cuda")
+    pws = torch.empty(max(16, l3.l3_gemm_workspace_size(cfg.pre_m, cfg.pre_n, cfg.pre_k)),
+                      dtype=torch.uint8, device="cuda")
     plan = l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16", cfg.ln_eps)
     out = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
     ws = plan.workspace(n)
@@ -376,7 +378,7 @@ def decode_bench(args, cfg, torch, l3, synth):
         l3.l3_prefetch(plan.handle, ids[s_], n, WKh, WVh, st, side, ready)
 
     def gemm():
-        l3.l3_gemm_bf16(pa, pb, pc, cfg.pre_m, cfg.pre_n, cfg.pre_k)
+        l3.l3_gemm_bf16(pa, pb, pc, cfg.pre_m, cfg.pre_n, cfg.pre_k, pws, pws.numel())
 
     def forward():
         l3.l3_forward_staged(st, x, n, Wup, g, b, Wmix, out, ws, ws.numel())

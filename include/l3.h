@@ -206,14 +206,18 @@ int l3_forward_staged(l3_staging_t staging, const void *x, int64_t n, const void
                       void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Dense bf16 GEMM on the library's MFMA kernel: C[M x N] = A[M x K] * B[N x K]^T
+ * Dense bf16 GEMM on the library's MFMA kernels: C[M x N] = A[M x K] * B[N x K]^T
  * (both operands k-contiguous, torch Linear layout), fp32 accumulate, bf16 out.
  * Used as the decode workload's stand-in for the layers before L^3.
- * K and N must be multiples of 64.  Errors: INVALID_ARG (also a pointer not
- * 16-byte aligned), UNSUPPORTED, HIP.
+ * K and N must be multiples of 64.  Batches of up to 512 rows take a split-K
+ * kernel whose fp32 partial sums need a device workspace of
+ * l3_gemm_workspace_size(M, N, K) bytes (0 for larger M: workspace may then be
+ * NULL); the workspace is overwritten.  Errors: INVALID_ARG (also a pointer not
+ * 16-byte aligned), CAPACITY (workspace too small), UNSUPPORTED, HIP.
  */
+size_t l3_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                 void *stream);
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Per-kernel timing for measurement.  While enabled, l3_forward records a

@@ -54,7 +54,8 @@ _SIG = {
     "l3_staging_destroy": (ctypes.c_int, [_P]),
     "l3_prefetch": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _P, _P]),
     "l3_forward_staged": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "l3_gemm_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "l3_gemm_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "l3_gemm_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "l3_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "l3_profile_read": (ctypes.c_int, [_P, _P, ctypes.c_int]),
 }
@@ -181,8 +182,19 @@ def l3_forward_staged(staging, x, n, W_up, ln_gamma, ln_beta, W_mix, out, worksp
                                   _stream(stream)), "l3_forward_staged")
 
 
-def l3_gemm_bf16(A, B, C, M, N, K, stream=None) -> None:
-    _check(_lib.l3_gemm_bf16(_ptr(A), _ptr(B), _ptr(C), M, N, K, _stream(stream)), "l3_gemm_bf16")
+def l3_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(_lib.l3_gemm_workspace_size(M, N, K))
+
+
+def l3_gemm_bf16(A, B, C, M, N, K, workspace=None, workspace_bytes=None, stream=None) -> None:
+    """C = A B^T; allocates the split-K workspace (torch device memory) when none is given."""
+    if workspace is None and l3_gemm_workspace_size(M, N, K) > 0:
+        import torch
+        workspace = torch.empty(l3_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.l3_gemm_bf16(_ptr(A), _ptr(B), _ptr(C), M, N, K, _ptr(workspace), workspace_bytes,
+                             _stream(stream)), "l3_gemm_bf16")
 
 
 def l3_profile_enable(enable: bool) -> None:

@@ -163,7 +163,20 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
             L3_HIP_TRY(launch_attn_light(a, D.dtype, s));
         }
     }
-    if (D.dtype == L3_BF16) {
+    if (D.dtype == L3_BF16 && n <= kSkinnyMaxM) {
+        float *part = ws_ptr<float>(ws, L.part);
+        {
+            StageTimer tm(3, s);
+            L3_HIP_TRY(launch_gemm_skinny_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h,
+                                               n, D.d_up, D.d_emb, lnp, part, s));
+        }
+        {
+            StageTimer tm(5, s);
+            L3_HIP_TRY(launch_gemm_mix_skinny_bf16((const uint16_t *)h, (const uint16_t *)x, lnp, gamma,
+                                                   beta, D.eps, (const uint16_t *)W_mix, (uint16_t *)out,
+                                                   n, D.d_up, D.d_in, D.d_out, part, s));
+        }
+    } else if (D.dtype == L3_BF16) {
         float *stats = ws_ptr<float>(ws, L.stats);
         void *fold = ws_ptr<char>(ws, L.fold);
         {
@@ -236,6 +249,10 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
     L.stats = take((size_t)n * 2 * 4);
     L.fold = take(d.dtype == L3_BF16 ? mix_fold_bytes(d.d_up, d.d_out) : 0);
+    const int64_t ns = std::min<int64_t>(n, kSkinnyMaxM);
+    L.part = take(d.dtype == L3_BF16 ? std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
+                                                 skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in))
+                                     : 0);
     L.total = off;
     return L;
 }
@@ -390,13 +407,24 @@ int l3_status(void *ws, void *stream) {
     return flag ? L3_ERR_TOKEN_RANGE : L3_OK;
 }
 
-int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                 void *stream) {
+size_t l3_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || M > kSkinnyMaxM) return 0;
+    return skinny_part_bytes(M, N, K);
+}
+
+int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, void *ws,
+                 size_t ws_bytes, void *stream) {
     if (!A || !B || !C || M < 0 || N < 0 || K <= 0) return L3_ERR_INVALID_ARG;
     if (K % 64 || N % 64) return L3_ERR_UNSUPPORTED;
-    if (!aligned16({A, B, C})) return L3_ERR_INVALID_ARG;
-    L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)A, (const uint16_t *)B, (uint16_t *)C, M, N, K,
-                                nullptr, (hipStream_t)stream));
+    if (!aligned16({A, B, C, ws})) return L3_ERR_INVALID_ARG;
+    const size_t need = l3_gemm_workspace_size(M, N, K);
+    if (need > 0 && (!ws || ws_bytes < need)) return L3_ERR_CAPACITY;
+    if (need > 0)
+        L3_HIP_TRY(launch_gemm_skinny_bf16((const uint16_t *)A, (const uint16_t *)B, (uint16_t *)C, M,
+                                           N, K, nullptr, (float *)ws, (hipStream_t)stream));
+    else
+        L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)A, (const uint16_t *)B, (uint16_t *)C, M, N, K,
+                                    nullptr, (hipStream_t)stream));
     return L3_OK;
 }
 

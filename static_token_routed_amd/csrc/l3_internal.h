@@ -44,6 +44,7 @@ struct WsLayout {
     size_t o, h, lnp;
     size_t stats;  // LayerNorm row statistics (mean, rstd)
     size_t fold;   // LayerNorm fold of W_mix (bf16 path)
+    size_t part;   // split-K partial slabs of the small-M path (bf16 path, n <= kSkinnyMaxM)
     size_t total;
     int64_t ntiles;
 };
@@ -118,6 +119,18 @@ size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
 hipError_t launch_stage_rows(const int64_t *coff, const int64_t *src, int64_t m, int64_t rows,
                              const void *WK_dev, const void *WV_dev, void *dK, void *dV,
                              int64_t row_k_bytes, int64_t row_v_bytes, hipStream_t s);
+// Small-M path (split K, fp32 partial slabs in `part`, skinny_part_bytes of them):
+// the plain GEMM (with the same optional LayerNorm partials as launch_gemm_bf16),
+// and out = W_mix [LN(h) ; x] with LayerNorm applied to h while it is staged,
+// its row statistics merged from the W_up partials `lnp` (no fold terms needed).
+constexpr int64_t kSkinnyMaxM = 512;  // batches up to this many tokens take the small-M path
+size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M,
+                                   int64_t N, int64_t K, float *ln_out, float *part, hipStream_t s);
+hipError_t launch_gemm_mix_skinny_bf16(const uint16_t *h, const uint16_t *x, const float *lnp,
+                                       const float *gamma, const float *beta, float eps,
+                                       const uint16_t *W_mix, uint16_t *out, int64_t M, int64_t d_up,
+                                       int64_t d_in, int64_t d_out, float *part, hipStream_t s);
 // fp32 variants (any dims): plain GEMM, and the mix GEMM with LayerNorm computed in a
 // separate per-row statistics pass.
 hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N,

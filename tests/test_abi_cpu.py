@@ -74,14 +74,24 @@ def test_null_and_size_checks():
     assert l3._lib.l3_workspace_size(None, 10) == 0
     assert l3._lib.l3_plan_destroy(None) == l3.L3_OK
     assert l3._lib.l3_staging_destroy(None) == l3.L3_OK
-    assert l3._lib.l3_gemm_bf16(None, None, None, 1, 64, 64, None) == l3.L3_ERR_INVALID_ARG
+    assert l3._lib.l3_gemm_bf16(None, None, None, 1, 64, 64, None, 0, None) == l3.L3_ERR_INVALID_ARG
 
 
 def test_gemm_shape_and_alignment_checks():
     # rejected on the host: the pointers are never dereferenced
     g = l3._lib.l3_gemm_bf16
     a, b, c = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
-    assert g(a, b, c, 64, 64, 96, None) == l3.L3_ERR_UNSUPPORTED   # K not a multiple of 64
-    assert g(a, b, c, 64, 96, 64, None) == l3.L3_ERR_UNSUPPORTED   # N not a multiple of 64
-    assert g(ctypes.c_void_p(0x1008), b, c, 64, 64, 64, None) == l3.L3_ERR_INVALID_ARG
-    assert g(a, b, ctypes.c_void_p(0x3002), 64, 64, 64, None) == l3.L3_ERR_INVALID_ARG
+    w = ctypes.c_void_p(0x4000)
+    big = 1 << 30
+    assert g(a, b, c, 64, 64, 96, w, big, None) == l3.L3_ERR_UNSUPPORTED   # K not a multiple of 64
+    assert g(a, b, c, 64, 96, 64, w, big, None) == l3.L3_ERR_UNSUPPORTED   # N not a multiple of 64
+    assert g(ctypes.c_void_p(0x1008), b, c, 64, 64, 64, w, big, None) == l3.L3_ERR_INVALID_ARG
+    assert g(a, b, ctypes.c_void_p(0x3002), 64, 64, 64, w, big, None) == l3.L3_ERR_INVALID_ARG
+    assert g(a, b, c, 64, 64, 64, ctypes.c_void_p(0x4004), big, None) == l3.L3_ERR_INVALID_ARG
+    # small M needs the split-K workspace: S = ceil(K / 256) fp32 slabs of M x N
+    need = l3.l3_gemm_workspace_size(64, 8192, 2048)
+    assert need == 8 * 64 * 8192 * 4
+    assert l3.l3_gemm_workspace_size(1, 64, 64) == 64 * 4
+    assert l3.l3_gemm_workspace_size(513, 1024, 4096) == 0   # large M: no workspace
+    assert g(a, b, c, 64, 8192, 2048, None, 0, None) == l3.L3_ERR_CAPACITY
+    assert g(a, b, c, 64, 8192, 2048, w, need - 1, None) == l3.L3_ERR_CAPACITY

@@ -90,6 +90,12 @@ SMALL_BF16 = [
     ("groups_d128_e64", 80, 300, 128, 64, 128, 128, 800, 8000),
     ("groups_d256_e256_k700", 60, 700, 256, 256, 256, 128, 600, 12000),
     ("groups_d1024_e512", 100, 260, 1024, 512, 256, 256, 700, 9000),
+    # small batches (split-K GEMMs, LayerNorm applied while staging h), random
+    # gamma / beta: a ragged 64-row tile, a W_mix K split that straddles the h|x
+    # seam (d_up 320), and the largest batch of that path
+    ("skinny_d1024_e256", 800, 64, 1024, 256, 512, 320, 200, 20000),
+    ("skinny_straddle", 300, 48, 1024, 128, 320, 192, 77, 8000),
+    ("skinny_d2048_e512_n512", 600, 96, 2048, 512, 512, 256, 512, 20000),
 ]
 
 
@@ -99,7 +105,7 @@ def test_small_bf16_full(spec):
     cfg = synth.small(name, vocab=vocab, k=k, d_in=d_in, d_emb=d_emb, d_up=d_up, d_out=d_out, n=n,
                       v=v, dtype="bf16", ids_s=1.05)
     print(f"bf16 case {name}", flush=True)
-    case = make_case(cfg)
+    case = make_case(cfg, ln_random=name.startswith("skinny"))
     g = Gpu(case)
     got = to_np(g.forward())
     err = rowwise_err(got, oracle_out(case))
@@ -108,9 +114,10 @@ def test_small_bf16_full(spec):
     g.close()
 
 
-def test_stage_identities():
+@pytest.mark.parametrize("n", [900, 200])
+def test_stage_identities(n):
     """W_mix = [0 | I] returns x exactly; W_mix = [I | 0] returns LN(h) (oracle's y)."""
-    cfg = synth.small("ident", vocab=300, k=32, d_in=256, d_emb=128, d_up=256, d_out=256, n=900,
+    cfg = synth.small("ident", vocab=300, k=32, d_in=256, d_emb=128, d_up=256, d_out=256, n=n,
                       v=3000, dtype="bf16")
     case = make_case(cfg)
     g = Gpu(case)
@@ -129,7 +136,8 @@ def test_stage_identities():
 
 def test_gemm_bf16_standalone():
     rng = np.random.default_rng(5)
-    for M, N, K in [(64, 8192, 2048), (300, 320, 192), (1, 64, 64), (513, 1024, 4096)]:
+    for M, N, K in [(64, 8192, 2048), (300, 320, 192), (1, 64, 64), (513, 1024, 4096),
+                    (65, 1024, 320), (512, 192, 2112), (16, 64, 4096)]:
         a = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
         b = synth.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) / np.sqrt(K))
         C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
