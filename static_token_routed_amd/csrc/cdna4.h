@@ -88,6 +88,41 @@ __device__ inline void async_ld16_sbo(const void *sbase, uint32_t voff, uint32_t
                      : "memory", "scc");
 }
 
+// Raw buffer resource (gfx9 layout): base address, no stride, num_records bytes;
+// loads at offsets >= num_records return zeros instead of touching memory.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline i32x4_t make_rsrc(const void *base, uint32_t num_records) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    i32x4_t r;
+    r.x = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    r.y = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffff);
+    r.z = (int32_t)__builtin_amdgcn_readfirstlane(num_records);
+    r.w = 0x00020000;
+    return r;
+}
+
+// Asynchronous 16-byte copy global -> LDS through a buffer resource
+// (buffer_load_dwordx4 ... offen lds): lane l reads rsrc base + voff + soff and its
+// 16 bytes land at lds_base + 16 * l (lds_base uniform).  Lanes whose voff is past
+// num_records deliver zeros.  Completion is tracked by vmcnt only, as for async_ld16.
+__device__ inline void async_buf16(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(m0v), "v"(voff), "s"(rsrc), "s"(so)
+                     : "memory");
+}
+
+// This lane's index in its wavefront, computed afresh (v_mbcnt) and hidden from the
+// optimiser, so values derived from it are recomputed where they are needed instead
+// of being kept live (or spilled) across long stretches of a kernel.
+__device__ inline uint32_t fresh_lane_id() {
+    uint32_t l;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // compile-time loop: f(std::integral_constant<int, I>) for I in [0, N)
 template <int N, int I = 0, typename F>
 __device__ inline void static_for(F &&f) {

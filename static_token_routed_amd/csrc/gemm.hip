@@ -9,16 +9,24 @@
 // 128 x 128 block of a 256 x 256 output tile as 8 x 8 v_mfma_f32_16x16x32_bf16
 // accumulators (256 fp32 per lane, in AGPRs): 64 MFMAs per 16 fragment reads.
 // K advances 64 columns per stage through two LDS buffers filled by
-// asynchronous global -> LDS copies (no register staging); the copies of stage
-// s + 1 are issued between stage s's MFMAs, and barriers wait for LDS traffic
-// only.  LDS rows are 128 bytes (64 bf16); 16-byte chunk c of row r sits at
-// physical chunk c ^ (r & 7) (applied to the copy's source address, since a
-// copy lands at a fixed lane-linear slot), so the 16 rows a fragment read
-// touches fall on distinct banks.  The MFMA takes the B tile as its first
-// operand, so each lane holds 4 consecutive output columns of one row: the
-// epilogue stores 8-byte segments.  Tiles are numbered so that the workgroups
-// the dispatcher sends to one XCD (workgroup id mod 8) form a contiguous,
-// grouped block of tiles, sharing A rows and B columns in that XCD's L2.
+// asynchronous global -> LDS copies (buffer_load ... lds: no register staging;
+// each operand is read through a buffer resource that ends with the matrix, so
+// the rows of a ragged edge tile read as zeros instead of being clamped).  The
+// copies of stage s + 1 are issued one at a time between stage s's MFMA rows,
+// as are the second 32-column step's fragment reads, so neither holds up the
+// MFMA issue for long; barriers wait for LDS traffic only, and the loops are
+// peeled where the kind of copy changes, so no stage carries a branch.  LDS rows
+// are 128 bytes (64 bf16); 16-byte chunk c of row r sits at physical chunk
+// c ^ (r & 7) (applied to the copy's source address, since a copy lands at a
+// fixed lane-linear slot), so the 16 rows a fragment read touches fall on
+// distinct banks.  Per-lane address offsets live in a small LDS table that each
+// stage re-reads: kept in registers across the LayerNorm rescale they get
+// spilled, and a scratch reload inside the stage loop would wait for every copy
+// in flight.  The MFMA takes the B tile as its first operand, so each lane
+// holds 4 consecutive output columns of one row: the epilogue stores 8-byte
+// segments.  Tiles are numbered so that the workgroups the dispatcher sends to
+// one XCD (workgroup id mod 8) form a contiguous, grouped block of tiles,
+// sharing A rows and B columns in that XCD's L2.
 //
 // LayerNorm and the concat [LN(h) ; x] are folded into the W_mix GEMM.  With
 // W_mix = [W1 | W2] (columns acting on LN(h) and on x), LN(h) = (h - mean) * rstd
@@ -75,15 +83,17 @@ __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
 template <bool LN_IN, bool LN_OUT>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * SLOT];
-    // LN_IN: (mean, rstd) of the tile's rows; c1, c2 of its columns
+    // LN_IN: (mean, rstd) of the tile's rows; c1 and c2 of its columns
     __shared__ float2 rowst[LN_IN ? BM : 1];
-    __shared__ float2 colc[LN_IN ? BN : 1];
+    __shared__ __attribute__((aligned(16))) float c1s[LN_IN ? BN : 1];
+    __shared__ __attribute__((aligned(16))) float c2s[LN_IN ? BN : 1];
+    // each thread's lane offsets (LaneOffs below), written once, re-read per stage
+    __shared__ uint4 lane_tab[256][2];
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int t = threadIdx.x, lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
     const uint32_t ring0 = lds_addr(ring);
     const int nst = (int)(p.K / BK);
@@ -91,39 +101,82 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
 
     // Copies: 32 per operand and stage, 1 KB = 8 rows x 128 bytes each; wave w issues
     // q = 8w + i.  Lane l fills row 8q + l/8, physical chunk l % 8, with global chunk
-    // (l % 8) ^ (l / 8) (= row & 7).  Rows past M (N) are clamped: they only feed
-    // accumulators that are never stored.  With LN_IN the columns [K1, K) come from
-    // A2 and B2, addressed as a wave-uniform tile base plus a 32-bit lane offset.
-    const int gch = (lane & 7) ^ (lane >> 3);
-    const uint16_t *srcA[8], *srcB[8];
-    uint32_t offA2[LN_IN ? 8 : 1], offB2[LN_IN ? 8 : 1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * (8 * w + i) + (lane >> 3);
-        const int64_t ra = min<int64_t>(m0 + row, p.M - 1), rb = min<int64_t>(n0 + row, p.N - 1);
-        srcA[i] = p.A + ra * p.lda + gch * 8;
-        srcB[i] = p.B + rb * p.ldb + gch * 8;
-        if constexpr (LN_IN) {
-            offA2[i] = (uint32_t)((ra - m0) * p.lda2 * 2 + gch * 16);
-            offB2[i] = (uint32_t)((rb - n0) * p.ldb2 * 2 + gch * 16);
-        }
+    // (l % 8) ^ (l / 8) (= row & 7).  Each operand is read through a buffer resource
+    // whose base is the tile's first row and whose size ends with the matrix's last
+    // row, so rows past M (N) read as zeros (they only feed accumulators that are
+    // never stored).  The lane's row and chunk go in the 32-bit vector offset, the
+    // stage's column offset in the scalar offset.  With LN_IN the columns [K1, K)
+    // come from A2 and B2 (second pair of resources).
+    auto rsrc = [&](const uint16_t *base, int64_t rows_left, int64_t ld, int64_t len) {
+        const uint64_t nb = rows_left > 0 ? (uint64_t)(rows_left - 1) * ld * 2 + (uint64_t)len * 2 : 0;
+        return make_rsrc(base, (uint32_t)min<uint64_t>(nb, 0xffffffffull));
+    };
+    const int64_t Ka = LN_IN ? p.K1 : p.K;
+    const i32x4_t rA = rsrc(p.A + m0 * p.lda, p.M - m0, p.lda, Ka);
+    const i32x4_t rB = rsrc(p.B + n0 * p.ldb, p.N - n0, p.ldb, Ka);
+    i32x4_t rA2{}, rB2{};
+    if constexpr (LN_IN) {
+        rA2 = rsrc(p.A2 + m0 * p.lda2, p.M - m0, p.lda2, p.K - p.K1);
+        rB2 = rsrc(p.B2 + n0 * p.ldb2, p.N - n0, p.ldb2, p.K - p.K1);
     }
-    const uint16_t *tileA2 = p.A2 + m0 * p.lda2 - p.K1, *tileB2 = p.B2 + n0 * p.ldb2 - p.K1;
-    // half h (copies 4h .. 4h + 3 of each operand) of stage st's copies
-    auto issue_half = [&](int st, int h) {
-        const int64_t k0 = (int64_t)st * BK;
-        const uint32_t base = ring0 + (uint32_t)((st & 1) * SLOT);
-        const bool first = !LN_IN || st < nst1;
+
+    // Per-lane offsets: fragment reads (16-row block rb, 32-column step ks: row
+    // 16 rb + (l & 15) of the wave's rows, logical chunk 4 ks + l/16 at physical chunk
+    // (4 ks + l/16) ^ (l & 7)) and copy sources of the columns [0, K1) (vA, vB) and
+    // [K1, K) (vA2, vB2).  Computed once into LDS and read back at the start of every
+    // stage: kept in registers they would live across the LayerNorm rescale, whose
+    // register pressure gets them spilled to scratch, and scratch reloads inside the
+    // stage loop wait for every copy in flight.
+    struct LaneOffs { uint32_t fA[2], fB[2], vA, vB, vA2, vB2; };
+    {
+        const uint32_t l = threadIdx.x & 63;
+        uint32_t fa[2], fb[2];
 #pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i) {
-            const uint32_t off = (uint32_t)((8 * w + i) * 1024);
-            if (first) {
-                async_ld16(srcA[i] + k0, base + off);
-                async_ld16(srcB[i] + k0, base + TILE + off);
-            } else if constexpr (LN_IN) {
-                async_ld16_sb(tileA2 + k0, offA2[i], base + off);
-                async_ld16_sb(tileB2 + k0, offB2[i], base + TILE + off);
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint32_t c = 16 * ((4 * ks + (l >> 4)) ^ (l & 7));
+            fa[ks] = (uint32_t)(wm * 128 + (l & 15)) * 128 + c;
+            fb[ks] = TILE + (uint32_t)(wn * 128 + (l & 15)) * 128 + c;
+        }
+        const uint32_t gch = (l & 7) ^ (l >> 3), rl = 64 * w + (l >> 3);
+        lane_tab[threadIdx.x][0] = make_uint4(fa[0], fa[1], fb[0], fb[1]);
+        lane_tab[threadIdx.x][1] = make_uint4(rl * (uint32_t)(p.lda * 2) + gch * 16,
+                                              rl * (uint32_t)(p.ldb * 2) + gch * 16,
+                                              rl * (uint32_t)(p.lda2 * 2) + gch * 16,
+                                              rl * (uint32_t)(p.ldb2 * 2) + gch * 16);
+    }
+    auto lane_offs = [&]() {
+        const uint32_t t = 64 * w + fresh_lane_id();  // = threadIdx.x, not kept live
+        const uint4 a = lane_tab[t][0], b = lane_tab[t][1];
+        LaneOffs o;
+        o.fA[0] = a.x; o.fA[1] = a.y; o.fB[0] = a.z; o.fB[1] = a.w;
+        o.vA = b.x; o.vB = b.y; o.vA2 = b.z; o.vB2 = b.w;
+        return o;
+    };
+    const uint32_t sA = (uint32_t)(16 * p.lda), sB = (uint32_t)(16 * p.ldb);  // 8 rows
+    const uint32_t sA2 = (uint32_t)(16 * p.lda2), sB2 = (uint32_t)(16 * p.ldb2);
+
+    // Copy c (0..15: operand c & 1, index c >> 1) of stage st.  KIND 1: columns
+    // [0, K1); 2: columns [K1, K) if st >= nst1, else [0, K1) (scalar selects, no
+    // branch); 0: none (last stage).  The empty asm keeps the 16 per-copy offsets from
+    // being hoisted out of the stage loop as 16 more live registers.
+    auto issue_one = [&](auto kind, int st, int c, const LaneOffs &o) {
+        constexpr int KIND = decltype(kind)::value;
+        const uint32_t base = ring0 + (uint32_t)((st & 1) * SLOT);
+        const int i = c >> 1;
+        const uint32_t off = (uint32_t)((8 * w + i) * 1024) + ((c & 1) ? TILE : 0);
+        if constexpr (KIND == 1) {
+            uint32_t v = (c & 1) ? o.vB : o.vA;
+            __asm__ volatile("" : "+v"(v));
+            const uint32_t so = (uint32_t)st * (BK * 2);
+            if (c & 1) async_buf16(rB, v + i * sB, so, base + off);
+            else async_buf16(rA, v + i * sA, so, base + off);
+        } else if constexpr (KIND == 2 && LN_IN) {
+            const bool sec = st >= nst1;
+            uint32_t v = (c & 1) ? (sec ? o.vB2 : o.vB) : (sec ? o.vA2 : o.vA);
+            __asm__ volatile("" : "+v"(v));
+            const uint32_t so = (uint32_t)(sec ? st - nst1 : st) * (BK * 2);
+            if (c & 1) async_buf16(sec ? rB2 : rB, v + i * (sec ? sB2 : sB), so, base + off);
+            else async_buf16(sec ? rA2 : rA, v + i * (sec ? sA2 : sA), so, base + off);
         }
     };
 
@@ -133,79 +186,99 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Fragment of 16-row block rb, 32-column step ks: row 16rb + (l & 15) of the wave's
-    // rows, logical chunk 4ks + l/16, at physical chunk (4ks + l/16) ^ (l & 7).
-    uint32_t fA[2], fB[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t c = 16 * ((4 * ks + (lane >> 4)) ^ (lane & 7));
-        fA[ks] = (uint32_t)(wm * 128 + (lane & 15)) * 128 + c;
-        fB[ks] = TILE + (uint32_t)(wn * 128 + (lane & 15)) * 128 + c;
-    }
-    auto load_frags = [&](int st, int ks, bf16x8_t (&fa)[8], bf16x8_t (&fb)[8]) {
-        const unsigned char *sb = ring + (st & 1) * SLOT;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            fa[r] = *reinterpret_cast<const bf16x8_t *>(sb + fA[ks] + 2048 * r);
-            fb[r] = *reinterpret_cast<const bf16x8_t *>(sb + fB[ks] + 2048 * r);
-        }
-    };
-
     if constexpr (LN_IN) {
         // written before any copy is in flight; the first barrier publishes them
+        const int t = threadIdx.x;
         const int64_t m = min<int64_t>(m0 + t, p.M - 1), n = min<int64_t>(n0 + t, p.N - 1);
         rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
-        colc[t] = make_float2(p.c1[n], p.c2[n]);
+        c1s[t] = p.c1[n];
+        c2s[t] = p.c2[n];
     }
-    // after the h columns: acc = rstd * (acc - mean * c1) per element
+    // after the h columns: acc = rstd * (acc - mean * c1) per element, one 16-row
+    // block at a time (few live VGPRs)
     auto fold = [&]() {
+        const uint32_t l = fresh_lane_id();
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float2 st2 = rowst[wm * 128 + 16 * i + (lane & 15)];
+            const float2 st2 = rowst[wm * 128 + 16 * i + (l & 15)];
+            const float rm = st2.x * st2.y;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(&colc[wn * 128 + 16 * j + 4 * (lane >> 4)]);
-                const float4 c4b = *reinterpret_cast<const float4 *>(&colc[wn * 128 + 16 * j + 4 * (lane >> 4) + 2]);
-                acc[i][j][0] = st2.y * (acc[i][j][0] - st2.x * c4.x);
-                acc[i][j][1] = st2.y * (acc[i][j][1] - st2.x * c4.z);
-                acc[i][j][2] = st2.y * (acc[i][j][2] - st2.x * c4b.x);
-                acc[i][j][3] = st2.y * (acc[i][j][3] - st2.x * c4b.z);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&c1s[wn * 128 + 16 * j + 4 * (l >> 4)]);
+                acc[i][j][0] = fmaf(-rm, c4.x, st2.y * acc[i][j][0]);
+                acc[i][j][1] = fmaf(-rm, c4.y, st2.y * acc[i][j][1]);
+                acc[i][j][2] = fmaf(-rm, c4.z, st2.y * acc[i][j][2]);
+                acc[i][j][3] = fmaf(-rm, c4.w, st2.y * acc[i][j][3]);
             }
-            __builtin_amdgcn_sched_barrier(0);  // one 16-row block at a time: few live VGPRs
-        }
-    };
-
-    // Double-buffered stages: wait for this stage's copies (the only global loads in
-    // flight), read the first 32-column step's fragments, then per step: read the
-    // next step's fragments, issue half of the next stage's copies, run the MFMAs
-    // (the scheduling barrier keeps the reads ahead of the MFMAs that hide them).
-    auto stage = [&](int st) {
-        wait_vmcnt<0>();
-        lds_barrier();
-        bf16x8_t fa[2][8], fb[2][8];
-        load_frags(st, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks == 0) load_frags(st, 1, fa[1], fb[1]);
-            if (st + 1 < nst) issue_half(st + 1, ks);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    issue_half(0, 0);
-    issue_half(0, 1);
-    // LN_IN: the h stages, the rescale, then the x stages (the copies of the first x
-    // stage are already in flight when the rescale runs)
-    for (int st = 0; st < nst1; ++st) stage(st);
-    if constexpr (LN_IN) fold();
-    for (int st = nst1; st < nst; ++st) stage(st);
+
+    // One stage: wait for its copies (the only global loads in flight), barrier, then
+    // two 32-column steps of 64 MFMAs.  Between the MFMA rows of the first step the
+    // second step's fragments are read (the first step's come first, in the order the
+    // MFMAs use them), and between all rows the next stage's copies (of kind KIND) are
+    // issued, one at a time, so neither blocks the MFMA issue for long.
+    auto stage = [&](auto kind, int st) {
+        const LaneOffs o = lane_offs();
+        wait_vmcnt<0>();
+        lds_barrier();
+        const unsigned char *sb = ring + (st & 1) * SLOT;
+        auto rd = [&](uint32_t a) { return *reinterpret_cast<const bf16x8_t *>(sb + a); };
+        bf16x8_t fa0[8], fb0[8], fa1[8], fb1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb0[j] = rd(o.fB[0] + 2048 * j);
+        fa0[0] = rd(o.fA[0]);
+        fa0[1] = rd(o.fA[0] + 2048);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+            if (i + 2 < 8) fa0[i + 2] = rd(o.fA[0] + 2048 * (i + 2));
+            fb1[i] = rd(o.fB[1] + 2048 * i);
+            fa1[i] = rd(o.fA[1] + 2048 * i);
+            issue_one(kind, st + 1, 2 * i, o);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+            issue_one(kind, st + 1, 2 * i + 1, o);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using KNone = std::integral_constant<int, 0>;
+    using KFirst = std::integral_constant<int, 1>;
+    using KSel = std::integral_constant<int, 2>;
+    if constexpr (!LN_IN) {
+        // the last stage is peeled so no stage carries a branch
+        {
+            const LaneOffs o = lane_offs();
+#pragma unroll
+            for (int c = 0; c < 16; ++c) issue_one(KFirst{}, 0, c, o);
+        }
+        for (int st = 0; st < nst - 1; ++st) stage(KFirst{}, st);
+        stage(KNone{}, nst - 1);
+    } else {
+        // the h stages (the last one issues the first x stage's copies), the rescale
+        // while those are in flight, then the x stages (nst > nst1: d_in >= 64)
+        {
+            const LaneOffs o = lane_offs();
+#pragma unroll
+            for (int c = 0; c < 16; ++c) issue_one(KFirst{}, 0, c, o);
+        }
+        for (int st = 0; st < nst1; ++st) stage(KSel{}, st);
+        fold();
+        for (int st = nst1; st < nst - 1; ++st) stage(KSel{}, st);
+        stage(KNone{}, nst - 1);
+    }
 
     // Epilogue.  acc[i][j] element e of lane l: row m0 + wm*128 + 16i + (l & 15),
     // column n0 + wn*128 + 16j + 4(l/16) + e.
+    const uint32_t lane = fresh_lane_id();
     const int64_t nbase = n0 + wn * 128;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -214,11 +287,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         for (int j = 0; j < 8; ++j) {
             const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
             if constexpr (LN_IN) {
-                const float2 *cc = &colc[wn * 128 + 16 * j + 4 * (lane >> 4)];
-                acc[i][j][0] += cc[0].y;
-                acc[i][j][1] += cc[1].y;
-                acc[i][j][2] += cc[2].y;
-                acc[i][j][3] += cc[3].y;
+                const float4 c4 = *reinterpret_cast<const float4 *>(&c2s[wn * 128 + 16 * j + 4 * (lane >> 4)]);
+                acc[i][j][0] += c4.x;
+                acc[i][j][1] += c4.y;
+                acc[i][j][2] += c4.z;
+                acc[i][j][3] += c4.w;
             }
             if (m < p.M && n < p.N)
                 *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
