@@ -194,6 +194,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         c1s[t] = p.c1[n];
         c2s[t] = p.c2[n];
     }
+    // the accumulators pinned to AGPRs around the rescale, so the stage loops on either
+    // side keep them in place instead of shuffling them between registers
+    auto pin_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    };
     // after the h columns: acc = rstd * (acc - mean * c1) per element, one 16-row
     // block at a time (few live VGPRs)
     auto fold = [&]() {
@@ -271,7 +279,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
             for (int c = 0; c < 16; ++c) issue_one(KFirst{}, 0, c, o);
         }
         for (int st = 0; st < nst1; ++st) stage(KSel{}, st);
+        pin_acc();
         fold();
+        pin_acc();
         for (int st = nst1; st < nst - 1; ++st) stage(KSel{}, st);
         stage(KNone{}, nst - 1);
     }
