@@ -257,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
             issue_one(kind, st + 1, 2 * i + 1, o);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pin_acc();
     };
     using KNone = std::integral_constant<int, 0>;
     using KFirst = std::integral_constant<int, 1>;
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         stage(KNone{}, nst - 1);
     }
 
+    pin_acc();
     // Epilogue.  acc[i][j] element e of lane l: row m0 + wm*128 + 16i + (l & 15),
     // column n0 + wn*128 + 16j + 4(l/16) + e.
     const uint32_t lane = fresh_lane_id();
