@@ -12,9 +12,11 @@
 //                  same digit find each other with 9 ballots, the lowest lane
 //                  reserves their places with one LDS atomic, so ranks are
 //                  stable; writes the tile's digit histogram (digit-major).
-//   k_scan         exclusive scan of the digit-major histogram.
-//   k_sort_scatter position = scanned histogram + rank.
-// Blocks: head flags of the sorted keys, counted per tile, scanned, written.
+//   k_sort_scatter each workgroup forms its tile's digit offsets from the whole
+//                  digit-major histogram (an exclusive prefix), then writes each
+//                  key to offset + rank.
+// Blocks: head flags of the sorted keys, counted per tile, then written at the
+// tile's offset (the sum of the earlier tiles' counts).
 // Nothing is read back to the host: counts stay on the device.
 #include "l3_internal.h"
 
@@ -97,48 +99,30 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
     }
 }
 
-// Exclusive scan of `len` int32 in place by one 1024-thread workgroup; the total is
-// written to *total when total != nullptr.
-__global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ data, int len,
-                                               int32_t *__restrict__ total) {
-    __shared__ int32_t part[1024];
-    __shared__ int32_t wsum[16];
-    const int t = threadIdx.x;
-    const int per = (len + 1023) / 1024;
-    const int beg = min(t * per, len), end = min(beg + per, len);
-    int32_t s = 0;
-    for (int i = beg; i < end; ++i) s += data[i];
-    // inclusive scan of s over the workgroup
-    const int lane = t & 63, w = t >> 6;
-    int32_t v = s;
+// Block-wide exclusive scan of one int32 per thread (256 threads); returns the
+// thread's exclusive prefix and writes the total to *total (all threads).
+__device__ inline int32_t block_scan_256(int32_t v, int32_t *wsum, int32_t *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int32_t u = __shfl_up(v, o);
-        if (lane >= o) v += u;
+        const int32_t u = __shfl_up(x, o);
+        if (lane >= o) x += u;
     }
-    if (lane == 63) wsum[w] = v;
+    if (lane == 63) wsum[w] = x;
     __syncthreads();
-    if (w == 0) {
-        int32_t x = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int32_t u = __shfl_up(x, o);
-            if (lane >= o) x += u;
-        }
-        if (lane < 16) wsum[lane] = x;
-    }
+    int32_t pre = 0;
+    for (int ww = 0; ww < w; ++ww) pre += wsum[ww];
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
-    const int32_t incl = v + (w > 0 ? wsum[w - 1] : 0);
-    part[t] = incl - s;
-    if (t == 1023 && total) *total = incl;
-    int32_t run = part[t];
-    for (int i = beg; i < end; ++i) {
-        const int32_t x = data[i];
-        data[i] = run;
-        run += x;
-    }
+    return pre + x - v;
 }
 
+// One workgroup per 2048-key tile.  The destination of digit d's keys in tile t
+// is the exclusive prefix of the digit-major histogram at (d, t): the keys of all
+// smaller digits, plus those of digit d in earlier tiles.  Each workgroup forms the
+// 512 offsets of its own tile from the histogram (no separate scan pass), then
+// scatters its keys to offset + rank.
 __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict__ keys_in,
                                                       const int32_t *__restrict__ vals_in, int n,
                                                       int shift, int from_ids, int vocab,
@@ -146,15 +130,41 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict_
                                                       const int32_t *__restrict__ rank,
                                                       int32_t *__restrict__ keys_out,
                                                       int32_t *__restrict__ vals_out) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n) return;
-    int key = keys_in[idx];
-    if (from_ids) key = key_of(key, vocab);
-    const uint32_t d = ((uint32_t)key >> shift) & (kRadix - 1);
-    const int pos = hist[(int64_t)d * ntiles + idx / kSortTile] + rank[idx];
-    if ((unsigned)pos >= (unsigned)n) return;  // cannot happen for a consistent ranking
-    keys_out[pos] = key;
-    vals_out[pos] = from_ids ? idx : vals_in[idx];
+    __shared__ int32_t off[kRadix];
+    __shared__ int32_t wsum[4];
+    const int t = blockIdx.x;
+    // thread j owns digits 2j, 2j + 1
+    int32_t tot[2], pre[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int32_t *h = hist + (int64_t)(2 * threadIdx.x + e) * ntiles;
+        int32_t a = 0, b = 0;
+#pragma unroll 8
+        for (int u = 0; u < ntiles; ++u) {
+            const int32_t c = h[u];
+            a += c;
+            b += u < t ? c : 0;
+        }
+        tot[e] = a;
+        pre[e] = b;
+    }
+    int32_t all;
+    const int32_t base = block_scan_256(tot[0] + tot[1], wsum, &all);
+    off[2 * threadIdx.x] = base + pre[0];
+    off[2 * threadIdx.x + 1] = base + tot[0] + pre[1];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortTile / 256; ++r) {
+        const int idx = t * kSortTile + r * 256 + threadIdx.x;
+        if (idx >= n) break;
+        int key = keys_in[idx];
+        if (from_ids) key = key_of(key, vocab);
+        const uint32_t d = ((uint32_t)key >> shift) & (kRadix - 1);
+        const int pos = off[d] + rank[idx];
+        if ((unsigned)pos >= (unsigned)n) continue;  // cannot happen for a consistent ranking
+        keys_out[pos] = key;
+        vals_out[pos] = from_ids ? idx : vals_in[idx];
+    }
 }
 
 // Per 2048-key tile: number of block heads; also the inverse permutation.
@@ -181,13 +191,38 @@ __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ s
     if (threadIdx.x == 0) tile_cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
-// Writes uniq[] and seg_start[] of the heads in one tile (8 consecutive keys per thread).
+// Writes uniq[] and seg_start[] of the heads in one tile (8 consecutive keys per
+// thread); the tile's first block index is the sum of the head counts of the tiles
+// before it (summed here, no separate scan pass).  The number of blocks m goes to
+// *nseg and seg_start[m] = n.
 __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ sk, int n,
-                                                   const int32_t *__restrict__ tile_off,
-                                                   const int32_t *__restrict__ nseg,
+                                                   const int32_t *__restrict__ tile_cnt, int ntiles,
+                                                   int32_t *__restrict__ nseg,
                                                    int32_t *__restrict__ uniq,
                                                    int32_t *__restrict__ seg_start) {
     __shared__ int32_t wsum[4];
+    __shared__ int32_t tile_sums[2];
+    int32_t before = 0, total = 0;
+    for (int u = threadIdx.x; u < ntiles; u += 256) {
+        const int32_t c = tile_cnt[u];
+        total += c;
+        before += u < (int)blockIdx.x ? c : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        before += __shfl_xor(before, o);
+        total += __shfl_xor(total, o);
+    }
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = before;
+    __syncthreads();
+    if (threadIdx.x == 0) tile_sums[0] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = total;
+    __syncthreads();
+    if (threadIdx.x == 0) tile_sums[1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    const int32_t tile_off = tile_sums[0], m = tile_sums[1];
+
     const int base = blockIdx.x * kSortTile + threadIdx.x * 8;
     int flags = 0, c = 0;
 #pragma unroll
@@ -197,18 +232,8 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
         flags |= f << i;
         c += f;
     }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int v = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o);
-        if (lane >= o) v += u;
-    }
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    int pre = 0;
-    for (int ww = 0; ww < w; ++ww) pre += wsum[ww];
-    int j = tile_off[blockIdx.x] + pre + v - c;
+    int32_t all;
+    int j = tile_off + block_scan_256(c, wsum, &all);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if ((flags & (1 << i)) && j < n) {
@@ -217,7 +242,10 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
             ++j;
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) seg_start[min(*nseg, n)] = n;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *nseg = m;
+        seg_start[min(m, n)] = n;
+    }
 }
 
 // One thread per block (segment): its size, and its work items appended to the light
@@ -303,9 +331,7 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
         const int from_ids = p == 0;
         hipLaunchKernelGGL(k_sort_rank, dim3((unsigned)ntiles), dim3(256), 0, s, kin, n, shift,
                            from_ids, (int)vocab, b.rank, b.hist, (int)ntiles, b.hdr + HDR_ERR);
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, b.hist, (int)(kRadix * ntiles),
-                           (int32_t *)nullptr);
-        hipLaunchKernelGGL(k_sort_scatter, dim3(blocks_for(n, 256)), dim3(256), 0, s, kin,
+        hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)ntiles), dim3(256), 0, s, kin,
                            vin ? vin : kin, n, shift, from_ids, (int)vocab, b.hist, (int)ntiles,
                            b.rank, kout, vout);
         kin = kout;
@@ -317,10 +343,8 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
     b.perm = const_cast<int32_t *>(vin);
     hipLaunchKernelGGL(k_seg_heads, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, b.perm,
                        n, b.tile_cnt, b.inv_perm);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, b.tile_cnt, (int)ntiles,
-                       b.hdr + HDR_NSEG);
     hipLaunchKernelGGL(k_seg_write, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, n,
-                       b.tile_cnt, b.hdr + HDR_NSEG, b.uniq, b.seg_start);
+                       b.tile_cnt, (int)ntiles, b.hdr + HDR_NSEG, b.uniq, b.seg_start);
     return hipGetLastError();
 }
 
