@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the L^3 forward pass (TEST INFRASTRUCTURE ONLY).
+"""fp64 CPU oracle of the L^3 forward and backward passes (TEST INFRASTRUCTURE ONLY).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the GPU library
@@ -6,6 +6,8 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 * ``forward``: the per-token fp64 loop of ``l3_oracle.c`` (plain C, OpenMP over
   tokens), taking any float inputs widened exactly to fp64.
+* ``backward``: the gradients of the same function (chain rule per token,
+  parameter gradients summed over tokens), single-threaded fp64 C.
 * ``route`` / ``route_bruteforce``: the stable sort by token ID and the per-ID
   blocks (``route.py``).
 """
@@ -52,6 +54,10 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.l3o_forward.argtypes = [I64, I64, I64, ctypes.c_int32, P, I64, I64, I64, I64,
                                 P, P, P, P, P, P, P, ctypes.c_double, P, P, P, P, P,
                                 ctypes.c_int]
+    lib.l3o_backward.restype = ctypes.c_int
+    lib.l3o_backward.argtypes = [I64, I64, I64, ctypes.c_int32, P, I64, I64, I64, I64,
+                                 P, P, P, P, P, P, P, ctypes.c_double, P, P,
+                                 P, P, P, P, P, P, P]
     lib.l3o_check_offsets.restype = ctypes.c_int
     lib.l3o_check_offsets.argtypes = [P, I64, I64, ctypes.c_int32]
     _libs[path] = lib
@@ -103,6 +109,35 @@ def forward(off, k: int, x, ids, W_K, W_V, W_up, gamma, beta, W_mix, eps: float 
     if rc:
         raise OracleError(rc)
     return (out, o, h, y) if stages else out
+
+
+def backward(off, k: int, x, ids, W_K, W_V, W_up, gamma, beta, W_mix, dout, eps: float = 1e-5,
+             v: int | None = None, lib: ctypes.CDLL | None = None) -> dict:
+    """Gradients of sum(dout * forward(...)) (fp64): dict with dx, dW_K, dW_V, dW_up,
+    dgamma, dbeta, dW_mix."""
+    lib = lib or load()
+    off = np.ascontiguousarray(off, dtype=np.int64)
+    vocab = len(off) - 1
+    v = int(off[-1]) if v is None else int(v)
+    x, W_K, W_V, W_up, W_mix, dout = map(_f64, (x, W_K, W_V, W_up, W_mix, dout))
+    gamma, beta = _f64(gamma), _f64(beta)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n = len(ids)
+    d_in, d_emb = W_K.shape[1], W_V.shape[1]
+    d_up, d_out = W_up.shape[0], W_mix.shape[0]
+    assert x.shape == (n, d_in) and dout.shape == (n, d_out)
+    assert W_mix.shape == (d_out, d_up + d_in) and W_up.shape == (d_up, d_emb)
+    g = {"dx": np.zeros((n, d_in)), "dW_K": np.zeros((v, d_in)), "dW_V": np.zeros((v, d_emb)),
+         "dW_up": np.zeros((d_up, d_emb)), "dgamma": np.zeros(d_up), "dbeta": np.zeros(d_up),
+         "dW_mix": np.zeros((d_out, d_up + d_in))}
+    rc = lib.l3o_backward(n, vocab, v, int(k), _p(off), d_in, d_emb, d_up, d_out,
+                          _p(x), _p(ids), _p(W_K), _p(W_V), _p(W_up), _p(gamma), _p(beta),
+                          float(eps), _p(W_mix), _p(dout),
+                          *[_p(g[key]) for key in ("dx", "dW_K", "dW_V", "dW_up", "dgamma",
+                                                   "dbeta", "dW_mix")])
+    if rc:
+        raise OracleError(rc)
+    return g
 
 
 def check_offsets(off, v: int, k: int, lib: ctypes.CDLL | None = None) -> int:

@@ -32,6 +32,14 @@
  * Every token is computed on its own (the layer mixes channels only, no
  * information crosses tokens), so the loop over tokens may run in any order;
  * OpenMP only splits that loop.  All arithmetic is double precision.
+ *
+ * l3o_backward is the gradient of the same function: the chain rule applied to
+ * the steps above in reverse order, one token at a time, the parameter
+ * gradients summed over the tokens.  The pages train the layer end to end
+ * (papernotes.org page, section 训练策略; kimjy99.github.io page, section
+ * "2. Efficient Training and Inference": sort, block-diagonal attention,
+ * inverse sort), but print no gradient formulas; these are the plain
+ * derivatives of the forward equations.
  */
 #include <math.h>
 #include <stdint.h>
@@ -161,5 +169,120 @@ int l3o_forward(int64_t n, int64_t vocab, int64_t v, int32_t k, const int64_t *o
         if (y_out) for (int64_t r = 0; r < d_up; ++r) y_out[i * d_up + r] = y[r];
     }
     free(scratch);
+    return L3O_OK;
+}
+
+/*
+ * Backward over n tokens for the upstream gradient dout [n x d_out]: writes
+ * (overwrites) dx [n x d_in], dWK [v x d_in], dWV [v x d_emb], dWup [d_up x d_emb],
+ * dgamma, dbeta [d_up] and dWmix [d_out x (d_up + d_in)].  Single-threaded (the
+ * parameter gradients are sums over tokens).  Per token, with W_mix = [W1 | W2],
+ * yhat = (h - mean) / sqrt(var + eps) and y = yhat * gamma + beta:
+ *     dWmix += dout [y ; x]^T          dy = W1^T dout      dx = W2^T dout
+ *     dgamma += dy * yhat              dbeta += dy
+ *     g = dy * gamma;  dh = rstd * (g - mean(g) - yhat * mean(g * yhat))
+ *     dWup += dh o^T                   do = Wup^T dh
+ *     dV_t[j] += p_j do                dp_j = <V_t[j], do>
+ *     ds_j = p_j (dp_j - sum_k p_k dp_k)
+ *     dK_t[j] += ds_j x                dx += sum_j ds_j K_t[j]
+ */
+int l3o_backward(int64_t n, int64_t vocab, int64_t v, int32_t k, const int64_t *off,
+                 int64_t d_in, int64_t d_emb, int64_t d_up, int64_t d_out,
+                 const double *x, const int32_t *ids,
+                 const double *WK, const double *WV, const double *Wup,
+                 const double *gamma, const double *beta, double eps,
+                 const double *Wmix, const double *dout,
+                 double *dx, double *dWK, double *dWV, double *dWup,
+                 double *dgamma, double *dbeta, double *dWmix)
+{
+    int rc = l3o_check_offsets(off, vocab, v, k);
+    if (rc) return rc;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= vocab) return L3O_TOKEN_RANGE;
+    const int64_t dz = d_up + d_in;
+    for (int64_t e = 0; e < v * d_in; ++e) dWK[e] = 0.0;
+    for (int64_t e = 0; e < v * d_emb; ++e) dWV[e] = 0.0;
+    for (int64_t e = 0; e < d_up * d_emb; ++e) dWup[e] = 0.0;
+    for (int64_t e = 0; e < d_up; ++e) dgamma[e] = dbeta[e] = 0.0;
+    for (int64_t e = 0; e < d_out * dz; ++e) dWmix[e] = 0.0;
+    /* scratch: p (k), dp (k), o (d_emb), do (d_emb), h, yhat, y, dy, dh (d_up), out (d_out) */
+    double *p = (double *)malloc(sizeof(double) * (size_t)(2 * k + 2 * d_emb + 5 * d_up + d_out));
+    if (!p) return L3O_NOMEM;
+    double *dp = p + k, *o = dp + k, *dov = o + d_emb, *h = dov + d_emb;
+    double *yh = h + d_up, *y = yh + d_up, *dy = y + d_up, *dh = dy + d_up, *tmp = dh + d_up;
+    for (int64_t i = 0; i < n; ++i) {
+        const double *xi = x + i * d_in, *go = dout + i * d_out;
+        const int64_t t = ids[i], a = off[t], d = off[t + 1] - off[t];
+        /* forward again: p, o, h, y (l3o_token; s doubles as p) */
+        l3o_token(xi, t, off, d_in, d_emb, d_up, d_out, WK, WV, Wup, gamma, beta, eps, Wmix,
+                  tmp, p, o, h, y);
+        /* the normalised h (before gamma, beta) and 1 / sqrt(var + eps) */
+        double mu = 0.0, ss = 0.0;
+        for (int64_t r = 0; r < d_up; ++r) mu += h[r];
+        mu /= (double)d_up;
+        for (int64_t r = 0; r < d_up; ++r) { const double c = h[r] - mu; ss += c * c; }
+        const double rstd = 1.0 / sqrt(ss / (double)d_up + eps);
+        for (int64_t r = 0; r < d_up; ++r) yh[r] = (h[r] - mu) * rstd;
+        /* out = W_mix [y ; x] */
+        for (int64_t q = 0; q < d_out; ++q) {
+            double *gr = dWmix + q * dz;
+            for (int64_t r = 0; r < d_up; ++r) gr[r] += go[q] * y[r];
+            for (int64_t c = 0; c < d_in; ++c) gr[d_up + c] += go[q] * xi[c];
+        }
+        for (int64_t r = 0; r < d_up; ++r) {
+            double acc = 0.0;
+            for (int64_t q = 0; q < d_out; ++q) acc += Wmix[q * dz + r] * go[q];
+            dy[r] = acc;
+        }
+        for (int64_t c = 0; c < d_in; ++c) {
+            double acc = 0.0;
+            for (int64_t q = 0; q < d_out; ++q) acc += Wmix[q * dz + d_up + c] * go[q];
+            dx[i * d_in + c] = acc;
+        }
+        /* y = yhat * gamma + beta, yhat = (h - mean) * rstd */
+        double mg = 0.0, mgy = 0.0;
+        for (int64_t r = 0; r < d_up; ++r) {
+            dgamma[r] += dy[r] * yh[r];
+            dbeta[r] += dy[r];
+            const double g = dy[r] * gamma[r];
+            mg += g;
+            mgy += g * yh[r];
+        }
+        mg /= (double)d_up;
+        mgy /= (double)d_up;
+        for (int64_t r = 0; r < d_up; ++r) dh[r] = rstd * (dy[r] * gamma[r] - mg - yh[r] * mgy);
+        /* h = W_up o */
+        for (int64_t r = 0; r < d_up; ++r)
+            for (int64_t c = 0; c < d_emb; ++c) dWup[r * d_emb + c] += dh[r] * o[c];
+        for (int64_t c = 0; c < d_emb; ++c) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < d_up; ++r) acc += Wup[r * d_emb + c] * dh[r];
+            dov[c] = acc;
+        }
+        /* o = V_t^T p */
+        double pdp = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            const double *vrow = WV + (a + j) * d_emb;
+            double *gv = dWV + (a + j) * d_emb;
+            double acc = 0.0;
+            for (int64_t c = 0; c < d_emb; ++c) {
+                gv[c] += p[j] * dov[c];
+                acc += vrow[c] * dov[c];
+            }
+            dp[j] = acc;
+            pdp += p[j] * acc;
+        }
+        /* p = softmax(s), s_j = <K_t[j], x> */
+        for (int64_t j = 0; j < d; ++j) {
+            const double ds = p[j] * (dp[j] - pdp);
+            const double *kr = WK + (a + j) * d_in;
+            double *gk = dWK + (a + j) * d_in;
+            for (int64_t c = 0; c < d_in; ++c) {
+                gk[c] += ds * xi[c];
+                dx[i * d_in + c] += ds * kr[c];
+            }
+        }
+    }
+    free(p);
     return L3O_OK;
 }

@@ -1,0 +1,91 @@
+"""Pins of the fp64 oracle's backward pass against facts that do not come from it.
+
+The gradient of the scalar sum(dout * forward(...)) is pinned against central
+finite differences of the oracle's forward pass (itself pinned by
+``oracle_pins.py``), and against exact special cases: rows of IDs absent from
+the batch get no gradient; with one row per ID the softmax is constant, so the
+key rows get none and dx is W2^T dout alone; the gradient is linear in dout.
+``test_oracle_backward.py`` runs these pins on the oracle and
+``test_oracle_mutants.py`` on copies of it with planted mistakes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle_pins import _case
+
+KEYS = ("dx", "dW_K", "dW_V", "dW_up", "dgamma", "dbeta", "dW_mix")
+ARGS = {"dx": "x", "dW_K": "W_K", "dW_V": "W_V", "dW_up": "W_up", "dgamma": "gamma",
+        "dbeta": "beta", "dW_mix": "W_mix"}
+
+
+def _bwd(lib, c, dout):
+    return oracle.backward(c["off"], c["k"], c["x"], c["ids"], c["W_K"], c["W_V"], c["W_up"],
+                           c["gamma"], c["beta"], c["W_mix"], dout, eps=c["eps"], lib=lib)
+
+
+def _loss(lib, c, dout, **kw):
+    a = dict(c)
+    a.update(kw)
+    out = oracle.forward(a["off"], a["k"], a["x"], a["ids"], a["W_K"], a["W_V"], a["W_up"],
+                         a["gamma"], a["beta"], a["W_mix"], eps=a["eps"], lib=lib)
+    return float(np.sum(out * dout))
+
+
+def _fd_check(lib, c, seed, tol=1e-6):
+    dout = np.random.default_rng(seed).standard_normal((len(c["ids"]), c["W_mix"].shape[0]))
+    g = _bwd(lib, c, dout)
+    for key in KEYS:
+        arr = c[ARGS[key]]
+        fd = np.zeros_like(arr, dtype=np.float64)
+        for idx in np.ndindex(arr.shape):
+            e = 1e-6 * max(1.0, abs(float(arr[idx])))
+            a1, a2 = arr.astype(np.float64).copy(), arr.astype(np.float64).copy()
+            a1[idx] += e
+            a2[idx] -= e
+            fd[idx] = (_loss(lib, c, dout, **{ARGS[key]: a1}) -
+                       _loss(lib, c, dout, **{ARGS[key]: a2})) / (2 * e)
+        err = float(np.max(np.abs(fd - g[key]))) / max(1e-9, float(np.max(np.abs(fd))))
+        assert err <= tol, f"{key}: finite-difference rel err {err:.2e}"
+
+
+def pin_bwd_finite_differences(lib):
+    # several rows per ID (softmax over up to 5 rows), random gamma / beta, repeated IDs
+    _fd_check(lib, _case(seed=21, vocab=4, k=5, d_in=4, d_emb=3, d_up=5, d_out=3, n=7), 1)
+    # mixed one-row and many-row IDs, d_up small (LayerNorm over 3 features)
+    _fd_check(lib, _case(seed=22, vocab=5, k=4, d_in=3, d_emb=4, d_up=3, d_out=4, n=6,
+                         d=[1, 4, 2, 1, 3]), 2)
+
+
+def pin_bwd_untouched_rows_zero(lib):
+    # the touched IDs own several rows (with one row the keys get no gradient)
+    c = _case(seed=23, vocab=6, k=3, n=5, d=[2, 3, 1, 2, 2, 3])
+    c["ids"] = np.array([1, 4, 1, 1, 4], np.int32)
+    g = _bwd(lib, c, np.random.default_rng(3).standard_normal((5, c["W_mix"].shape[0])))
+    off = c["off"]
+    for t in range(6):
+        rows = slice(off[t], off[t + 1])
+        touched = t in (1, 4)
+        for key in ("dW_K", "dW_V"):
+            assert (np.any(g[key][rows] != 0)) == touched, f"{key} rows of ID {t}"
+
+
+def pin_bwd_single_row_slices(lib):
+    c = _case(seed=24, vocab=5, k=3, n=8, d=[1, 1, 1, 1, 1])
+    dout = np.random.default_rng(4).standard_normal((8, c["W_mix"].shape[0]))
+    g = _bwd(lib, c, dout)
+    d_up = c["W_up"].shape[0]
+    assert np.all(g["dW_K"] == 0), "one row per ID: the keys get no gradient"
+    np.testing.assert_allclose(g["dx"], dout @ c["W_mix"][:, d_up:], rtol=1e-12, atol=1e-12)
+
+
+def pin_bwd_linear_in_dout(lib):
+    c = _case(seed=25, vocab=4, k=4, n=6)
+    dout = np.random.default_rng(5).standard_normal((6, c["W_mix"].shape[0]))
+    g1, g2 = _bwd(lib, c, dout), _bwd(lib, c, 2.0 * dout)
+    for key in KEYS:
+        assert np.array_equal(2.0 * g1[key], g2[key]), key
+
+
+BACKWARD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_bwd_")]

@@ -5,6 +5,7 @@ import os
 import pytest
 
 import oracle
+from oracle_backward_pins import BACKWARD_PINS
 from oracle_pins import PINS
 
 # (name, text in l3_oracle.c, replacement)
@@ -46,3 +47,35 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+# mistakes in the backward pass, each of which must fail a backward pin
+BACKWARD_MUTANTS = [
+    ("bwd_no_softmax_centering", "const double ds = p[j] * (dp[j] - pdp);",
+     "const double ds = p[j] * dp[j];"),
+    ("bwd_ln_no_mean_term", "dh[r] = rstd * (dy[r] * gamma[r] - mg - yh[r] * mgy);",
+     "dh[r] = rstd * (dy[r] * gamma[r] - yh[r] * mgy);"),
+    ("bwd_ln_no_projection_term", "dh[r] = rstd * (dy[r] * gamma[r] - mg - yh[r] * mgy);",
+     "dh[r] = rstd * (dy[r] * gamma[r] - mg);"),
+    ("bwd_w_up_transposed", "acc += Wup[r * d_emb + c] * dh[r];", "acc += Wup[c * d_up + r] * dh[r];"),
+    ("bwd_dgamma_unnormalised", "dgamma[r] += dy[r] * yh[r];", "dgamma[r] += dy[r] * h[r];"),
+    ("bwd_dx_no_attention_term", "dx[i * d_in + c] += ds * kr[c];", "(void)kr;"),
+    ("bwd_dv_first_row_only", "double *gv = dWV + (a + j) * d_emb;", "double *gv = dWV + a * d_emb;"),
+    ("bwd_dk_uses_dp", "gk[c] += ds * xi[c];", "gk[c] += dp[j] * xi[c];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
+def test_backward_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    p = tmp_path / f"{name}.c"
+    p.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(p), str(tmp_path / f"lib{name}.so")))
+    failed = []
+    for pin in BACKWARD_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every backward pin"
