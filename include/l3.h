@@ -133,6 +133,39 @@ int l3_forward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t 
                void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward pass (training).  The pages train the layer end to end, the batch
+ * sorted by token ID so attention is block diagonal and the sort undone after
+ * (sciencestack.ai page, Fig. 3 caption; kimjy99.github.io page, section "2.
+ * Efficient Training and Inference"); the gradients are the derivatives of the
+ * forward equation (papernotes.org page, section 整体框架).
+ *
+ * l3_backward_workspace_size -- device workspace bytes for up to n_max tokens
+ * (0 on a bad argument); 256-byte aligned, no initialisation needed.
+ *
+ * l3_backward -- gradients of sum(dout * L3(x, token_ids)) for n tokens.
+ * Inputs as for l3_forward (plan dtype), plus dout: dev [n x d_out] (plan dtype).
+ * Outputs, all dev fp32, 16-byte aligned:
+ *   dx [n x d_in]                 written (rows in the input token order);
+ *   dW_K [v x d_in], dW_V [v x d_emb]   ADDED TO, on the rows of the IDs present
+ *                                 in the batch (other rows untouched);
+ *   dW_up [d_up x d_emb], dln_gamma, dln_beta [d_up],
+ *   dW_mix [d_out x (d_up + d_in)]     ADDED TO.
+ * The caller zeroes the accumulated gradients when a new accumulation starts.
+ * The forward is recomputed inside (nothing is saved from l3_forward).  Every sum
+ * over tokens runs in a fixed order (no atomics): results are bit-for-bit
+ * reproducible.  Operands of the dense products are bf16 for bf16 plans
+ * (fp32 accumulation), fp32 otherwise.  Supports d_in <= 4096, d_emb <= 1024.
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, HIP.  IDs outside [0, vocab) set
+ * the status flag (l3_status) and contribute no attention gradient.
+ */
+size_t l3_backward_workspace_size(l3_plan_t plan, int64_t n_max);
+int l3_backward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t n,
+                const void *W_K, const void *W_V, const void *W_up, const float *ln_gamma,
+                const float *ln_beta, const void *W_mix, const void *dout, float *dx,
+                float *dW_K, float *dW_V, float *dW_up, float *dln_gamma, float *dln_beta,
+                float *dW_mix, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * l3_route -- the batch sort alone (what l3_forward does first).
  * Sorting is stable: tokens with equal IDs keep their batch order.  IDs outside
  * [0, vocab) sort as the key `vocab` after every valid ID and set the flag.

@@ -48,6 +48,9 @@ _SIG = {
     "l3_worklist_rule": (ctypes.c_int, [_P, _P, _P]),
     "l3_workspace_size": (_SZ, [_P, _I64]),
     "l3_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "l3_backward_workspace_size": (_SZ, [_P, _I64]),
+    "l3_backward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, _P, _SZ, _P]),
     "l3_route": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
     "l3_status": (ctypes.c_int, [_P, _P]),
     "l3_staging_create": (ctypes.c_int, [_P, _I64, _I64, ctypes.POINTER(_P)]),
@@ -137,6 +140,20 @@ def l3_forward(plan, x, token_ids, n, W_K, W_V, W_up, ln_gamma, ln_beta, W_mix, 
     _check(_lib.l3_forward(plan, _ptr(x), _ptr(token_ids), n, _ptr(W_K), _ptr(W_V), _ptr(W_up),
                            _ptr(ln_gamma), _ptr(ln_beta), _ptr(W_mix), _ptr(out), _ptr(workspace),
                            workspace_bytes, _stream(stream)), "l3_forward")
+
+
+def l3_backward_workspace_size(plan: int, n_max: int) -> int:
+    return int(_lib.l3_backward_workspace_size(plan, n_max))
+
+
+def l3_backward(plan, x, token_ids, n, W_K, W_V, W_up, ln_gamma, ln_beta, W_mix, dout, dx, dW_K,
+                dW_V, dW_up, dln_gamma, dln_beta, dW_mix, workspace, workspace_bytes,
+                stream=None) -> None:
+    _check(_lib.l3_backward(plan, _ptr(x), _ptr(token_ids), n, _ptr(W_K), _ptr(W_V), _ptr(W_up),
+                            _ptr(ln_gamma), _ptr(ln_beta), _ptr(W_mix), _ptr(dout), _ptr(dx),
+                            _ptr(dW_K), _ptr(dW_V), _ptr(dW_up), _ptr(dln_gamma), _ptr(dln_beta),
+                            _ptr(dW_mix), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "l3_backward")
 
 
 def l3_route(plan, token_ids, n, workspace, workspace_bytes, stream=None, perm=None,

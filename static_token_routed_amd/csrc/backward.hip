@@ -1,0 +1,347 @@
+// Backward pass of the L^3 layer ("L^3: Large Lookup Layers": the layer equation
+// on the papernotes.org page, section 整体框架, and the kimjy99.github.io page,
+// section "Method"; the pages train it end to end after sorting the batch by
+// token ID -- sciencestack.ai page, Fig. 3 caption; kimjy99.github.io page,
+// section "2. Efficient Training and Inference").  The gradients are the plain
+// derivatives of the forward steps, taken in reverse order:
+//   out = W_mix [y ; x]:  dW_mix += dout [y ; x]^T,  dy = W1^T dout,  dx = W2^T dout
+//   y = yhat * gamma + beta:  dgamma += dy * yhat,  dbeta += dy
+//   yhat = (h - mean) rstd:  dh = rstd (g - mean(g) - yhat mean(g yhat)),  g = dy * gamma
+//   h = W_up o:  dW_up += dh o^T,  do = W_up^T dh
+//   o = V_t^T p, p = softmax(K_t x):  dp_j = <V_t[j], do>,  ds_j = p_j (dp_j - <o, do>),
+//                                     dV_t[j] += p_j do,  dK_t[j] += ds_j x,  dx += K_t^T ds
+// The dense products run on the library's GEMMs (explicit transposes feed them
+// k-contiguous operands); this file holds the transposes, the LayerNorm backward,
+// the per-token attention backward and the per-block key / value gradients.
+// Parameter gradients are fp32 and accumulated (+=), in a fixed order (no atomics):
+// the batch is sorted by ID, so each table row's gradient is one workgroup's sum
+// over its block's tokens.
+#include <algorithm>
+
+#include "cdna4.h"
+#include "l3_internal.h"
+
+namespace l3 {
+namespace {
+
+template <typename T> __device__ inline float ld(const T *p);
+template <> __device__ inline float ld<float>(const float *p) { return *p; }
+template <> __device__ inline float ld<uint16_t>(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+template <typename T> __device__ inline void st(T *p, float v);
+template <> __device__ inline void st<float>(float *p, float v) { *p = v; }
+template <> __device__ inline void st<uint16_t>(uint16_t *p, float v) { *p = (uint16_t)f2bf(v); }
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_pad (dst row stride
+// ld_dst); 64 x 64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, int64_t ld_src,
+                                                   int64_t rows, int64_t cols, T *__restrict__ dst,
+                                                   int64_t ld_dst, int64_t rows_pad) {
+    __shared__ T tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        T v{};
+        if (r < rows && c < cols) v = src[r * ld_src + c];
+        tile[i][tx] = v;
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows_pad) dst[c * ld_dst + r] = tile[tx][i];
+    }
+}
+
+// One wavefront per row: g = dy * gamma, dh = rstd (g - mean(g) - yhat mean(g yhat)),
+// and y = yhat * gamma + beta (the W_mix operand of dW_mix).
+template <typename T>
+__global__ __launch_bounds__(256) void k_ln_bwd(const T *__restrict__ h, const float *__restrict__ stats,
+                                                const float *__restrict__ gamma,
+                                                const float *__restrict__ beta,
+                                                const float *__restrict__ dy, int64_t n, int64_t d_up,
+                                                T *__restrict__ dh, T *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+    const T *hr = h + row * d_up;
+    const float *gr = dy + row * d_up;
+    float sg = 0.f, sgy = 0.f;
+    for (int64_t c = lane; c < d_up; c += 64) {
+        const float yh = (ld(hr + c) - mean) * rstd, g = gr[c] * gamma[c];
+        sg += g;
+        sgy += g * yh;
+    }
+    sg = wave_sum(sg) / (float)d_up;
+    sgy = wave_sum(sgy) / (float)d_up;
+    for (int64_t c = lane; c < d_up; c += 64) {
+        const float yh = (ld(hr + c) - mean) * rstd, g = gr[c] * gamma[c];
+        st(dh + row * d_up + c, rstd * (g - sg - yh * sgy));
+        st(y + row * d_up + c, yh * gamma[c] + beta[c]);
+    }
+}
+
+// Column partial sums of dy * yhat and dy over a chunk of kLnRows rows:
+// part[chunk][c] = (sum dy*yhat, sum dy).
+constexpr int kLnRows = 256;
+template <typename T>
+__global__ __launch_bounds__(256) void k_ln_param_part(const T *__restrict__ h,
+                                                       const float *__restrict__ stats,
+                                                       const float *__restrict__ dy, int64_t n,
+                                                       int64_t d_up, float2 *__restrict__ part) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= d_up) return;
+    const int64_t r0 = (int64_t)blockIdx.y * kLnRows, r1 = std::min<int64_t>(r0 + kLnRows, n);
+    float a = 0.f, b = 0.f;
+    for (int64_t r = r0; r < r1; ++r) {
+        const float g = dy[r * d_up + c];
+        a += g * (ld(h + r * d_up + c) - stats[2 * r]) * stats[2 * r + 1];
+        b += g;
+    }
+    part[blockIdx.y * d_up + c] = make_float2(a, b);
+}
+
+// dgamma[c] += sum over chunks (in chunk order) of part.x, dbeta[c] += of part.y.
+__global__ __launch_bounds__(256) void k_ln_param_reduce(const float2 *__restrict__ part, int nchunk,
+                                                         int64_t d_up, float *__restrict__ dgamma,
+                                                         float *__restrict__ dbeta) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= d_up) return;
+    float a = 0.f, b = 0.f;
+    for (int k = 0; k < nchunk; ++k) {
+        const float2 v = part[k * d_up + c];
+        a += v.x;
+        b += v.y;
+    }
+    dgamma[c] += a;
+    dbeta[c] += b;
+}
+
+// One wavefront per token (a light work item of one token: sorted position, count,
+// first table row, d_t).  Pass 1 over the block's rows: scores, running max and sum,
+// and o = V_t^T p, giving <o, do>.  Pass 2: p_j, dp_j = <V_t[j], do>, ds_j, dx +=
+// sum_j ds_j K_t[j] (dx holds W2^T dout already), and P, dS stored per sorted
+// position for the key / value gradients.  Lane l handles elements l + 64 q.
+template <typename T, int QI, int QE>
+__global__ __launch_bounds__(256) void k_attn_bwd(const T *__restrict__ x, const T *__restrict__ WK,
+                                                  const T *__restrict__ WV,
+                                                  const int32_t *__restrict__ perm,
+                                                  const int4 *__restrict__ items,
+                                                  const int32_t *__restrict__ hdr,
+                                                  const float *__restrict__ dov, int64_t d_in,
+                                                  int64_t d_emb, int max_d, float *__restrict__ dx,
+                                                  float *__restrict__ P, float *__restrict__ dS) {
+    const int lane = threadIdx.x & 63;
+    const int nitems = hdr[HDR_NLIGHT];
+    const int nw = gridDim.x * 4;
+    for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += nw) {
+        const int4 item = items[it];
+        if (item.w < 0) continue;  // ID out of range: no gradient (flagged by the route)
+        const int s = item.x, tok = perm[s];
+        const int64_t r0 = item.z;
+        const int d = item.w;
+        float xv[QI], dxv[QI], dv[QE], ov[QE];
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+            const int64_t c = lane + 64 * q;
+            xv[q] = c < d_in ? ld(x + (int64_t)tok * d_in + c) : 0.f;
+            dxv[q] = 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < QE; ++q) {
+            const int64_t c = lane + 64 * q;
+            dv[q] = c < d_emb ? dov[(int64_t)tok * d_emb + c] : 0.f;
+            ov[q] = 0.f;
+        }
+        auto score = [&](int j) {
+            const T *kr = WK + (r0 + j) * d_in;
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < QI; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < d_in) a += ld(kr + c) * xv[q];
+            }
+            return wave_sum(a);
+        };
+        // pass 1: max, sum, o
+        float m = -INFINITY, l = 0.f;
+        for (int j = 0; j < d; ++j) {
+            const float sc = score(j);
+            const float mn = fmaxf(m, sc), alpha = __expf(m - mn), e = __expf(sc - mn);
+            l = l * alpha + e;
+            const T *vr = WV + (r0 + j) * d_emb;
+#pragma unroll
+            for (int q = 0; q < QE; ++q) {
+                const int64_t c = lane + 64 * q;
+                ov[q] = ov[q] * alpha + (c < d_emb ? e * ld(vr + c) : 0.f);
+            }
+            m = mn;
+        }
+        const float inv = 1.f / l;
+        float od = 0.f;
+#pragma unroll
+        for (int q = 0; q < QE; ++q) od += ov[q] * inv * dv[q];
+        od = wave_sum(od);
+        // pass 2
+        for (int j = 0; j < d; ++j) {
+            const float p = __expf(score(j) - m) * inv;
+            const T *vr = WV + (r0 + j) * d_emb;
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < QE; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < d_emb) a += ld(vr + c) * dv[q];
+            }
+            const float dp = wave_sum(a), ds = p * (dp - od);
+            const T *kr = WK + (r0 + j) * d_in;
+#pragma unroll
+            for (int q = 0; q < QI; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < d_in) dxv[q] += ds * ld(kr + c);
+            }
+            if (lane == 0) {
+                P[(int64_t)s * max_d + j] = p;
+                dS[(int64_t)s * max_d + j] = ds;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+            const int64_t c = lane + 64 * q;
+            if (c < d_in) dx[(int64_t)tok * d_in + c] += dxv[q];
+        }
+    }
+}
+
+// One workgroup per ID block, its rows spread over the four wavefronts: row j of
+// the block gets dK_j = sum over the block's tokens (in sorted order) of dS x and
+// dV_j = sum of P do, added to its table row.
+template <typename T, int QI, int QE>
+__global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const int64_t *__restrict__ off,
+                                                 const int32_t *__restrict__ uniq,
+                                                 const int32_t *__restrict__ seg_start,
+                                                 const int32_t *__restrict__ perm,
+                                                 const int32_t *__restrict__ hdr, int64_t vocab,
+                                                 const float *__restrict__ dov, int64_t d_in,
+                                                 int64_t d_emb, int max_d,
+                                                 const float *__restrict__ P,
+                                                 const float *__restrict__ dS,
+                                                 float *__restrict__ dWK, float *__restrict__ dWV) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = hdr[HDR_NSEG];
+    for (int b = blockIdx.x; b < m; b += gridDim.x) {
+        const int t = uniq[b];
+        if (t < 0 || t >= vocab) continue;
+        const int64_t r0 = off[t];
+        const int d = (int)(off[t + 1] - r0);
+        const int s0 = seg_start[b], s1 = seg_start[b + 1];
+        for (int j = w; j < d; j += 4) {
+            float gk[QI], gv[QE];
+#pragma unroll
+            for (int q = 0; q < QI; ++q) gk[q] = 0.f;
+#pragma unroll
+            for (int q = 0; q < QE; ++q) gv[q] = 0.f;
+            for (int s = s0; s < s1; ++s) {
+                const int tok = perm[s];
+                const float ds = dS[(int64_t)s * max_d + j], p = P[(int64_t)s * max_d + j];
+#pragma unroll
+                for (int q = 0; q < QI; ++q) {
+                    const int64_t c = lane + 64 * q;
+                    if (c < d_in) gk[q] += ds * ld(x + (int64_t)tok * d_in + c);
+                }
+#pragma unroll
+                for (int q = 0; q < QE; ++q) {
+                    const int64_t c = lane + 64 * q;
+                    if (c < d_emb) gv[q] += p * dov[(int64_t)tok * d_emb + c];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < QI; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < d_in) dWK[(r0 + j) * d_in + c] += gk[q];
+            }
+#pragma unroll
+            for (int q = 0; q < QE; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < d_emb) dWV[(r0 + j) * d_emb + c] += gv[q];
+            }
+        }
+    }
+}
+
+template <typename T, int QI, int QE>
+hipError_t launch_token_kernels(const BwdArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((k_attn_bwd<T, QI, QE>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
+                       (const T *)a.WK, (const T *)a.WV, a.perm, a.items, a.hdr, a.dov, a.d_in,
+                       a.d_emb, a.max_d, a.dx, a.P, a.dS);
+    hipLaunchKernelGGL((k_kv_grad<T, QI, QE>), dim3(1024), dim3(256), 0, s, (const T *)a.x, a.off,
+                       a.uniq, a.seg_start, a.perm, a.hdr, a.vocab, a.dov, a.d_in, a.d_emb, a.max_d,
+                       a.P, a.dS, a.dWK, a.dWV);
+    return hipGetLastError();
+}
+
+template <typename T, int QI>
+hipError_t launch_token_qe(const BwdArgs &a, hipStream_t s) {
+    if (a.d_emb <= 256) return launch_token_kernels<T, QI, 4>(a, s);
+    if (a.d_emb <= 512) return launch_token_kernels<T, QI, 8>(a, s);
+    return launch_token_kernels<T, QI, 16>(a, s);
+}
+
+template <typename T>
+hipError_t launch_token_t(const BwdArgs &a, hipStream_t s) {
+    if (a.d_in <= 256) return launch_token_qe<T, 4>(a, s);
+    if (a.d_in <= 1024) return launch_token_qe<T, 16>(a, s);
+    if (a.d_in <= 2048) return launch_token_qe<T, 32>(a, s);
+    return launch_token_qe<T, 64>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const void *src, int64_t ld_src, int64_t rows, int64_t cols, void *dst,
+                            int64_t ld_dst, int64_t rows_pad, int dtype, hipStream_t s) {
+    if (rows_pad <= 0 || cols <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
+    if (dtype == L3_BF16)
+        hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t *)src, ld_src,
+                           rows, cols, (uint16_t *)dst, ld_dst, rows_pad);
+    else
+        hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, (const float *)src, ld_src, rows,
+                           cols, (float *)dst, ld_dst, rows_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, const float *beta,
+                         const float *dy, int64_t n, int64_t d_up, void *dh, void *y, float2 *part,
+                         float *dgamma, float *dbeta, int dtype, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const dim3 g1((unsigned)((n + 3) / 4)), g2((unsigned)((d_up + 255) / 256), (unsigned)ln_param_chunks(n));
+    if (dtype == L3_BF16) {
+        hipLaunchKernelGGL(k_ln_bwd<uint16_t>, g1, dim3(256), 0, s, (const uint16_t *)h, stats, gamma,
+                           beta, dy, n, d_up, (uint16_t *)dh, (uint16_t *)y);
+        hipLaunchKernelGGL(k_ln_param_part<uint16_t>, g2, dim3(256), 0, s, (const uint16_t *)h, stats, dy,
+                           n, d_up, part);
+    } else {
+        hipLaunchKernelGGL(k_ln_bwd<float>, g1, dim3(256), 0, s, (const float *)h, stats, gamma, beta, dy,
+                           n, d_up, (float *)dh, (float *)y);
+        hipLaunchKernelGGL(k_ln_param_part<float>, g2, dim3(256), 0, s, (const float *)h, stats, dy, n,
+                           d_up, part);
+    }
+    hipLaunchKernelGGL(k_ln_param_reduce, dim3((unsigned)((d_up + 255) / 256)), dim3(256), 0, s, part,
+                       ln_param_chunks(n), d_up, dgamma, dbeta);
+    return hipGetLastError();
+}
+
+int ln_param_chunks(int64_t n) { return (int)std::max<int64_t>(1, (n + kLnRows - 1) / kLnRows); }
+
+hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s) {
+    if (a.d_in > 4096 || a.d_emb > 1024) return hipErrorInvalidValue;
+    return dtype == L3_BF16 ? launch_token_t<uint16_t>(a, s) : launch_token_t<float>(a, s);
+}
+
+}  // namespace l3

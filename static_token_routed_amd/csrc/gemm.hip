@@ -55,7 +55,8 @@ constexpr int GROUP_M = 8;
 struct GemmP {
     const uint16_t *A, *A2;  // A columns [0, K1) from A (row stride lda), [K1, K) from A2 (lda2)
     const uint16_t *B, *B2;  // B columns [0, K1) from B (ldb), [K1, K) from B2 (ldb2)
-    uint16_t *C;             // M x N, row stride N
+    uint16_t *C;             // M x N, row stride N (bf16 output)
+    float *Cf;               // M x N, row stride N (fp32 output, OUT = 1 write, 2 add)
     int64_t lda, lda2, ldb, ldb2, K1;
     int64_t M, N, K;
     const float *row_stats;  // [M x 2] (mean, rstd) of the A rows in [0, K1)  (LN_IN)
@@ -80,7 +81,7 @@ __device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
     tn = in / gsz;
 }
 
-template <bool LN_IN, bool LN_OUT>
+template <bool LN_IN, bool LN_OUT, int OUT = 0>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * SLOT];
     // LN_IN: (mean, rstd) of the tile's rows; c1 and c2 of its columns
@@ -305,9 +306,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
                 acc[i][j][2] += c4.z;
                 acc[i][j][3] += c4.w;
             }
-            if (m < p.M && n < p.N)
-                *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
-                    make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+            if (m < p.M && n < p.N) {
+                if constexpr (OUT == 0) {
+                    *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
+                        make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+                } else {
+                    float4 *dst = reinterpret_cast<float4 *>(p.Cf + m * p.N + n);
+                    float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                    if constexpr (OUT == 2) {
+                        const float4 c = *dst;
+                        v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+                    }
+                    *dst = v;
+                }
+            }
         }
         if constexpr (LN_OUT) {
             // partial statistics of this row's stored (bf16) values over each 64
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
                                                   int64_t K, int64_t K1,
                                                   const float *__restrict__ stats,
                                                   const float *__restrict__ gamma,
-                                                  const float *__restrict__ beta) {
+                                                  const float *__restrict__ beta, int accum) {
     __shared__ float as[16][65], bs[16][65];
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
@@ -421,7 +433,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
-            if (m < M && n < N) C[m * N + n] = acc[i][j];
+            if (m < M && n < N) C[m * N + n] = accum ? C[m * N + n] + acc[i][j] : acc[i][j];
         }
 }
 
@@ -521,6 +533,17 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_bf16_f32out(const uint16_t *A, const uint16_t *B, float *C, int64_t M,
+                                   int64_t N, int64_t K, bool accumulate, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    GemmP p = make_plain(A, B, nullptr, M, N, K);
+    p.Cf = C;
+    const dim3 grid(p.tiles_m * p.tiles_n);
+    if (accumulate) hipLaunchKernelGGL((k_gemm_bf16<false, false, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_bf16<false, false, 1>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_ln_finalize(const float *lnp, int64_t M, int64_t d_up, float eps, float *stats,
                               hipStream_t s) {
     if (M <= 0) return hipSuccess;
@@ -570,7 +593,25 @@ hipError_t launch_gemm_f32(const float *A, const float *B, float *C, int64_t M, 
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL((k_gemm_f32<false>), grid, dim3(256), 0, s, A, (const float *)nullptr, B, C,
                        M, N, K, K, (const float *)nullptr, (const float *)nullptr,
-                       (const float *)nullptr);
+                       (const float *)nullptr, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32_acc(const float *A, const float *B, float *C, int64_t M, int64_t N,
+                               int64_t K, bool accumulate, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL((k_gemm_f32<false>), grid, dim3(256), 0, s, A, (const float *)nullptr, B, C,
+                       M, N, K, K, (const float *)nullptr, (const float *)nullptr,
+                       (const float *)nullptr, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_stats_f32(const float *h, int64_t M, int64_t d_up, float eps, float *stats,
+                               hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_ln_stats_f32, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, h, M, d_up, eps,
+                       stats);
     return hipGetLastError();
 }
 
@@ -582,7 +623,7 @@ hipError_t launch_gemm_mix_f32(const float *h, const float *x, float *stats, con
                        eps, stats);
     const dim3 grid((unsigned)((d_out + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL((k_gemm_f32<true>), grid, dim3(256), 0, s, h, x, W_mix, out, M, d_out,
-                       d_up + d_in, d_up, (const float *)stats, gamma, beta);
+                       d_up + d_in, d_up, (const float *)stats, gamma, beta, 0);
     return hipGetLastError();
 }
 

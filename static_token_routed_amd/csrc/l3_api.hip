@@ -109,14 +109,11 @@ int check_offsets(const int64_t *off, int64_t vocab, int64_t v, int32_t k, int32
     return L3_OK;
 }
 
-// One forward over any CSR/table view (the full tables, or a staging's compact copy).
-int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t n, const void *WK,
-                 const void *WV, const void *W_up, const float *gamma, const float *beta,
-                 const void *W_mix, void *out, void *ws, size_t ws_bytes, hipStream_t s) {
+// Route and gather-attention over any CSR/table view: fills the route buffers, the
+// work lists and o (L.o) in the workspace.
+int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                 const void *WV, void *ws, const WsLayout &L, RouteBufs &b, hipStream_t s) {
     const Dims &D = P.dims;
-    const WsLayout L = ws_layout(D, n, P.max_d);
-    if (ws_bytes < L.total) return L3_ERR_CAPACITY;
-    RouteBufs b{};
     b.hdr = ws_ptr<int32_t>(ws, L.hdr);
     b.keys_a = ws_ptr<int32_t>(ws, L.keys_a);
     b.vals_a = ws_ptr<int32_t>(ws, L.vals_a);
@@ -133,8 +130,6 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     int2 *heavy = ws_ptr<int2>(ws, L.heavy);
     int2 *dense = ws_ptr<int2>(ws, L.dense);
     void *o = ws_ptr<char>(ws, L.o);
-    void *h = ws_ptr<char>(ws, L.h);
-    float *lnp = ws_ptr<float>(ws, L.lnp);
 
     const int light_tok = attn_light_tokens(D.d_in, D.dtype);
     const int heavy_min = attn_heavy_min_tokens(D.d_in, D.d_emb, D.dtype, P.max_d);
@@ -163,6 +158,23 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
             L3_HIP_TRY(launch_attn_light(a, D.dtype, s));
         }
     }
+    return L3_OK;
+}
+
+// One forward over any CSR/table view (the full tables, or a staging's compact copy).
+int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                 const void *WV, const void *W_up, const float *gamma, const float *beta,
+                 const void *W_mix, void *out, void *ws, size_t ws_bytes, hipStream_t s) {
+    const Dims &D = P.dims;
+    const WsLayout L = ws_layout(D, n, P.max_d);
+    if (ws_bytes < L.total) return L3_ERR_CAPACITY;
+    RouteBufs b{};
+    const int rc = route_attend(P, x, ids, n, WK, WV, ws, L, b, s);
+    if (rc != L3_OK) return rc;
+    void *o = ws_ptr<char>(ws, L.o);
+    void *h = ws_ptr<char>(ws, L.h);
+    float *lnp = ws_ptr<float>(ws, L.lnp);
+
     if (D.dtype == L3_BF16 && n <= kSkinnyMaxM) {
         float *part = ws_ptr<float>(ws, L.part);
         {
@@ -209,6 +221,123 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
                                            D.d_out, s));
         }
     }
+    return L3_OK;
+}
+
+
+// Backward workspace: the forward's regions, then those of the backward pass.
+struct BwdLayout {
+    WsLayout f;
+    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, total;
+    int64_t n_pad;
+};
+
+BwdLayout bwd_layout(const Dims &d, int64_t n_max, int32_t max_d) {
+    BwdLayout B{};
+    B.f = ws_layout(d, n_max, max_d);
+    const int64_t n = std::max<int64_t>(n_max, 1);
+    B.n_pad = (n + 63) / 64 * 64;
+    const size_t es = esize(d.dtype);
+    const int64_t Z = d.d_up + d.d_in;
+    size_t off = B.f.total;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    B.wmt = take((size_t)Z * d.d_out * es);
+    B.dy = take((size_t)n * d.d_up * 4);
+    B.dh = take((size_t)n * d.d_up * es);
+    B.y = take((size_t)n * d.d_up * es);
+    B.doutT = take((size_t)d.d_out * B.n_pad * es);
+    B.zT = take((size_t)Z * B.n_pad * es);
+    B.dhT = take((size_t)d.d_up * B.n_pad * es);
+    B.oT = take((size_t)d.d_emb * B.n_pad * es);
+    B.wupT = take((size_t)d.d_emb * d.d_up * es);
+    B.dov = take((size_t)n * d.d_emb * 4);
+    B.P = take((size_t)n * std::max(max_d, 1) * 4);
+    B.dS = take((size_t)n * std::max(max_d, 1) * 4);
+    B.part = take((size_t)ln_param_chunks(n) * d.d_up * 8);
+    B.total = off;
+    return B;
+}
+
+// C = A B^T (A: M x K, B: N x K), fp32 output written or added, by dtype.
+hipError_t gemm_f32out(int dtype, const void *A, const void *B, float *C, int64_t M, int64_t N,
+                       int64_t K, bool acc, hipStream_t s) {
+    if (dtype == L3_BF16)
+        return launch_gemm_bf16_f32out((const uint16_t *)A, (const uint16_t *)B, C, M, N, K, acc, s);
+    return launch_gemm_f32_acc((const float *)A, (const float *)B, C, M, N, K, acc, s);
+}
+
+int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                  const void *WV, const void *W_up, const float *gamma, const float *beta,
+                  const void *W_mix, const void *dout, float *dx, float *dWK, float *dWV, float *dWup,
+                  float *dgamma, float *dbeta, float *dWmix, void *ws, size_t ws_bytes,
+                  hipStream_t s) {
+    const Dims &D = P.dims;
+    const BwdLayout B = bwd_layout(D, n, P.max_d);
+    if (ws_bytes < B.total) return L3_ERR_CAPACITY;
+    const WsLayout &L = B.f;
+    const int dt = D.dtype;
+    const size_t es = esize(dt);
+    const int64_t Z = D.d_up + D.d_in, np = B.n_pad;
+    // forward again up to LayerNorm's statistics: o, h, (mean, rstd)
+    RouteBufs b{};
+    int rc = route_attend(P, x, ids, n, WK, WV, ws, L, b, s);
+    if (rc != L3_OK) return rc;
+    void *o = ws_ptr<char>(ws, L.o), *h = ws_ptr<char>(ws, L.h);
+    float *lnp = ws_ptr<float>(ws, L.lnp), *stats = ws_ptr<float>(ws, L.stats);
+    if (dt == L3_BF16) {
+        if (n <= kSkinnyMaxM)
+            L3_HIP_TRY(launch_gemm_skinny_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h,
+                                               n, D.d_up, D.d_emb, lnp, ws_ptr<float>(ws, L.part), s));
+        else
+            L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h, n,
+                                        D.d_up, D.d_emb, lnp, s));
+        L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
+    } else {
+        L3_HIP_TRY(launch_gemm_f32((const float *)o, (const float *)W_up, (float *)h, n, D.d_up, D.d_emb,
+                                   s));
+        L3_HIP_TRY(launch_ln_stats_f32((const float *)h, n, D.d_up, D.eps, stats, s));
+    }
+    char *wmt = ws_ptr<char>(ws, B.wmt);
+    float *dy = ws_ptr<float>(ws, B.dy), *dov = ws_ptr<float>(ws, B.dov);
+    void *dh = ws_ptr<char>(ws, B.dh), *y = ws_ptr<char>(ws, B.y);
+    char *doutT = ws_ptr<char>(ws, B.doutT), *zT = ws_ptr<char>(ws, B.zT);
+    void *dhT = ws_ptr<char>(ws, B.dhT), *oT = ws_ptr<char>(ws, B.oT), *wupT = ws_ptr<char>(ws, B.wupT);
+    // dy = W1^T dout, dx = W2^T dout  (W_mix^T rows [0, d_up) and [d_up, Z))
+    L3_HIP_TRY(launch_transpose(W_mix, Z, D.d_out, Z, wmt, D.d_out, D.d_out, dt, s));
+    L3_HIP_TRY(gemm_f32out(dt, dout, wmt, dy, n, D.d_up, D.d_out, false, s));
+    L3_HIP_TRY(gemm_f32out(dt, dout, wmt + (size_t)D.d_up * D.d_out * es, dx, n, D.d_in, D.d_out, false,
+                           s));
+    // LayerNorm: dh, y, dgamma, dbeta
+    L3_HIP_TRY(launch_ln_bwd(h, stats, gamma, beta, dy, n, D.d_up, dh, y, ws_ptr<float2>(ws, B.part),
+                             dgamma, dbeta, dt, s));
+    // dW_mix += dout^T [y ; x]   (K = tokens, zero-padded to a multiple of 64)
+    L3_HIP_TRY(launch_transpose(dout, D.d_out, n, D.d_out, doutT, np, np, dt, s));
+    L3_HIP_TRY(launch_transpose(y, D.d_up, n, D.d_up, zT, np, np, dt, s));
+    L3_HIP_TRY(launch_transpose(x, D.d_in, n, D.d_in, zT + (size_t)D.d_up * np * es, np, np, dt, s));
+    L3_HIP_TRY(gemm_f32out(dt, doutT, zT, dWmix, D.d_out, Z, np, true, s));
+    // dW_up += dh o^T, do = W_up^T dh
+    L3_HIP_TRY(launch_transpose(dh, D.d_up, n, D.d_up, dhT, np, np, dt, s));
+    L3_HIP_TRY(launch_transpose(o, D.d_emb, n, D.d_emb, oT, np, np, dt, s));
+    L3_HIP_TRY(gemm_f32out(dt, dhT, oT, dWup, D.d_up, D.d_emb, np, true, s));
+    L3_HIP_TRY(launch_transpose(W_up, D.d_emb, D.d_up, D.d_emb, wupT, D.d_up, D.d_up, dt, s));
+    L3_HIP_TRY(gemm_f32out(dt, dh, wupT, dov, n, D.d_emb, D.d_up, false, s));
+    // attention: one-token items over every block, then the key / value gradients
+    int4 *items = ws_ptr<int4>(ws, L.light);
+    L3_HIP_TRY(launch_zero_i32(b.hdr + HDR_NLIGHT, 3, s));
+    L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, INT32_MAX, INT32_MAX, 1, items,
+                               ws_ptr<int2>(ws, L.heavy), ws_ptr<int2>(ws, L.dense), s));
+    BwdArgs a{};
+    a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
+    a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
+    a.items = items; a.dov = dov;
+    a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab; a.max_d = P.max_d;
+    a.dx = dx; a.P = ws_ptr<float>(ws, B.P); a.dS = ws_ptr<float>(ws, B.dS);
+    a.dWK = dWK; a.dWV = dWV;
+    L3_HIP_TRY(launch_attn_bwd(a, dt, s));
     return L3_OK;
 }
 
@@ -355,6 +484,30 @@ int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const 
     if (reinterpret_cast<uintptr_t>(ids) & 3) return L3_ERR_INVALID_ARG;
     return forward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, out, ws, ws_bytes,
                         (hipStream_t)stream);
+}
+
+size_t l3_backward_workspace_size(l3_plan_t p, int64_t n_max) {
+    if (!p || n_max < 0) return 0;
+    return bwd_layout(p->dims, n_max, p->max_d).total;
+}
+
+int l3_backward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                const void *WV, const void *W_up, const float *gamma, const float *beta,
+                const void *W_mix, const void *dout, float *dx, float *dWK, float *dWV, float *dWup,
+                float *dgamma, float *dbeta, float *dWmix, void *ws, size_t ws_bytes, void *stream) {
+    if (!p || n < 0) return L3_ERR_INVALID_ARG;
+    if (n == 0) return L3_OK;
+    if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
+    if (!x || !ids || !WK || !WV || !W_up || !gamma || !beta || !W_mix || !dout || !dx || !dWK ||
+        !dWV || !dWup || !dgamma || !dbeta || !dWmix || !ws)
+        return L3_ERR_INVALID_ARG;
+    if (!aligned16({x, WK, WV, W_up, gamma, beta, W_mix, dout, dx, dWK, dWV, dWup, dgamma, dbeta,
+                    dWmix, ws}))
+        return L3_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(ids) & 3) return L3_ERR_INVALID_ARG;
+    if (p->dims.d_in > 4096 || p->dims.d_emb > 1024) return L3_ERR_UNSUPPORTED;
+    return backward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, dout, dx, dWK, dWV, dWup,
+                         dgamma, dbeta, dWmix, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_bytes, void *stream,

@@ -139,4 +139,38 @@ hipError_t launch_gemm_mix_f32(const float *h, const float *x, float *stats, con
                                const float *beta, float eps, const float *W_mix, float *out,
                                int64_t M, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 
+// ---- backward pass
+// fp32 GEMMs with fp32 output, written or added to C (C = A B^T as above)
+hipError_t launch_gemm_bf16_f32out(const uint16_t *A, const uint16_t *B, float *C, int64_t M,
+                                   int64_t N, int64_t K, bool accumulate, hipStream_t s);
+hipError_t launch_gemm_f32_acc(const float *A, const float *B, float *C, int64_t M, int64_t N,
+                               int64_t K, bool accumulate, hipStream_t s);
+// stats [M x 2] = (mean, 1/sqrt(var + eps)) per row of an fp32 h
+hipError_t launch_ln_stats_f32(const float *h, int64_t M, int64_t d_up, float eps, float *stats,
+                               hipStream_t s);
+// dst [cols x ld_dst] = src^T (rows >= `rows` up to rows_pad zero-filled), element
+// type by dtype
+hipError_t launch_transpose(const void *src, int64_t ld_src, int64_t rows, int64_t cols, void *dst,
+                            int64_t ld_dst, int64_t rows_pad, int dtype, hipStream_t s);
+// LayerNorm backward: dh and y = LN(h) per row, and dgamma += sum dy*yhat, dbeta +=
+// sum dy (column partials of ln_param_chunks(n) row chunks, reduced in order)
+int ln_param_chunks(int64_t n);
+hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, const float *beta,
+                         const float *dy, int64_t n, int64_t d_up, void *dh, void *y, float2 *part,
+                         float *dgamma, float *dbeta, int dtype, hipStream_t s);
+struct BwdArgs {
+    const void *x, *WK, *WV;
+    const int64_t *off;
+    const int32_t *uniq, *seg_start, *perm, *hdr;
+    const int4 *items;   // one token per item (first sorted position, 1, first row, d_t)
+    const float *dov;    // dL/do [n x d_emb]
+    int64_t d_in, d_emb, vocab;
+    int max_d;
+    float *dx;           // [n x d_in], holds W2^T dout; the attention term is added
+    float *P, *dS;       // [n x max_d] per sorted position
+    float *dWK, *dWV;    // accumulated
+};
+// attention backward per token, then the key / value gradients per ID block
+hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s);
+
 }  // namespace l3
