@@ -219,57 +219,87 @@ __global__ __launch_bounds__(256) void k_attn_bwd(const T *__restrict__ x, const
     }
 }
 
-// One workgroup per ID block, its rows spread over the four wavefronts: row j of
-// the block gets dK_j = sum over the block's tokens (in sorted order) of dS x and
-// dV_j = sum of P do, added to its table row.
-template <typename T, int QI, int QE>
+// Work items of the key / value gradients: (block, 16-row tile) pairs, appended
+// one thread per block (the order of items does not affect the results: each item
+// owns its rows' gradients outright).
+constexpr int kKvRows = 16;
+constexpr int kKvTok = 32;
+__global__ __launch_bounds__(256) void k_kv_items(const int64_t *__restrict__ off,
+                                                  const int32_t *__restrict__ uniq,
+                                                  int32_t *__restrict__ hdr, int64_t vocab,
+                                                  int2 *__restrict__ items, int cap) {
+    const int m = hdr[HDR_NSEG];
+    for (int b = blockIdx.x * 256 + threadIdx.x; b < m; b += gridDim.x * 256) {
+        const int t = uniq[b];
+        if (t < 0 || t >= vocab) continue;
+        const int d = (int)(off[t + 1] - off[t]);
+        const int nt = (d + kKvRows - 1) / kKvRows;
+        const int at = atomicAdd(&hdr[HDR_NKV], nt);
+        for (int r = 0; r < nt && at + r < cap; ++r) items[at + r] = make_int2(b, r * kKvRows);
+    }
+}
+
+// One workgroup per item: rows j0 .. j0+15 of block b, every column of K (d_in) and V
+// (d_emb); thread t owns columns t, t + 256, ...  For each chunk of 32 tokens (sorted
+// order) the workgroup stages their dS and P values for the 16 rows and their
+// token indices in LDS; each thread then adds dS * x (K columns) or P * do (V
+// columns) over the chunk into 16 accumulators per column.
+template <typename T>
 __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const int64_t *__restrict__ off,
                                                  const int32_t *__restrict__ uniq,
                                                  const int32_t *__restrict__ seg_start,
                                                  const int32_t *__restrict__ perm,
-                                                 const int32_t *__restrict__ hdr, int64_t vocab,
+                                                 const int32_t *__restrict__ hdr,
+                                                 const int2 *__restrict__ items, int cap,
                                                  const float *__restrict__ dov, int64_t d_in,
                                                  int64_t d_emb, int max_d,
                                                  const float *__restrict__ P,
                                                  const float *__restrict__ dS,
                                                  float *__restrict__ dWK, float *__restrict__ dWV) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int m = hdr[HDR_NSEG];
-    for (int b = blockIdx.x; b < m; b += gridDim.x) {
-        const int t = uniq[b];
-        if (t < 0 || t >= vocab) continue;
+    __shared__ float sds[kKvTok][kKvRows], sp[kKvTok][kKvRows];
+    __shared__ int stok[kKvTok];
+    const int nitems = min(hdr[HDR_NKV], cap);
+    const int64_t ncol = d_in + d_emb;
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        const int2 item = items[it];
+        const int t = uniq[item.x];
         const int64_t r0 = off[t];
-        const int d = (int)(off[t + 1] - r0);
-        const int s0 = seg_start[b], s1 = seg_start[b + 1];
-        for (int j = w; j < d; j += 4) {
-            float gk[QI], gv[QE];
+        const int d = (int)(off[t + 1] - r0), j0 = item.y;
+        const int nr = min(kKvRows, d - j0);
+        const int s0 = seg_start[item.x], s1 = seg_start[item.x + 1];
+        for (int64_t cb = 0; cb < ncol; cb += 256) {
+            const int64_t c = cb + threadIdx.x;
+            const bool isk = c < d_in;
+            float acc[kKvRows];
 #pragma unroll
-            for (int q = 0; q < QI; ++q) gk[q] = 0.f;
-#pragma unroll
-            for (int q = 0; q < QE; ++q) gv[q] = 0.f;
-            for (int s = s0; s < s1; ++s) {
-                const int tok = perm[s];
-                const float ds = dS[(int64_t)s * max_d + j], p = P[(int64_t)s * max_d + j];
-#pragma unroll
-                for (int q = 0; q < QI; ++q) {
-                    const int64_t c = lane + 64 * q;
-                    if (c < d_in) gk[q] += ds * ld(x + (int64_t)tok * d_in + c);
+            for (int r = 0; r < kKvRows; ++r) acc[r] = 0.f;
+            for (int sc = s0; sc < s1; sc += kKvTok) {
+                const int nt = min(kKvTok, s1 - sc);
+                __syncthreads();
+                for (int e = threadIdx.x; e < kKvTok * kKvRows; e += 256) {
+                    const int tt = e / kKvRows, r = e % kKvRows;
+                    const bool ok = tt < nt && r < nr;
+                    sds[tt][r] = ok ? dS[(int64_t)(sc + tt) * max_d + j0 + r] : 0.f;
+                    sp[tt][r] = ok ? P[(int64_t)(sc + tt) * max_d + j0 + r] : 0.f;
                 }
+                if (threadIdx.x < kKvTok) stok[threadIdx.x] = threadIdx.x < nt ? perm[sc + threadIdx.x] : 0;
+                __syncthreads();
+                if (c < ncol) {
+                    for (int tt = 0; tt < nt; ++tt) {
+                        const int tok = stok[tt];
+                        const float xv = isk ? ld(x + (int64_t)tok * d_in + c)
+                                             : dov[(int64_t)tok * d_emb + (c - d_in)];
+                        const float *w = isk ? sds[tt] : sp[tt];
 #pragma unroll
-                for (int q = 0; q < QE; ++q) {
-                    const int64_t c = lane + 64 * q;
-                    if (c < d_emb) gv[q] += p * dov[(int64_t)tok * d_emb + c];
+                        for (int r = 0; r < kKvRows; ++r) acc[r] = fmaf(w[r], xv, acc[r]);
+                    }
                 }
             }
-#pragma unroll
-            for (int q = 0; q < QI; ++q) {
-                const int64_t c = lane + 64 * q;
-                if (c < d_in) dWK[(r0 + j) * d_in + c] += gk[q];
-            }
-#pragma unroll
-            for (int q = 0; q < QE; ++q) {
-                const int64_t c = lane + 64 * q;
-                if (c < d_emb) dWV[(r0 + j) * d_emb + c] += gv[q];
+            if (c < ncol) {
+                for (int r = 0; r < nr; ++r) {
+                    if (isk) dWK[(r0 + j0 + r) * d_in + c] += acc[r];
+                    else dWV[(r0 + j0 + r) * d_emb + (c - d_in)] += acc[r];
+                }
             }
         }
     }
@@ -280,9 +310,11 @@ hipError_t launch_token_kernels(const BwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((k_attn_bwd<T, QI, QE>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
                        (const T *)a.WK, (const T *)a.WV, a.perm, a.items, a.hdr, a.dov, a.d_in,
                        a.d_emb, a.max_d, a.dx, a.P, a.dS);
-    hipLaunchKernelGGL((k_kv_grad<T, QI, QE>), dim3(1024), dim3(256), 0, s, (const T *)a.x, a.off,
-                       a.uniq, a.seg_start, a.perm, a.hdr, a.vocab, a.dov, a.d_in, a.d_emb, a.max_d,
-                       a.P, a.dS, a.dWK, a.dWV);
+    hipLaunchKernelGGL(k_kv_items, dim3(64), dim3(256), 0, s, a.off, a.uniq, const_cast<int32_t *>(a.hdr),
+                       a.vocab, a.kv_items, a.kv_cap);
+    hipLaunchKernelGGL((k_kv_grad<T>), dim3(2048), dim3(256), 0, s, (const T *)a.x, a.off, a.uniq,
+                       a.seg_start, a.perm, a.hdr, a.kv_items, a.kv_cap, a.dov, a.d_in, a.d_emb,
+                       a.max_d, a.P, a.dS, a.dWK, a.dWV);
     return hipGetLastError();
 }
 
@@ -335,6 +367,10 @@ hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, 
     hipLaunchKernelGGL(k_ln_param_reduce, dim3((unsigned)((d_up + 255) / 256)), dim3(256), 0, s, part,
                        ln_param_chunks(n), d_up, dgamma, dbeta);
     return hipGetLastError();
+}
+
+int kv_item_capacity(int64_t n, int64_t rows) {
+    return (int)std::min<int64_t>(INT32_MAX, n + rows / kKvRows + 1);
 }
 
 int ln_param_chunks(int64_t n) { return (int)std::max<int64_t>(1, (n + kLnRows - 1) / kLnRows); }

@@ -228,7 +228,8 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
 // Backward workspace: the forward's regions, then those of the backward pass.
 struct BwdLayout {
     WsLayout f;
-    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, total;
+    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, kv, total;
+    int kv_cap;
     int64_t n_pad;
 };
 
@@ -258,6 +259,9 @@ BwdLayout bwd_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     B.P = take((size_t)n * std::max(max_d, 1) * 4);
     B.dS = take((size_t)n * std::max(max_d, 1) * 4);
     B.part = take((size_t)ln_param_chunks(n) * d.d_up * 8);
+    // distinct rows of a batch: at most n tokens' worth of max_d rows
+    B.kv_cap = kv_item_capacity(n, (int64_t)n * std::max(max_d, 1));
+    B.kv = take((size_t)B.kv_cap * 8);
     B.total = off;
     return B;
 }
@@ -327,7 +331,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     L3_HIP_TRY(gemm_f32out(dt, dh, wupT, dov, n, D.d_emb, D.d_up, false, s));
     // attention: one-token items over every block, then the key / value gradients
     int4 *items = ws_ptr<int4>(ws, L.light);
-    L3_HIP_TRY(launch_zero_i32(b.hdr + HDR_NLIGHT, 3, s));
+    L3_HIP_TRY(launch_zero_i32(b.hdr + HDR_NLIGHT, 4, s));  // NLIGHT, NHEAVY, NDENSE, NKV
     L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, INT32_MAX, INT32_MAX, 1, items,
                                ws_ptr<int2>(ws, L.heavy), ws_ptr<int2>(ws, L.dense), s));
     BwdArgs a{};
@@ -337,6 +341,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab; a.max_d = P.max_d;
     a.dx = dx; a.P = ws_ptr<float>(ws, B.P); a.dS = ws_ptr<float>(ws, B.dS);
     a.dWK = dWK; a.dWV = dWV;
+    a.kv_items = ws_ptr<int2>(ws, B.kv); a.kv_cap = B.kv_cap;
     L3_HIP_TRY(launch_attn_bwd(a, dt, s));
     return L3_OK;
 }

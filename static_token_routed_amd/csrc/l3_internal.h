@@ -27,8 +27,8 @@ constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ..
 constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense items
 
 // Workspace header (int32 words), zeroed at the start of every call.
-enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_QUEUE = 8,
-       HDR_WORDS = 64 };
+enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_NKV = 5,
+       HDR_QUEUE = 8, HDR_WORDS = 64 };
 
 struct Dims {
     int64_t d_in, d_emb, d_up, d_out;
@@ -169,7 +169,11 @@ struct BwdArgs {
     float *dx;           // [n x d_in], holds W2^T dout; the attention term is added
     float *P, *dS;       // [n x max_d] per sorted position
     float *dWK, *dWV;    // accumulated
+    int2 *kv_items;      // (block, first row) items of the key / value gradients
+    int kv_cap;          // their capacity (kv_item_capacity)
 };
+// items of the key / value gradients: at most one per block plus one per 16 rows
+int kv_item_capacity(int64_t n, int64_t rows);
 // attention backward per token, then the key / value gradients per ID block
 hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s);
 
