@@ -124,12 +124,34 @@ __global__ __launch_bounds__(256) void k_ln_param_reduce(const float2 *__restric
     dbeta[c] += b;
 }
 
-// One wavefront per token (a light work item of one token: sorted position, count,
-// first table row, d_t).  Pass 1 over the block's rows: scores, running max and sum,
-// and o = V_t^T p, giving <o, do>.  Pass 2: p_j, dp_j = <V_t[j], do>, ds_j, dx +=
-// sum_j ds_j K_t[j] (dx holds W2^T dout already), and P, dS stored per sorted
-// position for the key / value gradients.  Lane l handles elements l + 64 q.
-template <typename T, int QI, int QE>
+// 16-byte chunk c (elements CH c .. CH c + CH - 1) of a row, as floats.
+template <typename T, int CH>
+__device__ inline void load_chunk(const T *row, int64_t c, float (&v)[CH]) {
+    if constexpr (sizeof(T) == 2 && CH == 8) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(row + c * 8);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    } else if constexpr (sizeof(T) == 4 && CH == 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(row + c * 4);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < CH; ++e) v[e] = ld(row + c * CH + e);
+    }
+}
+
+// One wavefront per work item: up to TB tokens of one block (sorted positions
+// s0 .. s0 + cnt - 1), the block's rows r0 .. r0 + d - 1.  Lane l holds 16-byte
+// chunks l, l + 64, ... of each row (NI chunks of d_in, NE of d_emb).  Pass 1 over
+// the rows: scores, running max and sum, and o = V_t^T p, giving <o, do> per
+// token.  Pass 2: p_j, dp_j = <V_t[j], do>, ds_j, dx += ds_j K_t[j] (the K row is
+// still in registers from the score), and P, dS stored per sorted position for
+// the key / value gradients.  Every row is read once per pass for all TB tokens.
+template <typename T, int CH, int NI, int NE, int TB>
 __global__ __launch_bounds__(256) void k_attn_bwd(const T *__restrict__ x, const T *__restrict__ WK,
                                                   const T *__restrict__ WV,
                                                   const int32_t *__restrict__ perm,
@@ -141,80 +163,145 @@ __global__ __launch_bounds__(256) void k_attn_bwd(const T *__restrict__ x, const
     const int lane = threadIdx.x & 63;
     const int nitems = hdr[HDR_NLIGHT];
     const int nw = gridDim.x * 4;
+    const int64_t ci = d_in / CH, ce = d_emb / CH;  // chunks per row
     for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += nw) {
         const int4 item = items[it];
         if (item.w < 0) continue;  // ID out of range: no gradient (flagged by the route)
-        const int s = item.x, tok = perm[s];
+        const int s0 = item.x, cnt = item.y;
         const int64_t r0 = item.z;
         const int d = item.w;
-        float xv[QI], dxv[QI], dv[QE], ov[QE];
+        int tok[TB];
+        float xv[TB][NI][CH], dxv[TB][NI][CH], dv[TB][NE][CH], ov[TB][NE][CH];
 #pragma unroll
-        for (int q = 0; q < QI; ++q) {
-            const int64_t c = lane + 64 * q;
-            xv[q] = c < d_in ? ld(x + (int64_t)tok * d_in + c) : 0.f;
-            dxv[q] = 0.f;
-        }
+        for (int b = 0; b < TB; ++b) {
+            tok[b] = b < cnt ? perm[s0 + b] : perm[s0];
 #pragma unroll
-        for (int q = 0; q < QE; ++q) {
-            const int64_t c = lane + 64 * q;
-            dv[q] = c < d_emb ? dov[(int64_t)tok * d_emb + c] : 0.f;
-            ov[q] = 0.f;
-        }
-        auto score = [&](int j) {
-            const T *kr = WK + (r0 + j) * d_in;
-            float a = 0.f;
-#pragma unroll
-            for (int q = 0; q < QI; ++q) {
+            for (int q = 0; q < NI; ++q) {
                 const int64_t c = lane + 64 * q;
-                if (c < d_in) a += ld(kr + c) * xv[q];
+                if (c < ci) load_chunk<T, CH>(x + (int64_t)tok[b] * d_in, c, xv[b][q]);
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    if (c >= ci) xv[b][q][e] = 0.f;
+                    dxv[b][q][e] = 0.f;
+                }
             }
-            return wave_sum(a);
+#pragma unroll
+            for (int q = 0; q < NE; ++q) {
+                const int64_t c = lane + 64 * q;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    dv[b][q][e] = c < ce ? dov[(int64_t)tok[b] * d_emb + c * CH + e] : 0.f;
+                    ov[b][q][e] = 0.f;
+                }
+            }
+        }
+        // the K row's chunks, and the TB scores against it
+        auto krow = [&](int j, float (&kv)[NI][CH], float (&sc)[TB]) {
+            const T *kr = WK + (r0 + j) * d_in;
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < ci) load_chunk<T, CH>(kr, c, kv[q]);
+                else
+#pragma unroll
+                    for (int e = 0; e < CH; ++e) kv[q][e] = 0.f;
+            }
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int e = 0; e < CH; ++e) a = fmaf(kv[q][e], xv[b][q][e], a);
+                sc[b] = a;
+            }
+#pragma unroll
+            for (int b = 0; b < TB; ++b) sc[b] = wave_sum(sc[b]);
+        };
+        auto vrow = [&](int j, float (&vv)[NE][CH]) {
+            const T *vr = WV + (r0 + j) * d_emb;
+#pragma unroll
+            for (int q = 0; q < NE; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < ce) load_chunk<T, CH>(vr, c, vv[q]);
+                else
+#pragma unroll
+                    for (int e = 0; e < CH; ++e) vv[q][e] = 0.f;
+            }
         };
         // pass 1: max, sum, o
-        float m = -INFINITY, l = 0.f;
-        for (int j = 0; j < d; ++j) {
-            const float sc = score(j);
-            const float mn = fmaxf(m, sc), alpha = __expf(m - mn), e = __expf(sc - mn);
-            l = l * alpha + e;
-            const T *vr = WV + (r0 + j) * d_emb;
+        float m[TB], l[TB];
 #pragma unroll
-            for (int q = 0; q < QE; ++q) {
-                const int64_t c = lane + 64 * q;
-                ov[q] = ov[q] * alpha + (c < d_emb ? e * ld(vr + c) : 0.f);
+        for (int b = 0; b < TB; ++b) { m[b] = -INFINITY; l[b] = 0.f; }
+        for (int j = 0; j < d; ++j) {
+            float kv[NI][CH], sc[TB], vv[NE][CH];
+            krow(j, kv, sc);
+            vrow(j, vv);
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                const float mn = fmaxf(m[b], sc[b]), alpha = __expf(m[b] - mn), e = __expf(sc[b] - mn);
+                l[b] = l[b] * alpha + e;
+                m[b] = mn;
+#pragma unroll
+                for (int q = 0; q < NE; ++q)
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) ov[b][q][c] = fmaf(e, vv[q][c], ov[b][q][c] * alpha);
             }
-            m = mn;
         }
-        const float inv = 1.f / l;
-        float od = 0.f;
+        float inv[TB], od[TB];
 #pragma unroll
-        for (int q = 0; q < QE; ++q) od += ov[q] * inv * dv[q];
-        od = wave_sum(od);
-        // pass 2
-        for (int j = 0; j < d; ++j) {
-            const float p = __expf(score(j) - m) * inv;
-            const T *vr = WV + (r0 + j) * d_emb;
+        for (int b = 0; b < TB; ++b) {
+            inv[b] = 1.f / l[b];
             float a = 0.f;
 #pragma unroll
-            for (int q = 0; q < QE; ++q) {
-                const int64_t c = lane + 64 * q;
-                if (c < d_emb) a += ld(vr + c) * dv[q];
-            }
-            const float dp = wave_sum(a), ds = p * (dp - od);
-            const T *kr = WK + (r0 + j) * d_in;
+            for (int q = 0; q < NE; ++q)
 #pragma unroll
-            for (int q = 0; q < QI; ++q) {
-                const int64_t c = lane + 64 * q;
-                if (c < d_in) dxv[q] += ds * ld(kr + c);
+                for (int c = 0; c < CH; ++c) a = fmaf(ov[b][q][c] * inv[b], dv[b][q][c], a);
+            od[b] = a;
+        }
+#pragma unroll
+        for (int b = 0; b < TB; ++b) od[b] = wave_sum(od[b]);
+        // pass 2
+        for (int j = 0; j < d; ++j) {
+            float kv[NI][CH], sc[TB], vv[NE][CH], dp[TB];
+            krow(j, kv, sc);
+            vrow(j, vv);
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < NE; ++q)
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) a = fmaf(vv[q][c], dv[b][q][c], a);
+                dp[b] = a;
             }
-            if (lane == 0) {
-                P[(int64_t)s * max_d + j] = p;
-                dS[(int64_t)s * max_d + j] = ds;
+#pragma unroll
+            for (int b = 0; b < TB; ++b) dp[b] = wave_sum(dp[b]);
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                const float p = __expf(sc[b] - m[b]) * inv[b], ds = p * (dp[b] - od[b]);
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) dxv[b][q][c] = fmaf(ds, kv[q][c], dxv[b][q][c]);
+                if (lane == 0 && b < cnt) {
+                    P[(int64_t)(s0 + b) * max_d + j] = p;
+                    dS[(int64_t)(s0 + b) * max_d + j] = ds;
+                }
             }
         }
 #pragma unroll
-        for (int q = 0; q < QI; ++q) {
-            const int64_t c = lane + 64 * q;
-            if (c < d_in) dx[(int64_t)tok * d_in + c] += dxv[q];
+        for (int b = 0; b < TB; ++b) {
+            if (b >= cnt) break;
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                const int64_t c = lane + 64 * q;
+                if (c < ci) {
+                    float *dst = dx + (int64_t)tok[b] * d_in + c * CH;
+#pragma unroll
+                    for (int e = 0; e < CH; ++e) dst[e] += dxv[b][q][e];
+                }
+            }
         }
     }
 }
@@ -240,11 +327,12 @@ __global__ __launch_bounds__(256) void k_kv_items(const int64_t *__restrict__ of
 }
 
 // One workgroup per item: rows j0 .. j0+15 of block b, every column of K (d_in) and V
-// (d_emb); thread t owns columns t, t + 256, ...  For each chunk of 32 tokens (sorted
-// order) the workgroup stages their dS and P values for the 16 rows and their
-// token indices in LDS; each thread then adds dS * x (K columns) or P * do (V
-// columns) over the chunk into 16 accumulators per column.
-template <typename T>
+// (d_emb).  Thread t owns one 16-byte chunk of columns per pass (CH elements of x for
+// K, 4 floats of do for V).  For each chunk of 32 tokens (sorted order) the workgroup
+// stages their dS and P values for the 16 rows and their token indices in LDS;
+// each thread then adds dS * x (K) or P * do (V) over the chunk into 16 x CH
+// accumulators: one vector load feeds 16 CH multiply-adds.
+template <typename T, int CH>
 __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const int64_t *__restrict__ off,
                                                  const int32_t *__restrict__ uniq,
                                                  const int32_t *__restrict__ seg_start,
@@ -258,8 +346,9 @@ __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const 
                                                  float *__restrict__ dWK, float *__restrict__ dWV) {
     __shared__ float sds[kKvTok][kKvRows], sp[kKvTok][kKvRows];
     __shared__ int stok[kKvTok];
+    constexpr int CV = CH == 8 ? 4 : CH;  // floats of do per chunk
     const int nitems = min(hdr[HDR_NKV], cap);
-    const int64_t ncol = d_in + d_emb;
+    const int64_t ck = d_in / CH, cv = d_emb / CV;  // chunks per row
     for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
         const int2 item = items[it];
         const int t = uniq[item.x];
@@ -267,12 +356,15 @@ __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const 
         const int d = (int)(off[t + 1] - r0), j0 = item.y;
         const int nr = min(kKvRows, d - j0);
         const int s0 = seg_start[item.x], s1 = seg_start[item.x + 1];
-        for (int64_t cb = 0; cb < ncol; cb += 256) {
+        // passes of 256 chunks: first the K chunks, then the V chunks
+        for (int64_t cb = 0; cb < ck + cv; cb += 256) {
             const int64_t c = cb + threadIdx.x;
-            const bool isk = c < d_in;
-            float acc[kKvRows];
+            const bool isk = c < ck, live = c < ck + cv;
+            float acc[kKvRows][CH];
 #pragma unroll
-            for (int r = 0; r < kKvRows; ++r) acc[r] = 0.f;
+            for (int r = 0; r < kKvRows; ++r)
+#pragma unroll
+                for (int e = 0; e < CH; ++e) acc[r][e] = 0.f;
             for (int sc = s0; sc < s1; sc += kKvTok) {
                 const int nt = min(kKvTok, s1 - sc);
                 __syncthreads();
@@ -284,53 +376,67 @@ __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const 
                 }
                 if (threadIdx.x < kKvTok) stok[threadIdx.x] = threadIdx.x < nt ? perm[sc + threadIdx.x] : 0;
                 __syncthreads();
-                if (c < ncol) {
-                    for (int tt = 0; tt < nt; ++tt) {
-                        const int tok = stok[tt];
-                        const float xv = isk ? ld(x + (int64_t)tok * d_in + c)
-                                             : dov[(int64_t)tok * d_emb + (c - d_in)];
-                        const float *w = isk ? sds[tt] : sp[tt];
+                if (!live) continue;
+                for (int tt = 0; tt < nt; ++tt) {
+                    const int tok = stok[tt];
+                    float v[CH];
+                    const float *w;
+                    if (isk) {
+                        load_chunk<T, CH>(x + (int64_t)tok * d_in, c, v);
+                        w = sds[tt];
+                    } else {
+                        const float *src = dov + (int64_t)tok * d_emb + (c - ck) * CV;
 #pragma unroll
-                        for (int r = 0; r < kKvRows; ++r) acc[r] = fmaf(w[r], xv, acc[r]);
+                        for (int e = 0; e < CH; ++e) v[e] = e < CV ? src[e] : 0.f;
+                        w = sp[tt];
                     }
+#pragma unroll
+                    for (int r = 0; r < kKvRows; ++r)
+#pragma unroll
+                        for (int e = 0; e < CH; ++e) acc[r][e] = fmaf(w[r], v[e], acc[r][e]);
                 }
             }
-            if (c < ncol) {
-                for (int r = 0; r < nr; ++r) {
-                    if (isk) dWK[(r0 + j0 + r) * d_in + c] += acc[r];
-                    else dWV[(r0 + j0 + r) * d_emb + (c - d_in)] += acc[r];
-                }
+            if (!live) continue;
+            for (int r = 0; r < nr; ++r) {
+                float *dst = isk ? dWK + (r0 + j0 + r) * d_in + c * CH
+                                 : dWV + (r0 + j0 + r) * d_emb + (c - ck) * CV;
+                const int ne = isk ? CH : CV;
+#pragma unroll
+                for (int e = 0; e < CH; ++e)
+                    if (e < ne) dst[e] += acc[r][e];
             }
         }
     }
 }
 
-template <typename T, int QI, int QE>
+template <typename T, int CH, int NI, int NE, int TB>
 hipError_t launch_token_kernels(const BwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((k_attn_bwd<T, QI, QE>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
+    hipLaunchKernelGGL((k_attn_bwd<T, CH, NI, NE, TB>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
                        (const T *)a.WK, (const T *)a.WV, a.perm, a.items, a.hdr, a.dov, a.d_in,
                        a.d_emb, a.max_d, a.dx, a.P, a.dS);
     hipLaunchKernelGGL(k_kv_items, dim3(64), dim3(256), 0, s, a.off, a.uniq, const_cast<int32_t *>(a.hdr),
                        a.vocab, a.kv_items, a.kv_cap);
-    hipLaunchKernelGGL((k_kv_grad<T>), dim3(2048), dim3(256), 0, s, (const T *)a.x, a.off, a.uniq,
+    hipLaunchKernelGGL((k_kv_grad<T, CH>), dim3(2048), dim3(256), 0, s, (const T *)a.x, a.off, a.uniq,
                        a.seg_start, a.perm, a.hdr, a.kv_items, a.kv_cap, a.dov, a.d_in, a.d_emb,
                        a.max_d, a.P, a.dS, a.dWK, a.dWV);
     return hipGetLastError();
 }
 
-template <typename T, int QI>
-hipError_t launch_token_qe(const BwdArgs &a, hipStream_t s) {
-    if (a.d_emb <= 256) return launch_token_kernels<T, QI, 4>(a, s);
-    if (a.d_emb <= 512) return launch_token_kernels<T, QI, 8>(a, s);
-    return launch_token_kernels<T, QI, 16>(a, s);
+// chunks per lane for d_in (NI) and d_emb (NE): rows of up to 64 * NI * CH elements
+template <typename T, int CH, int NI>
+hipError_t launch_token_ne(const BwdArgs &a, hipStream_t s) {
+    constexpr int TB = NI * CH <= 32 ? 2 : 1;
+    if (a.d_emb <= 64 * CH) return launch_token_kernels<T, CH, NI, 1, TB>(a, s);
+    if (a.d_emb <= 128 * CH) return launch_token_kernels<T, CH, NI, 2, TB>(a, s);
+    return launch_token_kernels<T, CH, NI, (1024 + 64 * CH - 1) / (64 * CH), TB>(a, s);
 }
 
-template <typename T>
-hipError_t launch_token_t(const BwdArgs &a, hipStream_t s) {
-    if (a.d_in <= 256) return launch_token_qe<T, 4>(a, s);
-    if (a.d_in <= 1024) return launch_token_qe<T, 16>(a, s);
-    if (a.d_in <= 2048) return launch_token_qe<T, 32>(a, s);
-    return launch_token_qe<T, 64>(a, s);
+template <typename T, int CH>
+hipError_t launch_token_ch(const BwdArgs &a, hipStream_t s) {
+    if (a.d_in <= 64 * CH) return launch_token_ne<T, CH, 1>(a, s);
+    if (a.d_in <= 128 * CH) return launch_token_ne<T, CH, 2>(a, s);
+    if (a.d_in <= 256 * CH) return launch_token_ne<T, CH, 4>(a, s);
+    return launch_token_ne<T, CH, (4096 + 64 * CH - 1) / (64 * CH)>(a, s);
 }
 
 }  // namespace
@@ -375,9 +481,18 @@ int kv_item_capacity(int64_t n, int64_t rows) {
 
 int ln_param_chunks(int64_t n) { return (int)std::max<int64_t>(1, (n + kLnRows - 1) / kLnRows); }
 
+int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype) {
+    // the kernel's TB for its chunk width: two tokens while a lane's share of d_in
+    // (NI * CH elements) is at most 32
+    const int64_t ch = dtype == L3_BF16 ? 8 : (d_in % 4 == 0 && d_emb % 4 == 0 ? 4 : 1);
+    return d_in <= 256 * ch && 4 * ch <= 32 ? 2 : 1;
+}
+
 hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s) {
     if (a.d_in > 4096 || a.d_emb > 1024) return hipErrorInvalidValue;
-    return dtype == L3_BF16 ? launch_token_t<uint16_t>(a, s) : launch_token_t<float>(a, s);
+    if (dtype == L3_BF16) return launch_token_ch<uint16_t, 8>(a, s);  // bf16 dims are multiples of 64
+    if (a.d_in % 4 == 0 && a.d_emb % 4 == 0) return launch_token_ch<float, 4>(a, s);
+    return launch_token_ch<float, 1>(a, s);
 }
 
 }  // namespace l3

@@ -329,10 +329,11 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     L3_HIP_TRY(gemm_f32out(dt, dhT, oT, dWup, D.d_up, D.d_emb, np, true, s));
     L3_HIP_TRY(launch_transpose(W_up, D.d_emb, D.d_up, D.d_emb, wupT, D.d_up, D.d_up, dt, s));
     L3_HIP_TRY(gemm_f32out(dt, dh, wupT, dov, n, D.d_emb, D.d_up, false, s));
-    // attention: one-token items over every block, then the key / value gradients
+    // attention: items of one or two tokens over every block, then the key / value gradients
     int4 *items = ws_ptr<int4>(ws, L.light);
     L3_HIP_TRY(launch_zero_i32(b.hdr + HDR_NLIGHT, 4, s));  // NLIGHT, NHEAVY, NDENSE, NKV
-    L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, INT32_MAX, INT32_MAX, 1, items,
+    L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, INT32_MAX, INT32_MAX,
+                               attn_bwd_tokens(D.d_in, D.d_emb, dt), items,
                                ws_ptr<int2>(ws, L.heavy), ws_ptr<int2>(ws, L.dense), s));
     BwdArgs a{};
     a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;

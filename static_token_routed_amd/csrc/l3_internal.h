@@ -162,7 +162,7 @@ struct BwdArgs {
     const void *x, *WK, *WV;
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
-    const int4 *items;   // one token per item (first sorted position, 1, first row, d_t)
+    const int4 *items;   // attn_bwd_tokens tokens per item (first sorted position, count, first row, d_t)
     const float *dov;    // dL/do [n x d_emb]
     int64_t d_in, d_emb, vocab;
     int max_d;
@@ -174,7 +174,9 @@ struct BwdArgs {
 };
 // items of the key / value gradients: at most one per block plus one per 16 rows
 int kv_item_capacity(int64_t n, int64_t rows);
-// attention backward per token, then the key / value gradients per ID block
+// tokens per attention-backward work item (all of one block) for these dims
+int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype);
+// attention backward per work item, then the key / value gradients per ID block
 hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s);
 
 }  // namespace l3
