@@ -1,6 +1,6 @@
 """Benchmark of the L^3 forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload paper_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload paper_bf16] [--backward]
 
 One step = one l3_forward over the whole batch (route, gather-attention, W_up,
 W_mix) with every input already resident in HBM; the 256 MB MALL is flushed
@@ -8,7 +8,9 @@ before each timed step.  Prints one JSON line: tokens/s over K timed steps (HIP
 events around each forward), the roofline of the dominant kernel (algorithmic
 bytes or FLOPs per launch over its HIP-event duration, measured inside the
 library on the launch stream), all stage rooflines, and the fp64 oracle timed
-on a bounded token sample on the host cores.
+on a bounded token sample on the host cores.  `--backward` times l3_backward (the
+training pass) the same way; `--workload decode_bf16` times decode steps with the
+tables in pinned host memory.
 """
 from __future__ import annotations
 
@@ -40,6 +42,8 @@ def parse():
                     help="timed steps (default 20; a decode workload's own step count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paper_bf16")
+    ap.add_argument("--backward", action="store_true",
+                    help="time l3_backward (the training pass) instead of the forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the oracle timing on the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
@@ -191,6 +195,9 @@ def main():
     torch.cuda.set_device(0)
     if cfg.steps:
         decode_bench(args, cfg, torch, l3, synth)
+        return
+    if args.backward:
+        backward_bench(args, cfg, torch, l3, synth)
         return
     t0 = time.time()
     off = synth.offsets(cfg)
@@ -463,6 +470,108 @@ def decode_bench(args, cfg, torch, l3, synth):
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
+
+
+VALU_F32_PEAK_TF = 157.3  # MI355X fp32 vector
+
+
+def backward_bench(args, cfg, torch, l3, synth):
+    """Backward (training) pass: gradients of sum(dout * L3(x, ids)) for one batch, fp32
+    gradients; dW_K / dW_V accumulate into full-size fp32 tables.  Timed like the
+    forward (HIP events, last-level cache flushed before each step)."""
+    t0 = time.time()
+    off, ids = synth.offsets(cfg), synth.token_ids(cfg)
+    x, WK, WV = synth.hidden(cfg), synth.table(cfg, "W_K"), synth.table(cfg, "W_V")
+    Wup, Wmix = synth.dense(cfg, "W_up"), synth.dense(cfg, "W_mix")
+    g, b = synth.ln_params(cfg)
+    n, v = cfg.n, int(off[-1])
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    dout = torch.from_numpy(synth.f32_to_bf16_bits(
+        np.random.default_rng(cfg.seed + 7).standard_normal((n, cfg.d_out), dtype=np.float32))
+        .view(np.int16)).view(torch.bfloat16).cuda()
+    args_in = [dev(x), torch.from_numpy(ids).cuda(), n, dev(WK), dev(WV), dev(Wup),
+               torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(), dev(Wmix), dout]
+    z = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device="cuda")
+    grads = [z(n, cfg.d_in), z(v, cfg.d_in), z(v, cfg.d_emb), z(cfg.d_up, cfg.d_emb), z(cfg.d_up),
+             z(cfg.d_up), z(cfg.d_out, cfg.d_up + cfg.d_in)]
+    plan = l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16", cfg.ln_eps)
+    ws = torch.empty(l3.l3_backward_workspace_size(plan.handle, n), dtype=torch.uint8, device="cuda")
+    print(f"[bench] {cfg.name} backward: inputs ready in {time.time() - t0:.1f}s, workspace "
+          f"{ws.numel() / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    def step():
+        l3.l3_backward(plan.handle, *args_in, *grads, ws, ws.numel())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        flush_buf.add_(1)
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    l3.l3_profile_enable(True)
+    for _ in range(args.steps):
+        flush_buf.add_(1)
+        step()
+    st_ms, launches = l3.l3_profile_read(10)
+    l3.l3_profile_enable(False)
+    del flush_buf
+    assert plan.status() == l3.L3_OK
+    names = {0: "route", 1: "gather_mfma", 2: "gather_light", 6: "recompute_h", 7: "dense_bwd",
+             8: "attn_bwd", 9: "kv_grad"}
+    avg = {nm: st_ms[i] / max(1, launches[i]) for i, nm in names.items()}
+    # algorithmic work: per (token, row of its block) the attention backward needs the
+    # score, o, dp and dx (4 d_in + 4 d_emb FLOP), the key / value gradients 2 (d_in + d_emb)
+    tok_rows = float((off[ids + 1] - off[ids]).sum())
+    attn_fl = tok_rows * (4 * cfg.d_in + 4 * cfg.d_emb)
+    kv_fl = tok_rows * 2 * (cfg.d_in + cfg.d_emb)
+    Z = cfg.d_up + cfg.d_in
+    dense_fl = 2.0 * n * (2 * cfg.d_out * Z + 2 * cfg.d_up * cfg.d_emb)
+    kernels = {
+        "attn_bwd": {"bound": "alu", "achieved": attn_fl / (avg["attn_bwd"] * 1e-3) / 1e12,
+                     "peak": VALU_F32_PEAK_TF, "unit": "TFLOP/s",
+                     "work_per_launch": f"{attn_fl:.4g} FLOP ({tok_rows:.4g} token-rows)"},
+        "kv_grad": {"bound": "alu", "achieved": kv_fl / (avg["kv_grad"] * 1e-3) / 1e12,
+                    "peak": VALU_F32_PEAK_TF, "unit": "TFLOP/s", "work_per_launch": f"{kv_fl:.4g} FLOP"},
+        "dense_bwd": {"bound": "mfma", "achieved": dense_fl / (avg["dense_bwd"] * 1e-3) / 1e12,
+                      "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                      "work_per_launch": f"{dense_fl:.4g} FLOP (dz, dW_mix, dW_up, do GEMMs; "
+                                         f"transposes and LayerNorm backward in the same stage)"},
+    }
+    for k_, v_ in kernels.items():
+        v_["frac"] = v_["achieved"] / v_["peak"]
+        v_["ms"] = avg[k_]
+        v_["traffic"] = None
+    dominant = max(kernels, key=lambda k_: kernels[k_]["ms"])
+    roof = {k_: kernels[dominant][k_] for k_ in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dominant
+    mean = float(np.mean(ms))
+    line = {
+        "metric": "L3 backward tokens/s (fp32 gradients of x, W_K, W_V, W_up, LayerNorm, W_mix)",
+        "value": n / (mean * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": mean, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf token IDs, Zipf-shaped allocation, N(0, 1/sqrt(fan_in)) "
+                "weights, N(0, 1) upstream gradient)",
+        "config": {"workload": f"{cfg.name}: vocab {cfg.vocab}, v {cfg.v}, k {cfg.k}, d_in {cfg.d_in}, "
+                               f"d_emb {cfg.d_emb}, d_up {cfg.d_up}, d_out {cfg.d_out}, {n} tokens",
+                   "global_batch": n},
+        "roofline": roof, "kernels": kernels, "stage_ms": avg,
+        "timing": {"method": "HIP events around each backward, MALL flushed before each",
+                   "ms_median": float(np.median(ms)), "ms_min": float(min(ms)), "ms_max": float(max(ms))},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
 
 
 def cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, seconds):

@@ -253,14 +253,16 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Per-kernel timing for measurement.  While enabled, l3_forward records a
- * pair of HIP events on its stream around each of its kernel stages and
- * accumulates their elapsed time; l3_profile_read synchronises those events.
- * Stages: 0 route (sort + blocks + work lists), 1 gather-attention on the
- * matrix cores (heavy work list), 2 gather-attention, one wavefront per item
- * (light work list), 3 W_up GEMM, 4 W_mix preparation (LayerNorm statistics and
- * the LayerNorm fold of W_mix), 5 W_mix GEMM.  max_stages <= 8.  Not
- * thread-safe; for benchmarking only.
+ * Per-kernel timing for measurement.  While enabled, l3_forward and
+ * l3_backward record a pair of HIP events on their stream around each of their
+ * kernel stages and accumulate their elapsed time; l3_profile_read synchronises
+ * those events.  Stages: 0 route (sort + blocks + work lists), 1 gather-attention
+ * on the matrix cores (heavy work list), 2 gather-attention, one wavefront per
+ * item (light work list), 3 W_up GEMM, 4 W_mix preparation (LayerNorm statistics
+ * and the LayerNorm fold of W_mix), 5 W_mix GEMM; backward (which also runs
+ * stages 0-2): 6 recompute of h and its LayerNorm statistics, 7 dense products
+ * and the LayerNorm backward, 8 attention backward, 9 key / value gradients.
+ * max_stages <= 10.  Not thread-safe; for benchmarking only.
  */
 int l3_profile_enable(int enable);
 int l3_profile_read(double *ms_total, int64_t *launches, int max_stages);

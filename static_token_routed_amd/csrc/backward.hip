@@ -410,10 +410,13 @@ __global__ __launch_bounds__(256) void k_kv_grad(const T *__restrict__ x, const 
 }
 
 template <typename T, int CH, int NI, int NE, int TB>
-hipError_t launch_token_kernels(const BwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((k_attn_bwd<T, CH, NI, NE, TB>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
-                       (const T *)a.WK, (const T *)a.WV, a.perm, a.items, a.hdr, a.dov, a.d_in,
-                       a.d_emb, a.max_d, a.dx, a.P, a.dS);
+hipError_t launch_token_kernels(const BwdArgs &a, int part, hipStream_t s) {
+    if (part == 0) {
+        hipLaunchKernelGGL((k_attn_bwd<T, CH, NI, NE, TB>), dim3(1024), dim3(256), 0, s, (const T *)a.x,
+                           (const T *)a.WK, (const T *)a.WV, a.perm, a.items, a.hdr, a.dov, a.d_in,
+                           a.d_emb, a.max_d, a.dx, a.P, a.dS);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_kv_items, dim3(64), dim3(256), 0, s, a.off, a.uniq, const_cast<int32_t *>(a.hdr),
                        a.vocab, a.kv_items, a.kv_cap);
     hipLaunchKernelGGL((k_kv_grad<T, CH>), dim3(2048), dim3(256), 0, s, (const T *)a.x, a.off, a.uniq,
@@ -424,19 +427,19 @@ hipError_t launch_token_kernels(const BwdArgs &a, hipStream_t s) {
 
 // chunks per lane for d_in (NI) and d_emb (NE): rows of up to 64 * NI * CH elements
 template <typename T, int CH, int NI>
-hipError_t launch_token_ne(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_token_ne(const BwdArgs &a, int part, hipStream_t s) {
     constexpr int TB = NI * CH <= 32 ? 2 : 1;
-    if (a.d_emb <= 64 * CH) return launch_token_kernels<T, CH, NI, 1, TB>(a, s);
-    if (a.d_emb <= 128 * CH) return launch_token_kernels<T, CH, NI, 2, TB>(a, s);
-    return launch_token_kernels<T, CH, NI, (1024 + 64 * CH - 1) / (64 * CH), TB>(a, s);
+    if (a.d_emb <= 64 * CH) return launch_token_kernels<T, CH, NI, 1, TB>(a, part, s);
+    if (a.d_emb <= 128 * CH) return launch_token_kernels<T, CH, NI, 2, TB>(a, part, s);
+    return launch_token_kernels<T, CH, NI, (1024 + 64 * CH - 1) / (64 * CH), TB>(a, part, s);
 }
 
 template <typename T, int CH>
-hipError_t launch_token_ch(const BwdArgs &a, hipStream_t s) {
-    if (a.d_in <= 64 * CH) return launch_token_ne<T, CH, 1>(a, s);
-    if (a.d_in <= 128 * CH) return launch_token_ne<T, CH, 2>(a, s);
-    if (a.d_in <= 256 * CH) return launch_token_ne<T, CH, 4>(a, s);
-    return launch_token_ne<T, CH, (4096 + 64 * CH - 1) / (64 * CH)>(a, s);
+hipError_t launch_token_ch(const BwdArgs &a, int part, hipStream_t s) {
+    if (a.d_in <= 64 * CH) return launch_token_ne<T, CH, 1>(a, part, s);
+    if (a.d_in <= 128 * CH) return launch_token_ne<T, CH, 2>(a, part, s);
+    if (a.d_in <= 256 * CH) return launch_token_ne<T, CH, 4>(a, part, s);
+    return launch_token_ne<T, CH, (4096 + 64 * CH - 1) / (64 * CH)>(a, part, s);
 }
 
 }  // namespace
@@ -488,11 +491,11 @@ int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype) {
     return d_in <= 256 * ch && 4 * ch <= 32 ? 2 : 1;
 }
 
-hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s) {
+hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, int part, hipStream_t s) {
     if (a.d_in > 4096 || a.d_emb > 1024) return hipErrorInvalidValue;
-    if (dtype == L3_BF16) return launch_token_ch<uint16_t, 8>(a, s);  // bf16 dims are multiples of 64
-    if (a.d_in % 4 == 0 && a.d_emb % 4 == 0) return launch_token_ch<float, 4>(a, s);
-    return launch_token_ch<float, 1>(a, s);
+    if (dtype == L3_BF16) return launch_token_ch<uint16_t, 8>(a, part, s);  // bf16 dims: multiples of 64
+    if (a.d_in % 4 == 0 && a.d_emb % 4 == 0) return launch_token_ch<float, 4>(a, part, s);
+    return launch_token_ch<float, 1>(a, part, s);
 }
 
 }  // namespace l3

@@ -39,13 +39,17 @@ namespace {
 size_t esize(int dtype) { return dtype == L3_BF16 ? 2 : 4; }
 
 // ---- stage timing (benchmark aid)
+// forward: 0 route, 1 gather (matrix cores), 2 gather (wavefront), 3 W_up, 4 W_mix
+// preparation, 5 W_mix; backward: 6 forward recompute of h and its statistics,
+// 7 dense products and LayerNorm backward, 8 attention backward, 9 key / value gradients
+constexpr int kProfStages = 10;
 struct Prof {
     bool on = false;
     struct Pair { hipEvent_t a, b; int stage; };
     std::vector<Pair> pending;
     std::vector<hipEvent_t> pool;
-    double ms[8] = {};
-    int64_t launches[8] = {};
+    double ms[kProfStages] = {};
+    int64_t launches[kProfStages] = {};
 } g_prof;
 
 hipEvent_t prof_event() {
@@ -292,6 +296,8 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     if (rc != L3_OK) return rc;
     void *o = ws_ptr<char>(ws, L.o), *h = ws_ptr<char>(ws, L.h);
     float *lnp = ws_ptr<float>(ws, L.lnp), *stats = ws_ptr<float>(ws, L.stats);
+    {
+    StageTimer tm(6, s);
     if (dt == L3_BF16) {
         if (n <= kSkinnyMaxM)
             L3_HIP_TRY(launch_gemm_skinny_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h,
@@ -305,11 +311,14 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
                                    s));
         L3_HIP_TRY(launch_ln_stats_f32((const float *)h, n, D.d_up, D.eps, stats, s));
     }
+    }
     char *wmt = ws_ptr<char>(ws, B.wmt);
     float *dy = ws_ptr<float>(ws, B.dy), *dov = ws_ptr<float>(ws, B.dov);
     void *dh = ws_ptr<char>(ws, B.dh), *y = ws_ptr<char>(ws, B.y);
     char *doutT = ws_ptr<char>(ws, B.doutT), *zT = ws_ptr<char>(ws, B.zT);
     void *dhT = ws_ptr<char>(ws, B.dhT), *oT = ws_ptr<char>(ws, B.oT), *wupT = ws_ptr<char>(ws, B.wupT);
+    {
+    StageTimer tm(7, s);
     // dy = W1^T dout, dx = W2^T dout  (W_mix^T rows [0, d_up) and [d_up, Z))
     L3_HIP_TRY(launch_transpose(W_mix, Z, D.d_out, Z, wmt, D.d_out, D.d_out, dt, s));
     L3_HIP_TRY(gemm_f32out(dt, dout, wmt, dy, n, D.d_up, D.d_out, false, s));
@@ -329,6 +338,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     L3_HIP_TRY(gemm_f32out(dt, dhT, oT, dWup, D.d_up, D.d_emb, np, true, s));
     L3_HIP_TRY(launch_transpose(W_up, D.d_emb, D.d_up, D.d_emb, wupT, D.d_up, D.d_up, dt, s));
     L3_HIP_TRY(gemm_f32out(dt, dh, wupT, dov, n, D.d_emb, D.d_up, false, s));
+    }
     // attention: items of one or two tokens over every block, then the key / value gradients
     int4 *items = ws_ptr<int4>(ws, L.light);
     L3_HIP_TRY(launch_zero_i32(b.hdr + HDR_NLIGHT, 4, s));  // NLIGHT, NHEAVY, NDENSE, NKV
@@ -343,7 +353,14 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     a.dx = dx; a.P = ws_ptr<float>(ws, B.P); a.dS = ws_ptr<float>(ws, B.dS);
     a.dWK = dWK; a.dWV = dWV;
     a.kv_items = ws_ptr<int2>(ws, B.kv); a.kv_cap = B.kv_cap;
-    L3_HIP_TRY(launch_attn_bwd(a, dt, s));
+    {
+        StageTimer tm(8, s);
+        L3_HIP_TRY(launch_attn_bwd(a, dt, 0, s));
+    }
+    {
+        StageTimer tm(9, s);
+        L3_HIP_TRY(launch_attn_bwd(a, dt, 1, s));
+    }
     return L3_OK;
 }
 
@@ -732,7 +749,7 @@ int l3_profile_read(double *ms_total, int64_t *launches, int max_stages) {
         g_prof.pool.push_back(pr.b);
     }
     g_prof.pending.clear();
-    for (int i = 0; i < max_stages && i < 8; ++i) {
+    for (int i = 0; i < max_stages && i < kProfStages; ++i) {
         if (ms_total) ms_total[i] = g_prof.ms[i];
         if (launches) launches[i] = g_prof.launches[i];
     }

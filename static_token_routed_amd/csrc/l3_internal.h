@@ -176,7 +176,8 @@ struct BwdArgs {
 int kv_item_capacity(int64_t n, int64_t rows);
 // tokens per attention-backward work item (all of one block) for these dims
 int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype);
-// attention backward per work item, then the key / value gradients per ID block
-hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, hipStream_t s);
+// part 0: attention backward per work item; part 1: the key / value gradients per
+// ID block (after part 0)
+hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, int part, hipStream_t s);
 
 }  // namespace l3
