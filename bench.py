@@ -209,7 +209,9 @@ def main():
     def dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
-    dx, dWK, dWV, dWup, dWmix = dev(x), dev(WK), dev(WV), dev(Wup), dev(Wmix)
+    dx, dWK, dWup, dWmix = dev(x), dev(WK), dev(Wup), dev(Wmix)
+    # tied configuration: one device table serves as W_K and W_V
+    dWV = dWK if cfg.tied else dev(WV)
     dids = torch.from_numpy(ids).cuda()
     dg, db = torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda()
     print(f"[bench] {cfg.name}: inputs generated and uploaded in {time.time() - t0:.1f}s",
@@ -272,7 +274,8 @@ def main():
     d = off[u + 1] - off[u]
     min_tok, min_rows = l3.l3_worklist_rule(plan.handle)
     heavy = (cnt >= min_tok) | (d >= min_rows)
-    row_b = (cfg.d_in + cfg.d_emb) * 2
+    # a tied configuration's row serves both roles: its algorithmic bytes are one row
+    row_b = (cfg.d_in + (0 if cfg.tied else cfg.d_emb)) * 2
     R = int(d.sum())
     kv = {"gather_attention": R * row_b, "gather_mfma": int(d[heavy].sum()) * row_b,
           "gather_light": int(d[~heavy].sum()) * row_b}

@@ -57,6 +57,7 @@ class Config:
     ids_s: float = 1.1
     seed: int = 0
     ln_eps: float = 1e-5
+    tied: bool = False           # W_V is W_K (needs d_emb == d_in)
     # decode workload only
     steps: int = 0
     pre_m: int = 0
@@ -77,6 +78,12 @@ CONFIGS = {
     "decode_bf16": Config("decode_bf16", vocab=32000, v=131072, k=128, d_in=1024,
                           d_emb=256, d_up=1024, d_out=1024, n=64, ids_s=1.05,
                           steps=256, pre_m=64, pre_k=2048, pre_n=8192),
+    # the tied variant (W_V = W_K, one table read for both roles): d_in = d_emb = 512
+    "tied_bf16": Config("tied_bf16", vocab=180000, v=710000, k=512, d_in=512, d_emb=512,
+                        d_up=2048, d_out=2048, n=16 * 2048, ids_s=1.05, tied=True),
+    # the same dims with separate tables, for comparison
+    "untied512_bf16": Config("untied512_bf16", vocab=180000, v=710000, k=512, d_in=512,
+                             d_emb=512, d_up=2048, d_out=2048, n=16 * 2048, ids_s=1.05),
     "skew_bf16": Config("skew_bf16", vocab=180000, v=710000, k=512, d_in=4096,
                         d_emb=512, d_up=4096, d_out=4096, n=64 * 2048,
                         alloc="skew", ids="skew"),
@@ -258,7 +265,10 @@ def _chunked_normal(seed: int, key: int, rows: int, cols: int, std: float,
 
 
 def table(cfg: Config, which: str, rows: np.ndarray | None = None) -> np.ndarray:
-    """W_K (v x d_in) or W_V (v x d_emb), or only the given rows of it."""
+    """W_K (v x d_in) or W_V (v x d_emb), or only the given rows of it.  A tied
+    configuration's W_V is its W_K."""
+    if which == "W_V" and cfg.tied:
+        return table(cfg, "W_K", rows)
     if which == "W_K":
         return _chunked_normal(cfg.seed, KEY_WK, cfg.v, cfg.d_in, cfg.d_in ** -0.5, cfg.dtype, rows)
     if which == "W_V":

@@ -303,3 +303,20 @@ def test_full_size_sampled(name):
     assert err <= case.tol
     assert np.all(np.isfinite(got))
     g.close()
+
+
+@pytest.mark.parametrize("n", [300, 1200])
+def test_tied_tables(n):
+    """W_V = W_K (one device table passed for both; d_emb = d_in): the forward equals
+    the oracle's with equal tables (the pages' tied variant)."""
+    cfg = dataclasses.replace(
+        synth.small("tied", vocab=500, k=48, d_in=256, d_emb=256, d_up=256, d_out=192, n=n,
+                    v=6000, dtype="bf16", seed=11), ids_s=1.05, tied=True)
+    case = make_case(cfg)
+    assert np.array_equal(case.WK, case.WV)
+    g = Gpu(case)
+    got = to_np(g.plan.forward(g.x, g.ids, g.WK, g.WK, g.Wup, g.gamma, g.beta, g.Wmix))
+    err = rowwise_err(got, oracle_out(case))
+    print(f"tied n={n}: err {err:.2e}", flush=True)
+    assert err <= case.tol
+    g.close()
