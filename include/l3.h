@@ -124,7 +124,9 @@ size_t l3_workspace_size(l3_plan_t plan, int64_t n_max);
  * workspace: dev, >= l3_workspace_size(plan, n) bytes (workspace_bytes).
  * The batch is sorted by token ID so each distinct ID's K_t / V_t rows are
  * read once per call (the pages' batch sort: sciencestack.ai page, Fig. 3
- * caption); the result does not depend on the batch order.
+ * caption); the result does not depend on the batch order.  W_V may be the same
+ * buffer as W_K when d_emb == d_in (the pages' tied variant, papernotes.org page,
+ * ablation table): the second read of each row then mostly hits the caches.
  * Errors: INVALID_ARG, CAPACITY (workspace too small), HIP.
  */
 int l3_forward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t n,
