@@ -99,6 +99,23 @@ int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k,
 /* Frees a plan (NULL is accepted). */
 int l3_plan_destroy(l3_plan_t plan);
 
+/*
+ * l3_allocate_lzw -- the allocation D itself, from a token corpus (host code, no
+ * GPU): the pages' LZW-style rule (kimjy99.github.io page, section "1. Embedding
+ * Allocation"; papernotes.org page, section 关键设计 item 2).  The corpus is
+ * parsed LZW-style into codewords with frequencies (a new codeword counts 1, the
+ * codeword without its first token +1); every token gets one embedding, then the
+ * codewords by decreasing frequency (ties: shorter, then by token sequence) each
+ * give one to the token they end with, up to k per token, in passes until v.
+ * corpus: host int32 [n] in [0, vocab); offsets: host int64 [vocab + 1], written
+ * (off[0] = 0, off[t+1] - off[t] = d_t), ready for l3_plan.
+ * Errors: INVALID_ARG (also v outside [vocab, vocab * k]), TOKEN_RANGE (a corpus
+ * token outside [0, vocab)), CAPACITY (the codewords cannot place all of v:
+ * every token they end with is already at k).
+ */
+int l3_allocate_lzw(const int32_t *corpus, int64_t n, int64_t vocab, int64_t v, int32_t k,
+                    int64_t *offsets);
+
 /* Plan facts: vocab, v, k and the largest d_t (any pointer may be NULL). */
 int l3_plan_info(l3_plan_t plan, int64_t *vocab, int64_t *v, int32_t *k,
                  int32_t *max_d);

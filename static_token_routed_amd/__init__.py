@@ -49,6 +49,7 @@ _SIG = {
     "l3_workspace_size": (_SZ, [_P, _I64]),
     "l3_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "l3_backward_workspace_size": (_SZ, [_P, _I64]),
+    "l3_allocate_lzw": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int32, _P]),
     "l3_backward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _SZ, _P]),
     "l3_route": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -140,6 +141,15 @@ def l3_forward(plan, x, token_ids, n, W_K, W_V, W_up, ln_gamma, ln_beta, W_mix, 
     _check(_lib.l3_forward(plan, _ptr(x), _ptr(token_ids), n, _ptr(W_K), _ptr(W_V), _ptr(W_up),
                            _ptr(ln_gamma), _ptr(ln_beta), _ptr(W_mix), _ptr(out), _ptr(workspace),
                            workspace_bytes, _stream(stream)), "l3_forward")
+
+
+def l3_allocate_lzw(corpus, vocab: int, v: int, k: int) -> np.ndarray:
+    """CSR offsets (int64 [vocab + 1]) of the LZW-style allocation of v embeddings."""
+    c = np.ascontiguousarray(corpus, dtype=np.int32)
+    off = np.zeros(vocab + 1, dtype=np.int64)
+    _check(_lib.l3_allocate_lzw(c.ctypes.data if c.size else None, c.size, vocab, v, k,
+                                off.ctypes.data), "l3_allocate_lzw")
+    return off
 
 
 def l3_backward_workspace_size(plan: int, n_max: int) -> int:

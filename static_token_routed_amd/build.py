@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libl3.so")
-SOURCES = ["route.hip", "attn.hip", "gemm.hip", "gemm_skinny.hip", "stage.hip", "backward.hip", "l3_api.hip"]
+SOURCES = ["route.hip", "attn.hip", "gemm.hip", "gemm_skinny.hip", "stage.hip", "backward.hip", "alloc.hip", "l3_api.hip"]
 HEADERS = ["cdna4.h", "l3_internal.h"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
