@@ -249,6 +249,23 @@ int l3_prefetch(l3_plan_t plan, const int32_t *token_ids_host, int64_t n,
                 void *side_stream, void *ready_event);
 
 /*
+ * l3_staging_set_cache -- keep the rows of hot_ids (host int32 [n_hot], the IDs
+ * whose rows should stay on the device, e.g. the most frequent ones) in a
+ * device-resident cache owned by the staging: later prefetches copy those IDs'
+ * rows from the cache (HBM) and only the others over PCIe.  Fills the cache from
+ * the pinned tables on `stream` and returns when it is filled; replaces any
+ * previous cache (after waiting for the device to go idle); n_hot = 0 drops it.
+ * Allocates device memory.  Errors: INVALID_ARG (also tables without a device
+ * mapping), TOKEN_RANGE, HIP.
+ *
+ * l3_staging_stats -- rows staged by the last prefetch, and how many of them the
+ * cache served (either pointer may be NULL).
+ */
+int l3_staging_set_cache(l3_staging_t staging, const int32_t *hot_ids, int64_t n_hot,
+                         const void *W_K_host, const void *W_V_host, void *stream);
+int l3_staging_stats(l3_staging_t staging, int64_t *rows, int64_t *cached_rows);
+
+/*
  * l3_forward_staged -- l3_forward over the rows the last l3_prefetch staged,
  * for the same n tokens in the same order.  workspace: >= l3_workspace_size
  * (plan, n) bytes.  Errors: INVALID_ARG, CAPACITY, HIP.

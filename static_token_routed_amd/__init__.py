@@ -50,6 +50,8 @@ _SIG = {
     "l3_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "l3_backward_workspace_size": (_SZ, [_P, _I64]),
     "l3_allocate_lzw": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int32, _P]),
+    "l3_staging_set_cache": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P]),
+    "l3_staging_stats": (ctypes.c_int, [_P, _P, _P]),
     "l3_backward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _SZ, _P]),
     "l3_route": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -200,6 +202,19 @@ def l3_prefetch(plan, token_ids_host: np.ndarray, n, W_K_host, W_V_host, staging
         ev = ready_event.cuda_event
     _check(_lib.l3_prefetch(plan, ids.ctypes.data, n, _ptr(W_K_host), _ptr(W_V_host), staging,
                             _stream(side_stream), ev), "l3_prefetch")
+
+
+def l3_staging_set_cache(staging, hot_ids, W_K_host, W_V_host, stream=None) -> None:
+    ids = np.ascontiguousarray(hot_ids, dtype=np.int32)
+    _check(_lib.l3_staging_set_cache(staging, ids.ctypes.data if ids.size else None, ids.size,
+                                     _ptr(W_K_host), _ptr(W_V_host), _stream(stream)),
+           "l3_staging_set_cache")
+
+
+def l3_staging_stats(staging) -> tuple[int, int]:
+    rows, cached = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.l3_staging_stats(staging, ctypes.byref(rows), ctypes.byref(cached)), "l3_staging_stats")
+    return rows.value, cached.value
 
 
 def l3_forward_staged(staging, x, n, W_up, ln_gamma, ln_beta, W_mix, out, workspace,

@@ -32,6 +32,10 @@ struct l3_staging_s {
     hipEvent_t small_done = nullptr;  // last copy out of h_meta
     bool small_pending = false;
     int64_t n = 0, m = 0, rows = 0, max_d = 0;
+    // device-resident cache of hot IDs' rows (l3_staging_set_cache)
+    void *c_K = nullptr, *c_V = nullptr;
+    std::vector<int64_t> cache_row;  // per ID: first cache row, or -1
+    int64_t cached_rows = 0;         // rows of the last prefetch served by the cache
 };
 
 namespace {
@@ -639,6 +643,8 @@ int l3_staging_destroy(l3_staging_t st) {
     if (st->d_K) (void)hipFree(st->d_K);
     if (st->d_V) (void)hipFree(st->d_V);
     if (st->d_meta) (void)hipFree(st->d_meta);
+    if (st->c_K) (void)hipFree(st->c_K);
+    if (st->c_V) (void)hipFree(st->c_V);
     if (st->h_meta) (void)hipHostFree(st->h_meta);
     if (st->small_done) (void)hipEventDestroy(st->small_done);
     delete st;
@@ -680,10 +686,15 @@ int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
     int64_t *h_src = h_coff + (m + 1);
     int32_t *h_ids = reinterpret_cast<int32_t *>(h_src + m);
     h_coff[0] = 0;
+    int64_t cached = 0;
     for (int64_t i = 0; i < m; ++i) {
-        h_coff[i + 1] = h_coff[i] + (p->h_off[u[i] + 1] - p->h_off[u[i]]);
-        h_src[i] = p->h_off[u[i]];
+        const int64_t d = p->h_off[u[i] + 1] - p->h_off[u[i]];
+        h_coff[i + 1] = h_coff[i] + d;
+        const int64_t cr = st->cache_row.empty() ? -1 : st->cache_row[u[i]];
+        h_src[i] = cr >= 0 ? -1 - cr : p->h_off[u[i]];
+        if (cr >= 0) cached += d;
     }
+    st->cached_rows = cached;
     for (int64_t i = 0; i < n; ++i)
         h_ids[i] = (int32_t)(std::lower_bound(u.begin(), u.end(), ids[i]) - u.begin());
     int64_t *d_coff = reinterpret_cast<int64_t *>(st->d_meta);
@@ -695,14 +706,80 @@ int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
         L3_HIP_TRY(hipEventRecord(st->small_done, s));
         st->small_pending = true;
         const size_t es = esize(p->dims.dtype);
-        L3_HIP_TRY(launch_stage_rows(d_coff, d_coff + (m + 1), m, rows, WK_dev, WV_dev, st->d_K,
-                                     st->d_V, p->dims.d_in * es, p->dims.d_emb * es, s));
+        L3_HIP_TRY(launch_stage_rows(d_coff, d_coff + (m + 1), m, rows, WK_dev, WV_dev, st->c_K,
+                                     st->c_V, st->d_K, st->d_V, p->dims.d_in * es, p->dims.d_emb * es,
+                                     s));
     }
     if (ready_event) L3_HIP_TRY(hipEventRecord((hipEvent_t)ready_event, s));
     st->n = n;
     st->m = m;
     st->rows = rows;
     st->max_d = max_d;
+    return L3_OK;
+}
+
+int l3_staging_set_cache(l3_staging_t st, const int32_t *hot_ids, int64_t n_hot, const void *WK_host,
+                         const void *WV_host, void *stream) {
+    if (!st || n_hot < 0 || (n_hot > 0 && (!hot_ids || !WK_host || !WV_host))) return L3_ERR_INVALID_ARG;
+    l3_plan_s *p = st->plan;
+    hipStream_t s = (hipStream_t)stream;
+    // drop the previous cache (work enqueued earlier, on any stream, may still read it)
+    if (st->c_K || st->c_V) L3_HIP_TRY(hipDeviceSynchronize());
+    if (st->small_pending) L3_HIP_TRY(hipEventSynchronize(st->small_done));
+    st->small_pending = false;
+    if (st->c_K) (void)hipFree(st->c_K);
+    if (st->c_V) (void)hipFree(st->c_V);
+    st->c_K = st->c_V = nullptr;
+    st->cache_row.clear();
+    if (n_hot == 0) return L3_OK;
+    void *WK_dev = nullptr, *WV_dev = nullptr;
+    if (hipHostGetDevicePointer(&WK_dev, const_cast<void *>(WK_host), 0) != hipSuccess ||
+        hipHostGetDevicePointer(&WV_dev, const_cast<void *>(WV_host), 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return L3_ERR_INVALID_ARG;
+    }
+    if (!aligned16({WK_host, WV_host, WK_dev, WV_dev})) return L3_ERR_INVALID_ARG;
+    std::vector<int32_t> u(hot_ids, hot_ids + n_hot);
+    for (int32_t t : u)
+        if (t < 0 || t >= p->vocab) return L3_ERR_TOKEN_RANGE;
+    std::sort(u.begin(), u.end());
+    u.erase(std::unique(u.begin(), u.end()), u.end());
+    const int64_t m = (int64_t)u.size();
+    std::vector<int64_t> meta(2 * m + 1);
+    meta[0] = 0;
+    std::vector<int64_t> row(p->vocab, -1);
+    for (int64_t i = 0; i < m; ++i) {
+        row[u[i]] = meta[i];
+        meta[i + 1] = meta[i] + (p->h_off[u[i] + 1] - p->h_off[u[i]]);
+        meta[m + 1 + i] = p->h_off[u[i]];
+    }
+    const int64_t rows = meta[m];
+    const size_t es = esize(p->dims.dtype);
+    int64_t *d_meta = nullptr;
+    bool ok = hipMalloc(&st->c_K, rows * p->dims.d_in * es) == hipSuccess &&
+              hipMalloc(&st->c_V, rows * p->dims.d_emb * es) == hipSuccess &&
+              hipMalloc(&d_meta, meta.size() * sizeof(int64_t)) == hipSuccess;
+    ok = ok && hipMemcpyAsync(d_meta, meta.data(), meta.size() * sizeof(int64_t), hipMemcpyHostToDevice,
+                              s) == hipSuccess;
+    // the same gather kernel, from the host tables into the cache
+    ok = ok && launch_stage_rows(d_meta, d_meta + m + 1, m, rows, WK_dev, WV_dev, nullptr, nullptr,
+                                 st->c_K, st->c_V, p->dims.d_in * es, p->dims.d_emb * es, s) == hipSuccess;
+    ok = ok && hipStreamSynchronize(s) == hipSuccess;
+    if (d_meta) (void)hipFree(d_meta);
+    if (!ok) {
+        if (st->c_K) (void)hipFree(st->c_K);
+        if (st->c_V) (void)hipFree(st->c_V);
+        st->c_K = st->c_V = nullptr;
+        return L3_ERR_HIP;
+    }
+    st->cache_row.swap(row);
+    return L3_OK;
+}
+
+int l3_staging_stats(l3_staging_t st, int64_t *rows, int64_t *cached_rows) {
+    if (!st) return L3_ERR_INVALID_ARG;
+    if (rows) *rows = st->rows;
+    if (cached_rows) *cached_rows = st->cached_rows;
     return L3_OK;
 }
 

@@ -114,11 +114,13 @@ hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const floa
                            void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
 // Decode staging: destination row r of the compact tables belongs to compact ID i
-// with coff[i] <= r < coff[i+1] and comes from table row src[i] + (r - coff[i]);
-// WK_dev / WV_dev are the device mappings of the pinned host tables.
+// with coff[i] <= r < coff[i+1] and comes from table row src[i] + (r - coff[i]) of
+// the pinned host tables (device mappings WK_dev / WV_dev), or, for src[i] < 0, from
+// row -1 - src[i] + (r - coff[i]) of the device cache cK / cV.
 hipError_t launch_stage_rows(const int64_t *coff, const int64_t *src, int64_t m, int64_t rows,
-                             const void *WK_dev, const void *WV_dev, void *dK, void *dV,
-                             int64_t row_k_bytes, int64_t row_v_bytes, hipStream_t s);
+                             const void *WK_dev, const void *WV_dev, const void *cK, const void *cV,
+                             void *dK, void *dV, int64_t row_k_bytes, int64_t row_v_bytes,
+                             hipStream_t s);
 // Small-M path (split K, fp32 partial slabs in `part`, skinny_part_bytes of them):
 // the plain GEMM (with the same optional LayerNorm partials as launch_gemm_bf16),
 // and out = W_mix [LN(h) ; x] with LayerNorm applied to h while it is staged,

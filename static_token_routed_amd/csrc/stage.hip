@@ -23,10 +23,12 @@ constexpr int kStageBatch = 4;  // 16-byte chunks each lane has in flight per ro
 // binary search over the compact offsets, then its lanes move the row's K part
 // (rk chunks of 16 bytes) and V part (rv chunks) in rounds of kStageBatch loads
 // followed by kStageBatch stores.
+// src[i] >= 0: the ID's first row in the host tables; src[i] < 0: its first row in
+// the device-resident cache of hot rows is -1 - src[i] (cK, cV).
 __global__ __launch_bounds__(64 * kStageWaves) void k_stage_rows(
     const int64_t *__restrict__ coff, const int64_t *__restrict__ src, int64_t m, int64_t rows,
-    const uint4 *__restrict__ WK, const uint4 *__restrict__ WV, uint4 *__restrict__ dK,
-    uint4 *__restrict__ dV, int rk, int rv) {
+    const uint4 *__restrict__ WK, const uint4 *__restrict__ WV, const uint4 *__restrict__ cK,
+    const uint4 *__restrict__ cV, uint4 *__restrict__ dK, uint4 *__restrict__ dV, int rk, int rv) {
     const int lane = threadIdx.x & 63;
     const int64_t nw = (int64_t)gridDim.x * kStageWaves;
     const int rt = rk + rv;
@@ -37,8 +39,10 @@ __global__ __launch_bounds__(64 * kStageWaves) void k_stage_rows(
             const int64_t mid = (lo + hi) >> 1;
             if (coff[mid] <= r) lo = mid; else hi = mid;
         }
-        const int64_t s = src[lo] + (r - coff[lo]);
-        const uint4 *sk = WK + s * rk, *sv = WV + s * rv;
+        const int64_t s0 = src[lo];
+        const bool cached = s0 < 0;
+        const int64_t s = (cached ? -1 - s0 : s0) + (r - coff[lo]);
+        const uint4 *sk = (cached ? cK : WK) + s * rk, *sv = (cached ? cV : WV) + s * rv;
         uint4 *tk = dK + r * rk, *tv = dV + r * rv;
         for (int c0 = 0; c0 < rt; c0 += 64 * kStageBatch) {
             uint4 buf[kStageBatch];
@@ -61,15 +65,17 @@ __global__ __launch_bounds__(64 * kStageWaves) void k_stage_rows(
 }  // namespace
 
 hipError_t launch_stage_rows(const int64_t *coff, const int64_t *src, int64_t m, int64_t rows,
-                             const void *WK_dev, const void *WV_dev, void *dK, void *dV,
-                             int64_t row_k_bytes, int64_t row_v_bytes, hipStream_t s) {
+                             const void *WK_dev, const void *WV_dev, const void *cK, const void *cV,
+                             void *dK, void *dV, int64_t row_k_bytes, int64_t row_v_bytes,
+                             hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     // enough wavefronts for a few hundred KB of reads in flight, and no more than
     // one per destination row
     const int64_t want = (rows + kStageWaves - 1) / kStageWaves;
     const int grid = (int)std::min<int64_t>(want, 1024);
     hipLaunchKernelGGL(k_stage_rows, dim3(grid), dim3(64 * kStageWaves), 0, s, coff, src, m, rows,
-                       (const uint4 *)WK_dev, (const uint4 *)WV_dev, (uint4 *)dK, (uint4 *)dV,
+                       (const uint4 *)WK_dev, (const uint4 *)WV_dev, (const uint4 *)cK,
+                       (const uint4 *)cV, (uint4 *)dK, (uint4 *)dV,
                        (int)(row_k_bytes / 16), (int)(row_v_bytes / 16));
     return hipGetLastError();
 }

@@ -278,6 +278,22 @@ def test_decode_staged_equals_resident(name):
     with pytest.raises(l3.L3Error) as e:
         l3.l3_prefetch(g.plan.handle, np.array([cfg.vocab], np.int32), 1, WKh, WVh, st, side, ev)
     assert e.value.code == l3.L3_ERR_TOKEN_RANGE
+    # a device cache of the hot IDs' rows: same bits, fewer rows over PCIe
+    hot = np.argsort(-np.bincount(case.ids, minlength=cfg.vocab))[:40].astype(np.int32)
+    l3.l3_staging_set_cache(st, hot, WKh, WVh)
+    for step in (0, 5):
+        n = 64
+        ids = np.ascontiguousarray(case.ids, dtype=np.int32) if step == 0 else synth.token_ids(cfg, n=n, step=step)
+        x = g.x if step == 0 else dev(synth.hidden(cfg, n=n, step=step), cfg.dtype)
+        l3.l3_prefetch(g.plan.handle, ids, n, WKh, WVh, st, side, ev)
+        torch.cuda.current_stream().wait_event(ev)
+        out = torch.empty((n, cfg.d_out), dtype=x.dtype, device="cuda")
+        l3.l3_forward_staged(st, x, n, g.Wup, g.gamma, g.beta, g.Wmix, out, ws, ws.numel())
+        ref = g.forward(x=x, ids=torch.from_numpy(ids).cuda())
+        assert torch.equal(out, ref), f"cached step {step}"
+        rows, cached = l3.l3_staging_stats(st)
+        assert 0 < cached <= rows, (rows, cached)
+    l3.l3_staging_set_cache(st, np.zeros(0, np.int32), WKh, WVh)
     # tables in pageable host memory have no device mapping: refused, nothing enqueued
     pageable = torch.from_numpy(np.ascontiguousarray(case.WK[:16]))
     with pytest.raises(l3.L3Error) as e:
