@@ -15,6 +15,7 @@ tables in pinned host memory.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -42,6 +43,11 @@ def parse():
                     help="timed steps (default 20; a decode workload's own step count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paper_bf16")
+    ap.add_argument("--cache-rows", type=int, default=0,
+                    help="decode: keep the rows of the most frequent IDs (up to this many rows) in a "
+                         "device-resident cache")
+    ap.add_argument("--layers", type=int, default=1, choices=(1, 2),
+                    help="decode: also time a two-layer pipeline (both prefetches issued at step start)")
     ap.add_argument("--backward", action="store_true",
                     help="time l3_backward (the training pass) instead of the forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -380,6 +386,12 @@ def decode_bench(args, cfg, torch, l3, synth):
     out = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
     ws = plan.workspace(n)
     st = l3.l3_staging_create(plan.handle, n * cfg.k, n)
+    # hot-row cache: the token stream is Zipf over the IDs in rank order, so the most
+    # frequent IDs are 0, 1, 2, ...; keep whole IDs until the row budget is used
+    dts = np.diff(off)
+    hot = np.arange(int(np.searchsorted(np.cumsum(dts), args.cache_rows, side="right")), dtype=np.int32)
+    if len(hot):
+        l3.l3_staging_set_cache(st, hot, WKh, WVh)
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     ready = torch.cuda.Event()
@@ -400,9 +412,12 @@ def decode_bench(args, cfg, torch, l3, synth):
         forward()
         main.synchronize()
 
+    staged = {}
+
     def copy_only(s_):
         prefetch(s_)
         ready.synchronize()
+        staged[s_] = l3.l3_staging_stats(st)
 
     def gemm_only(s_):
         gemm()
@@ -435,9 +450,15 @@ def decode_bench(args, cfg, torch, l3, synth):
     t_fwd = timed(lambda s_: (forward(), main.synchronize()))
     assert plan.status() == l3.L3_OK
 
-    rows = np.array([int((off[np.unique(i) + 1] - off[np.unique(i)]).sum()) for i in ids])
+    rows = np.array([int(dts[np.unique(i)].sum()) for i in ids])
+    cached = np.array([int(dts[np.intersect1d(np.unique(i), hot)].sum()) for i in ids])
+    # the library's own count of staged and cache-served rows must agree
+    assert all(staged[s_] == (rows[s_], cached[s_]) for s_ in range(S)), "staging stats disagree"
     row_b = (cfg.d_in + cfg.d_emb) * 2
-    h2d = rows * row_b
+    cfrac = float(cached.sum() / rows.sum())
+    h2d = (rows - cached) * row_b
+    pipe = decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st, plan, WKh, WVh, x, Wup, g, b,
+                            Wmix, gemm, side, ready, timed) if args.layers == 2 else None
     med = lambda a: float(np.median(a))
     ov = med(t_copy) + med(t_gemm) - med(t_conc)
     pcie = float(h2d.mean()) / (med(t_copy) * 1e-6) / 1e9
@@ -467,6 +488,9 @@ def decode_bench(args, cfg, torch, l3, synth):
             "overlap_us": ov, "f_copy_hidden": ov / med(t_copy), "f_gemm_covered": ov / med(t_gemm),
             "rows_per_step": {"mean": float(rows.mean()), "max": int(rows.max())},
             "h2d_bytes_per_step": float(h2d.mean()),
+            "cache": {"rows": int(dts[hot].sum()) if len(hot) else 0, "ids": int(len(hot)),
+                      "fraction_of_step_rows_served": cfrac},
+            "pipeline_2layer": pipe,
             "timing": "host clock from issuing the step's work to its synchronisation; medians "
                       "over the steps unless named",
         },
@@ -575,6 +599,80 @@ def backward_bench(args, cfg, torch, l3, synth):
     }
     print(json.dumps(line), flush=True)
     plan.close()
+
+
+def decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st1, plan1, WKh1, WVh1, x, Wup1, g1, b1,
+                     Wmix1, gemm, side1, ready1, timed):
+    """Two lookup layers per decode step, as the pages place L^3 after several decoder
+    layers: both layers' prefetches are issued when the step starts (layer 2 on its
+    own side stream and staging, with its own tables), then the main stream runs the
+    pre-layer GEMM, layer 1, the same GEMM again for the layers in between, and
+    layer 2 (whose input is layer 1's output).  t_copies: both prefetches alone;
+    t_compute: the same step with its rows already staged; ov = t_copies + t_compute -
+    t_step."""
+    n = cfg.n
+    assert cfg.d_out == cfg.d_in, "layer 2 reads layer 1's output"
+    c2 = dataclasses.replace(cfg, seed=cfg.seed + 1)
+
+    def pinned(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).pin_memory()
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    WKh2, WVh2 = pinned(synth.table(c2, "W_K")), pinned(synth.table(c2, "W_V"))
+    Wup2, Wmix2 = dev(synth.dense(c2, "W_up")), dev(synth.dense(c2, "W_mix"))
+    plan2 = l3.L3Plan(synth.offsets(cfg), cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16",
+                      cfg.ln_eps)
+    st2 = l3.l3_staging_create(plan2.handle, n * cfg.k, n)
+    if len(hot):
+        l3.l3_staging_set_cache(st2, hot, WKh2, WVh2)
+    ws1, ws2 = plan1.workspace(n), plan2.workspace(n)
+    out1 = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+    main = torch.cuda.current_stream()
+    side2 = torch.cuda.Stream()
+    ready2 = torch.cuda.Event()
+
+    def prefetch2(s_):
+        l3.l3_prefetch(plan1.handle, ids[s_], n, WKh1, WVh1, st1, side1, ready1)
+        l3.l3_prefetch(plan2.handle, ids[s_], n, WKh2, WVh2, st2, side2, ready2)
+
+    def compute():
+        gemm()
+        main.wait_stream(side1)
+        l3.l3_forward_staged(st1, x, n, Wup1, g1, b1, Wmix1, out1, ws1, ws1.numel())
+        gemm()
+        main.wait_stream(side2)
+        l3.l3_forward_staged(st2, out1, n, Wup2, g1, b1, Wmix2, out2, ws2, ws2.numel())
+
+    def step(s_):
+        prefetch2(s_)
+        compute()
+        main.synchronize()
+
+    def copies(s_):
+        prefetch2(s_)
+        ready1.synchronize()
+        ready2.synchronize()
+
+    def compute_only(s_):
+        compute()
+        main.synchronize()
+
+    for _ in range(max(1, args.warmup)):
+        step(0)
+    t_step, t_cp = timed(step), timed(copies)
+    t_cmp = timed(compute_only)
+    l3.l3_staging_destroy(st2)
+    plan2.close()
+    med = lambda a: float(np.median(a))
+    ov = med(t_cp) + med(t_cmp) - med(t_step)
+    return {"t_step_us": {"median": med(t_step), "p99": float(np.percentile(t_step, 99)),
+                          "mean": float(t_step.mean())},
+            "t_copies_us": med(t_cp), "t_compute_us": med(t_cmp), "overlap_us": ov,
+            "f_copy_hidden": ov / med(t_cp),
+            "tokens_per_s": n / (float(t_step.mean()) * 1e-6)}
 
 
 def cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, seconds):
