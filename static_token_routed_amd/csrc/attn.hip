@@ -523,7 +523,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     const int nitems = a.hdr[HDR_NHEAVY];
     // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
     // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
-    // items from its own counter, in order.
+    // items from its own counter, in order, and once it is empty take the other
+    // XCDs' remaining items, so no XCD idles while another still has a queue.
     const int xcd = blockIdx.x & 7;
 
     // LDS read addresses as per-lane bases plus compile-time offsets.
@@ -566,11 +567,20 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         lds_barrier();  // the next item's copies reuse the LDS and its index slot
     }
     lds_barrier();  // every wavefront has read the last dense index before it is rewritten
+    int steal = 0;  // queues found empty so far (thread 0 only): own XCD's first, then the others'
     for (;;) {
         if (t == 0) {
-            const int n = atomicAdd(&a.queue[xcd], 1);
-            const int it = ((n / QCHUNK) * 8 + xcd) * QCHUNK + n % QCHUNK;
-            *s_item = it < nitems ? it : -1;
+            int it = -1;
+            for (; steal < 8; ++steal) {
+                const int q = (xcd + steal) & 7;
+                const int n = atomicAdd(&a.queue[q], 1);
+                const int c = ((n / QCHUNK) * 8 + q) * QCHUNK + n % QCHUNK;
+                if (c < nitems) {
+                    it = c;
+                    break;
+                }
+            }
+            *s_item = it;
         }
         lds_barrier();
         const int it = *s_item;
