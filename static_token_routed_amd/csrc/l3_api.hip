@@ -144,10 +144,15 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     const int dense_min = attn_dense_min_tokens(D.d_in, D.d_emb, D.dtype);
     {
         StageTimer tm(0, s);
-        L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
-        L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));
-        L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
-                                   heavy, dense, s));
+        if (n <= kRouteSmallMax) {
+            L3_HIP_TRY(launch_route_small(ids, n, P.vocab, P.d_off, heavy_min, dense_min, light_tok, b,
+                                          light, heavy, dense, s));
+        } else {
+            L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
+            L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));
+            L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
+                                       heavy, dense, s));
+        }
     }
     {
         AttnArgs a{};
@@ -560,11 +565,17 @@ int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_byt
     b.uniq = ws_ptr<int32_t>(ws, L.uniq);
     b.counts = ws_ptr<int32_t>(ws, L.counts);
     b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
-    L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
-    L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
-    L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
-                               ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
-                               ws_ptr<int2>(ws, L.dense), s));
+    if (n <= kRouteSmallMax) {
+        L3_HIP_TRY(launch_route_small(ids, n, p->vocab, p->d_off, INT32_MAX, INT32_MAX, 1, b,
+                                      ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
+                                      ws_ptr<int2>(ws, L.dense), s));
+    } else {
+        L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
+        L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
+        L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
+                                   ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
+                                   ws_ptr<int2>(ws, L.dense), s));
+    }
     const size_t nb = (size_t)n * 4;
     auto cp = [&](int32_t *dst, const int32_t *src, size_t bytes) -> hipError_t {
         return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) : hipSuccess;

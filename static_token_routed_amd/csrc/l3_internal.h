@@ -16,6 +16,8 @@
 namespace l3 {
 
 constexpr int kSortTile = 2048;    // keys ranked per workgroup and pass
+constexpr int kRouteSmallMax = 1024;  // batches up to this size are routed by one workgroup
+constexpr int kSmallThreads = 1024;   // its threads (one token each)
 constexpr int kRadixBits = 9;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 features
@@ -75,6 +77,12 @@ hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs 
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
                            int heavy_min_tokens, int dense_min_tokens, int light_tokens,
                            int4 *light, int2 *heavy, int2 *dense, hipStream_t s);
+// The header zeroing, the route and the work lists of a batch of 1 .. kRouteSmallMax
+// tokens in one single-workgroup launch (same outputs; sorted keys and permutation
+// in keys_a / vals_a).
+hipError_t launch_route_small(const int32_t *ids, int64_t n, int64_t vocab, const int64_t *off,
+                              int heavy_min_tokens, int dense_min_tokens, int light_tokens, RouteBufs &b,
+                              int4 *light, int2 *heavy, int2 *dense, hipStream_t s);
 
 struct AttnArgs {
     const void *x, *WK, *WV;

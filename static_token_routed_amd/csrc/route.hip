@@ -248,6 +248,42 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
     }
 }
 
+// Work items of one block (segment) j with S tokens from sorted position sb and ID t
+// (t == vocab: IDs outside [0, vocab)).  The MFMA paths take blocks with many tokens
+// or many rows (long row chains stall the wavefront-per-item path); long blocks of
+// short enough rows are taken in dense items, the rest in streaming items.
+struct BlockItems {
+    int nl = 0, nh = 0, nd = 0, r0 = 0, d = 0;
+};
+
+__device__ inline BlockItems block_items(int S, int t, const int64_t *off, int vocab, int heavy_min,
+                                         int dense_min, int light_tok) {
+    BlockItems b;
+    b.d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
+    b.r0 = t < vocab ? (int)off[t] : 0;
+    if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || b.d >= kHeavyMinRows)) {
+        if (S >= dense_min && b.d <= kDenseMaxD)
+            b.nd = (S + kDenseTile - 1) / kDenseTile;
+        else
+            b.nh = (S + kHeavyTile - 1) / kHeavyTile;
+    } else {
+        b.nl = (S + light_tok - 1) / light_tok;
+    }
+    return b;
+}
+
+// Writes block j's items at list positions bl, bh, bd.  Light items carry what the
+// kernel needs, so it starts loading rows at once.
+__device__ inline void write_items(const BlockItems &b, int j, int sb, int S, bool in_range,
+                                   int light_tok, int bl, int bh, int bd, int4 *light, int2 *heavy,
+                                   int2 *dense) {
+    for (int q = 0; q < b.nl; ++q)
+        light[bl + q] = make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), b.r0,
+                                  in_range ? b.d : -1);
+    for (int q = 0; q < b.nh; ++q) heavy[bh + q] = make_int2(j, q * kHeavyTile);
+    for (int q = 0; q < b.nd; ++q) dense[bd + q] = make_int2(j, q * kDenseTile);
+}
+
 // One thread per block (segment): its size, and its work items appended to the light
 // or heavy list (one wave-aggregated atomic per list; item order does not affect
 // results, only scheduling).
@@ -263,26 +299,16 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int m = hdr[HDR_NSEG];
     const int lane = threadIdx.x & 63;
-    int nl = 0, nh = 0, nd = 0, S = 0, sb = 0, r0 = 0, d = 0;
+    int S = 0, sb = 0, t = vocab;
+    BlockItems bi;
     if (j < m) {
         sb = seg_start[j];
         S = seg_start[j + 1] - sb;
         counts[j] = S;
-        const int t = uniq[j];
-        d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
-        r0 = t < vocab ? (int)off[t] : 0;
-        // the MFMA paths take blocks with many tokens or many rows (long row chains
-        // stall the wavefront-per-item path); long blocks of short enough rows are
-        // taken in 128-token dense items, the rest in 32-token streaming items
-        if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || d >= kHeavyMinRows)) {
-            if (S >= dense_min && d <= kDenseMaxD)
-                nd = (S + kDenseTile - 1) / kDenseTile;
-            else
-                nh = (S + kHeavyTile - 1) / kHeavyTile;
-        } else {
-            nl = (S + light_tok - 1) / light_tok;
-        }
+        t = uniq[j];
+        bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
     }
+    const int nl = bi.nl, nh = bi.nh, nd = bi.nd;
     // wave-inclusive scans of nl, nh and nd
     int sl = nl, sh = nh, sd = nd;
 #pragma unroll
@@ -299,12 +325,106 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     bl = __shfl(bl, 63) + sl - nl;
     bh = __shfl(bh, 63) + sh - nh;
     bd = __shfl(bd, 63) + sd - nd;
-    // light items carry what the kernel needs, so it starts loading rows at once
-    for (int q = 0; q < nl; ++q)
-        light[bl + q] = make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), r0,
-                                  j < m && uniq[j] < vocab ? d : -1);
-    for (int q = 0; q < nh; ++q) heavy[bh + q] = make_int2(j, q * kHeavyTile);
-    for (int q = 0; q < nd; ++q) dense[bd + q] = make_int2(j, q * kDenseTile);
+    write_items(bi, j, sb, S, t < vocab, light_tok, bl, bh, bd, light, heavy, dense);
+}
+
+// Block-wide exclusive scan over kSmallThreads threads (one int32 each); the total
+// goes to *total.  wsum holds kSmallThreads / 64 words.
+__device__ inline int32_t block_scan_small(int32_t v, int32_t *wsum, int32_t *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(x, o);
+        if (lane >= o) x += u;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t pre = 0, all = 0;
+    for (int ww = 0; ww < kSmallThreads / 64; ++ww) {
+        pre += ww < w ? wsum[ww] : 0;
+        all += wsum[ww];
+    }
+    *total = all;
+    __syncthreads();
+    return pre + x - v;
+}
+
+// The whole route of a batch of at most kRouteSmallMax tokens in one workgroup (one
+// token per thread), for small batches where the multi-kernel route is all launch
+// latency.  Same outputs as the multi-kernel route and k_worklist: the header words
+// are zeroed here, each key's stable rank is the number of keys that are smaller or
+// equal and earlier (every thread compares its key with all keys in LDS), the
+// sorted keys give the block heads, and one block scan per list places each
+// block's items (in block order).
+__global__ __launch_bounds__(kSmallThreads) void k_route_small(
+    const int32_t *__restrict__ ids, int n, int vocab, const int64_t *__restrict__ off, int heavy_min,
+    int dense_min, int light_tok, int32_t *__restrict__ hdr, int32_t *__restrict__ sorted,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm, int32_t *__restrict__ uniq,
+    int32_t *__restrict__ counts, int32_t *__restrict__ seg_start, int4 *__restrict__ light,
+    int2 *__restrict__ heavy, int2 *__restrict__ dense) {
+    __shared__ int32_t keys[kRouteSmallMax], skeys[kRouteSmallMax];
+    __shared__ int32_t sstart[kRouteSmallMax + 1];
+    __shared__ int32_t wsum[kSmallThreads / 64];
+    const int i = threadIdx.x;
+    if (i < HDR_WORDS) hdr[i] = 0;
+    int key = INT32_MAX, bad = 0;
+    if (i < n) {
+        const int id = ids[i];
+        key = (id >= 0 && id < vocab) ? id : vocab;
+        bad = key != id;
+        keys[i] = key;
+    }
+    int32_t nbad;
+    block_scan_small(bad, wsum, &nbad);  // (its barrier also publishes keys[])
+    if (i < n) {
+        int r = 0;
+        for (int q = 0; q < n; ++q) {
+            const int kq = keys[q];
+            r += (kq < key) | ((kq == key) & (q < i));
+        }
+        skeys[r] = key;
+        sorted[r] = key;
+        perm[r] = i;
+        inv_perm[i] = r;
+    }
+    __syncthreads();
+    // blocks: heads of the sorted keys
+    const int head = (i < n) && (i == 0 || skeys[i] != skeys[i - 1]);
+    int32_t m;
+    const int j = block_scan_small(head, wsum, &m);
+    if (head) {
+        uniq[j] = skeys[i];
+        seg_start[j] = i;
+        sstart[j] = i;
+    }
+    if (i == 0) {
+        sstart[m] = n;
+        seg_start[m] = n;
+        hdr[HDR_NSEG] = m;
+        if (nbad) hdr[HDR_ERR] = 1;
+    }
+    __syncthreads();
+    // work lists: thread i describes block i
+    int S = 0, sb = 0, t = vocab;
+    BlockItems bi;
+    if (i < m) {
+        sb = sstart[i];
+        S = sstart[i + 1] - sb;
+        counts[i] = S;
+        t = skeys[sb];
+        bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
+    }
+    int32_t tl, th, td;
+    const int bl = block_scan_small(bi.nl, wsum, &tl);
+    const int bh = block_scan_small(bi.nh, wsum, &th);
+    const int bd = block_scan_small(bi.nd, wsum, &td);
+    write_items(bi, i, sb, S, t < vocab, light_tok, bl, bh, bd, light, heavy, dense);
+    if (i == 0) {
+        hdr[HDR_NLIGHT] = tl;
+        hdr[HDR_NHEAVY] = th;
+        hdr[HDR_NDENSE] = td;
+    }
 }
 
 inline int blocks_for(int64_t n, int per) { return (int)((n + per - 1) / per); }
@@ -345,6 +465,18 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
                        n, b.tile_cnt, b.inv_perm);
     hipLaunchKernelGGL(k_seg_write, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, n,
                        b.tile_cnt, (int)ntiles, b.hdr + HDR_NSEG, b.uniq, b.seg_start);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small(const int32_t *ids, int64_t n, int64_t vocab, const int64_t *off,
+                              int heavy_min_tokens, int dense_min_tokens, int light_tokens, RouteBufs &b,
+                              int4 *light, int2 *heavy, int2 *dense, hipStream_t s) {
+    if (n <= 0 || n > kRouteSmallMax) return hipErrorInvalidValue;
+    b.sorted_ids = b.keys_a;
+    b.perm = b.vals_a;
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(kSmallThreads), 0, s, ids, (int)n, (int)vocab, off,
+                       heavy_min_tokens, dense_min_tokens, light_tokens, b.hdr, b.keys_a, b.vals_a,
+                       b.inv_perm, b.uniq, b.counts, b.seg_start, light, heavy, dense);
     return hipGetLastError();
 }
 

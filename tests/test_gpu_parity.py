@@ -37,13 +37,22 @@ def _route_case(name):
     elif name == "out_of_range":
         ids = rng.integers(-3, vocab + 3, size=2500).astype(np.int32)
         ids[:6] = [-1, vocab, vocab + 100, 2 ** 31 - 1, -(2 ** 31), 5]
+    # batches of at most 1024 tokens take the one-workgroup route
+    elif name == "small_zipf":
+        ids = synth.token_ids(synth.CONFIGS["paper_bf16"])[:1000].copy()
+    elif name == "small_out_of_range":
+        ids = rng.integers(-2, 40, size=700).astype(np.int32)
+        ids[:4] = [vocab, -(2 ** 31), 2 ** 31 - 1, vocab + 7]
+    elif name in ("n1024", "n1025"):
+        ids = rng.integers(0, 300, size=int(name[1:])).astype(np.int32)
     else:
         raise KeyError(name)
     return off, ids
 
 
 ROUTE_CASES = ["tiny_f32", "small_bf16", "paper_bf16", "skew_bf16", "all_equal", "all_distinct",
-               "single", "ragged", "max_id", "out_of_range"]
+               "single", "ragged", "max_id", "out_of_range", "small_zipf", "small_out_of_range",
+               "n1024", "n1025"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
