@@ -298,6 +298,8 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
  * and the LayerNorm fold of W_mix), 5 W_mix GEMM; backward (which also runs
  * stages 0-2): 6 recompute of h and its LayerNorm statistics, 7 dense products
  * and the LayerNorm backward, 8 attention backward, 9 key / value gradients.
+ * bf16 batches of at most 512 tokens run one split-row gather-attention (row
+ * chunks, then a merge per token) recorded as stage 2, with no stage 1.
  * max_stages <= 10.  Not thread-safe; for benchmarking only.
  */
 int l3_profile_enable(int enable);

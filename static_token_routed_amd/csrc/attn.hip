@@ -13,6 +13,7 @@
 // d_t rows is an online (running max / running sum) fp32 softmax, so any d_t
 // streams through registers.  The result row goes to the token's original
 // batch position, which undoes the sort in the store.
+#include <algorithm>
 #include <type_traits>
 
 #include "cdna4.h"
@@ -65,6 +66,33 @@ __device__ inline void store_o(uint16_t *p, const float (&v)[VE]) {
         *reinterpret_cast<uint32_t *>(p) = pack2(v[0], v[1]);
     } else {
         *p = (uint16_t)f2bf(v[0]);
+    }
+}
+
+// A V row slice (VE bf16) kept as loaded and widened to fp32 where it is used.
+template <int VE> struct VRawS { uint4 u; };
+template <> struct VRawS<4> { uint2 u; };
+template <> struct VRawS<2> { uint32_t u; };
+template <> struct VRawS<1> { uint16_t u; };
+
+template <int VE>
+__device__ inline VRawS<VE> load_vraws(const uint16_t *p) {
+    VRawS<VE> r;
+    r.u = *reinterpret_cast<const decltype(r.u) *>(p);
+    return r;
+}
+
+template <int VE>
+__device__ inline void vraws_f32(const VRawS<VE> &r, float (&v)[VE]) {
+    if constexpr (VE == 8) {
+        v[0] = bf_lo(r.u.x); v[1] = bf_hi(r.u.x); v[2] = bf_lo(r.u.y); v[3] = bf_hi(r.u.y);
+        v[4] = bf_lo(r.u.z); v[5] = bf_hi(r.u.z); v[6] = bf_lo(r.u.w); v[7] = bf_hi(r.u.w);
+    } else if constexpr (VE == 4) {
+        v[0] = bf_lo(r.u.x); v[1] = bf_hi(r.u.x); v[2] = bf_lo(r.u.y); v[3] = bf_hi(r.u.y);
+    } else if constexpr (VE == 2) {
+        v[0] = bf_lo(r.u); v[1] = bf_hi(r.u);
+    } else {
+        v[0] = __uint_as_float((uint32_t)r.u << 16);
     }
 }
 
@@ -836,6 +864,166 @@ hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- small batches
+// Split-row gather-attention.  With few tokens per block, the per-block paths
+// above are one long row chain per wavefront or workgroup and the batch's time is
+// that chain's latency.  Here every block's rows are cut into chunks of RC rows
+// (RC d_in = 8192 columns, so a chunk's K and V rows fit in registers at once)
+// and its tokens into groups of TG; one wavefront per (chunk, group) item loads
+// the whole chunk and the group's x rows in one go, forms the scores (v_dot2,
+// wavefront sums), and stores for each token the chunk's softmax partial: the
+// max m_c, the sum l_c of exp(s - m_c) and the fp32 row sum_r exp(s_r - m_c) V_r.
+// A second kernel, one wavefront per token, merges its block's chunks in chunk
+// order: M = max_c m_c, o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.  The
+// result is the same softmax, summed in another order.
+// d_in / 512 rounded up to the slice counts the kernels are built for (1, 2, 4, 8)
+inline int64_t next_pow2_nci(int64_t d_in) {
+    const int64_t nci = (d_in + 511) / 512;
+    return nci <= 1 ? 1 : (nci <= 2 ? 2 : (nci <= 4 ? 4 : 8));
+}
+template <int NCI> constexpr int split_rc() { return 16 / NCI; }
+template <int NCI> constexpr int split_tg() { return NCI <= 2 ? 4 : (NCI == 4 ? 2 : 1); }
+
+template <int NCI, int VE>
+__global__ __launch_bounds__(256) void k_attn_split(SplitArgs a) {
+    constexpr int RC = split_rc<NCI>(), TG = split_tg<NCI>();
+    const int lane = threadIdx.x & 63;
+    const int nitems = a.hdr[HDR_NSPLIT];
+    const int64_t d_in = a.d_in, d_emb = a.d_emb;
+    const uint16_t *X = static_cast<const uint16_t *>(a.x);
+    const uint16_t *WK = static_cast<const uint16_t *>(a.WK);
+    const uint16_t *WV = static_cast<const uint16_t *>(a.WV);
+    for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += gridDim.x * 4) {
+        const int4 item = a.items[it];
+        const int j = __builtin_amdgcn_readfirstlane(item.x);
+        const int c = __builtin_amdgcn_readfirstlane(item.y);
+        const int g = __builtin_amdgcn_readfirstlane(item.z);
+        const int4 bi = a.blkinfo[j];
+        const int slot0 = __builtin_amdgcn_readfirstlane(bi.x);
+        const int S = __builtin_amdgcn_readfirstlane(bi.z);
+        const int sb = __builtin_amdgcn_readfirstlane(bi.w);
+        const int id = __builtin_amdgcn_readfirstlane(a.uniq[j]);
+        const int64_t r0 = a.off[id];
+        const int d = (int)(a.off[id + 1] - r0);
+        const int rb = c * RC, nr = min(RC, d - rb);
+        const int k0 = g * TG, nt = min(TG, S - k0);
+        // every load first (tokens and rows past the item's repeat its last one)
+        uint4 xv[TG][NCI], kr[RC][NCI];
+        VRawS<VE> vr[RC];
+#pragma unroll
+        for (int q = 0; q < TG; ++q) {
+            const int tok = a.perm[sb + k0 + min(q, nt - 1)];
+#pragma unroll
+            for (int cc = 0; cc < NCI; ++cc) {
+                const int64_t col = cc * 512 + lane * 8;
+                xv[q][cc] = col < d_in ? *reinterpret_cast<const uint4 *>(X + (int64_t)tok * d_in + col)
+                                       : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RC; ++r) {
+            const int64_t row = r0 + rb + min(r, nr - 1);
+#pragma unroll
+            for (int cc = 0; cc < NCI; ++cc) {
+                const int64_t col = cc * 512 + lane * 8;
+                kr[r][cc] = col < d_in ? *reinterpret_cast<const uint4 *>(WK + row * d_in + col)
+                                       : make_uint4(0, 0, 0, 0);
+            }
+            vr[r] = load_vraws<VE>(WV + row * d_emb + lane * VE);
+        }
+        float sc[TG][RC];
+#pragma unroll
+        for (int q = 0; q < TG; ++q)
+#pragma unroll
+            for (int r = 0; r < RC; ++r) {
+                float p = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < NCI; ++cc) {
+                    p = dot2(kr[r][cc].x, xv[q][cc].x, p);
+                    p = dot2(kr[r][cc].y, xv[q][cc].y, p);
+                    p = dot2(kr[r][cc].z, xv[q][cc].z, p);
+                    p = dot2(kr[r][cc].w, xv[q][cc].w, p);
+                }
+                sc[q][r] = wave_sum(p);
+            }
+#pragma unroll
+        for (int q = 0; q < TG; ++q) {
+            if (q >= nt) break;
+            float m = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < RC; ++r)
+                if (r < nr) m = fmaxf(m, sc[q][r]);
+            float l = 0.f, acc[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int r = 0; r < RC; ++r) {
+                if (r >= nr) break;
+                const float p = __expf(sc[q][r] - m);
+                l += p;
+                float v[VE];
+                vraws_f32<VE>(vr[r], v);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc[e] = fmaf(p, v[e], acc[e]);
+            }
+            const int64_t slot = slot0 + (int64_t)c * S + k0 + q;
+            float *dst = a.po + slot * d_emb + lane * VE;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) dst[e] = acc[e];
+            if (lane == 0) a.pml[slot] = make_float2(m, l);
+        }
+    }
+}
+
+template <int VE>
+__global__ __launch_bounds__(256) void k_attn_merge(SplitArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t d_emb = a.d_emb;
+    uint16_t *O = static_cast<uint16_t *>(a.o);
+    for (int p = blockIdx.x * 4 + (threadIdx.x >> 6); p < a.n; p += gridDim.x * 4) {
+        const int j = __builtin_amdgcn_readfirstlane(a.blk_of[p]);
+        const int4 bi = a.blkinfo[j];
+        const int slot0 = __builtin_amdgcn_readfirstlane(bi.x);
+        const int nc = __builtin_amdgcn_readfirstlane(bi.y);
+        const int S = __builtin_amdgcn_readfirstlane(bi.z);
+        const int k = p - __builtin_amdgcn_readfirstlane(bi.w);
+        float res[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) res[e] = 0.f;
+        if (nc > 0) {  // else an ID outside [0, vocab): its row is zero (the flag is set)
+            float M = -INFINITY;
+            for (int c = 0; c < nc; ++c) M = fmaxf(M, a.pml[slot0 + (int64_t)c * S + k].x);
+            float L = 0.f;
+            for (int c = 0; c < nc; ++c) {
+                const int64_t slot = slot0 + (int64_t)c * S + k;
+                const float2 ml = a.pml[slot];
+                const float w = __expf(ml.x - M);
+                L = fmaf(ml.y, w, L);
+                const float *src = a.po + slot * d_emb + lane * VE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) res[e] = fmaf(w, src[e], res[e]);
+            }
+            const float inv = 1.f / L;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) res[e] *= inv;
+        }
+        store_o<VE>(O + (int64_t)a.perm[p] * d_emb + lane * VE, res);
+    }
+}
+
+template <int NCI>
+hipError_t launch_split_nci(const SplitArgs &sa, int64_t d_emb, int nblocks, hipStream_t s) {
+    switch (d_emb / 64) {
+        case 1: hipLaunchKernelGGL((k_attn_split<NCI, 1>), dim3(nblocks), dim3(256), 0, s, sa); break;
+        case 2: hipLaunchKernelGGL((k_attn_split<NCI, 2>), dim3(nblocks), dim3(256), 0, s, sa); break;
+        case 4: hipLaunchKernelGGL((k_attn_split<NCI, 4>), dim3(nblocks), dim3(256), 0, s, sa); break;
+        case 8: hipLaunchKernelGGL((k_attn_split<NCI, 8>), dim3(nblocks), dim3(256), 0, s, sa); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int attn_light_tokens(int64_t d_in, int dtype) {
@@ -858,6 +1046,41 @@ hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {
                  a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.dense, a.d_in,
                  (uint16_t *)a.o};
     return launch_heavy(ha, a.d_emb, s);
+}
+
+int split_rows(int64_t d_in) { return 16 / (int)std::min<int64_t>(8, next_pow2_nci(d_in)); }
+int split_tokens(int64_t d_in) {
+    const int64_t nci = next_pow2_nci(d_in);
+    return nci <= 2 ? 4 : (nci == 4 ? 2 : 1);
+}
+
+int64_t split_slots(const Dims &d, int64_t n, int32_t max_d) {
+    if (d.dtype != L3_BF16 || n < 1 || n > kSplitMaxN || d.d_in > 4096) return 0;
+    if (d.d_emb != 64 && d.d_emb != 128 && d.d_emb != 256 && d.d_emb != 512) return 0;
+    const int rc = split_rows(d.d_in);
+    const int64_t slots = n * ((std::max<int64_t>(max_d, 1) + rc - 1) / rc);
+    return slots <= kSplitMaxSlots ? slots : 0;
+}
+
+hipError_t launch_attn_split(const SplitArgs &sa, hipStream_t s) {
+    // items: at most one per (chunk, token); a grid of up to 1024 workgroups strides over them
+    const int64_t nci = next_pow2_nci(sa.d_in);
+    const int nblocks = 1024;
+    hipError_t e;
+    if (nci <= 1) e = launch_split_nci<1>(sa, sa.d_emb, nblocks, s);
+    else if (nci <= 2) e = launch_split_nci<2>(sa, sa.d_emb, nblocks, s);
+    else if (nci <= 4) e = launch_split_nci<4>(sa, sa.d_emb, nblocks, s);
+    else e = launch_split_nci<8>(sa, sa.d_emb, nblocks, s);
+    if (e != hipSuccess) return e;
+    const int mb = (int)std::min<int64_t>((sa.n + 3) / 4, 1024);
+    switch (sa.d_emb / 64) {
+        case 1: hipLaunchKernelGGL((k_attn_merge<1>), dim3(mb), dim3(256), 0, s, sa); break;
+        case 2: hipLaunchKernelGGL((k_attn_merge<2>), dim3(mb), dim3(256), 0, s, sa); break;
+        case 4: hipLaunchKernelGGL((k_attn_merge<4>), dim3(mb), dim3(256), 0, s, sa); break;
+        case 8: hipLaunchKernelGGL((k_attn_merge<8>), dim3(mb), dim3(256), 0, s, sa); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_attn_light(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -139,6 +139,25 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     int2 *dense = ws_ptr<int2>(ws, L.dense);
     void *o = ws_ptr<char>(ws, L.o);
 
+    if (L.slots > 0) {
+        // small batch: split-row gather-attention (no light / heavy / dense lists)
+        const SplitLists sl{ws_ptr<int4>(ws, L.sitems), ws_ptr<int4>(ws, L.blkinfo),
+                            ws_ptr<int32_t>(ws, L.blk_of)};
+        {
+            StageTimer tm(0, s);
+            L3_HIP_TRY(launch_route_small_split(ids, n, P.vocab, P.d_off, split_rows(D.d_in),
+                                                split_tokens(D.d_in), b, sl, s));
+        }
+        SplitArgs sa{};
+        sa.x = x; sa.WK = WK; sa.WV = WV; sa.off = P.d_off;
+        sa.uniq = b.uniq; sa.perm = b.perm; sa.hdr = b.hdr; sa.blk_of = sl.blk_of;
+        sa.items = sl.items; sa.blkinfo = sl.blkinfo;
+        sa.n = n; sa.d_in = D.d_in; sa.d_emb = D.d_emb;
+        sa.pml = ws_ptr<float2>(ws, L.pml); sa.po = ws_ptr<float>(ws, L.po); sa.o = o;
+        StageTimer tm(2, s);
+        L3_HIP_TRY(launch_attn_split(sa, s));
+        return L3_OK;
+    }
     const int light_tok = attn_light_tokens(D.d_in, D.dtype);
     const int heavy_min = attn_heavy_min_tokens(D.d_in, D.d_emb, D.dtype, P.max_d);
     const int dense_min = attn_dense_min_tokens(D.d_in, D.d_emb, D.dtype);
@@ -414,6 +433,12 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.part = take(d.dtype == L3_BF16 ? std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
                                                  skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in))
                                      : 0);
+    L.slots = split_slots(d, n, max_d);
+    L.sitems = take((size_t)L.slots * 16);
+    L.blkinfo = take(L.slots ? (size_t)n * 16 : 0);
+    L.blk_of = take(L.slots ? (size_t)n * 4 : 0);
+    L.pml = take((size_t)L.slots * 8);
+    L.po = take((size_t)L.slots * d.d_emb * 4);
     L.total = off;
     return L;
 }
@@ -499,9 +524,12 @@ int l3_worklist_rule(l3_plan_t p, int32_t *min_tokens, int32_t *min_rows) {
     return L3_OK;
 }
 
+// Batches of up to kSplitMaxN tokens take a larger layout per token (the split-row
+// partials), so a workspace sized for n_max must also cover those sizes.
 size_t l3_workspace_size(l3_plan_t p, int64_t n_max) {
     if (!p || n_max < 0) return 0;
-    return ws_layout(p->dims, n_max, p->max_d).total;
+    return std::max(ws_layout(p->dims, n_max, p->max_d).total,
+                    ws_layout(p->dims, std::min<int64_t>(n_max, kSplitMaxN), p->max_d).total);
 }
 
 int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
@@ -520,7 +548,8 @@ int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const 
 
 size_t l3_backward_workspace_size(l3_plan_t p, int64_t n_max) {
     if (!p || n_max < 0) return 0;
-    return bwd_layout(p->dims, n_max, p->max_d).total;
+    return std::max(bwd_layout(p->dims, n_max, p->max_d).total,
+                    bwd_layout(p->dims, std::min<int64_t>(n_max, kSplitMaxN), p->max_d).total);
 }
 
 int l3_backward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,

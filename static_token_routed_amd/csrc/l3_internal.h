@@ -30,6 +30,7 @@ constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense 
 
 // Workspace header (int32 words), zeroed at the start of every call.
 enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_NKV = 5,
+       HDR_NSPLIT = 6,
        HDR_QUEUE = 8, HDR_WORDS = 64 };
 
 struct Dims {
@@ -47,6 +48,11 @@ struct WsLayout {
     size_t stats;  // LayerNorm row statistics (mean, rstd)
     size_t fold;   // LayerNorm fold of W_mix (bf16 path)
     size_t part;   // split-K partial slabs of the small-M path (bf16 path, n <= kSkinnyMaxM)
+    // split-row gather-attention of small batches (split_slots() > 0): row-chunk
+    // items, per-block {slot base, chunks, tokens, first sorted position}, each sorted
+    // position's block, and per (token, chunk) partial (max, sum) and output rows
+    size_t sitems, blkinfo, blk_of, pml, po;
+    int64_t slots;  // 0: the small-batch split path is off for this size
     size_t total;
     int64_t ntiles;
 };
@@ -83,6 +89,37 @@ hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, in
 hipError_t launch_route_small(const int32_t *ids, int64_t n, int64_t vocab, const int64_t *off,
                               int heavy_min_tokens, int dense_min_tokens, int light_tokens, RouteBufs &b,
                               int4 *light, int2 *heavy, int2 *dense, hipStream_t s);
+
+// Split-row gather-attention for small bf16 batches: each block's rows are cut into
+// chunks of split_rows(d_in) rows and its tokens into groups of split_tokens(d_in);
+// one wavefront per (chunk, group) item forms the chunk's softmax partials, and one
+// wavefront per token merges its block's chunks.  Used when n <= kSplitMaxN and the
+// partial slots (<= n * ceil(max_d / split_rows)) stay within kSplitMaxSlots.
+constexpr int kSplitMaxN = 512;
+constexpr int64_t kSplitMaxSlots = 32768;
+int split_rows(int64_t d_in);
+int split_tokens(int64_t d_in);
+int64_t split_slots(const Dims &d, int64_t n, int32_t max_d);  // 0: path off
+struct SplitLists {
+    int4 *items, *blkinfo;
+    int32_t *blk_of;
+};
+// The single-workgroup route that also writes the split-row items (instead of the
+// light / heavy / dense lists).
+hipError_t launch_route_small_split(const int32_t *ids, int64_t n, int64_t vocab, const int64_t *off,
+                                    int rows, int tokens, RouteBufs &b, const SplitLists &sl,
+                                    hipStream_t s);
+struct SplitArgs {
+    const void *x, *WK, *WV;
+    const int64_t *off;
+    const int32_t *uniq, *perm, *hdr, *blk_of;
+    const int4 *items, *blkinfo;
+    int64_t n, d_in, d_emb;
+    float2 *pml;
+    float *po;
+    void *o;
+};
+hipError_t launch_attn_split(const SplitArgs &a, hipStream_t s);
 
 struct AttnArgs {
     const void *x, *WK, *WV;

@@ -357,12 +357,20 @@ __device__ inline int32_t block_scan_small(int32_t v, int32_t *wsum, int32_t *to
 // equal and earlier (every thread compares its key with all keys in LDS), the
 // sorted keys give the block heads, and one block scan per list places each
 // block's items (in block order).
+//
+// With SPLIT the work lists are the split-row items instead: block j's rows in
+// ceil(d_t / rows) chunks and its tokens in groups of `tokens`, one item per (chunk,
+// group), written in block order; blkinfo[j] = {first partial slot, chunks, tokens,
+// first sorted position} (slots: chunk-major, one per (chunk, token)); blk_of[p] =
+// the block of sorted position p.  IDs outside [0, vocab) get no chunks.
+template <bool SPLIT>
 __global__ __launch_bounds__(kSmallThreads) void k_route_small(
     const int32_t *__restrict__ ids, int n, int vocab, const int64_t *__restrict__ off, int heavy_min,
     int dense_min, int light_tok, int32_t *__restrict__ hdr, int32_t *__restrict__ sorted,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm, int32_t *__restrict__ uniq,
     int32_t *__restrict__ counts, int32_t *__restrict__ seg_start, int4 *__restrict__ light,
-    int2 *__restrict__ heavy, int2 *__restrict__ dense) {
+    int2 *__restrict__ heavy, int2 *__restrict__ dense, int4 *__restrict__ sitems,
+    int4 *__restrict__ blkinfo, int32_t *__restrict__ blk_of) {
     __shared__ int32_t keys[kRouteSmallMax], skeys[kRouteSmallMax];
     __shared__ int32_t sstart[kRouteSmallMax + 1];
     __shared__ int32_t wsum[kSmallThreads / 64];
@@ -398,6 +406,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(
         seg_start[j] = i;
         sstart[j] = i;
     }
+    if (SPLIT && i < n) blk_of[i] = j + head - 1;
     if (i == 0) {
         sstart[m] = n;
         seg_start[m] = n;
@@ -407,14 +416,30 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(
     __syncthreads();
     // work lists: thread i describes block i
     int S = 0, sb = 0, t = vocab;
-    BlockItems bi;
     if (i < m) {
         sb = sstart[i];
         S = sstart[i + 1] - sb;
         counts[i] = S;
         t = skeys[sb];
-        bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
     }
+    if constexpr (SPLIT) {
+        // here heavy_min = rows per chunk, light_tok = tokens per group
+        const int rows = heavy_min, tokens = light_tok;
+        const int d = (i < m && t < vocab) ? (int)(off[t + 1] - off[t]) : 0;
+        const int nc = (d + rows - 1) / rows, ng = (S + tokens - 1) / tokens;
+        int32_t ti, ts;
+        const int bi0 = block_scan_small(nc * ng, wsum, &ti);
+        const int bs0 = block_scan_small(nc * S, wsum, &ts);
+        if (i < m) {
+            blkinfo[i] = make_int4(bs0, nc, S, sb);
+            for (int c = 0; c < nc; ++c)
+                for (int g = 0; g < ng; ++g) sitems[bi0 + c * ng + g] = make_int4(i, c, g, 0);
+        }
+        if (i == 0) hdr[HDR_NSPLIT] = ti;
+        return;
+    }
+    BlockItems bi;
+    if (i < m) bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
     int32_t tl, th, td;
     const int bl = block_scan_small(bi.nl, wsum, &tl);
     const int bh = block_scan_small(bi.nh, wsum, &th);
@@ -474,9 +499,23 @@ hipError_t launch_route_small(const int32_t *ids, int64_t n, int64_t vocab, cons
     if (n <= 0 || n > kRouteSmallMax) return hipErrorInvalidValue;
     b.sorted_ids = b.keys_a;
     b.perm = b.vals_a;
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(kSmallThreads), 0, s, ids, (int)n, (int)vocab, off,
-                       heavy_min_tokens, dense_min_tokens, light_tokens, b.hdr, b.keys_a, b.vals_a,
-                       b.inv_perm, b.uniq, b.counts, b.seg_start, light, heavy, dense);
+    hipLaunchKernelGGL(k_route_small<false>, dim3(1), dim3(kSmallThreads), 0, s, ids, (int)n, (int)vocab,
+                       off, heavy_min_tokens, dense_min_tokens, light_tokens, b.hdr, b.keys_a, b.vals_a,
+                       b.inv_perm, b.uniq, b.counts, b.seg_start, light, heavy, dense, (int4 *)nullptr,
+                       (int4 *)nullptr, (int32_t *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small_split(const int32_t *ids, int64_t n, int64_t vocab, const int64_t *off,
+                                    int rows, int tokens, RouteBufs &b, const SplitLists &sl,
+                                    hipStream_t s) {
+    if (n <= 0 || n > kRouteSmallMax || rows < 1 || tokens < 1) return hipErrorInvalidValue;
+    b.sorted_ids = b.keys_a;
+    b.perm = b.vals_a;
+    hipLaunchKernelGGL(k_route_small<true>, dim3(1), dim3(kSmallThreads), 0, s, ids, (int)n, (int)vocab,
+                       off, rows, 0, tokens, b.hdr, b.keys_a, b.vals_a, b.inv_perm, b.uniq, b.counts,
+                       b.seg_start, (int4 *)nullptr, (int2 *)nullptr, (int2 *)nullptr, sl.items,
+                       sl.blkinfo, sl.blk_of);
     return hipGetLastError();
 }
 

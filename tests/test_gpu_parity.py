@@ -199,6 +199,22 @@ def test_determinism_and_batch_independence(small_cfg_gpu):
     print(f"sub-batch err {e1:.2e}, shuffled err {e2:.2e}", flush=True)
 
 
+def test_out_of_range_ids_small_batch(small_cfg_gpu):
+    # 300 tokens take the small-batch route and the split-row gather
+    g = small_cfg_gpu
+    x, ids = g.x[:300].contiguous(), g.ids[:300].clone()
+    ids[7] = -5
+    ids[250] = g.case.cfg.vocab + 1
+    out = g.forward(x=x, ids=ids)
+    assert g.plan.status() == l3.L3_ERR_TOKEN_RANGE
+    good = g.forward(x=x, ids=g.ids[:300].contiguous())
+    assert g.plan.status() == l3.L3_OK
+    keep = torch.ones(300, dtype=torch.bool, device="cuda")
+    keep[7] = keep[250] = False
+    assert torch.equal(out[keep], good[keep])
+    assert torch.isfinite(out.float()).all()
+
+
 def test_out_of_range_ids_flag(small_cfg_gpu):
     g = small_cfg_gpu
     ids = g.ids.clone()
