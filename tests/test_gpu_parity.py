@@ -105,6 +105,13 @@ SMALL_BF16 = [
     ("skinny_d1024_e256", 800, 64, 1024, 256, 512, 320, 200, 20000),
     ("skinny_straddle", 300, 48, 1024, 128, 320, 192, 77, 8000),
     ("skinny_d2048_e512_n512", 600, 96, 2048, 512, 512, 256, 512, 20000),
+    # batches of at most 512 tokens take the split-row gather: d_in below one
+    # 512-column slice (masked lanes, 16-row chunks) at the largest such batch, the
+    # widest d_in (2-row chunks, one token per group), and one token past the limit
+    # (the single-workgroup route with the per-block gather kernels)
+    ("split_d192_n512", 300, 90, 192, 64, 128, 64, 512, 9000),
+    ("split_d4096_e128", 200, 40, 4096, 128, 128, 128, 100, 4000),
+    ("nosplit_d192_n513", 300, 90, 192, 64, 128, 64, 513, 9000),
 ]
 
 
