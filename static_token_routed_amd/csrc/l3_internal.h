@@ -15,7 +15,9 @@
 
 namespace l3 {
 
-constexpr int kSortTile = 2048;    // keys ranked per workgroup and pass
+constexpr int kSortTile = 512;     // keys ranked per workgroup and pass
+constexpr int kSortPer = kSortTile / 256;  // keys per thread of a 256-thread tile
+static_assert(kSortTile % 256 == 0 && kSortPer <= 32, "sort tile");
 constexpr int kRouteSmallMax = 1024;  // batches up to this size are routed by one workgroup
 constexpr int kSmallThreads = 1024;   // its threads (one token each)
 constexpr int kRadixBits = 9;

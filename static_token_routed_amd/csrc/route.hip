@@ -7,8 +7,8 @@
 //
 // Stable LSD radix sort of the keys (token ID, or `vocab` for an ID outside
 // [0, vocab)) in 9-bit digits.  Per pass:
-//   k_sort_rank    each workgroup ranks 2048 keys: every wave takes 512
-//                  consecutive keys, 64 at a time in batch order; lanes with the
+//   k_sort_rank    each workgroup ranks kSortTile (512) keys: every wave takes
+//                  kSortTile / 4 consecutive keys, 64 at a time in batch order; lanes with the
 //                  same digit find each other with 9 ballots, the lowest lane
 //                  reserves their places with one LDS atomic, so ranks are
 //                  stable; writes the tile's digit histogram (digit-major).
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_zero_i32(int32_t *p, int64_t count) {
     if (i < count) p[i] = 0;
 }
 
-// Ranks the keys of one 2048-key tile for the digit at `shift`.
+// Ranks the keys of one kSortTile-key tile for the digit at `shift`.
 __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ keys, int n,
                                                    int shift, int from_ids, int vocab,
                                                    int32_t *__restrict__ rank,
@@ -46,10 +46,10 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
     __syncthreads();
 
     const int base = tile * kSortTile + w * (kSortTile / 4);
-    uint32_t dig[8], rk[8];
+    uint32_t dig[kSortPer], rk[kSortPer];
     int bad = 0;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kSortPer; ++r) {
         const int idx = base + r * 64 + lane;
         const bool valid = idx < n;
         int key = 0;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kSortPer; ++r) {
         const int idx = base + r * 64 + lane;
         if (idx < n) rank[idx] = (int32_t)(cnt[w][dig[r]] + rk[r]);
     }
@@ -118,7 +118,7 @@ __device__ inline int32_t block_scan_256(int32_t v, int32_t *wsum, int32_t *tota
     return pre + x - v;
 }
 
-// One workgroup per 2048-key tile.  The destination of digit d's keys in tile t
+// One workgroup per kSortTile-key tile.  The destination of digit d's keys in tile t
 // is the exclusive prefix of the digit-major histogram at (d, t): the keys of all
 // smaller digits, plus those of digit d in earlier tiles.  Each workgroup forms the
 // 512 offsets of its own tile from the histogram (no separate scan pass), then
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict_
     }
 }
 
-// Per 2048-key tile: number of block heads; also the inverse permutation.
+// Per kSortTile-key tile: number of block heads; also the inverse permutation.
 __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ sk,
                                                    const int32_t *__restrict__ perm, int n,
                                                    int32_t *__restrict__ tile_cnt,
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ s
     const int base = blockIdx.x * kSortTile;
     int c = 0;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kSortPer; ++r) {
         const int s = base + r * 256 + threadIdx.x;
         if (s < n) {
             c += (s == 0 || sk[s] != sk[s - 1]);
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ s
     if (threadIdx.x == 0) tile_cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
-// Writes uniq[] and seg_start[] of the heads in one tile (8 consecutive keys per
+// Writes uniq[] and seg_start[] of the heads in one tile (kSortPer consecutive keys per
 // thread); the tile's first block index is the sum of the head counts of the tiles
 // before it (summed here, no separate scan pass).  The number of blocks m goes to
 // *nseg and seg_start[m] = n.
@@ -223,10 +223,10 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
     __syncthreads();
     const int32_t tile_off = tile_sums[0], m = tile_sums[1];
 
-    const int base = blockIdx.x * kSortTile + threadIdx.x * 8;
+    const int base = blockIdx.x * kSortTile + threadIdx.x * kSortPer;
     int flags = 0, c = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kSortPer; ++i) {
         const int s = base + i;
         const int f = (s < n) && (s == 0 || sk[s] != sk[s - 1]);
         flags |= f << i;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
     int32_t all;
     int j = tile_off + block_scan_256(c, wsum, &all);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kSortPer; ++i) {
         if ((flags & (1 << i)) && j < n) {
             uniq[j] = sk[base + i];
             seg_start[j] = base + i;
