@@ -850,7 +850,7 @@ hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
     }
 }
 
-constexpr int kAttnBlocks = 2048;
+constexpr int kAttnBlocks = 4096;  // enough wavefronts for one light item each at 32768 tokens
 
 template <int NCI>
 hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
