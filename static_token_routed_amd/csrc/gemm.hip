@@ -50,7 +50,7 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int TILE = BM * BK * 2;          // bytes of one operand tile of a stage
 constexpr int SLOT = 2 * TILE;             // one stage (double-buffered)
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 
 struct GemmP {
     const uint16_t *A, *A2;  // A columns [0, K1) from A (row stride lda), [K1, K) from A2 (lda2)
