@@ -123,7 +123,9 @@ int l3_plan_info(l3_plan_t plan, int64_t *vocab, int64_t *v, int32_t *k,
 /* Which distinct IDs of a batch the matrix-core gather-attention takes (the rest
  * go one wavefront per item): those with at least *min_tokens tokens in the
  * batch or at least *min_rows rows (d_t); both are INT32_MAX when the plan's
- * dims have no matrix-core path.  Either pointer may be NULL. */
+ * dims have no matrix-core path.  Either pointer may be NULL.  The rule applies
+ * to batches of more than 512 tokens: smaller bf16 batches whose partials fit
+ * (see l3_profile_enable) take the split-row gather for every ID. */
 int l3_worklist_rule(l3_plan_t plan, int32_t *min_tokens, int32_t *min_rows);
 
 /* Bytes of device workspace l3_forward / l3_route need for up to n_max tokens
