@@ -293,73 +293,93 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     // column n0 + wn*128 + 16j + 4(l/16) + e.
     const uint32_t lane = fresh_lane_id();
     const int64_t nbase = n0 + wn * 128;
+    auto epilogue = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
+        for (int i = 0; i < 8; ++i) {
+            const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
+            uint32_t pk[LN_OUT ? 8 : 1][2];  // the stored bf16 values (all 8 kept for LN_OUT)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
-            if constexpr (LN_IN) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(&c2s[wn * 128 + 16 * j + 4 * (lane >> 4)]);
-                acc[i][j][0] += c4.x;
-                acc[i][j][1] += c4.y;
-                acc[i][j][2] += c4.z;
-                acc[i][j][3] += c4.w;
-            }
-            if (m < p.M && n < p.N) {
+            for (int j = 0; j < 8; ++j) {
+                const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
+                if constexpr (LN_IN) {
+                    const float4 c4 = *reinterpret_cast<const float4 *>(&c2s[wn * 128 + 16 * j + 4 * (lane >> 4)]);
+                    acc[i][j][0] += c4.x;
+                    acc[i][j][1] += c4.y;
+                    acc[i][j][2] += c4.z;
+                    acc[i][j][3] += c4.w;
+                }
                 if constexpr (OUT == 0) {
-                    *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
-                        make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
-                } else {
-                    float4 *dst = reinterpret_cast<float4 *>(p.Cf + m * p.N + n);
-                    float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                    if constexpr (OUT == 2) {
-                        const float4 c = *dst;
-                        v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+                    pk[j & (LN_OUT ? 7 : 0)][0] = pack2(acc[i][j][0], acc[i][j][1]);
+                    pk[j & (LN_OUT ? 7 : 0)][1] = pack2(acc[i][j][2], acc[i][j][3]);
+                }
+                if (FULL || (m < p.M && n < p.N)) {
+                    if constexpr (OUT == 0) {
+                        *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
+                            make_uint2(pk[j & (LN_OUT ? 7 : 0)][0], pk[j & (LN_OUT ? 7 : 0)][1]);
+                    } else {
+                        float4 *dst = reinterpret_cast<float4 *>(p.Cf + m * p.N + n);
+                        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                        if constexpr (OUT == 2) {
+                            const float4 c = *dst;
+                            v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+                        }
+                        *dst = v;
                     }
-                    *dst = v;
+                }
+            }
+            if constexpr (LN_OUT && OUT == 0) {
+                // partial statistics of this row's stored (bf16) values over each 64
+                // columns (4 blocks of 16)
+                auto stored = [&](int j, int e) {
+                    const uint32_t w2 = pk[j][e >> 1];
+                    const float v = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                    if constexpr (FULL) return v;
+                    const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
+                    return n < p.N ? v : 0.f;
+                };
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const int64_t c0 = nbase + 64 * part;
+                    const int64_t width = FULL ? kLnPart : min<int64_t>(kLnPart, p.N - c0);
+                    if (!FULL && width <= 0) continue;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int j = 4 * part; j < 4 * part + 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sum += stored(j, e);
+                    sum += __shfl_xor(sum, 16);
+                    sum += __shfl_xor(sum, 32);
+                    // kLnPart is a power of two: the product is the exact quotient
+                    const float mean = FULL ? sum * (1.f / kLnPart) : sum / (float)width;
+                    float q = 0.f;
+#pragma unroll
+                    for (int j = 4 * part; j < 4 * part + 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float dv = stored(j, e) - mean;
+                            if constexpr (FULL) {
+                                q += dv * dv;
+                            } else {
+                                const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
+                                q += n < p.N ? dv * dv : 0.f;
+                            }
+                        }
+                    q += __shfl_xor(q, 16);
+                    q += __shfl_xor(q, 32);
+                    if (lane < 16 && (FULL || m < p.M)) {
+                        float *dst = p.ln_out + (m * p.npart_out + c0 / kLnPart) * 2;
+                        dst[0] = mean;
+                        dst[1] = q;
+                    }
                 }
             }
         }
-        if constexpr (LN_OUT) {
-            // partial statistics of this row's stored (bf16) values over each 64
-            // columns (4 blocks of 16)
-            auto stored = [&](int j, int e) {
-                const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
-                return n < p.N ? __uint_as_float(f2bf(acc[i][j][e]) << 16) : 0.f;
-            };
-#pragma unroll
-            for (int part = 0; part < 2; ++part) {
-                const int64_t c0 = nbase + 64 * part;
-                const int64_t width = min<int64_t>(kLnPart, p.N - c0);
-                if (width <= 0) continue;
-                float sum = 0.f;
-#pragma unroll
-                for (int j = 4 * part; j < 4 * part + 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sum += stored(j, e);
-                sum += __shfl_xor(sum, 16);
-                sum += __shfl_xor(sum, 32);
-                const float mean = sum / (float)width;
-                float q = 0.f;
-#pragma unroll
-                for (int j = 4 * part; j < 4 * part + 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
-                        const float dv = stored(j, e) - mean;
-                        q += n < p.N ? dv * dv : 0.f;
-                    }
-                q += __shfl_xor(q, 16);
-                q += __shfl_xor(q, 32);
-                if (lane < 16 && m < p.M) {
-                    float *dst = p.ln_out + (m * p.npart_out + c0 / kLnPart) * 2;
-                    dst[0] = mean;
-                    dst[1] = q;
-                }
-            }
-        }
-    }
+    };
+    // (only the W_up GEMM, whose statistics double the per-element work, gets the
+    // unchecked copy; the others keep one copy of the code)
+    if (LN_OUT && m0 + BM <= p.M && n0 + BN <= p.N) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
 }
 
 // Row statistics of h from the W_up epilogue's partials: one thread per row,
