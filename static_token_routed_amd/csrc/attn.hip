@@ -875,8 +875,8 @@ hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
 // wavefront sums), and stores for each token the chunk's softmax partial: the
 // max m_c, the sum l_c of exp(s - m_c) and the fp32 row sum_r exp(s_r - m_c) V_r.
 // A second kernel, one wavefront per token, merges its block's chunks in chunk
-// order: M = max_c m_c, o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.  The
-// result is the same softmax, summed in another order.
+// order with a running max (o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c,
+// M = max_c m_c).  The result is the same softmax, summed in another order.
 // d_in / 512 rounded up to the slice counts the kernels are built for (1, 2, 4, 8)
 inline int64_t next_pow2_nci(int64_t d_in) {
     const int64_t nci = (d_in + 511) / 512;
@@ -976,6 +976,8 @@ __global__ __launch_bounds__(256) void k_attn_split(SplitArgs a) {
     }
 }
 
+constexpr int kMergeU = 4;  // chunks whose partials are loaded together in the merge
+
 template <int VE>
 __global__ __launch_bounds__(256) void k_attn_merge(SplitArgs a) {
     const int lane = threadIdx.x & 63;
@@ -992,17 +994,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) res[e] = 0.f;
         if (nc > 0) {  // else an ID outside [0, vocab): its row is zero (the flag is set)
-            float M = -INFINITY;
-            for (int c = 0; c < nc; ++c) M = fmaxf(M, a.pml[slot0 + (int64_t)c * S + k].x);
-            float L = 0.f;
-            for (int c = 0; c < nc; ++c) {
-                const int64_t slot = slot0 + (int64_t)c * S + k;
-                const float2 ml = a.pml[slot];
-                const float w = __expf(ml.x - M);
-                L = fmaf(ml.y, w, L);
-                const float *src = a.po + slot * d_emb + lane * VE;
+            // one pass with a running max, kMergeU chunks' loads in flight at a time
+            // (chunks past nc re-read the last one and are skipped)
+            float M = -INFINITY, L = 0.f;
+            for (int c0 = 0; c0 < nc; c0 += kMergeU) {
+                float2 ml[kMergeU];
+                float src[kMergeU][VE];
 #pragma unroll
-                for (int e = 0; e < VE; ++e) res[e] = fmaf(w, src[e], res[e]);
+                for (int u = 0; u < kMergeU; ++u) {
+                    const int64_t slot = slot0 + (int64_t)min(c0 + u, nc - 1) * S + k;
+                    ml[u] = a.pml[slot];
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) src[u][e] = a.po[slot * d_emb + lane * VE + e];
+                }
+#pragma unroll
+                for (int u = 0; u < kMergeU; ++u) {
+                    if (c0 + u >= nc) break;
+                    const float mn = fmaxf(M, ml[u].x);
+                    const float al = __expf(M - mn), w = __expf(ml[u].x - mn);
+                    L = fmaf(L, al, ml[u].y * w);
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) res[e] = fmaf(w, src[u][e], res[e] * al);
+                    M = mn;
+                }
             }
             const float inv = 1.f / L;
 #pragma unroll
