@@ -167,8 +167,7 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
             L3_HIP_TRY(launch_route_small(ids, n, P.vocab, P.d_off, heavy_min, dense_min, light_tok, b,
                                           light, heavy, dense, s));
         } else {
-            L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
-            L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));
+            L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));  // clears the header too
             L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
                                        heavy, dense, s));
         }
@@ -599,8 +598,7 @@ int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_byt
                                       ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
                                       ws_ptr<int2>(ws, L.dense), s));
     } else {
-        L3_HIP_TRY(launch_zero_i32(b.hdr, HDR_WORDS, s));
-        L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));
+        L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));  // clears the header too
         L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
                                    ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
                                    ws_ptr<int2>(ws, L.dense), s));

@@ -75,6 +75,8 @@ struct RouteBufs {
 
 // ---- launchers (all enqueue on `s`; return hipError_t of the last launch)
 hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s);
+// The multi-kernel route; it also clears the header (the first sort pass) and
+// sets the out-of-range flag (the block writer), so no separate clear is needed.
 hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs &b, int64_t ntiles,
                         hipStream_t s);
 // Work lists for the gather-attention kernels (reads the route outputs).

@@ -37,17 +37,19 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
                                                    int shift, int from_ids, int vocab,
                                                    int32_t *__restrict__ rank,
                                                    int32_t *__restrict__ hist, int ntiles,
-                                                   int32_t *__restrict__ err) {
+                                                   int32_t *__restrict__ hdr) {
     __shared__ uint32_t cnt[4][kRadix];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int tile = blockIdx.x;
     for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+    // the first pass clears the header words the later launches count into (the
+    // out-of-range flag is written outright by k_seg_write)
+    if (from_ids && tile == 0 && threadIdx.x < HDR_WORDS && threadIdx.x != HDR_ERR) hdr[threadIdx.x] = 0;
     __syncthreads();
 
     const int base = tile * kSortTile + w * (kSortTile / 4);
     uint32_t dig[kSortPer], rk[kSortPer];
-    int bad = 0;
 #pragma unroll
     for (int r = 0; r < kSortPer; ++r) {
         const int idx = base + r * 64 + lane;
@@ -55,11 +57,7 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
         int key = 0;
         if (valid) {
             key = keys[idx];
-            if (from_ids) {
-                const int k2 = key_of(key, vocab);
-                bad |= (k2 != key);
-                key = k2;
-            }
+            if (from_ids) key = key_of(key, vocab);
         }
         const uint32_t d = ((uint32_t)key >> shift) & (kRadix - 1);
         uint64_t mask = __ballot(valid);
@@ -76,9 +74,6 @@ __global__ __launch_bounds__(256) void k_sort_rank(const int32_t *__restrict__ k
         old = __shfl(old, leader);
         dig[r] = d;
         rk[r] = old + below;
-    }
-    if (from_ids) {
-        if (__ballot(bad) != 0ull && lane == 0) atomicOr(err, 1);
     }
     __syncthreads();
     for (int d = threadIdx.x; d < kRadix; d += 256) {
@@ -197,7 +192,7 @@ __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ s
 // *nseg and seg_start[m] = n.
 __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ sk, int n,
                                                    const int32_t *__restrict__ tile_cnt, int ntiles,
-                                                   int32_t *__restrict__ nseg,
+                                                   int32_t *__restrict__ hdr, int vocab,
                                                    int32_t *__restrict__ uniq,
                                                    int32_t *__restrict__ seg_start) {
     __shared__ int32_t wsum[4];
@@ -243,8 +238,10 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
         }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *nseg = m;
+        hdr[HDR_NSEG] = m;
         seg_start[min(m, n)] = n;
+        // IDs outside [0, vocab) have the key vocab, the largest, so they sort last
+        hdr[HDR_ERR] = n > 0 && sk[n - 1] == vocab;
     }
 }
 
@@ -475,7 +472,7 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
         const int shift = p * kRadixBits;
         const int from_ids = p == 0;
         hipLaunchKernelGGL(k_sort_rank, dim3((unsigned)ntiles), dim3(256), 0, s, kin, n, shift,
-                           from_ids, (int)vocab, b.rank, b.hist, (int)ntiles, b.hdr + HDR_ERR);
+                           from_ids, (int)vocab, b.rank, b.hist, (int)ntiles, b.hdr);
         hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)ntiles), dim3(256), 0, s, kin,
                            vin ? vin : kin, n, shift, from_ids, (int)vocab, b.hist, (int)ntiles,
                            b.rank, kout, vout);
@@ -489,7 +486,7 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
     hipLaunchKernelGGL(k_seg_heads, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, b.perm,
                        n, b.tile_cnt, b.inv_perm);
     hipLaunchKernelGGL(k_seg_write, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, n,
-                       b.tile_cnt, (int)ntiles, b.hdr + HDR_NSEG, b.uniq, b.seg_start);
+                       b.tile_cnt, (int)ntiles, b.hdr, (int)vocab, b.uniq, b.seg_start);
     return hipGetLastError();
 }
 
