@@ -442,6 +442,219 @@ hipError_t launch_token_ch(const BwdArgs &a, int part, hipStream_t s) {
     return launch_token_ne<T, CH, (4096 + 64 * CH - 1) / (64 * CH)>(a, part, s);
 }
 
+// ---------------------------------------------------------------- matrix cores (bf16)
+// Attention backward on the matrix cores, for bf16 plans with d_in in {512, 1024,
+// 2048} and d_emb in {128, 256, 512}.  One workgroup per item of up to 16 tokens of
+// one block (sorted positions s0 .. s0 + cnt - 1; token j of the item is MFMA
+// column j), so each K row is read twice per 16 tokens instead of twice per token:
+//  * the block's rows stream through LDS in 16-row stages (double-buffered
+//    asynchronous copies); pass 1 forms the scores and the softmax max and sum per
+//    token, pass 2 the scores again, P, dP = V dO^T, dS = P (dP - <dO, o>) (o is the
+//    forward output the recompute left in the workspace), stores P and dS for the
+//    key / value gradients, and adds dx^T += K_t^T dS per 16-column block;
+//  * wavefront w of NW (4, or 8 at d_in 2048 to keep x and the dx sums in
+//    registers) owns 1/NW of d_in (scores' partial sums, dx columns) and of d_emb
+//    (dP's partial sums); the wavefronts' partial scores and dP are added through
+//    LDS in a fixed order;
+//  * scores use v_mfma_f32_16x16x32_bf16 with K rows as the first operand, so a
+//    lane holds rows 4 (l / 16) + v of token l % 16 -- which is the layout the
+//    second operand of v_mfma_f32_16x16x16_bf16 wants for dS; the first operand
+//    (K transposed) comes from ds_read_b64_tr_b16: lane (g, j) passing the address
+//    of row 4g + j / 4, columns c0 + 4 (j % 4) .. +3 receives rows 4g .. 4g + 3 of
+//    column c0 + j.
+// dO enters the dP product rounded to bf16 (the other products already take bf16
+// operands); everything accumulates in fp32.
+constexpr int kBwdT = 16;  // tokens per matrix-core item
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <int XQ, int DE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
+    constexpr int d_in = 64 * XQ;
+    constexpr int KROW = d_in * 2 + 48;   // LDS bytes per K row (padding: conflict-free reads)
+    constexpr int KST = 16 * KROW;        // one 16-row stage
+    constexpr int CPR = d_in / 512;       // 1 KB copies per row
+    constexpr int CPW = 16 * CPR / NW;    // copies per wavefront and stage
+    constexpr int QI = d_in / NW;         // d_in columns per wavefront
+    constexpr int NXK = QI / 32;          // their 32-column steps
+    constexpr int QE = DE / NW;           // d_emb columns per wavefront
+    constexpr int NEK = QE / 32;
+    constexpr int NCB = QI / 16;          // 16-column dx blocks per wavefront
+    constexpr int XB = NW * 64 * 16;      // bytes of one exchange area (a f32x4 per lane)
+    static_assert(CPR >= 1 && CPW * NW == 16 * CPR && NEK >= 1 && 2 * KST + 2 * XB <= 163840,
+                  "bwd stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * KST + 2 * XB];
+    f32x4_t *const spart = reinterpret_cast<f32x4_t *>(lds + 2 * KST);
+    f32x4_t *const dpart = reinterpret_cast<f32x4_t *>(lds + 2 * KST + XB);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l16 = lane & 15, kg = lane >> 4;
+    const uint16_t *X = static_cast<const uint16_t *>(a.x);
+    const uint16_t *WK = static_cast<const uint16_t *>(a.WK);
+    const uint16_t *WV = static_cast<const uint16_t *>(a.WV);
+    const uint16_t *O = static_cast<const uint16_t *>(a.o);
+    const uint32_t lds0 = lds_addr(lds);
+    const int nitems = a.hdr[HDR_NLIGHT];
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        const int4 item = a.items[it];
+        const int s0 = __builtin_amdgcn_readfirstlane(item.x);
+        const int cnt = __builtin_amdgcn_readfirstlane(item.y);
+        const int64_t r0 = __builtin_amdgcn_readfirstlane(item.z);
+        const int d = __builtin_amdgcn_readfirstlane(item.w);
+        if (d < 0) continue;  // ID out of range: no gradient (flagged by the route)
+        const int nc = (d + 15) / 16;
+        const int tok = a.perm[s0 + min(l16, cnt - 1)];
+        // this lane's token: x and dO over the wavefront's quarters, and <dO, o>
+        bf16x8_t xf[NXK], df[NEK];
+#pragma unroll
+        for (int ks = 0; ks < NXK; ++ks)
+            xf[ks] = *reinterpret_cast<const bf16x8_t *>(X + (int64_t)tok * d_in + w * QI + 32 * ks + 8 * kg);
+#pragma unroll
+        for (int ks = 0; ks < NEK; ++ks) {
+            const float4 *dp = reinterpret_cast<const float4 *>(a.dov + (int64_t)tok * DE + w * QE + 32 * ks + 8 * kg);
+            const float4 u0 = dp[0], u1 = dp[1];
+            df[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(pack2(u0.x, u0.y), pack2(u0.z, u0.w),
+                                                             pack2(u1.x, u1.y), pack2(u1.z, u1.w)));
+        }
+        float D = 0.f;
+#pragma unroll 2
+        for (int j = 0; j < DE / 32; ++j) {
+            const int64_t e0 = (int64_t)tok * DE + 32 * j + 8 * kg;
+            const float4 *dp = reinterpret_cast<const float4 *>(a.dov + e0);
+            const float4 u0 = dp[0], u1 = dp[1];
+            const uint4 ov = *reinterpret_cast<const uint4 *>(O + e0);
+            D = fmaf(u0.x, bf_lo(ov.x), D); D = fmaf(u0.y, bf_hi(ov.x), D);
+            D = fmaf(u0.z, bf_lo(ov.y), D); D = fmaf(u0.w, bf_hi(ov.y), D);
+            D = fmaf(u1.x, bf_lo(ov.z), D); D = fmaf(u1.y, bf_hi(ov.z), D);
+            D = fmaf(u1.z, bf_lo(ov.w), D); D = fmaf(u1.w, bf_hi(ov.w), D);
+        }
+        D += __shfl_xor(D, 16);
+        D += __shfl_xor(D, 32);
+
+        f32x4_t acc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY, l = 0.f, inv_l = 0.f;
+
+        // stage st (pass st / nc, chunk st % nc): K rows [16c, +16) (past d_t: row d_t - 1)
+        auto issue = [&](int st) {
+            const int c = st < nc ? st : st - nc;
+            const uint32_t base = lds0 + (uint32_t)((st & 1) * KST);
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int q = w * CPW + i, row = q / CPR, piece = q % CPR;
+                const int64_t grow = r0 + min(16 * c + row, d - 1);
+                async_ld16(WK + grow * d_in + piece * 512 + lane * 8, base + row * KROW + piece * 1024);
+            }
+        };
+        issue(0);
+        for (int st = 0; st < 2 * nc; ++st) {
+            const bool p2 = st >= nc;
+            const int c = p2 ? st - nc : st;
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (st + 1 < 2 * nc) issue(st + 1);
+            const unsigned char *kt = lds + (st & 1) * KST;
+            f32x4_t sp = {0.f, 0.f, 0.f, 0.f}, dpp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NXK; ++ks) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(kt + l16 * KROW + (w * QI + 32 * ks + 8 * kg) * 2);
+                sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xf[ks], sp, 0, 0, 0);
+            }
+            if (p2) {
+                const uint16_t *vr = WV + (r0 + min(16 * c + l16, d - 1)) * DE + w * QE + 8 * kg;
+#pragma unroll
+                for (int ks = 0; ks < NEK; ++ks) {
+                    const bf16x8_t Av = *reinterpret_cast<const bf16x8_t *>(vr + 32 * ks);
+                    dpp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, df[ks], dpp, 0, 0, 0);
+                }
+            }
+            spart[w * 64 + lane] = sp;
+            if (p2) dpart[w * 64 + lane] = dpp;
+            lds_barrier();
+            f32x4_t S = spart[lane];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) S += spart[64 * ww + lane];
+            const int rb = 16 * c + 4 * kg;  // this lane's rows rb .. rb + 3 (of token l16)
+            if (!p2) {
+                float cm = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (rb + v < d) cm = fmaxf(cm, S[v]);
+                cm = fmaxf(cm, __shfl_xor(cm, 16));
+                cm = fmaxf(cm, __shfl_xor(cm, 32));
+                const float mn = fmaxf(m, cm);
+                float ls = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ls += rb + v < d ? __expf(S[v] - mn) : 0.f;
+                ls += __shfl_xor(ls, 16);
+                ls += __shfl_xor(ls, 32);
+                l = fmaf(l, __expf(m - mn), ls);
+                m = mn;
+                if (st == nc - 1) inv_l = 1.f / l;
+            } else {
+                f32x4_t dP = dpart[lane];
+#pragma unroll
+                for (int ww = 1; ww < NW; ++ww) dP += dpart[64 * ww + lane];
+                float pv[4], ds[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pv[v] = rb + v < d ? __expf(S[v] - m) * inv_l : 0.f;
+                    ds[v] = pv[v] * (dP[v] - D);
+                }
+                if (w == 0 && l16 < cnt) {
+                    float *Pp = a.P + (int64_t)(s0 + l16) * a.max_d, *dSp = a.dS + (int64_t)(s0 + l16) * a.max_d;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (rb + v < d) {
+                            Pp[rb + v] = pv[v];
+                            dSp[rb + v] = ds[v];
+                        }
+                }
+                const i16x4_t B = __builtin_bit_cast(i16x4_t, make_uint2(pack2(ds[0], ds[1]), pack2(ds[2], ds[3])));
+                const unsigned char *trb = kt + (4 * kg + (l16 >> 2)) * KROW + (w * QI + 4 * (l16 & 3)) * 2;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const i16x4_t Ak = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t *)(trb + 32 * cb));
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ak, B, acc[cb], 0, 0, 0);
+                }
+            }
+        }
+        // dx[token][columns] += dx^T: lane holds columns 16 cb + 4 kg .. + 3 of token l16
+        if (l16 < cnt) {
+            float *dxr = a.dx + (int64_t)tok * d_in + w * QI + 4 * kg;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                float4 *dst = reinterpret_cast<float4 *>(dxr + 16 * cb);
+                float4 v = *dst;
+                v.x += acc[cb][0]; v.y += acc[cb][1]; v.z += acc[cb][2]; v.w += acc[cb][3];
+                *dst = v;
+            }
+        }
+        lds_barrier();  // the next item's first copies reuse the stages and the exchange area
+    }
+}
+
+template <int XQ, int NW>
+hipError_t launch_bwd_mfma_xq(const BwdArgs &a, hipStream_t s) {
+    const dim3 g(256), b(64 * NW);
+    switch (a.d_emb) {
+        case 128: if constexpr (NW == 4) { hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 128, NW>), g, b, 0, s, a); break; }
+                  return hipErrorInvalidValue;
+        case 256: hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 256, NW>), g, b, 0, s, a); break;
+        case 512: hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 512, NW>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// d_in 2048 takes eight wavefronts, whose d_emb share must hold a 32-column step
+bool bwd_mfma_dims(int64_t d_in, int64_t d_emb, int dtype) {
+    if (dtype != L3_BF16) return false;
+    if (d_in == 512 || d_in == 1024) return d_emb == 128 || d_emb == 256 || d_emb == 512;
+    return d_in == 2048 && (d_emb == 256 || d_emb == 512);
+}
+
 }  // namespace
 
 hipError_t launch_transpose(const void *src, int64_t ld_src, int64_t rows, int64_t cols, void *dst,
@@ -485,6 +698,7 @@ int kv_item_capacity(int64_t n, int64_t rows) {
 int ln_param_chunks(int64_t n) { return (int)std::max<int64_t>(1, (n + kLnRows - 1) / kLnRows); }
 
 int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype) {
+    if (bwd_mfma_dims(d_in, d_emb, dtype)) return kBwdT;
     // the kernel's TB for its chunk width: two tokens while a lane's share of d_in
     // (NI * CH elements) is at most 32
     const int64_t ch = dtype == L3_BF16 ? 8 : (d_in % 4 == 0 && d_emb % 4 == 0 ? 4 : 1);
@@ -493,6 +707,11 @@ int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype) {
 
 hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, int part, hipStream_t s) {
     if (a.d_in > 4096 || a.d_emb > 1024) return hipErrorInvalidValue;
+    if (part == 0 && bwd_mfma_dims(a.d_in, a.d_emb, dtype)) {
+        if (a.d_in == 512) return launch_bwd_mfma_xq<8, 4>(a, s);
+        if (a.d_in == 1024) return launch_bwd_mfma_xq<16, 4>(a, s);
+        return launch_bwd_mfma_xq<32, 8>(a, s);
+    }
     if (dtype == L3_BF16) return launch_token_ch<uint16_t, 8>(a, part, s);  // bf16 dims: multiples of 64
     if (a.d_in % 4 == 0 && a.d_emb % 4 == 0) return launch_token_ch<float, 4>(a, part, s);
     return launch_token_ch<float, 1>(a, part, s);

@@ -375,7 +375,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     BwdArgs a{};
     a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
     a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
-    a.items = items; a.dov = dov;
+    a.items = items; a.dov = dov; a.o = o;
     a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab; a.max_d = P.max_d;
     a.dx = dx; a.P = ws_ptr<float>(ws, B.P); a.dS = ws_ptr<float>(ws, B.dS);
     a.dWK = dWK; a.dWV = dWV;

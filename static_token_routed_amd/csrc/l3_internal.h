@@ -215,6 +215,7 @@ struct BwdArgs {
     const int32_t *uniq, *seg_start, *perm, *hdr;
     const int4 *items;   // attn_bwd_tokens tokens per item (first sorted position, count, first row, d_t)
     const float *dov;    // dL/do [n x d_emb]
+    const void *o;       // the forward's o [n x d_emb] (recomputed), for <dO, o>
     int64_t d_in, d_emb, vocab;
     int max_d;
     float *dx;           // [n x d_in], holds W2^T dout; the attention term is added

@@ -28,9 +28,13 @@ CASES = {
     # bf16, 1100 tokens (ragged against every tile): the 256x256 GEMM
     "bf16_n1100": synth.small("bb2", vocab=600, k=64, d_in=512, d_emb=256, d_up=512, d_out=256,
                               n=1100, v=9000, dtype="bf16", seed=9, ids_s=1.05),
-    # bf16, the paper's d_in and d_emb
+    # bf16, the paper's d_in and d_emb (matrix-core attention backward, 8 wavefronts)
     "bf16_d2048": synth.small("bb3", vocab=300, k=96, d_in=2048, d_emb=512, d_up=512, d_out=256,
                               n=700, v=6000, dtype="bf16", seed=10, ids_s=1.05),
+    # bf16, d_in 1024 / d_emb 128 (matrix-core attention backward, 4 wavefronts), blocks
+    # longer than 16 tokens and 16 rows, and a ragged last row chunk (k = 70)
+    "bf16_d1024_e128": synth.small("bb4", vocab=150, k=70, d_in=1024, d_emb=128, d_up=256,
+                                   d_out=128, n=900, v=4000, dtype="bf16", seed=11, ids_s=1.05),
 }
 KEYS = ["dx", "dW_K", "dW_V", "dW_up", "dgamma", "dbeta", "dW_mix"]
 
