@@ -635,14 +635,141 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
     }
 }
 
+// Key / value gradients on the matrix cores (bf16, the same dims as the matrix-core
+// attention backward).  One workgroup per (block, 16-row) item, as k_kv_grad, over
+// the block's tokens in tiles of 16:
+//   dW_K[rows] += dS^T x,  dW_V[rows] += P^T dO
+// as dW^T (columns x rows) += x^T (columns x tokens) dS (tokens x rows) with
+// v_mfma_f32_16x16x16_bf16: the tile's x rows (and its dO rows, rounded to bf16)
+// are staged in LDS and read transposed (ds_read_b64_tr_b16, as above), dS and P
+// (fp32, stored by the attention backward) are rounded to bf16 into the second
+// operand, and a lane ends with 4 consecutive columns of one row, added to the
+// fp32 gradient as one 16-byte read-modify-write.  Wavefront w owns 1/NW of the
+// columns of W_K and of W_V.
+template <int XQ, int DE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_kv_grad_mfma(BwdArgs a) {
+    constexpr int d_in = 64 * XQ;
+    constexpr int XROW = d_in * 2 + 48, VROW = DE * 2 + 48;  // padded LDS rows
+    constexpr int XT = 16 * XROW;
+    constexpr int CPR = d_in / 512;    // 1 KB copies per x row
+    constexpr int CPW = 16 * CPR / NW; // x copies per wavefront
+    constexpr int QI = d_in / NW, QE = DE / NW;
+    constexpr int NKB = QI / 16, NVB = QE / 16;
+    static_assert(CPW * NW == 16 * CPR && NVB >= 1 && XT + 16 * VROW <= 163840, "kv stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[XT + 16 * VROW];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l16 = lane & 15, kg = lane >> 4;
+    const uint16_t *X = static_cast<const uint16_t *>(a.x);
+    const uint32_t lds0 = lds_addr(lds);
+    const int nitems = min(a.hdr[HDR_NKV], a.kv_cap);
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        const int2 item = a.kv_items[it];
+        const int b = __builtin_amdgcn_readfirstlane(item.x);
+        const int j0 = __builtin_amdgcn_readfirstlane(item.y);
+        const int t = __builtin_amdgcn_readfirstlane(a.uniq[b]);
+        const int64_t r0 = a.off[t];
+        const int d = (int)(a.off[t + 1] - r0), nr = min(16, d - j0);
+        const int s0 = __builtin_amdgcn_readfirstlane(a.seg_start[b]);
+        const int s1 = __builtin_amdgcn_readfirstlane(a.seg_start[b + 1]);
+        f32x4_t ak[NKB], av[NVB];
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb) ak[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < NVB; ++cb) av[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tb = s0; tb < s1; tb += 16) {
+            const int nt = min(16, s1 - tb);
+            lds_barrier();  // every wavefront is done with the previous tile
+            // x rows of the tile's tokens (past nt: its last token, whose dS and P are
+            // zeroed below), 1 KB asynchronous copies
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int q = w * CPW + i, row = q / CPR, piece = q % CPR;
+                const int tok = __builtin_amdgcn_readfirstlane(a.perm[tb + min(row, nt - 1)]);
+                async_ld16(X + (int64_t)tok * d_in + piece * 512 + lane * 8, lds0 + row * XROW + piece * 1024);
+            }
+            // dO rows, rounded to bf16, 8 values per thread and step
+            for (int ch = threadIdx.x; ch < 16 * DE / 8; ch += 64 * NW) {
+                const int row = ch / (DE / 8), c8 = ch % (DE / 8);
+                const int tok = a.perm[tb + min(row, nt - 1)];
+                const float4 *src = reinterpret_cast<const float4 *>(a.dov + (int64_t)tok * DE + 8 * c8);
+                const float4 u0 = src[0], u1 = src[1];
+                *reinterpret_cast<uint4 *>(lds + XT + row * VROW + 16 * c8) =
+                    make_uint4(pack2(u0.x, u0.y), pack2(u0.z, u0.w), pack2(u1.x, u1.y), pack2(u1.z, u1.w));
+            }
+            // dS and P of tokens tb + 4kg .. +3 at row j0 + l16
+            float dsv[4], pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = 4 * kg + i < nt && l16 < nr;
+                const int64_t at = (int64_t)(tb + 4 * kg + i) * a.max_d + j0 + l16;
+                dsv[i] = ok ? a.dS[at] : 0.f;
+                pv[i] = ok ? a.P[at] : 0.f;
+            }
+            const i16x4_t Bds = __builtin_bit_cast(i16x4_t, make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3])));
+            const i16x4_t Bp = __builtin_bit_cast(i16x4_t, make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3])));
+            wait_vmcnt<0>();
+            lds_barrier();
+            const unsigned char *xr = lds + (4 * kg + (l16 >> 2)) * XROW + (w * QI + 4 * (l16 & 3)) * 2;
+#pragma unroll
+            for (int cb = 0; cb < NKB; ++cb) {
+                const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(xr + 32 * cb));
+                ak[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, Bds, ak[cb], 0, 0, 0);
+            }
+            const unsigned char *vr = lds + XT + (4 * kg + (l16 >> 2)) * VROW + (w * QE + 4 * (l16 & 3)) * 2;
+#pragma unroll
+            for (int cb = 0; cb < NVB; ++cb) {
+                const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vr + 32 * cb));
+                av[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, Bp, av[cb], 0, 0, 0);
+            }
+        }
+        // lane: columns 16 cb + 4 kg .. + 3 of row j0 + l16
+        if (l16 < nr) {
+            float *dk = a.dWK + (r0 + j0 + l16) * d_in + w * QI + 4 * kg;
+#pragma unroll
+            for (int cb = 0; cb < NKB; ++cb) {
+                float4 *dst = reinterpret_cast<float4 *>(dk + 16 * cb);
+                float4 v = *dst;
+                v.x += ak[cb][0]; v.y += ak[cb][1]; v.z += ak[cb][2]; v.w += ak[cb][3];
+                *dst = v;
+            }
+            float *dv = a.dWV + (r0 + j0 + l16) * DE + w * QE + 4 * kg;
+#pragma unroll
+            for (int cb = 0; cb < NVB; ++cb) {
+                float4 *dst = reinterpret_cast<float4 *>(dv + 16 * cb);
+                float4 v = *dst;
+                v.x += av[cb][0]; v.y += av[cb][1]; v.z += av[cb][2]; v.w += av[cb][3];
+                *dst = v;
+            }
+        }
+    }
+}
+
+template <int XQ, int NW, int DE>
+void launch_bwd_mfma_de(const BwdArgs &a, int part, hipStream_t s) {
+    const dim3 b(64 * NW);
+    if (part == 0) {
+        hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, DE, NW>), dim3(256), b, 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k_kv_items, dim3(64), dim3(256), 0, s, a.off, a.uniq, const_cast<int32_t *>(a.hdr),
+                           a.vocab, a.kv_items, a.kv_cap);
+        hipLaunchKernelGGL((k_kv_grad_mfma<XQ, DE, NW>), dim3(1024), b, 0, s, a);
+    }
+}
+
 template <int XQ, int NW>
-hipError_t launch_bwd_mfma_xq(const BwdArgs &a, hipStream_t s) {
-    const dim3 g(256), b(64 * NW);
+hipError_t launch_bwd_mfma_xq(const BwdArgs &a, int part, hipStream_t s) {
     switch (a.d_emb) {
-        case 128: if constexpr (NW == 4) { hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 128, NW>), g, b, 0, s, a); break; }
-                  return hipErrorInvalidValue;
-        case 256: hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 256, NW>), g, b, 0, s, a); break;
-        case 512: hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, 512, NW>), g, b, 0, s, a); break;
+        case 128:
+            if constexpr (NW == 4) {
+                launch_bwd_mfma_de<XQ, NW, 128>(a, part, s);
+                break;
+            }
+            return hipErrorInvalidValue;
+        case 256: launch_bwd_mfma_de<XQ, NW, 256>(a, part, s); break;
+        case 512: launch_bwd_mfma_de<XQ, NW, 512>(a, part, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -707,10 +834,10 @@ int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype) {
 
 hipError_t launch_attn_bwd(const BwdArgs &a, int dtype, int part, hipStream_t s) {
     if (a.d_in > 4096 || a.d_emb > 1024) return hipErrorInvalidValue;
-    if (part == 0 && bwd_mfma_dims(a.d_in, a.d_emb, dtype)) {
-        if (a.d_in == 512) return launch_bwd_mfma_xq<8, 4>(a, s);
-        if (a.d_in == 1024) return launch_bwd_mfma_xq<16, 4>(a, s);
-        return launch_bwd_mfma_xq<32, 8>(a, s);
+    if (bwd_mfma_dims(a.d_in, a.d_emb, dtype)) {
+        if (a.d_in == 512) return launch_bwd_mfma_xq<8, 4>(a, part, s);
+        if (a.d_in == 1024) return launch_bwd_mfma_xq<16, 4>(a, part, s);
+        return launch_bwd_mfma_xq<32, 8>(a, part, s);
     }
     if (dtype == L3_BF16) return launch_token_ch<uint16_t, 8>(a, part, s);  // bf16 dims: multiples of 64
     if (a.d_in % 4 == 0 && a.d_emb % 4 == 0) return launch_token_ch<float, 4>(a, part, s);
