@@ -39,6 +39,7 @@
 // chunk, the mean and the sum of squared deviations of the stored bf16 values),
 // merged with Chan's pairwise update.  The concatenated operand never exists in
 // memory and the inner loop carries no LayerNorm arithmetic.
+#include <algorithm>
 #include <type_traits>
 
 #include "cdna4.h"
@@ -64,12 +65,13 @@ struct GemmP {
     float *ln_out;           // [M x npart_out x 2] partial statistics of the stored rows
     int npart_out;
     int tiles_m, tiles_n;
+    int splits;       // OUT == 1: K cut in `splits` ranges of ksplit columns, one output slab each
+    int64_t ksplit;
 };
 
 // tile id -> (tm, tn): XCD-contiguous, then grouped by GROUP_M tile rows.
-__device__ inline void tile_coords(const GemmP &p, int &tm, int &tn) {
+__device__ inline void tile_coords(const GemmP &p, int bid, int &tm, int &tn) {
     const int nt = p.tiles_m * p.tiles_n;
-    const int bid = blockIdx.x;
     const int xcd = bid & 7, q = nt >> 3, r = nt & 7;
     const int tl = xcd * q + min(xcd, r) + (bid >> 3);
     const int per_group = GROUP_M * p.tiles_n;
@@ -91,8 +93,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     // each thread's lane offsets (LaneOffs below), written once, re-read per stage
     __shared__ uint4 lane_tab[256][2];
 
+    int bid = blockIdx.x;
+    if constexpr (OUT == 1) {
+        // split K: workgroup bid / tiles takes columns [k0, k0 + ksplit) into slab sp
+        if (p.splits > 1) {
+            const int nt = p.tiles_m * p.tiles_n;
+            const int sp = bid / nt;
+            bid -= sp * nt;
+            const int64_t k0 = (int64_t)sp * p.ksplit;
+            p.A += k0;
+            p.B += k0;
+            p.A2 = p.A;
+            p.B2 = p.B;
+            p.K = min(p.ksplit, p.K - k0);
+            p.K1 = p.K;
+            p.Cf += (int64_t)sp * p.M * p.N;
+        }
+    }
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, bid, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
@@ -526,6 +545,21 @@ size_t mix_fold_w1p_bytes(int64_t d_up, int64_t d_out) {
     return ((size_t)d_out * d_up * 2 + 255) & ~(size_t)255;
 }
 
+// C[i] += sum of the split-K slabs at i, in slab order (float4 per thread)
+__global__ __launch_bounds__(256) void k_split_add(const float4 *__restrict__ part, int splits, int64_t n4,
+                                                   float4 *__restrict__ C) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 acc = part[i];
+    for (int sp = 1; sp < splits; ++sp) {
+        const float4 v = part[(int64_t)sp * n4 + i];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    float4 c = C[i];
+    c.x += acc.x; c.y += acc.y; c.z += acc.z; c.w += acc.w;
+    C[i] = c;
+}
+
 GemmP make_plain(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N, int64_t K) {
     GemmP p{};
     p.A = A; p.A2 = A; p.B = B; p.B2 = B; p.C = C;
@@ -561,6 +595,34 @@ hipError_t launch_gemm_bf16_f32out(const uint16_t *A, const uint16_t *B, float *
     const dim3 grid(p.tiles_m * p.tiles_n);
     if (accumulate) hipLaunchKernelGGL((k_gemm_bf16<false, false, 2>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((k_gemm_bf16<false, false, 1>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+int gemm_f32_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(256 / std::max<int64_t>(tiles, 1), K / 2048));
+}
+
+size_t gemm_f32_split_bytes(int64_t M, int64_t N, int64_t K) {
+    const int sp = gemm_f32_splits(M, N, K);
+    return sp > 1 ? (size_t)sp * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_bf16_f32acc_split(const uint16_t *A, const uint16_t *B, float *C, int64_t M,
+                                         int64_t N, int64_t K, float *part, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const int sp = gemm_f32_splits(M, N, K);
+    if (sp <= 1 || !part) return launch_gemm_bf16_f32out(A, B, C, M, N, K, true, s);
+    GemmP p = make_plain(A, B, nullptr, M, N, K);
+    p.Cf = part;
+    p.splits = sp;
+    p.ksplit = ((K + sp - 1) / sp + BK - 1) / BK * BK;
+    p.splits = (int)((K + p.ksplit - 1) / p.ksplit);
+    hipLaunchKernelGGL((k_gemm_bf16<false, false, 1>), dim3(p.tiles_m * p.tiles_n * p.splits), dim3(256), 0,
+                       s, p);
+    const int64_t n4 = M * N / 4;
+    hipLaunchKernelGGL(k_split_add, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       (const float4 *)part, p.splits, n4, (float4 *)C);
     return hipGetLastError();
 }
 

@@ -259,7 +259,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
 // Backward workspace: the forward's regions, then those of the backward pass.
 struct BwdLayout {
     WsLayout f;
-    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, kv, total;
+    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, kv, splitk, total;
     int kv_cap;
     int64_t n_pad;
 };
@@ -293,6 +293,10 @@ BwdLayout bwd_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     // distinct rows of a batch: at most n tokens' worth of max_d rows
     B.kv_cap = kv_item_capacity(n, (int64_t)n * std::max(max_d, 1));
     B.kv = take((size_t)B.kv_cap * 8);
+    // split-K slabs of the two parameter-gradient products (K = tokens), bf16 plans
+    B.splitk = take(d.dtype == L3_BF16 ? std::max(gemm_f32_split_bytes(d.d_out, Z, B.n_pad),
+                                                   gemm_f32_split_bytes(d.d_up, d.d_emb, B.n_pad))
+                                       : 0);
     B.total = off;
     return B;
 }
@@ -358,11 +362,20 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     L3_HIP_TRY(launch_transpose(dout, D.d_out, n, D.d_out, doutT, np, np, dt, s));
     L3_HIP_TRY(launch_transpose(y, D.d_up, n, D.d_up, zT, np, np, dt, s));
     L3_HIP_TRY(launch_transpose(x, D.d_in, n, D.d_in, zT + (size_t)D.d_up * np * es, np, np, dt, s));
-    L3_HIP_TRY(gemm_f32out(dt, doutT, zT, dWmix, D.d_out, Z, np, true, s));
+    float *splitk = ws_ptr<float>(ws, B.splitk);
+    if (dt == L3_BF16)
+        L3_HIP_TRY(launch_gemm_bf16_f32acc_split((const uint16_t *)doutT, (const uint16_t *)zT, dWmix,
+                                                 D.d_out, Z, np, splitk, s));
+    else
+        L3_HIP_TRY(gemm_f32out(dt, doutT, zT, dWmix, D.d_out, Z, np, true, s));
     // dW_up += dh o^T, do = W_up^T dh
     L3_HIP_TRY(launch_transpose(dh, D.d_up, n, D.d_up, dhT, np, np, dt, s));
     L3_HIP_TRY(launch_transpose(o, D.d_emb, n, D.d_emb, oT, np, np, dt, s));
-    L3_HIP_TRY(gemm_f32out(dt, dhT, oT, dWup, D.d_up, D.d_emb, np, true, s));
+    if (dt == L3_BF16)
+        L3_HIP_TRY(launch_gemm_bf16_f32acc_split((const uint16_t *)dhT, (const uint16_t *)oT, dWup, D.d_up,
+                                                 D.d_emb, np, splitk, s));
+    else
+        L3_HIP_TRY(gemm_f32out(dt, dhT, oT, dWup, D.d_up, D.d_emb, np, true, s));
     L3_HIP_TRY(launch_transpose(W_up, D.d_emb, D.d_up, D.d_emb, wupT, D.d_up, D.d_up, dt, s));
     L3_HIP_TRY(gemm_f32out(dt, dh, wupT, dov, n, D.d_emb, D.d_up, false, s));
     }

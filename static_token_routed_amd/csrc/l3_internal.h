@@ -192,6 +192,13 @@ hipError_t launch_gemm_mix_f32(const float *h, const float *x, float *stats, con
 
 // ---- backward pass
 // fp32 GEMMs with fp32 output, written or added to C (C = A B^T as above)
+// C[M x N] (fp32) += A B^T with K cut into gemm_f32_splits(M, N, K) ranges when the
+// output has too few tiles to fill the chip: one launch writes a slab per range into
+// `part` (gemm_f32_split_bytes), a second adds the slabs to C in range order.
+int gemm_f32_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_f32_split_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_bf16_f32acc_split(const uint16_t *A, const uint16_t *B, float *C, int64_t M,
+                                         int64_t N, int64_t K, float *part, hipStream_t s);
 hipError_t launch_gemm_bf16_f32out(const uint16_t *A, const uint16_t *B, float *C, int64_t M,
                                    int64_t N, int64_t K, bool accumulate, hipStream_t s);
 hipError_t launch_gemm_f32_acc(const float *A, const float *B, float *C, int64_t M, int64_t N,
