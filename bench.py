@@ -499,9 +499,6 @@ def decode_bench(args, cfg, torch, l3, synth):
     print(json.dumps(line), flush=True)
 
 
-VALU_F32_PEAK_TF = 157.3  # MI355X fp32 vector
-
-
 def backward_bench(args, cfg, torch, l3, synth):
     """Backward (training) pass: gradients of sum(dout * L3(x, ids)) for one batch, fp32
     gradients; dW_K / dW_V accumulate into full-size fp32 tables.  Timed like the
@@ -556,19 +553,27 @@ def backward_bench(args, cfg, torch, l3, synth):
     names = {0: "route", 1: "gather_mfma", 2: "gather_light", 6: "recompute_h", 7: "dense_bwd",
              8: "attn_bwd", 9: "kv_grad"}
     avg = {nm: st_ms[i] / max(1, launches[i]) for i, nm in names.items()}
-    # algorithmic work: per (token, row of its block) the attention backward needs the
-    # score, o, dp and dx (4 d_in + 4 d_emb FLOP), the key / value gradients 2 (d_in + d_emb)
+    # algorithmic bytes (both kernels are bound by memory traffic, not arithmetic):
+    # the attention backward reads each distinct K / V row once, each token's x row,
+    # dO (fp32) and o (bf16), and adds its term to dx (fp32, read + write); the key /
+    # value gradients add into the fp32 gradient rows of the batch's distinct rows
+    # (read + write) from each token's x row and dO row.
     tok_rows = float((off[ids + 1] - off[ids]).sum())
-    attn_fl = tok_rows * (4 * cfg.d_in + 4 * cfg.d_emb)
-    kv_fl = tok_rows * 2 * (cfg.d_in + cfg.d_emb)
+    uids = np.unique(ids)
+    rows = float((off[uids + 1] - off[uids]).sum())
+    attn_b = rows * (cfg.d_in + cfg.d_emb) * 2 + n * (cfg.d_in * 2 + cfg.d_emb * 6 + cfg.d_in * 8)
+    kv_b = rows * (cfg.d_in + cfg.d_emb) * 8 + n * (cfg.d_in * 2 + cfg.d_emb * 4)
     Z = cfg.d_up + cfg.d_in
     dense_fl = 2.0 * n * (2 * cfg.d_out * Z + 2 * cfg.d_up * cfg.d_emb)
     kernels = {
-        "attn_bwd": {"bound": "alu", "achieved": attn_fl / (avg["attn_bwd"] * 1e-3) / 1e12,
-                     "peak": VALU_F32_PEAK_TF, "unit": "TFLOP/s",
-                     "work_per_launch": f"{attn_fl:.4g} FLOP ({tok_rows:.4g} token-rows)"},
-        "kv_grad": {"bound": "alu", "achieved": kv_fl / (avg["kv_grad"] * 1e-3) / 1e12,
-                    "peak": VALU_F32_PEAK_TF, "unit": "TFLOP/s", "work_per_launch": f"{kv_fl:.4g} FLOP"},
+        "attn_bwd": {"bound": "hbm", "achieved": attn_b / (avg["attn_bwd"] * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "work_per_launch": f"{attn_b:.4g} B ({rows:.0f} distinct K/V rows once, x, dO, o, "
+                                        f"dx read + write; {tok_rows:.4g} token-rows)"},
+        "kv_grad": {"bound": "hbm", "achieved": kv_b / (avg["kv_grad"] * 1e-3) / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "work_per_launch": f"{kv_b:.4g} B (fp32 gradient rows of {rows:.0f} distinct rows "
+                                       f"read + written, x and dO once)"},
         "dense_bwd": {"bound": "mfma", "achieved": dense_fl / (avg["dense_bwd"] * 1e-3) / 1e12,
                       "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
                       "work_per_launch": f"{dense_fl:.4g} FLOP (dz, dW_mix, dW_up, do GEMMs; "

@@ -636,114 +636,184 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
 }
 
 // Key / value gradients on the matrix cores (bf16, the same dims as the matrix-core
-// attention backward).  One workgroup per (block, 16-row) item, as k_kv_grad, over
-// the block's tokens in tiles of 16:
+// attention backward):
 //   dW_K[rows] += dS^T x,  dW_V[rows] += P^T dO
-// as dW^T (columns x rows) += x^T (columns x tokens) dS (tokens x rows) with
-// v_mfma_f32_16x16x16_bf16: the tile's x rows (and its dO rows, rounded to bf16)
-// are staged in LDS and read transposed (ds_read_b64_tr_b16, as above), dS and P
-// (fp32, stored by the attention backward) are rounded to bf16 into the second
-// operand, and a lane ends with 4 consecutive columns of one row, added to the
-// fp32 gradient as one 16-byte read-modify-write.  Wavefront w owns 1/NW of the
-// columns of W_K and of W_V.
-template <int XQ, int DE, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_kv_grad_mfma(BwdArgs a) {
+// taken as dW^T (columns x rows) += x^T (columns x tokens) dS (tokens x rows) with
+// v_mfma_f32_16x16x16_bf16.  Work items are (block, 64 rows, column slice): a slice
+// is 256 columns of W_K or of W_V (all of d_emb when it is 128), so a staged token
+// tile feeds 64 table rows (a block's x rows are read once per 64 rows and slice,
+// not per 16 rows) and the item's accumulators (64 rows x 256 columns over 4
+// wavefronts) stay in registers; four workgroups share a CU, so one's start-up and
+// read-modify-write overlap the others' streaming.  The block's tokens go by in
+// tiles of 16 through a ring of three LDS slots, two tiles in flight while one is
+// multiplied: per tile and wavefront, two 1 KB asynchronous copies of two token rows
+// each (x, or dO rounded to bf16 beforehand) and four 256-byte copies of tokens' dS
+// (or P) values for the item's rows, whose token indices come through the scalar
+// cache so that no vector load drains the copies in flight.  Token rows are read
+// transposed (ds_read_b64_tr_b16: lane (g, j) passing the address of row 4g + j / 4,
+// columns c0 + 4 (j % 4) .. +3 receives rows 4g .. 4g + 3 of column c0 + j) as the
+// first operand; the dS / P values, rounded to bf16, are the second.  A lane ends
+// with 4 consecutive columns of one row per 16 x 16 block, added to the fp32
+// gradient by one 16-byte read-modify-write per block.  Every row's gradient is one
+// workgroup's ordered sum over the block's tokens (no atomics).
+constexpr int kKvGroup = 64;     // table rows per item
+constexpr int kKvSlice = 256;    // columns per item
+constexpr int kKvRing = 3;       // LDS slots (token tiles)
+
+__host__ __device__ constexpr int kv_slices(int64_t d_in, int64_t d_emb) {
+    return (int)(d_in / kKvSlice + (d_emb > kKvSlice ? d_emb / kKvSlice : 1));
+}
+
+__global__ __launch_bounds__(256) void k_kv_items_sliced(const int64_t *__restrict__ off,
+                                                         const int32_t *__restrict__ uniq,
+                                                         int32_t *__restrict__ hdr, int64_t vocab,
+                                                         int2 *__restrict__ items, int cap, int nslice) {
+    const int m = hdr[HDR_NSEG];
+    for (int b = blockIdx.x * 256 + threadIdx.x; b < m; b += gridDim.x * 256) {
+        const int t = uniq[b];
+        if (t < 0 || t >= vocab) continue;
+        const int d = (int)(off[t + 1] - off[t]);
+        const int nt = (d + kKvGroup - 1) / kKvGroup * nslice;
+        const int at = atomicAdd(&hdr[HDR_NKV], nt);
+        // (block, first row * 16 + slice)
+        for (int r = 0; r < nt && at + r < cap; ++r)
+            items[at + r] = make_int2(b, (r / nslice) * kKvGroup * 16 + r % nslice);
+    }
+}
+
+// dO rounded to bf16, 8 values per thread (the key / value gradients' token rows)
+__global__ __launch_bounds__(256) void k_round_bf16(const float4 *__restrict__ src, int64_t n8,
+                                                    uint4 *__restrict__ dst) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+        const float4 u0 = src[2 * i], u1 = src[2 * i + 1];
+        dst[i] = make_uint4(pack2(u0.x, u0.y), pack2(u0.z, u0.w), pack2(u1.x, u1.y), pack2(u1.z, u1.w));
+    }
+}
+
+template <int XQ, int DE>
+__global__ __launch_bounds__(256, 4) void k_kv_grad_mfma(BwdArgs a) {
     constexpr int d_in = 64 * XQ;
-    constexpr int XROW = d_in * 2 + 48, VROW = DE * 2 + 48;  // padded LDS rows
-    constexpr int XT = 16 * XROW;
-    constexpr int CPR = d_in / 512;    // 1 KB copies per x row
-    constexpr int CPW = 16 * CPR / NW; // x copies per wavefront
-    constexpr int QI = d_in / NW, QE = DE / NW;
-    constexpr int NKB = QI / 16, NVB = QE / 16;
-    static_assert(CPW * NW == 16 * CPR && NVB >= 1 && XT + 16 * VROW <= 163840, "kv stages");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[XT + 16 * VROW];
+    constexpr int KS = d_in / kKvSlice;            // W_K slices; then the W_V slices
+    constexpr int VW = DE < kKvSlice ? DE : kKvSlice;  // W_V slice width
+    constexpr int PAIR = 4 * kKvSlice + 48;        // LDS: two token rows (bf16) + pad
+    constexpr int TSTR = 4 * kKvGroup + 16;        // LDS: one token's dS / P values (fp32) + pad
+    constexpr int SLOT = 8 * PAIR + 16 * TSTR;
+    static_assert(KS >= 1 && DE % 128 == 0 && 4 * kKvRing * SLOT <= 163840, "kv slices");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kKvRing * SLOT];
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // 4 wavefronts
     const int l16 = lane & 15, kg = lane >> 4;
     const uint16_t *X = static_cast<const uint16_t *>(a.x);
     const uint32_t lds0 = lds_addr(lds);
     const int nitems = min(a.hdr[HDR_NKV], a.kv_cap);
+    // this lane's transposed-read row (4 kg + l16 / 4) within a slot
+    const int rr = 4 * kg + (l16 >> 2);
+    const uint32_t xrow = (uint32_t)((rr >> 1) * PAIR + (rr & 1) * 2 * kKvSlice);
+
+    auto run = [&](auto vslice, int b, int j0, int sl) {
+        constexpr bool V = decltype(vslice)::value;
+        constexpr int WCOL = V ? VW / 4 : kKvSlice / 4;  // columns per wavefront
+        constexpr int NCB = WCOL / 16;
+        const int t = __builtin_amdgcn_readfirstlane(a.uniq[b]);
+        const int64_t r0 = a.off[t];
+        const int d = (int)(a.off[t + 1] - r0);
+        const int nr = __builtin_amdgcn_readfirstlane(min(kKvGroup, d - j0));
+        const int nrb = (nr + 15) >> 4;
+        const int s0 = __builtin_amdgcn_readfirstlane(a.seg_start[b]);
+        const int s1 = __builtin_amdgcn_readfirstlane(a.seg_start[b + 1]);
+        const int ntile = (s1 - s0 + 15) >> 4;
+        const int c0 = (V ? sl - KS : sl) * kKvSlice;  // the slice's first column
+        const uint16_t *rows = V ? a.dob : X;
+        const int64_t ld = V ? DE : d_in;
+        const float *bsrc = V ? a.P : a.dS;
+        const int bcol = min(j0 + lane, a.max_d - 1);
+        // lane's 16-byte piece of a token row: lanes 0-31 the first row of a pair,
+        // 32-63 the second (pieces past the slice repeat its last one)
+        const int rc = c0 + min(lane & 31, (V ? VW : kKvSlice) / 8 - 1) * 8;
+        // tile k -> slot k % kKvRing: token rows 4w .. 4w + 3 (rows past the block's
+        // end repeat its last token; their dS / P are zeroed when read)
+        auto issue = [&](int k) {
+            const int tb = s0 + 16 * k, last = s1 - 1;
+            const uint32_t base = lds0 + (uint32_t)((k % kKvRing) * SLOT);
+            int p[4], tok[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = min(tb + 4 * w + i, last);
+            scalar_ld2(a.perm + p[0], a.perm + p[1], tok[0], tok[1]);
+            scalar_ld2(a.perm + p[2], a.perm + p[3], tok[2], tok[3]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tk = lane < 32 ? tok[2 * h] : tok[2 * h + 1];
+                async_ld16(rows + (int64_t)tk * ld + rc, base + (uint32_t)((2 * w + h) * PAIR));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                async_ld4(bsrc + (int64_t)p[i] * a.max_d + bcol, base + 8 * PAIR + (uint32_t)((4 * w + i) * TSTR));
+        };
+        f32x4_t acc[4][NCB];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lds_barrier();  // the previous item's last tile is read by every wavefront
+#pragma unroll
+        for (int k = 0; k < kKvRing - 1; ++k)
+            if (k < ntile) issue(k);
+        for (int k = 0; k < ntile; ++k) {
+            // this wavefront's 6 copies of tile k have landed (those of k + 1 may not)
+            if (k + 1 < ntile) wait_vmcnt<6 * (kKvRing - 2)>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            // the slot of tile k + 2 was last read in tile k - 1, which every wavefront finished
+            if (k + kKvRing - 1 < ntile) issue(k + kKvRing - 1);
+            const int nt = min(16, s1 - s0 - 16 * k);
+            const unsigned char *slot = lds + (k % kKvRing) * SLOT;
+            i16x4_t B[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                if (rb < nrb) {
+                    const int row = 16 * rb + l16;
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 4 * kg + i;
+                        const float f = *reinterpret_cast<const float *>(slot + 8 * PAIR + tk * TSTR + 4 * row);
+                        v[i] = (tk < nt && row < nr) ? f : 0.f;
+                    }
+                    B[rb] = __builtin_bit_cast(i16x4_t, make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3])));
+                }
+            }
+            const unsigned char *xr = slot + xrow + (w * WCOL + 4 * (l16 & 3)) * 2;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(xr + 32 * cb));
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    if (rb < nrb) acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B[rb], acc[rb][cb], 0, 0, 0);
+            }
+        }
+        // lane: columns c0 + w WCOL + 16 cb + 4 kg .. + 3 of row j0 + 16 rb + l16
+        float *g = (V ? a.dWV : a.dWK) + (r0 + j0) * ld + c0 + w * WCOL + 4 * kg;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            if (rb < nrb && 16 * rb + l16 < nr) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float4 *dst = reinterpret_cast<float4 *>(g + (int64_t)(16 * rb + l16) * ld + 16 * cb);
+                    float4 v = *dst;
+                    v.x += acc[rb][cb][0]; v.y += acc[rb][cb][1]; v.z += acc[rb][cb][2]; v.w += acc[rb][cb][3];
+                    *dst = v;
+                }
+            }
+        }
+    };
     for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
         const int2 item = a.kv_items[it];
         const int b = __builtin_amdgcn_readfirstlane(item.x);
-        const int j0 = __builtin_amdgcn_readfirstlane(item.y);
-        const int t = __builtin_amdgcn_readfirstlane(a.uniq[b]);
-        const int64_t r0 = a.off[t];
-        const int d = (int)(a.off[t + 1] - r0), nr = min(16, d - j0);
-        const int s0 = __builtin_amdgcn_readfirstlane(a.seg_start[b]);
-        const int s1 = __builtin_amdgcn_readfirstlane(a.seg_start[b + 1]);
-        f32x4_t ak[NKB], av[NVB];
-#pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) ak[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cb = 0; cb < NVB; ++cb) av[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int tb = s0; tb < s1; tb += 16) {
-            const int nt = min(16, s1 - tb);
-            lds_barrier();  // every wavefront is done with the previous tile
-            // x rows of the tile's tokens (past nt: its last token, whose dS and P are
-            // zeroed below), 1 KB asynchronous copies
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                const int q = w * CPW + i, row = q / CPR, piece = q % CPR;
-                const int tok = __builtin_amdgcn_readfirstlane(a.perm[tb + min(row, nt - 1)]);
-                async_ld16(X + (int64_t)tok * d_in + piece * 512 + lane * 8, lds0 + row * XROW + piece * 1024);
-            }
-            // dO rows, rounded to bf16, 8 values per thread and step
-            for (int ch = threadIdx.x; ch < 16 * DE / 8; ch += 64 * NW) {
-                const int row = ch / (DE / 8), c8 = ch % (DE / 8);
-                const int tok = a.perm[tb + min(row, nt - 1)];
-                const float4 *src = reinterpret_cast<const float4 *>(a.dov + (int64_t)tok * DE + 8 * c8);
-                const float4 u0 = src[0], u1 = src[1];
-                *reinterpret_cast<uint4 *>(lds + XT + row * VROW + 16 * c8) =
-                    make_uint4(pack2(u0.x, u0.y), pack2(u0.z, u0.w), pack2(u1.x, u1.y), pack2(u1.z, u1.w));
-            }
-            // dS and P of tokens tb + 4kg .. +3 at row j0 + l16
-            float dsv[4], pv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = 4 * kg + i < nt && l16 < nr;
-                const int64_t at = (int64_t)(tb + 4 * kg + i) * a.max_d + j0 + l16;
-                dsv[i] = ok ? a.dS[at] : 0.f;
-                pv[i] = ok ? a.P[at] : 0.f;
-            }
-            const i16x4_t Bds = __builtin_bit_cast(i16x4_t, make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3])));
-            const i16x4_t Bp = __builtin_bit_cast(i16x4_t, make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3])));
-            wait_vmcnt<0>();
-            lds_barrier();
-            const unsigned char *xr = lds + (4 * kg + (l16 >> 2)) * XROW + (w * QI + 4 * (l16 & 3)) * 2;
-#pragma unroll
-            for (int cb = 0; cb < NKB; ++cb) {
-                const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(xr + 32 * cb));
-                ak[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, Bds, ak[cb], 0, 0, 0);
-            }
-            const unsigned char *vr = lds + XT + (4 * kg + (l16 >> 2)) * VROW + (w * QE + 4 * (l16 & 3)) * 2;
-#pragma unroll
-            for (int cb = 0; cb < NVB; ++cb) {
-                const i16x4_t A = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(vr + 32 * cb));
-                av[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, Bp, av[cb], 0, 0, 0);
-            }
-        }
-        // lane: columns 16 cb + 4 kg .. + 3 of row j0 + l16
-        if (l16 < nr) {
-            float *dk = a.dWK + (r0 + j0 + l16) * d_in + w * QI + 4 * kg;
-#pragma unroll
-            for (int cb = 0; cb < NKB; ++cb) {
-                float4 *dst = reinterpret_cast<float4 *>(dk + 16 * cb);
-                float4 v = *dst;
-                v.x += ak[cb][0]; v.y += ak[cb][1]; v.z += ak[cb][2]; v.w += ak[cb][3];
-                *dst = v;
-            }
-            float *dv = a.dWV + (r0 + j0 + l16) * DE + w * QE + 4 * kg;
-#pragma unroll
-            for (int cb = 0; cb < NVB; ++cb) {
-                float4 *dst = reinterpret_cast<float4 *>(dv + 16 * cb);
-                float4 v = *dst;
-                v.x += av[cb][0]; v.y += av[cb][1]; v.z += av[cb][2]; v.w += av[cb][3];
-                *dst = v;
-            }
-        }
+        const int j0 = __builtin_amdgcn_readfirstlane(item.y >> 4);
+        const int sl = __builtin_amdgcn_readfirstlane(item.y & 15);
+        if (sl < KS) run(std::false_type{}, b, j0, sl);
+        else run(std::true_type{}, b, j0, sl);
     }
 }
 
@@ -753,9 +823,12 @@ void launch_bwd_mfma_de(const BwdArgs &a, int part, hipStream_t s) {
     if (part == 0) {
         hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, DE, NW>), dim3(256), b, 0, s, a);
     } else {
-        hipLaunchKernelGGL(k_kv_items, dim3(64), dim3(256), 0, s, a.off, a.uniq, const_cast<int32_t *>(a.hdr),
-                           a.vocab, a.kv_items, a.kv_cap);
-        hipLaunchKernelGGL((k_kv_grad_mfma<XQ, DE, NW>), dim3(1024), b, 0, s, a);
+        const int64_t n8 = a.n * DE / 8;
+        hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)std::min<int64_t>(4096, (n8 + 255) / 256)), dim3(256), 0,
+                           s, reinterpret_cast<const float4 *>(a.dov), n8, reinterpret_cast<uint4 *>(a.dob));
+        hipLaunchKernelGGL(k_kv_items_sliced, dim3(64), dim3(256), 0, s, a.off, a.uniq,
+                           const_cast<int32_t *>(a.hdr), a.vocab, a.kv_items, a.kv_cap, kv_slices(64 * XQ, DE));
+        hipLaunchKernelGGL((k_kv_grad_mfma<XQ, DE>), dim3(1024), dim3(256), 0, s, a);
     }
 }
 
@@ -818,8 +891,10 @@ hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, 
     return hipGetLastError();
 }
 
-int kv_item_capacity(int64_t n, int64_t rows) {
-    return (int)std::min<int64_t>(INT32_MAX, n + rows / kKvRows + 1);
+int kv_item_capacity(int64_t n, int64_t rows, int64_t d_in, int64_t d_emb, int dtype) {
+    int64_t c = n + rows / kKvRows + 1;
+    if (bwd_mfma_dims(d_in, d_emb, dtype)) c = std::max<int64_t>(c, (n + rows / kKvGroup + 1) * kv_slices(d_in, d_emb));
+    return (int)std::min<int64_t>(INT32_MAX, c);
 }
 
 int ln_param_chunks(int64_t n) { return (int)std::max<int64_t>(1, (n + kLnRows - 1) / kLnRows); }

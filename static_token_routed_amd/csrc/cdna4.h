@@ -48,6 +48,31 @@ __device__ inline void async_ld16(const void *gptr, uint32_t lds_base) {
                      : "memory");
 }
 
+// Asynchronous 4-byte copy global -> LDS (global_load_lds_dword): lane l's 4 bytes
+// land at lds_base + 4 * l; otherwise as async_ld16.
+__device__ inline void async_ld4(const void *gptr, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                     :
+                     : "s"(m0v), "v"(gptr)
+                     : "memory");
+}
+
+// Two wave-uniform 32-bit loads through the scalar cache, waited for in the same
+// statement: unlike a vector load they leave vmcnt alone, so a loop that keeps
+// asynchronous copies in flight can look up addresses without draining them.
+__device__ inline void scalar_ld2(const int32_t *p0, const int32_t *p1, int &v0, int &v1) {
+    const uint64_t b0 = (uint64_t)(uintptr_t)p0, b1 = (uint64_t)(uintptr_t)p1;
+    const uint64_t s0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b0 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b0);
+    const uint64_t s1 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b1 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b1);
+    __asm__ volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&s"(v0), "=&s"(v1)
+                     : "s"(s0), "s"(s1)
+                     : "memory");
+}
+
 // The same copy addressed as a wave-uniform 64-bit base plus a 32-bit per-lane
 // byte offset (the scalar-base form of the instruction).
 __device__ inline void async_ld16_sb(const void *sbase, uint32_t voff, uint32_t lds_base) {

@@ -259,7 +259,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
 // Backward workspace: the forward's regions, then those of the backward pass.
 struct BwdLayout {
     WsLayout f;
-    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, P, dS, part, kv, splitk, total;
+    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, dob, P, dS, part, kv, splitk, total;
     int kv_cap;
     int64_t n_pad;
 };
@@ -287,11 +287,12 @@ BwdLayout bwd_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     B.oT = take((size_t)d.d_emb * B.n_pad * es);
     B.wupT = take((size_t)d.d_emb * d.d_up * es);
     B.dov = take((size_t)n * d.d_emb * 4);
+    B.dob = take(d.dtype == L3_BF16 ? (size_t)n * d.d_emb * 2 : 0);
     B.P = take((size_t)n * std::max(max_d, 1) * 4);
     B.dS = take((size_t)n * std::max(max_d, 1) * 4);
     B.part = take((size_t)ln_param_chunks(n) * d.d_up * 8);
     // distinct rows of a batch: at most n tokens' worth of max_d rows
-    B.kv_cap = kv_item_capacity(n, (int64_t)n * std::max(max_d, 1));
+    B.kv_cap = kv_item_capacity(n, (int64_t)n * std::max(max_d, 1), d.d_in, d.d_emb, d.dtype);
     B.kv = take((size_t)B.kv_cap * 8);
     // split-K slabs of the two parameter-gradient products (K = tokens), bf16 plans
     B.splitk = take(d.dtype == L3_BF16 ? std::max(gemm_f32_split_bytes(d.d_out, Z, B.n_pad),
@@ -393,6 +394,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     a.dx = dx; a.P = ws_ptr<float>(ws, B.P); a.dS = ws_ptr<float>(ws, B.dS);
     a.dWK = dWK; a.dWV = dWV;
     a.kv_items = ws_ptr<int2>(ws, B.kv); a.kv_cap = B.kv_cap;
+    a.n = n; a.dob = dt == L3_BF16 ? ws_ptr<uint16_t>(ws, B.dob) : nullptr;
     {
         StageTimer tm(8, s);
         L3_HIP_TRY(launch_attn_bwd(a, dt, 0, s));

@@ -228,11 +228,14 @@ struct BwdArgs {
     float *dx;           // [n x d_in], holds W2^T dout; the attention term is added
     float *P, *dS;       // [n x max_d] per sorted position
     float *dWK, *dWV;    // accumulated
-    int2 *kv_items;      // (block, first row) items of the key / value gradients
+    int2 *kv_items;      // items of the key / value gradients
     int kv_cap;          // their capacity (kv_item_capacity)
+    int64_t n;           // tokens
+    uint16_t *dob;       // [n x d_emb] dO rounded to bf16 (matrix-core key / value gradients)
 };
-// items of the key / value gradients: at most one per block plus one per 16 rows
-int kv_item_capacity(int64_t n, int64_t rows);
+// items of the key / value gradients: at most one per block plus one per 16 rows, or
+// for the matrix-core kernel (one per block plus one per 64 rows) per column slice
+int kv_item_capacity(int64_t n, int64_t rows, int64_t d_in, int64_t d_emb, int dtype);
 // tokens per attention-backward work item (all of one block) for these dims
 int attn_bwd_tokens(int64_t d_in, int64_t d_emb, int dtype);
 // part 0: attention backward per work item; part 1: the key / value gradients per

@@ -35,6 +35,10 @@ CASES = {
     # longer than 16 tokens and 16 rows, and a ragged last row chunk (k = 70)
     "bf16_d1024_e128": synth.small("bb4", vocab=150, k=70, d_in=1024, d_emb=128, d_up=256,
                                    d_out=128, n=900, v=4000, dtype="bf16", seed=11, ids_s=1.05),
+    # bf16, 4200 tokens: the parameter-gradient GEMMs (K = tokens, few output tiles)
+    # split K into fp32 slabs added in order
+    "bf16_n4200_splitk": synth.small("bb5", vocab=500, k=16, d_in=1024, d_emb=128, d_up=256,
+                                     d_out=128, n=4200, v=3000, dtype="bf16", seed=12, ids_s=1.05),
 }
 KEYS = ["dx", "dW_K", "dW_V", "dW_up", "dgamma", "dbeta", "dW_mix"]
 
@@ -82,8 +86,9 @@ def test_backward_matches_oracle(name):
         assert err <= tol, f"{name} {k}: {err:.3e} > {tol}"
 
 
-def test_backward_deterministic_and_accumulates():
-    case = make_case(CASES["bf16_n200"])
+@pytest.mark.parametrize("name", ["bf16_n200", "bf16_n4200_splitk"])
+def test_backward_deterministic_and_accumulates(name):
+    case = make_case(CASES[name])
     a, _ = _run(case)
     b, _ = _run(case)
     for k in KEYS:
