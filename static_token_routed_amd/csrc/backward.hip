@@ -446,12 +446,17 @@ hipError_t launch_token_ch(const BwdArgs &a, int part, hipStream_t s) {
 // Attention backward on the matrix cores, for bf16 plans with d_in in {512, 1024,
 // 2048} and d_emb in {128, 256, 512}.  One workgroup per item of up to 16 tokens of
 // one block (sorted positions s0 .. s0 + cnt - 1; token j of the item is MFMA
-// column j), so each K row is read twice per 16 tokens instead of twice per token:
+// column j), so each K and V row is read once per 16 tokens:
 //  * the block's rows stream through LDS in 16-row stages (double-buffered
-//    asynchronous copies); pass 1 forms the scores and the softmax max and sum per
-//    token, pass 2 the scores again, P, dP = V dO^T, dS = P (dP - <dO, o>) (o is the
-//    forward output the recompute left in the workspace), stores P and dS for the
-//    key / value gradients, and adds dx^T += K_t^T dS per 16-column block;
+//    asynchronous copies; the lane's slice of the stage's V row is loaded into
+//    registers one stage ahead);
+//  * one pass with an online softmax: D = <dO, o> is known beforehand (o is the
+//    forward output the recompute left in the workspace), so with the running max m
+//    and sum l, dx^T accumulates K_t^T (e^(s - m) (dP - D)), rescaled by e^(m_old -
+//    m) when m grows and divided by l at the end, which is dx^T += K_t^T dS with
+//    dS = P (dP - D), dP = V dO^T; the raw scores and dP go to the P and dS arrays,
+//    and the token's (lse, D, d_t) to tstat, from which k_bwd_normalize forms P and
+//    dS for the key / value gradients;
 //  * wavefront w of NW (4, or 8 at d_in 2048 to keep x and the dx sums in
 //    registers) owns 1/NW of d_in (scores' partial sums, dx columns) and of d_emb
 //    (dP's partial sums); the wavefronts' partial scores and dP are added through
@@ -500,7 +505,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
         const int cnt = __builtin_amdgcn_readfirstlane(item.y);
         const int64_t r0 = __builtin_amdgcn_readfirstlane(item.z);
         const int d = __builtin_amdgcn_readfirstlane(item.w);
-        if (d < 0) continue;  // ID out of range: no gradient (flagged by the route)
+        if (d < 0) {  // ID out of range: no gradient (flagged by the route)
+            if (w == 0 && lane < cnt) a.tstat[s0 + lane] = make_float4(0.f, 0.f, __int_as_float(0), 0.f);
+            continue;
+        }
         const int nc = (d + 15) / 16;
         const int tok = a.perm[s0 + min(l16, cnt - 1)];
         // this lane's token: x and dO over the wavefront's quarters, and <dO, o>
@@ -533,12 +541,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
         f32x4_t acc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        float m = -INFINITY, l = 0.f, inv_l = 0.f;
+        float m = -INFINITY, l = 0.f;
 
-        // stage st (pass st / nc, chunk st % nc): K rows [16c, +16) (past d_t: row d_t - 1)
-        auto issue = [&](int st) {
-            const int c = st < nc ? st : st - nc;
-            const uint32_t base = lds0 + (uint32_t)((st & 1) * KST);
+        // stage c: K rows [16c, +16) (past d_t: row d_t - 1) by asynchronous copies, and
+        // this lane's slice of V row 16c + l16 into registers (issued after the copies,
+        // consumed in the next stage, so no vector load waits on copies in flight)
+        auto issue = [&](int c) {
+            const uint32_t base = lds0 + (uint32_t)((c & 1) * KST);
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
                 const int q = w * CPW + i, row = q / CPR, piece = q % CPR;
@@ -546,92 +555,121 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_bwd_mfma(BwdArgs a) {
                 async_ld16(WK + grow * d_in + piece * 512 + lane * 8, base + row * KROW + piece * 1024);
             }
         };
+        auto load_v = [&](int c, bf16x8_t (&v)[NEK]) {
+            const uint16_t *vr = WV + (r0 + min(16 * c + l16, d - 1)) * DE + w * QE + 8 * kg;
+#pragma unroll
+            for (int ks = 0; ks < NEK; ++ks) v[ks] = *reinterpret_cast<const bf16x8_t *>(vr + 32 * ks);
+        };
+        bf16x8_t vcur[NEK], vnext[NEK];
         issue(0);
-        for (int st = 0; st < 2 * nc; ++st) {
-            const bool p2 = st >= nc;
-            const int c = p2 ? st - nc : st;
+        load_v(0, vcur);
+        for (int c = 0; c < nc; ++c) {
             wait_vmcnt<0>();
             lds_barrier();
-            if (st + 1 < 2 * nc) issue(st + 1);
-            const unsigned char *kt = lds + (st & 1) * KST;
+            if (c + 1 < nc) {
+                issue(c + 1);
+                load_v(c + 1, vnext);
+            }
+            const unsigned char *kt = lds + (c & 1) * KST;
             f32x4_t sp = {0.f, 0.f, 0.f, 0.f}, dpp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NXK; ++ks) {
                 const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(kt + l16 * KROW + (w * QI + 32 * ks + 8 * kg) * 2);
                 sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xf[ks], sp, 0, 0, 0);
             }
-            if (p2) {
-                const uint16_t *vr = WV + (r0 + min(16 * c + l16, d - 1)) * DE + w * QE + 8 * kg;
 #pragma unroll
-                for (int ks = 0; ks < NEK; ++ks) {
-                    const bf16x8_t Av = *reinterpret_cast<const bf16x8_t *>(vr + 32 * ks);
-                    dpp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, df[ks], dpp, 0, 0, 0);
-                }
-            }
+            for (int ks = 0; ks < NEK; ++ks)
+                dpp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur[ks], df[ks], dpp, 0, 0, 0);
             spart[w * 64 + lane] = sp;
-            if (p2) dpart[w * 64 + lane] = dpp;
+            dpart[w * 64 + lane] = dpp;
             lds_barrier();
-            f32x4_t S = spart[lane];
+            f32x4_t S = spart[lane], dP = dpart[lane];
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) S += spart[64 * ww + lane];
-            const int rb = 16 * c + 4 * kg;  // this lane's rows rb .. rb + 3 (of token l16)
-            if (!p2) {
-                float cm = -INFINITY;
+            for (int ww = 1; ww < NW; ++ww) {
+                S += spart[64 * ww + lane];
+                dP += dpart[64 * ww + lane];
+            }
+            // online softmax over this lane's rows rb .. rb + 3 of token l16: the running
+            // max m and sum l, and dx^T accumulated from e^(s - m) (dP - D), rescaled
+            // whenever m grows
+            const int rb = 16 * c + 4 * kg;
+            float cm = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (rb + v < d) cm = fmaxf(cm, S[v]);
+            cm = fmaxf(cm, __shfl_xor(cm, 16));
+            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            const float mn = fmaxf(m, cm);
+            const float sc = __expf(m - mn);
+            float e[4], ls = 0.f, dsv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                e[v] = rb + v < d ? __expf(S[v] - mn) : 0.f;
+                ls += e[v];
+                dsv[v] = e[v] * (dP[v] - D);
+            }
+            ls += __shfl_xor(ls, 16);
+            ls += __shfl_xor(ls, 32);
+            l = fmaf(l, sc, ls);
+            m = mn;
+            // raw scores and dP per sorted position; normalised into P and dS afterwards
+            if (w == 0 && l16 < cnt) {
+                float *Sp = a.P + (int64_t)(s0 + l16) * a.max_d, *dPp = a.dS + (int64_t)(s0 + l16) * a.max_d;
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (rb + v < d) cm = fmaxf(cm, S[v]);
-                cm = fmaxf(cm, __shfl_xor(cm, 16));
-                cm = fmaxf(cm, __shfl_xor(cm, 32));
-                const float mn = fmaxf(m, cm);
-                float ls = 0.f;
+                    if (rb + v < d) {
+                        Sp[rb + v] = S[v];
+                        dPp[rb + v] = dP[v];
+                    }
+            }
+            const i16x4_t B = __builtin_bit_cast(i16x4_t, make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3])));
+            const unsigned char *trb = kt + (4 * kg + (l16 >> 2)) * KROW + (w * QI + 4 * (l16 & 3)) * 2;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) ls += rb + v < d ? __expf(S[v] - mn) : 0.f;
-                ls += __shfl_xor(ls, 16);
-                ls += __shfl_xor(ls, 32);
-                l = fmaf(l, __expf(m - mn), ls);
-                m = mn;
-                if (st == nc - 1) inv_l = 1.f / l;
-            } else {
-                f32x4_t dP = dpart[lane];
+            for (int cb = 0; cb < NCB; ++cb) {
+                const i16x4_t Ak = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(trb + 32 * cb));
+                acc[cb] *= sc;
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ak, B, acc[cb], 0, 0, 0);
+            }
+            if (c + 1 < nc) {
 #pragma unroll
-                for (int ww = 1; ww < NW; ++ww) dP += dpart[64 * ww + lane];
-                float pv[4], ds[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    pv[v] = rb + v < d ? __expf(S[v] - m) * inv_l : 0.f;
-                    ds[v] = pv[v] * (dP[v] - D);
-                }
-                if (w == 0 && l16 < cnt) {
-                    float *Pp = a.P + (int64_t)(s0 + l16) * a.max_d, *dSp = a.dS + (int64_t)(s0 + l16) * a.max_d;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (rb + v < d) {
-                            Pp[rb + v] = pv[v];
-                            dSp[rb + v] = ds[v];
-                        }
-                }
-                const i16x4_t B = __builtin_bit_cast(i16x4_t, make_uint2(pack2(ds[0], ds[1]), pack2(ds[2], ds[3])));
-                const unsigned char *trb = kt + (4 * kg + (l16 >> 2)) * KROW + (w * QI + 4 * (l16 & 3)) * 2;
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const i16x4_t Ak = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4_t *)(trb + 32 * cb));
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ak, B, acc[cb], 0, 0, 0);
-                }
+                for (int ks = 0; ks < NEK; ++ks) vcur[ks] = vnext[ks];
             }
         }
-        // dx[token][columns] += dx^T: lane holds columns 16 cb + 4 kg .. + 3 of token l16
+        // dx[token][columns] += dx^T / l: lane holds columns 16 cb + 4 kg .. + 3 of token l16
+        const float inv_l = 1.f / l;
         if (l16 < cnt) {
             float *dxr = a.dx + (int64_t)tok * d_in + w * QI + 4 * kg;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 float4 *dst = reinterpret_cast<float4 *>(dxr + 16 * cb);
                 float4 v = *dst;
-                v.x += acc[cb][0]; v.y += acc[cb][1]; v.z += acc[cb][2]; v.w += acc[cb][3];
+                v.x += acc[cb][0] * inv_l; v.y += acc[cb][1] * inv_l;
+                v.z += acc[cb][2] * inv_l; v.w += acc[cb][3] * inv_l;
                 *dst = v;
             }
+            if (w == 0 && kg == 0)
+                a.tstat[s0 + l16] = make_float4(m + __logf(l), D, __int_as_float(d), 0.f);
         }
         lds_barrier();  // the next item's first copies reuse the stages and the exchange area
+    }
+}
+
+// P = e^(s - lse) and dS = P (dP - D) in place of the raw scores and dP the
+// matrix-core attention backward stored, for rows j < d_t of every sorted position
+// (d_t = 0 for tokens whose ID is out of range).
+__global__ __launch_bounds__(256) void k_bwd_normalize(const float4 *__restrict__ tstat, int64_t n, int max_d,
+                                                       float *__restrict__ P, float *__restrict__ dS) {
+    const int64_t total = n * max_d;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t pos = i / max_d;
+        const int j = (int)(i - pos * max_d);
+        const float4 st = tstat[pos];
+        if (j < __float_as_int(st.z)) {
+            const float p = __expf(P[i] - st.x);
+            P[i] = p;
+            dS[i] = p * (dS[i] - st.y);
+        }
     }
 }
 
@@ -823,6 +861,8 @@ void launch_bwd_mfma_de(const BwdArgs &a, int part, hipStream_t s) {
     if (part == 0) {
         hipLaunchKernelGGL((k_attn_bwd_mfma<XQ, DE, NW>), dim3(256), b, 0, s, a);
     } else {
+        hipLaunchKernelGGL(k_bwd_normalize, dim3((unsigned)std::min<int64_t>(8192, (a.n * a.max_d + 255) / 256)),
+                           dim3(256), 0, s, a.tstat, a.n, a.max_d, a.P, a.dS);
         const int64_t n8 = a.n * DE / 8;
         hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)std::min<int64_t>(4096, (n8 + 255) / 256)), dim3(256), 0,
                            s, reinterpret_cast<const float4 *>(a.dov), n8, reinterpret_cast<uint4 *>(a.dob));

@@ -259,7 +259,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
 // Backward workspace: the forward's regions, then those of the backward pass.
 struct BwdLayout {
     WsLayout f;
-    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, dob, P, dS, part, kv, splitk, total;
+    size_t wmt, dy, dh, y, doutT, zT, dhT, oT, wupT, dov, dob, tstat, P, dS, part, kv, splitk, total;
     int kv_cap;
     int64_t n_pad;
 };
@@ -288,6 +288,7 @@ BwdLayout bwd_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     B.wupT = take((size_t)d.d_emb * d.d_up * es);
     B.dov = take((size_t)n * d.d_emb * 4);
     B.dob = take(d.dtype == L3_BF16 ? (size_t)n * d.d_emb * 2 : 0);
+    B.tstat = take(d.dtype == L3_BF16 ? (size_t)n * 16 : 0);
     B.P = take((size_t)n * std::max(max_d, 1) * 4);
     B.dS = take((size_t)n * std::max(max_d, 1) * 4);
     B.part = take((size_t)ln_param_chunks(n) * d.d_up * 8);
@@ -395,6 +396,7 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     a.dWK = dWK; a.dWV = dWV;
     a.kv_items = ws_ptr<int2>(ws, B.kv); a.kv_cap = B.kv_cap;
     a.n = n; a.dob = dt == L3_BF16 ? ws_ptr<uint16_t>(ws, B.dob) : nullptr;
+    a.tstat = dt == L3_BF16 ? ws_ptr<float4>(ws, B.tstat) : nullptr;
     {
         StageTimer tm(8, s);
         L3_HIP_TRY(launch_attn_bwd(a, dt, 0, s));

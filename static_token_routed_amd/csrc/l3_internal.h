@@ -232,6 +232,7 @@ struct BwdArgs {
     int kv_cap;          // their capacity (kv_item_capacity)
     int64_t n;           // tokens
     uint16_t *dob;       // [n x d_emb] dO rounded to bf16 (matrix-core key / value gradients)
+    float4 *tstat;       // [n] per sorted position: (lse, <dO, o>, d_t as int bits, 0) (matrix cores)
 };
 // items of the key / value gradients: at most one per block plus one per 16 rows, or
 // for the matrix-core kernel (one per block plus one per 64 rows) per column slice

@@ -43,26 +43,36 @@ CASES = {
 KEYS = ["dx", "dW_K", "dW_V", "dW_up", "dgamma", "dbeta", "dW_mix"]
 
 
-def _run(case, fill=0.0, reps=1):
+def _dout(case):
     cfg = case.cfg
-    dt = cfg.dtype
     rng = np.random.default_rng(cfg.seed + 100)
     dout32 = rng.standard_normal((cfg.n, cfg.d_out)).astype(np.float32)
-    dout = synth.f32_to_bf16_bits(dout32) if dt == "bf16" else dout32
+    return synth.f32_to_bf16_bits(dout32) if cfg.dtype == "bf16" else dout32
+
+
+def _run(case, fill=0.0, reps=1, x=None, ids=None, dout=None, status=None):
+    """l3_backward on the case (or on x / ids / dout given for a changed batch)."""
+    cfg = case.cfg
+    dt = cfg.dtype
+    x = case.x if x is None else x
+    ids = case.ids if ids is None else ids
+    dout = _dout(case) if dout is None else dout
+    n = len(ids)
     plan = l3.L3Plan(case.off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, dt, cfg.ln_eps)
     v = int(case.off[-1])
     z = lambda *shape: torch.full(shape, fill, dtype=torch.float32, device="cuda")
-    g = {"dx": z(cfg.n, cfg.d_in), "dW_K": z(v, cfg.d_in), "dW_V": z(v, cfg.d_emb),
+    g = {"dx": z(n, cfg.d_in), "dW_K": z(v, cfg.d_in), "dW_V": z(v, cfg.d_emb),
          "dW_up": z(cfg.d_up, cfg.d_emb), "dgamma": z(cfg.d_up), "dbeta": z(cfg.d_up),
          "dW_mix": z(cfg.d_out, cfg.d_up + cfg.d_in)}
-    ws = torch.empty(l3.l3_backward_workspace_size(plan.handle, cfg.n), dtype=torch.uint8, device="cuda")
-    args = [dev(case.x, dt), torch.from_numpy(case.ids).cuda(), cfg.n, dev(case.WK, dt), dev(case.WV, dt),
-            dev(case.Wup, dt), torch.from_numpy(case.gamma).cuda(), torch.from_numpy(case.beta).cuda(),
-            dev(case.Wmix, dt), dev(dout, dt)]
+    ws = torch.empty(l3.l3_backward_workspace_size(plan.handle, n), dtype=torch.uint8, device="cuda")
+    args = [dev(x, dt), torch.from_numpy(np.ascontiguousarray(ids)).cuda(), n, dev(case.WK, dt),
+            dev(case.WV, dt), dev(case.Wup, dt), torch.from_numpy(case.gamma).cuda(),
+            torch.from_numpy(case.beta).cuda(), dev(case.Wmix, dt), dev(dout, dt)]
     for _ in range(reps):
         l3.l3_backward(plan.handle, *args, *[g[k] for k in KEYS], ws, ws.numel())
     torch.cuda.synchronize()
-    assert plan.status() == l3.L3_OK
+    # the route's flag sits at the start of the backward workspace
+    assert l3.l3_status(ws) == (l3.L3_OK if status is None else status)
     plan.close()
     return {k: to_np(t) for k, t in g.items()}, synth.as_f32(dout, dt)
 
@@ -108,3 +118,25 @@ def test_backward_untouched_rows():
         touched[case.off[t]:case.off[t + 1]] = True
     for k in ("dW_K", "dW_V"):
         assert np.all(got[k][~touched] == 7.0), f"{k}: rows of absent IDs changed"
+
+
+def test_backward_out_of_range_ids():
+    # IDs outside [0, vocab) are flagged and add no attention gradient.  They sort
+    # after every valid ID, so every other token keeps its sorted place: the key /
+    # value gradients and the other tokens' dx equal, bit for bit, those of the batch
+    # without those tokens (matrix-core kernels: d_in 1024, d_emb 128).
+    case = make_case(CASES["bf16_d1024_e128"])
+    cfg = case.cfg
+    dout = _dout(case)
+    bad = [5, 300, 301]
+    ids = case.ids.copy()
+    ids[5], ids[300], ids[301] = -3, cfg.vocab, cfg.vocab + 7
+    got, _ = _run(case, ids=ids, dout=dout, status=l3.L3_ERR_TOKEN_RANGE)
+    keep = np.ones(cfg.n, bool)
+    keep[bad] = False
+    ref, _ = _run(case, x=case.x[keep], ids=case.ids[keep], dout=dout[keep])
+    for k in KEYS:
+        assert np.all(np.isfinite(got[k])), k
+    assert np.array_equal(got["dW_K"], ref["dW_K"])
+    assert np.array_equal(got["dW_V"], ref["dW_V"])
+    assert np.array_equal(got["dx"][keep], ref["dx"])
