@@ -90,7 +90,97 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const T *__restrict__ h, const f
 
 // Column partial sums of dy * yhat and dy over a chunk of kLnRows rows:
 // part[chunk][c] = (sum dy*yhat, sum dy).
-constexpr int kLnRows = 256;
+constexpr int kLnRows = 64;
+
+// Both of the above in one pass for bf16 plans with d_up = 512 NCH (NCH 1, 2, 4): a workgroup per
+// chunk of kLnRows rows, 16 consecutive rows per wavefront, lane l holding columns
+// 512 i + 8 l .. + 7 of the row (h and dy read once, kept in registers).  The
+// column partials are summed over each wavefront's rows in order, then over the 4
+// wavefronts in order (through LDS), and written per chunk as k_ln_param_part does.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_ln_bwd_bf16(const uint16_t *__restrict__ h,
+                                                     const float *__restrict__ stats,
+                                                     const float *__restrict__ gamma,
+                                                     const float *__restrict__ beta,
+                                                     const float *__restrict__ dy, int64_t n,
+                                                     uint16_t *__restrict__ dh, uint16_t *__restrict__ y,
+                                                     float2 *__restrict__ part) {
+    constexpr int d_up = 512 * NCH;
+    static_assert(kLnRows == 64, "16 rows per wavefront");
+    __shared__ __attribute__((aligned(16))) float2 red[4][d_up];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float pa[NCH][8], pb[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pa[c][e] = pb[c][e] = 0.f;
+    const int64_t r0 = (int64_t)blockIdx.x * kLnRows + 16 * w;
+    for (int i = 0; i < 16; ++i) {
+        const int64_t row = r0 + i;
+        if (row >= n) break;
+        const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+        float yh[NCH][8], g[NCH][8];
+        float sg = 0.f, sgy = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t col = 512 * c + 8 * lane;
+            const uint4 hv = *reinterpret_cast<const uint4 *>(h + row * d_up + col);
+            const float4 d0 = *reinterpret_cast<const float4 *>(dy + row * d_up + col);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dy + row * d_up + col + 4);
+            const float4 g0 = *reinterpret_cast<const float4 *>(gamma + col);
+            const float4 g1 = *reinterpret_cast<const float4 *>(gamma + col + 4);
+            const float hf[8] = {bf_lo(hv.x), bf_hi(hv.x), bf_lo(hv.y), bf_hi(hv.y),
+                                 bf_lo(hv.z), bf_hi(hv.z), bf_lo(hv.w), bf_hi(hv.w)};
+            const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const float gf[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                yh[c][e] = (hf[e] - mean) * rstd;
+                g[c][e] = df[e] * gf[e];
+                sg += g[c][e];
+                sgy += g[c][e] * yh[c][e];
+                pa[c][e] += df[e] * yh[c][e];
+                pb[c][e] += df[e];
+            }
+        }
+        sg = wave_sum(sg) / (float)d_up;
+        sgy = wave_sum(sgy) / (float)d_up;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t col = 512 * c + 8 * lane;
+            const float4 g0 = *reinterpret_cast<const float4 *>(gamma + col);
+            const float4 g1 = *reinterpret_cast<const float4 *>(gamma + col + 4);
+            const float4 b0 = *reinterpret_cast<const float4 *>(beta + col);
+            const float4 b1 = *reinterpret_cast<const float4 *>(beta + col + 4);
+            const float gf[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float bf[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            float o[8], yo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = rstd * (g[c][e] - sg - yh[c][e] * sgy);
+                yo[e] = yh[c][e] * gf[e] + bf[e];
+            }
+            *reinterpret_cast<uint4 *>(dh + row * d_up + col) =
+                make_uint4(pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7]));
+            *reinterpret_cast<uint4 *>(y + row * d_up + col) =
+                make_uint4(pack2(yo[0], yo[1]), pack2(yo[2], yo[3]), pack2(yo[4], yo[5]), pack2(yo[6], yo[7]));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[w][512 * c + 8 * lane + e] = make_float2(pa[c][e], pb[c][e]);
+    __syncthreads();
+    for (int q = threadIdx.x; q < d_up; q += 256) {
+        float2 v = red[0][q];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+            v.x += red[ww][q].x;
+            v.y += red[ww][q].y;
+        }
+        part[(int64_t)blockIdx.x * d_up + q] = v;
+    }
+}
 template <typename T>
 __global__ __launch_bounds__(256) void k_ln_param_part(const T *__restrict__ h,
                                                        const float *__restrict__ stats,
@@ -915,7 +1005,16 @@ hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, 
                          float *dgamma, float *dbeta, int dtype, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const dim3 g1((unsigned)((n + 3) / 4)), g2((unsigned)((d_up + 255) / 256), (unsigned)ln_param_chunks(n));
-    if (dtype == L3_BF16) {
+    if (dtype == L3_BF16 && (d_up == 512 || d_up == 1024 || d_up == 2048)) {
+        const dim3 gc((unsigned)ln_param_chunks(n));
+        const uint16_t *hb = (const uint16_t *)h;
+        uint16_t *dhb = (uint16_t *)dh, *yb = (uint16_t *)y;
+        switch (d_up / 512) {
+            case 1: hipLaunchKernelGGL(k_ln_bwd_bf16<1>, gc, dim3(256), 0, s, hb, stats, gamma, beta, dy, n, dhb, yb, part); break;
+            case 2: hipLaunchKernelGGL(k_ln_bwd_bf16<2>, gc, dim3(256), 0, s, hb, stats, gamma, beta, dy, n, dhb, yb, part); break;
+            default: hipLaunchKernelGGL(k_ln_bwd_bf16<4>, gc, dim3(256), 0, s, hb, stats, gamma, beta, dy, n, dhb, yb, part); break;
+        }
+    } else if (dtype == L3_BF16) {
         hipLaunchKernelGGL(k_ln_bwd<uint16_t>, g1, dim3(256), 0, s, (const uint16_t *)h, stats, gamma,
                            beta, dy, n, d_up, (uint16_t *)dh, (uint16_t *)y);
         hipLaunchKernelGGL(k_ln_param_part<uint16_t>, g2, dim3(256), 0, s, (const uint16_t *)h, stats, dy,
