@@ -59,6 +59,56 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, in
     }
 }
 
+// The same for bf16 with 16-byte loads and stores (8 elements per thread and step):
+// rows of the source tile go to LDS whole, and each thread gathers 8 consecutive
+// source rows of one column into a 16-byte piece of a destination row.  Needs
+// 16-byte aligned bases and row strides that are multiples of 8 (checked by the
+// launcher).
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restrict__ src, int64_t ld_src,
+                                                        int64_t rows, int64_t cols,
+                                                        uint16_t *__restrict__ dst, int64_t ld_dst,
+                                                        int64_t rows_pad) {
+    constexpr int TS = 72;  // LDS row stride (elements): 144 bytes keeps 16-byte alignment
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TS];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    for (int q = threadIdx.x; q < 512; q += 256) {
+        const int i = q >> 3, ch = q & 7;  // tile row i, columns 8 ch .. 8 ch + 7
+        const int64_t r = r0 + i, c = c0 + 8 * ch;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows) {
+            const uint16_t *sp = src + r * ld_src + c;
+            if (c + 8 <= cols) {
+                v = *reinterpret_cast<const uint4 *>(sp);
+            } else {
+                uint16_t e[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) e[k] = c + k < cols ? sp[k] : (uint16_t)0;
+                v = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                               e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+            }
+        }
+        *reinterpret_cast<uint4 *>(&tile[i * TS + 8 * ch]) = v;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 512; q += 256) {
+        const int j = q >> 3, ch = q & 7;  // destination row c0 + j, source rows 8 ch .. 8 ch + 7
+        const int64_t c = c0 + j, r = r0 + 8 * ch;
+        if (c >= cols || r >= rows_pad) continue;
+        uint16_t e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = tile[(8 * ch + k) * TS + j];
+        uint16_t *dp = dst + c * ld_dst + r;
+        if (r + 8 <= rows_pad) {
+            *reinterpret_cast<uint4 *>(dp) = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                                                         e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (r + k < rows_pad) dp[k] = e[k];
+        }
+    }
+}
+
 // One wavefront per row: g = dy * gamma, dh = rstd (g - mean(g) - yhat mean(g yhat)),
 // and y = yhat * gamma + beta (the W_mix operand of dW_mix).
 template <typename T>
@@ -991,7 +1041,11 @@ hipError_t launch_transpose(const void *src, int64_t ld_src, int64_t rows, int64
                             int64_t ld_dst, int64_t rows_pad, int dtype, hipStream_t s) {
     if (rows_pad <= 0 || cols <= 0) return hipSuccess;
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
-    if (dtype == L3_BF16)
+    const bool vec = ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0) && ld_src % 8 == 0 && ld_dst % 8 == 0;
+    if (dtype == L3_BF16 && vec)
+        hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, (const uint16_t *)src, ld_src, rows, cols,
+                           (uint16_t *)dst, ld_dst, rows_pad);
+    else if (dtype == L3_BF16)
         hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t *)src, ld_src,
                            rows, cols, (uint16_t *)dst, ld_dst, rows_pad);
     else
