@@ -248,20 +248,37 @@ __global__ __launch_bounds__(256) void k_ln_param_part(const T *__restrict__ h,
     part[blockIdx.y * d_up + c] = make_float2(a, b);
 }
 
-// dgamma[c] += sum over chunks (in chunk order) of part.x, dbeta[c] += of part.y.
+// dgamma[c] += sum over chunks of part.x, dbeta[c] += of part.y, in a fixed order:
+// 16 columns per workgroup, 16 threads per column each summing a contiguous range
+// of chunks in chunk order, then the 16 range sums added in range order.
 __global__ __launch_bounds__(256) void k_ln_param_reduce(const float2 *__restrict__ part, int nchunk,
                                                          int64_t d_up, float *__restrict__ dgamma,
                                                          float *__restrict__ dbeta) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= d_up) return;
+    __shared__ float2 red[16][16];
+    const int cl = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+    const int per = (nchunk + 15) / 16, k0 = g * per, k1 = min(nchunk, k0 + per);
     float a = 0.f, b = 0.f;
-    for (int k = 0; k < nchunk; ++k) {
-        const float2 v = part[k * d_up + c];
-        a += v.x;
-        b += v.y;
+    if (c < d_up) {
+#pragma unroll 8
+        for (int k = k0; k < k1; ++k) {
+            const float2 v = part[k * d_up + c];
+            a += v.x;
+            b += v.y;
+        }
     }
-    dgamma[c] += a;
-    dbeta[c] += b;
+    red[g][cl] = make_float2(a, b);
+    __syncthreads();
+    if (g == 0 && c < d_up) {
+        float2 t = red[0][cl];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            t.x += red[i][cl].x;
+            t.y += red[i][cl].y;
+        }
+        dgamma[c] += t.x;
+        dbeta[c] += t.y;
+    }
 }
 
 // 16-byte chunk c (elements CH c .. CH c + CH - 1) of a row, as floats.
@@ -1079,7 +1096,7 @@ hipError_t launch_ln_bwd(const void *h, const float *stats, const float *gamma, 
         hipLaunchKernelGGL(k_ln_param_part<float>, g2, dim3(256), 0, s, (const float *)h, stats, dy, n,
                            d_up, part);
     }
-    hipLaunchKernelGGL(k_ln_param_reduce, dim3((unsigned)((d_up + 255) / 256)), dim3(256), 0, s, part,
+    hipLaunchKernelGGL(k_ln_param_reduce, dim3((unsigned)((d_up + 15) / 16)), dim3(256), 0, s, part,
                        ln_param_chunks(n), d_up, dgamma, dbeta);
     return hipGetLastError();
 }
