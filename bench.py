@@ -549,7 +549,7 @@ def backward_bench(args, cfg, torch, l3, synth):
     st_ms, launches = l3.l3_profile_read(10)
     l3.l3_profile_enable(False)
     del flush_buf
-    assert plan.status() == l3.L3_OK
+    assert l3.l3_status(ws) == l3.L3_OK  # the route's flag, in the backward workspace
     names = {0: "route", 1: "gather_mfma", 2: "gather_light", 6: "recompute_h", 7: "dense_bwd",
              8: "attn_bwd", 9: "kv_grad"}
     avg = {nm: st_ms[i] / max(1, launches[i]) for i, nm in names.items()}
