@@ -7,7 +7,9 @@
 //
 // Kernel shape (gfx950): 256 threads = 4 wavefronts in 2 x 2, each owning a
 // 128 x 128 block of a 256 x 256 output tile as 8 x 8 v_mfma_f32_16x16x32_bf16
-// accumulators (256 fp32 per lane, in AGPRs): 64 MFMAs per 16 fragment reads.
+// accumulators (256 fp32 per lane, in AGPRs): 64 MFMAs per 16 fragment reads.  A
+// second shape, 8 wavefronts in 2 x 4 (128 x 64 each, two per SIMD), serves the
+// W_up GEMM, whose short K (d_emb) leaves more of each stage's start exposed.
 // K advances 64 columns per stage through two LDS buffers filled by
 // asynchronous global -> LDS copies (buffer_load ... lds: no register staging;
 // each operand is read through a buffer resource that ends with the matrix, so
@@ -83,15 +85,20 @@ __device__ inline void tile_coords(const GemmP &p, int bid, int &tm, int &tn) {
     tn = in / gsz;
 }
 
-template <bool LN_IN, bool LN_OUT, int OUT = 0>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
+template <bool LN_IN, bool LN_OUT, int OUT = 0, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
+    // NW wavefronts: 4 in 2 x 2 (128 x 128 each) or 8 in 2 x 4 (128 x 64 each)
+    static_assert(NW == 4 || NW == 8, "wavefronts");
+    constexpr int WN = NW == 4 ? 128 : 64;  // output columns per wavefront
+    constexpr int NJ = WN / 16;              // their 16-column blocks
+    constexpr int CPW = 32 / NW;             // copies per operand, wavefront and stage
     __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * SLOT];
     // LN_IN: (mean, rstd) of the tile's rows; c1 and c2 of its columns
     __shared__ float2 rowst[LN_IN ? BM : 1];
     __shared__ __attribute__((aligned(16))) float c1s[LN_IN ? BN : 1];
     __shared__ __attribute__((aligned(16))) float c2s[LN_IN ? BN : 1];
     // each thread's lane offsets (LaneOffs below), written once, re-read per stage
-    __shared__ uint4 lane_tab[256][2];
+    __shared__ uint4 lane_tab[64 * NW][2];
 
     int bid = blockIdx.x;
     if constexpr (OUT == 1) {
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     tile_coords(p, bid, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = NW == 4 ? w >> 1 : w >> 2, wn = NW == 4 ? w & 1 : w & 3;
     const uint32_t ring0 = lds_addr(ring);
     const int nst = (int)(p.K / BK);
     const int nst1 = LN_IN ? (int)(p.K1 / BK) : 0;  // stages over the h columns
@@ -155,9 +162,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         for (int ks = 0; ks < 2; ++ks) {
             const uint32_t c = 16 * ((4 * ks + (l >> 4)) ^ (l & 7));
             fa[ks] = (uint32_t)(wm * 128 + (l & 15)) * 128 + c;
-            fb[ks] = TILE + (uint32_t)(wn * 128 + (l & 15)) * 128 + c;
+            fb[ks] = TILE + (uint32_t)(wn * WN + (l & 15)) * 128 + c;
         }
-        const uint32_t gch = (l & 7) ^ (l >> 3), rl = 64 * w + (l >> 3);
+        const uint32_t gch = (l & 7) ^ (l >> 3), rl = 8 * CPW * w + (l >> 3);
         lane_tab[threadIdx.x][0] = make_uint4(fa[0], fa[1], fb[0], fb[1]);
         lane_tab[threadIdx.x][1] = make_uint4(rl * (uint32_t)(p.lda * 2) + gch * 16,
                                               rl * (uint32_t)(p.ldb * 2) + gch * 16,
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         constexpr int KIND = decltype(kind)::value;
         const uint32_t base = ring0 + (uint32_t)((st & 1) * SLOT);
         const int i = c >> 1;
-        const uint32_t off = (uint32_t)((8 * w + i) * 1024) + ((c & 1) ? TILE : 0);
+        const uint32_t off = (uint32_t)((CPW * w + i) * 1024) + ((c & 1) ? TILE : 0);
         if constexpr (KIND == 1) {
             uint32_t v = (c & 1) ? o.vB : o.vA;
             __asm__ volatile("" : "+v"(v));
@@ -200,19 +207,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         }
     };
 
-    f32x4_t acc[8][8];
+    f32x4_t acc[8][NJ];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if constexpr (LN_IN) {
         // written before any copy is in flight; the first barrier publishes them
         const int t = threadIdx.x;
-        const int64_t m = min<int64_t>(m0 + t, p.M - 1), n = min<int64_t>(n0 + t, p.N - 1);
-        rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
-        c1s[t] = p.c1[n];
-        c2s[t] = p.c2[n];
+        if (t < 256) {
+            const int64_t m = min<int64_t>(m0 + t, p.M - 1), n = min<int64_t>(n0 + t, p.N - 1);
+            rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
+            c1s[t] = p.c1[n];
+            c2s[t] = p.c2[n];
+        }
     }
     // the accumulators pinned to AGPRs around the rescale, so the stage loops on either
     // side keep them in place instead of shuffling them between registers
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+            for (int j = 0; j < NJ; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
     };
     // after the h columns: acc = rstd * (acc - mean * c1) per element, one 16-row
     // block at a time (few live VGPRs)
@@ -231,8 +240,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
             const float2 st2 = rowst[wm * 128 + 16 * i + (l & 15)];
             const float rm = st2.x * st2.y;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(&c1s[wn * 128 + 16 * j + 4 * (l >> 4)]);
+            for (int j = 0; j < NJ; ++j) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&c1s[wn * WN + 16 * j + 4 * (l >> 4)]);
                 acc[i][j][0] = fmaf(-rm, c4.x, st2.y * acc[i][j][0]);
                 acc[i][j][1] = fmaf(-rm, c4.y, st2.y * acc[i][j][1]);
                 acc[i][j][2] = fmaf(-rm, c4.z, st2.y * acc[i][j][2]);
@@ -253,28 +262,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         lds_barrier();
         const unsigned char *sb = ring + (st & 1) * SLOT;
         auto rd = [&](uint32_t a) { return *reinterpret_cast<const bf16x8_t *>(sb + a); };
-        bf16x8_t fa0[8], fb0[8], fa1[8], fb1[8];
+        bf16x8_t fa0[8], fb0[NJ], fa1[8], fb1[NJ];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fb0[j] = rd(o.fB[0] + 2048 * j);
+        for (int j = 0; j < NJ; ++j) fb0[j] = rd(o.fB[0] + 2048 * j);
         fa0[0] = rd(o.fA[0]);
         fa0[1] = rd(o.fA[0] + 2048);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
             if (i + 2 < 8) fa0[i + 2] = rd(o.fA[0] + 2048 * (i + 2));
-            fb1[i] = rd(o.fB[1] + 2048 * i);
+            if (i < NJ) fb1[i] = rd(o.fB[1] + 2048 * i);
             fa1[i] = rd(o.fA[1] + 2048 * i);
-            issue_one(kind, st + 1, 2 * i, o);
+            // 2 CPW copies per stage over the 16 MFMA rows: every row (4 wavefronts) or
+            // every other row (8)
+            if constexpr (NW == 4) issue_one(kind, st + 1, 2 * i, o);
+            else if (i % 2 == 0) issue_one(kind, st + 1, i / 2, o);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
-            issue_one(kind, st + 1, 2 * i + 1, o);
+            if constexpr (NW == 4) issue_one(kind, st + 1, 2 * i + 1, o);
+            else if (i % 2 == 0) issue_one(kind, st + 1, 4 + i / 2, o);
             __builtin_amdgcn_sched_barrier(0);
         }
         pin_acc();
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         {
             const LaneOffs o = lane_offs();
 #pragma unroll
-            for (int c = 0; c < 16; ++c) issue_one(KFirst{}, 0, c, o);
+            for (int c = 0; c < 2 * CPW; ++c) issue_one(KFirst{}, 0, c, o);
         }
         for (int st = 0; st < nst - 1; ++st) stage(KFirst{}, st);
         stage(KNone{}, nst - 1);
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
         {
             const LaneOffs o = lane_offs();
 #pragma unroll
-            for (int c = 0; c < 16; ++c) issue_one(KFirst{}, 0, c, o);
+            for (int c = 0; c < 2 * CPW; ++c) issue_one(KFirst{}, 0, c, o);
         }
         for (int st = 0; st < nst1; ++st) stage(KSel{}, st);
         pin_acc();
@@ -311,31 +324,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
     // Epilogue.  acc[i][j] element e of lane l: row m0 + wm*128 + 16i + (l & 15),
     // column n0 + wn*128 + 16j + 4(l/16) + e.
     const uint32_t lane = fresh_lane_id();
-    const int64_t nbase = n0 + wn * 128;
+    const int64_t nbase = n0 + wn * WN;
     auto epilogue = [&](auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
-            uint32_t pk[LN_OUT ? 8 : 1][2];  // the stored bf16 values (all 8 kept for LN_OUT)
+            uint32_t pk[LN_OUT ? NJ : 1][2];  // the stored bf16 values (all kept for LN_OUT)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
                 if constexpr (LN_IN) {
-                    const float4 c4 = *reinterpret_cast<const float4 *>(&c2s[wn * 128 + 16 * j + 4 * (lane >> 4)]);
+                    const float4 c4 = *reinterpret_cast<const float4 *>(&c2s[wn * WN + 16 * j + 4 * (lane >> 4)]);
                     acc[i][j][0] += c4.x;
                     acc[i][j][1] += c4.y;
                     acc[i][j][2] += c4.z;
                     acc[i][j][3] += c4.w;
                 }
                 if constexpr (OUT == 0) {
-                    pk[j & (LN_OUT ? 7 : 0)][0] = pack2(acc[i][j][0], acc[i][j][1]);
-                    pk[j & (LN_OUT ? 7 : 0)][1] = pack2(acc[i][j][2], acc[i][j][3]);
+                    pk[j & (LN_OUT ? NJ - 1 : 0)][0] = pack2(acc[i][j][0], acc[i][j][1]);
+                    pk[j & (LN_OUT ? NJ - 1 : 0)][1] = pack2(acc[i][j][2], acc[i][j][3]);
                 }
                 if (FULL || (m < p.M && n < p.N)) {
                     if constexpr (OUT == 0) {
                         *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
-                            make_uint2(pk[j & (LN_OUT ? 7 : 0)][0], pk[j & (LN_OUT ? 7 : 0)][1]);
+                            make_uint2(pk[j & (LN_OUT ? NJ - 1 : 0)][0], pk[j & (LN_OUT ? NJ - 1 : 0)][1]);
                     } else {
                         float4 *dst = reinterpret_cast<float4 *>(p.Cf + m * p.N + n);
                         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -358,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmP p) {
                     return n < p.N ? v : 0.f;
                 };
 #pragma unroll
-                for (int part = 0; part < 2; ++part) {
+                for (int part = 0; part < NJ / 4; ++part) {
                     const int64_t c0 = nbase + 64 * part;
                     const int64_t width = FULL ? kLnPart : min<int64_t>(kLnPart, p.N - c0);
                     if (!FULL && width <= 0) continue;
@@ -580,7 +593,9 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     if (ln_out) {
         p.ln_out = ln_out;
         p.npart_out = (int)((N + kLnPart - 1) / kLnPart);
-        hipLaunchKernelGGL((k_gemm_bf16<false, true>), grid, dim3(256), 0, s, p);
+        // W_up: K = d_emb is short, so two wavefronts per SIMD (8 per tile) hide more of
+        // each stage's start than one
+        hipLaunchKernelGGL((k_gemm_bf16<false, true, 0, 8>), grid, dim3(512), 0, s, p);
     } else {
         hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(256), 0, s, p);
     }
