@@ -335,10 +335,12 @@ def test_decode_staged_equals_resident(name):
     g.close()
 
 
-@pytest.mark.parametrize("name", ["paper_bf16"])
+@pytest.mark.parametrize("name", ["paper_bf16", "skew_bf16", "skew_uniform_bf16"])
 def test_full_size_sampled(name):
-    """The full-size workload, in the launch configuration the benchmark times;
-    oracle on sampled tokens (largest blocks, single-token blocks, random)."""
+    """Full-size workloads (the benchmark's, in the launch configuration it times, and
+    the skew stress pair: 131072 tokens, d_in 4096, half of them on the 200 IDs at the
+    k = 512 cap, with a Zipf-shaped or a uniform allocation); oracle on sampled tokens
+    (largest blocks, single-token blocks, random)."""
     cfg = synth.CONFIGS[name]
     print(f"generating {name}", flush=True)
     case = make_case(cfg)
