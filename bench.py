@@ -99,7 +99,7 @@ def copy_probe(mib: int):
 
 # kernel name prefix -> stage of one forward
 STAGE_OF_KERNEL = [("k_attn_mfma", "gather_mfma"), ("k_attn_light", "gather_light"),
-                   ("k_gemm_bf16<false, true, 0>", "w_up_gemm"), ("k_gemm_bf16<true, false, 0>", "w_mix_gemm"),
+                   ("k_gemm_bf16<false, true, 0,", "w_up_gemm"), ("k_gemm_bf16<true, false, 0,", "w_mix_gemm"),
                    ("k_ln_finalize", "mix_prep"), ("k_mix_fold", "mix_prep"),
                    ("k_sort", "route"), ("k_scan", "route"), ("k_seg", "route"),
                    ("k_worklist", "route"), ("k_zero_i32", "route"), ("k_route_small", "route")]
