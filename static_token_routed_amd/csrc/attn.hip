@@ -535,6 +535,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     constexpr int HW = XQ < 8 ? XQ : 8;       // fragments per wavefront and K stage
     static_assert(CPR >= 8 && RV % 32 == 0 && (NVH == 1 || OB == 2 * (DEV / 32)), "V stage shape");
     static_assert(HW % 2 == 0 && XQ % HW == 0, "K stage split");
+    // d_in 4096 (QU): a token's x row is too long for two 16-token groups side by side,
+    // so the four wavefronts share one group and each takes a quarter of every K stage
+    // (its x fragments: 128 VGPRs, as at d_in 2048) and of the d_emb columns; the
+    // item's two groups go one after the other.  Otherwise wavefront w takes group
+    // w & 1 and half w >> 1.
+    constexpr bool QU = XQ > 32;
+    constexpr int HWW = QU ? 4 : HW;      // fragment steps per wavefront and K stage
+    constexpr int OBW = QU ? OB / 2 : OB; // 16-column output blocks per wavefront
+    constexpr int NXR = QU ? XQ / 2 : XQ; // x fragments per lane
+    static_assert(!QU || (XQ == 64 && OBW >= 1), "quarter layout");
 
     // one 160 KB allocation: the streaming ring, then the score exchange area; the
     // dense path uses it as two 72 KB stages
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     const uint32_t ring0 = lds_addr(ring);
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) from here on
-    const int tg = w & 1, ch = w >> 1;
+    const int tg = QU ? 0 : (w & 1), ch = QU ? w : (w >> 1);
     const int l16 = lane & 15, kg = lane >> 4;
     const int ndense = a.hdr[HDR_NDENSE];
     const int nitems = a.hdr[HDR_NHEAVY];
@@ -561,24 +571,24 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     // 4 (kk ^ b) + cq with b = bit 2 of l16, cq = (kg ^ l16) & 3; kk ^ b is kk + b for
     // even kk and (kk - 1) + (1 - b) for odd kk.  Half ch starts at step ch HW.
     const int kb2 = (l16 >> 2) & 1, kcq = (kg ^ l16) & 3;
-    const uint32_t k_even = l16 * 1024 + 16 * kcq + 64 * kb2 + 64 * HW * ch;
-    const uint32_t k_odd = l16 * 1024 + 16 * kcq + 64 * (1 - kb2) + 64 * HW * ch;
+    const uint32_t k_even = l16 * 1024 + 16 * kcq + 64 * kb2 + 64 * HWW * ch;
+    const uint32_t k_odd = l16 * 1024 + 16 * kcq + 64 * (1 - kb2) + 64 * HWW * ch;
     // V stage: row r at 2 DEV r, chunk c at physical chunk c ^ 2 (r & 3).  A transposed
     // read for output block E (16 columns) takes row 4kg + l16/4 (+ 32kb, + 16) and
     // column quad l16 % 4: chunk 2E + h, h = (l16 & 3) / 2, byte (l16 & 1) * 8; with
     // r3 = (l16 / 4) & 3 the physical chunk is 2 (E ^ r3) + h.  Blocks E = eb0 + 4m + n
     // (eb0 a multiple of 4, or OB <= 2) sit at vbase[n] + 128 m.
-    const int eb0 = NVH == 1 ? ch * OB : 0;
+    const int eb0 = NVH == 1 ? ch * OBW : (QU ? (w & 1) * OBW : 0);
     const int r3 = (l16 >> 2) & 3;
-    uint32_t vbase[OB < 4 ? OB : 4];
+    uint32_t vbase[OBW < 4 ? OBW : 4];
 #pragma unroll
-    for (int n = 0; n < (OB < 4 ? OB : 4); ++n)
+    for (int n = 0; n < (OBW < 4 ? OBW : 4); ++n)
         vbase[n] = (4 * kg + (l16 >> 2)) * (2 * DEV) + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1) +
                    32 * ((eb0 + n) ^ r3);
 
     // dense items first (one shared counter), then the streaming items; the two loops
     // keep the two paths' registers apart
-    for (;;) {
+    for (; !QU;) {
         if (t == 0) {
             const int n = atomicAdd(&a.queue[8], 1);
             *s_item = n < ndense ? n : -1;
@@ -591,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         const int dn = min(kDenseTile, a.seg_start[di.x + 1] - dsb - di.y);
         const int did = a.uniq[di.x];
         const int64_t dr0 = a.off[did];
-        dense_item<XQ, DE>(a, ring, ring0, dsb, di.y, dn, dr0, (int)(a.off[did + 1] - dr0), w);
+        if constexpr (!QU) dense_item<XQ, DE>(a, ring, ring0, dsb, di.y, dn, dr0, (int)(a.off[did + 1] - dr0), w);
         lds_barrier();  // the next item's copies reuse the LDS and its index slot
     }
     lds_barrier();  // every wavefront has read the last dense index before it is rewritten
@@ -620,22 +630,25 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         const int id = a.uniq[j];
         const int64_t r0 = a.off[id];
         const int d = (int)(a.off[id + 1] - r0);
-        const bool active = 16 * tg < ntok;
-        const int qi = 16 * tg + l16;
+        for (int sub = 0; sub < (QU ? 2 : 1); ++sub) {
+        if (QU && 16 * sub >= ntok) break;
+        const int grp = QU ? sub : tg;  // this wavefront's 16-token group of the item
+        const bool active = 16 * grp < ntok;
+        const int qi = 16 * grp + l16;
         const int tok = a.perm[sb + tq + min(qi, ntok - 1)];
 
-        // x fragments: xr[f] = x[tok][32 kc + 8kg, +8) with kc = 16 (f / HW) + ch HW + f % HW
-        bf16x8_t xr[XQ];
+        // x fragments: xr[f] = x[tok][32 kc + 8kg, +8) with kc = 16 (f / HWW) + ch HWW + f % HWW
+        bf16x8_t xr[NXR];
         if (active) {
-            const uint16_t *xp = a.x + (int64_t)tok * d_in + 32 * HW * ch + 8 * kg;
+            const uint16_t *xp = a.x + (int64_t)tok * d_in + 32 * HWW * ch + 8 * kg;
 #pragma unroll
-            for (int f = 0; f < XQ; ++f)
-                xr[f] = *reinterpret_cast<const bf16x8_t *>(xp + 32 * (16 * (f / HW) + f % HW));
+            for (int f = 0; f < NXR; ++f)
+                xr[f] = *reinterpret_cast<const bf16x8_t *>(xp + 32 * (16 * (f / HWW) + f % HWW));
             // Take delivery of x here, before any copy of this item is in flight: the
             // compiler's own wait for these loads would otherwise be repeated in every
             // group and drain the copy ring (it does not count the asynchronous copies).
 #pragma unroll
-            for (int f = 0; f < XQ; ++f) __asm__ volatile("" ::"v"(xr[f]));
+            for (int f = 0; f < NXR; ++f) __asm__ volatile("" ::"v"(xr[f]));
         }
 
         // stage sequence: per group, nrb * nq K stages (16-row block major), then
@@ -695,9 +708,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         };
 
         float m_run = -INFINITY, l_run = 0.f;
-        f32x4_t O[OB];
+        f32x4_t O[OBW];
 #pragma unroll
-        for (int e = 0; e < OB; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < OBW; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         f32x4_t *const xw = reinterpret_cast<f32x4_t *>(xchg) + w * 8 * 64 + lane;
         const f32x4_t *const xo = reinterpret_cast<const f32x4_t *>(xchg) + (w ^ 2) * 8 * 64 + lane;
@@ -712,14 +725,14 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                 for (int q = 0; q < nq; ++q) {
                     const uint32_t kt = next_stage();
                     if (active) {
-                        bf16x8_t A[HW];
+                        bf16x8_t A[HWW];
 #pragma unroll
-                        for (int i = 0; i < HW; ++i)
+                        for (int i = 0; i < HWW; ++i)
                             A[i] = lds16(kt + ((i & 1) ? k_odd + 64 * (i - 1) : k_even + 64 * i));
 #pragma unroll
-                        for (int i = 0; i < HW; i += 2) {
-                            S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], xr[q * HW + i], S0, 0, 0, 0);
-                            S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i + 1], xr[q * HW + i + 1], S1, 0, 0, 0);
+                        for (int i = 0; i < HWW; i += 2) {
+                            S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], xr[q * HWW + i], S0, 0, 0, 0);
+                            S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i + 1], xr[q * HWW + i + 1], S1, 0, 0, 0);
                         }
                     }
                 }
@@ -731,7 +744,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
             lds_barrier();
             f32x4_t Sc[8];
 #pragma unroll
-            for (int rb = 0; rb < 8; ++rb) Sc[rb] = xw[rb * 64] + xo[rb * 64];
+            for (int rb = 0; rb < 8; ++rb) {
+                if constexpr (QU) {
+                    // the four quarters' partials, added in the same order by every wavefront
+                    const f32x4_t *const x0 = reinterpret_cast<const f32x4_t *>(xchg) + lane + rb * 64;
+                    Sc[rb] = ((x0[0] + x0[8 * 64]) + x0[16 * 64]) + x0[24 * 64];
+                } else {
+                    Sc[rb] = xw[rb * 64] + xo[rb * 64];
+                }
+            }
 
             // online softmax: lane holds rows 128g + 16rb + 4kg + i of token l16
             float gm = -INFINITY;
@@ -749,7 +770,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
             const float al = __expf(m_run - mn);
             m_run = mn;
 #pragma unroll
-            for (int e = 0; e < OB; ++e) O[e] *= al;
+            for (int e = 0; e < OBW; ++e) O[e] *= al;
             float ls = 0.f;
             uint4 Pk[4];
 #pragma unroll
@@ -777,7 +798,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
 #pragma unroll
                 for (int vh = 0; vh < NVH; ++vh) {
                     const uint32_t vt = next_stage();
-                    if (active && (NVH == 1 || vh == ch)) {
+                    if (active && (NVH == 1 || vh == (QU ? (w >> 1) : ch))) {
 #pragma unroll
                         for (int kb = 0; kb < RV / 32; ++kb) {
                             // P of rows [32 (vr RV/32 + kb), +32) of the group
@@ -789,7 +810,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                             }
                             const bf16x8_t P = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
-                            for (int e = 0; e < OB; ++e) {
+                            for (int e = 0; e < OBW; ++e) {
                                 // rows 32kb + 4kg + l16/4 (first read) and 16 rows further (second)
                                 const uint32_t pa = vt + vbase[e & 3] + 128 * (e >> 2) + 64 * DEV * kb;
                                 const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -808,15 +829,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
 
         if (active && qi < ntok) {
             const float inv = 1.f / l_run;
-            uint16_t *orow = a.o + (int64_t)tok * DE + 16 * OB * ch + 4 * kg;
+            uint16_t *orow = a.o + (int64_t)tok * DE + 16 * OBW * ch + 4 * kg;
 #pragma unroll
-            for (int e = 0; e < OB; ++e) {
+            for (int e = 0; e < OBW; ++e) {
                 const uint2 u = make_uint2(pack2(O[e][0] * inv, O[e][1] * inv),
                                            pack2(O[e][2] * inv, O[e][3] * inv));
                 *reinterpret_cast<uint2 *>(orow + e * 16) = u;
             }
         }
-        lds_barrier();  // the next item's copies reuse the ring and s_item
+        lds_barrier();  // the next group's or item's copies reuse the ring and s_item
+        }
     }
 }
 
@@ -834,7 +856,8 @@ hipError_t launch_heavy_xq(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
     return hipGetLastError();
 }
 
-// d_in widths the MFMA path is built for (each token's x row is held in registers)
+// d_in widths of the dense items (64 tokens' x rows held in registers); the streaming
+// items also take d_in 4096 (quarter layout)
 bool heavy_d_in(int64_t d_in) {
     return d_in == 128 || d_in == 256 || d_in == 512 || d_in == 1024 || d_in == 2048;
 }
@@ -846,6 +869,7 @@ hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
         case 512: return launch_heavy_xq<8>(ha, d_emb, s);
         case 1024: return launch_heavy_xq<16>(ha, d_emb, s);
         case 2048: return launch_heavy_xq<32>(ha, d_emb, s);
+        case 4096: return launch_heavy_xq<64>(ha, d_emb, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1052,7 +1076,12 @@ int attn_dense_min_tokens(int64_t d_in, int64_t, int dtype) {
 }
 
 int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
-    return dtype == L3_BF16 && heavy_d_in(d_in) ? kHeavyMinTokens : INT32_MAX;
+    // Streaming items also at d_in 4096 (the quarter layout; dense items only up to
+    // 2048).  There an item's two 16-token groups run one after the other, so blocks of
+    // few rows stay with the wavefront kernel unless they have many tokens.
+    if (dtype != L3_BF16) return INT32_MAX;
+    if (heavy_d_in(d_in)) return kHeavyMinTokens;
+    return d_in == 4096 ? kHeavyMinTokensWide : INT32_MAX;
 }
 
 hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {

@@ -26,6 +26,7 @@ constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 feat
 constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
+constexpr int kHeavyMinTokensWide = 64;  // the token threshold at d_in 4096
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
 constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...
 constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense items

@@ -93,6 +93,8 @@ SMALL_BF16 = [
     ("d1024_e256", 800, 64, 1024, 256, 512, 320, 2600, 20000),
     ("d2048_e512", 600, 96, 2048, 512, 512, 256, 1500, 20000),
     ("d4096_e512", 400, 64, 4096, 512, 256, 256, 700, 9000),
+    # d_in 4096 with d_emb 256: the streaming items' quarter layout with one V stage
+    ("d4096_e256", 300, 80, 4096, 256, 256, 256, 900, 9000),
     ("ragged_e64", 50, 200, 192, 64, 128, 64, 513, 3000),
     # MFMA path over several 128-row softmax groups, a partial last group, and
     # blocks longer than 512 rows, for each V stage shape (d_emb 64 / 256 / 512)
