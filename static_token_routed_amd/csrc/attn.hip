@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
 
     // dense items first (one shared counter), then the streaming items; the two loops
     // keep the two paths' registers apart
-    for (; !QU;) {
+    for (;;) {
         if (t == 0) {
             const int n = atomicAdd(&a.queue[8], 1);
             *s_item = n < ndense ? n : -1;
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         const int dn = min(kDenseTile, a.seg_start[di.x + 1] - dsb - di.y);
         const int did = a.uniq[di.x];
         const int64_t dr0 = a.off[did];
-        if constexpr (!QU) dense_item<XQ, DE>(a, ring, ring0, dsb, di.y, dn, dr0, (int)(a.off[did + 1] - dr0), w);
+        dense_item<XQ, DE>(a, ring, ring0, dsb, di.y, dn, dr0, (int)(a.off[did + 1] - dr0), w);
         lds_barrier();  // the next item's copies reuse the LDS and its index slot
     }
     lds_barrier();  // every wavefront has read the last dense index before it is rewritten
@@ -856,8 +856,9 @@ hipError_t launch_heavy_xq(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
     return hipGetLastError();
 }
 
-// d_in widths of the dense items (64 tokens' x rows held in registers); the streaming
-// items also take d_in 4096 (quarter layout)
+// d_in widths of the matrix-core kernel's two-group streaming items (each token's x
+// row held in registers); the dense items (x streamed through LDS) and the quarter
+// layout of the streaming items also take d_in 4096
 bool heavy_d_in(int64_t d_in) {
     return d_in == 128 || d_in == 256 || d_in == 512 || d_in == 1024 || d_in == 2048;
 }
@@ -1072,13 +1073,13 @@ int attn_light_tokens(int64_t d_in, int dtype) {
 }
 
 int attn_dense_min_tokens(int64_t d_in, int64_t, int dtype) {
-    return dtype == L3_BF16 && heavy_d_in(d_in) ? kDenseMinTokens : INT32_MAX;
+    return dtype == L3_BF16 && (heavy_d_in(d_in) || d_in == 4096) ? kDenseMinTokens : INT32_MAX;
 }
 
 int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
-    // Streaming items also at d_in 4096 (the quarter layout; dense items only up to
-    // 2048).  There an item's two 16-token groups run one after the other, so blocks of
-    // few rows stay with the wavefront kernel unless they have many tokens.
+    // Streaming items also at d_in 4096 (the quarter layout).  There an item's two
+    // 16-token groups run one after the other, so blocks of few rows stay with the
+    // wavefront kernel unless they have many tokens.
     if (dtype != L3_BF16) return INT32_MAX;
     if (heavy_d_in(d_in)) return kHeavyMinTokens;
     return d_in == 4096 ? kHeavyMinTokensWide : INT32_MAX;

@@ -30,6 +30,8 @@ constexpr int kHeavyMinTokensWide = 64;  // the token threshold at d_in 4096
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
 constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...
 constexpr int kDenseMaxD = 512;    // ... and at most this many rows take dense items
+constexpr int kDenseMinD = 64;     // ... and at least this many (a dense item's stages over
+                                   // d_in cost the same for any d_t, so few rows waste them)
 
 // Workspace header (int32 words), zeroed at the start of every call.
 enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_NKV = 5,
@@ -81,7 +83,7 @@ hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s);
 hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs &b, int64_t ntiles,
                         hipStream_t s);
 // Work lists for the gather-attention kernels (reads the route outputs).
-// Blocks go to the dense list (>= dense_min_tokens tokens, d_t <= kDenseMaxD, items of
+// Blocks go to the dense list (>= dense_min_tokens tokens, kDenseMinD <= d_t <= kDenseMaxD, items of
 // kDenseTile tokens), else the heavy list (>= heavy_min_tokens tokens or >= kHeavyMinRows
 // rows, items of kHeavyTile tokens), else the light list (items of light_tokens tokens,
 // written out as {first sorted position, tokens, first row, d_t (-1: ID out of range)}).

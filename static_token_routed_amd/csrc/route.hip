@@ -259,7 +259,7 @@ __device__ inline BlockItems block_items(int S, int t, const int64_t *off, int v
     b.d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
     b.r0 = t < vocab ? (int)off[t] : 0;
     if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || b.d >= kHeavyMinRows)) {
-        if (S >= dense_min && b.d <= kDenseMaxD)
+        if (S >= dense_min && b.d >= kDenseMinD && b.d <= kDenseMaxD)
             b.nd = (S + kDenseTile - 1) / kDenseTile;
         else
             b.nh = (S + kHeavyTile - 1) / kHeavyTile;
