@@ -457,8 +457,8 @@ def decode_bench(args, cfg, torch, l3, synth):
     row_b = (cfg.d_in + cfg.d_emb) * 2
     cfrac = float(cached.sum() / rows.sum())
     h2d = (rows - cached) * row_b
-    pipe = decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st, plan, WKh, WVh, x, Wup, g, b,
-                            Wmix, gemm, side, ready, timed) if args.layers == 2 else None
+    pipe = decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, WKh, WVh, x, Wup, g, b, Wmix, gemm,
+                            timed) if args.layers == 2 else None
     med = lambda a: float(np.median(a))
     ov = med(t_copy) + med(t_gemm) - med(t_conc)
     pcie = float(h2d.mean()) / (med(t_copy) * 1e-6) / 1e9
@@ -606,13 +606,14 @@ def backward_bench(args, cfg, torch, l3, synth):
     plan.close()
 
 
-def decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st1, plan1, WKh1, WVh1, x, Wup1, g1, b1,
-                     Wmix1, gemm, side1, ready1, timed):
+def decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, WKh1, WVh1, x, Wup1, g1, b1, Wmix1,
+                     gemm, timed):
     """Two lookup layers per decode step, as the pages place L^3 after several decoder
-    layers: both layers' prefetches are issued when the step starts (layer 2 on its
-    own side stream and staging, with its own tables), then the main stream runs the
-    pre-layer GEMM, layer 1, the same GEMM again for the layers in between, and
-    layer 2 (whose input is layer 1's output).  t_copies: both prefetches alone;
+    layers, through l3.DecodeLayers (the path tests/test_gpu_decode_pipeline.py checks
+    bit for bit): both layers' prefetches are issued when the step starts, each on its
+    own side stream and staging (layer 2 with its own tables), then the main stream
+    runs the pre-layer GEMM, layer 1, the same GEMM again for the layers in between,
+    and layer 2 (whose input is layer 1's output).  t_copies: both prefetches alone;
     t_compute: the same step with its rows already staged; ov = t_copies + t_compute -
     t_step."""
     n = cfg.n
@@ -625,41 +626,36 @@ def decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st1, plan1, WKh1, WV
     def dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
-    WKh2, WVh2 = pinned(synth.table(c2, "W_K")), pinned(synth.table(c2, "W_V"))
-    Wup2, Wmix2 = dev(synth.dense(c2, "W_up")), dev(synth.dense(c2, "W_mix"))
-    plan2 = l3.L3Plan(synth.offsets(cfg), cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16",
-                      cfg.ln_eps)
-    st2 = l3.l3_staging_create(plan2.handle, n * cfg.k, n)
+    off = synth.offsets(cfg)
+    mk = lambda: l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16", cfg.ln_eps)
+    layers = [
+        {"plan": mk(), "W_K_host": WKh1, "W_V_host": WVh1, "W_up": Wup1, "gamma": g1, "beta": b1,
+         "W_mix": Wmix1},
+        {"plan": mk(), "W_K_host": pinned(synth.table(c2, "W_K")),
+         "W_V_host": pinned(synth.table(c2, "W_V")), "W_up": dev(synth.dense(c2, "W_up")),
+         "gamma": g1, "beta": b1, "W_mix": dev(synth.dense(c2, "W_mix"))},
+    ]
+    pipe = l3.DecodeLayers(layers, max_tokens=n)
     if len(hot):
-        l3.l3_staging_set_cache(st2, hot, WKh2, WVh2)
-    ws1, ws2 = plan1.workspace(n), plan2.workspace(n)
-    out1 = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
-    out2 = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+        pipe.set_cache(0, hot)
+        pipe.set_cache(1, hot)
     main = torch.cuda.current_stream()
-    side2 = torch.cuda.Stream()
-    ready2 = torch.cuda.Event()
-
-    def prefetch2(s_):
-        l3.l3_prefetch(plan1.handle, ids[s_], n, WKh1, WVh1, st1, side1, ready1)
-        l3.l3_prefetch(plan2.handle, ids[s_], n, WKh2, WVh2, st2, side2, ready2)
 
     def compute():
         gemm()
-        main.wait_stream(side1)
-        l3.l3_forward_staged(st1, x, n, Wup1, g1, b1, Wmix1, out1, ws1, ws1.numel())
+        y1 = pipe.forward(0, x)
         gemm()
-        main.wait_stream(side2)
-        l3.l3_forward_staged(st2, out1, n, Wup2, g1, b1, Wmix2, out2, ws2, ws2.numel())
+        pipe.forward(1, y1)
 
     def step(s_):
-        prefetch2(s_)
+        pipe.prefetch(ids[s_])
         compute()
         main.synchronize()
 
     def copies(s_):
-        prefetch2(s_)
-        ready1.synchronize()
-        ready2.synchronize()
+        pipe.prefetch(ids[s_])
+        for lay in pipe.layers:
+            lay["ready"].synchronize()
 
     def compute_only(s_):
         compute()
@@ -669,8 +665,9 @@ def decode_pipeline2(args, cfg, torch, l3, synth, ids, hot, st1, plan1, WKh1, WV
         step(0)
     t_step, t_cp = timed(step), timed(copies)
     t_cmp = timed(compute_only)
-    l3.l3_staging_destroy(st2)
-    plan2.close()
+    pipe.close()
+    for lay in layers:
+        lay["plan"].close()
     med = lambda a: float(np.median(a))
     ov = med(t_cp) + med(t_cmp) - med(t_step)
     return {"t_step_us": {"median": med(t_step), "p99": float(np.percentile(t_step, 99)),

@@ -129,9 +129,13 @@ int l3_plan_info(l3_plan_t plan, int64_t *vocab, int64_t *v, int32_t *k,
 int l3_worklist_rule(l3_plan_t plan, int32_t *min_tokens, int32_t *min_rows);
 
 /* Bytes of device workspace l3_forward / l3_route need for up to n_max tokens
- * (0 on a bad argument).  The workspace is caller-allocated device memory,
- * 256-byte aligned; its contents need no initialisation. */
+ * (0 on a bad argument): enough for every batch size from 1 to n_max.  The
+ * workspace is caller-allocated device memory, 256-byte aligned; its contents
+ * need no initialisation.
+ * l3_workspace_size_dims -- the same figure before any plan exists (host only, no
+ * device needed): for a plan with these dims whose largest d_t is max_d. */
 size_t l3_workspace_size(l3_plan_t plan, int64_t n_max);
+size_t l3_workspace_size_dims(const l3_dims_t *dims, int32_t max_d, int64_t n_max);
 
 /*
  * l3_forward -- out = L3(x, token_ids) for n tokens.
@@ -238,10 +242,14 @@ int l3_staging_destroy(l3_staging_t staging);
  * `side_stream`, then one kernel on the same stream reads every row of those
  * IDs through the tables' device mapping (over PCIe) into the staging buffers.
  * `ready_event` (may be NULL) is recorded on `side_stream` after the kernel.
- * The caller orders the staged forward after it (hipStreamWaitEvent), and the
- * next prefetch into the same staging after that forward.  The host arrays are
- * read before the call returns (token_ids_host may be reused at once); the
- * pinned tables must stay valid until the kernel finishes.
+ * The caller orders the staged forward after it (hipStreamWaitEvent).  The next
+ * prefetch into the same staging is ordered after the last l3_forward_staged that
+ * read it by the library itself (an event recorded after that forward, waited on
+ * by `side_stream` before anything is overwritten), so decode steps may be issued
+ * back to back without host synchronisation; the host blocks only while the
+ * previous step's index block is still being copied out of its pinned mirror.
+ * The host arrays are read before the call returns (token_ids_host may be reused
+ * at once); the pinned tables must stay valid until the kernel finishes.
  * Errors: INVALID_ARG (also tables without a device mapping, e.g. pageable
  * memory), TOKEN_RANGE (an ID outside [0, vocab); nothing is enqueued),
  * CAPACITY (more than max_tokens tokens or max_rows rows), HIP.
@@ -270,7 +278,9 @@ int l3_staging_stats(l3_staging_t staging, int64_t *rows, int64_t *cached_rows);
 /*
  * l3_forward_staged -- l3_forward over the rows the last l3_prefetch staged,
  * for the same n tokens in the same order.  workspace: >= l3_workspace_size
- * (plan, n) bytes.  Errors: INVALID_ARG, CAPACITY, HIP.
+ * (plan, n) bytes.  Records the staging's "consumed" event on `stream` after its
+ * kernels (the next l3_prefetch into this staging waits for it).
+ * Errors: INVALID_ARG, CAPACITY, HIP.
  */
 int l3_forward_staged(l3_staging_t staging, const void *x, int64_t n, const void *W_up,
                       const float *ln_gamma, const float *ln_beta, const void *W_mix,

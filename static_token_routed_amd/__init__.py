@@ -47,6 +47,7 @@ _SIG = {
     "l3_plan_info": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "l3_worklist_rule": (ctypes.c_int, [_P, _P, _P]),
     "l3_workspace_size": (_SZ, [_P, _I64]),
+    "l3_workspace_size_dims": (_SZ, [ctypes.POINTER(l3_dims_t), _I32, _I64]),
     "l3_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "l3_backward_workspace_size": (_SZ, [_P, _I64]),
     "l3_allocate_lzw": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int32, _P]),
@@ -136,6 +137,12 @@ def l3_worklist_rule(plan) -> tuple[int, int]:
 
 def l3_workspace_size(plan: int, n_max: int) -> int:
     return int(_lib.l3_workspace_size(plan, n_max))
+
+
+def l3_workspace_size_dims(d_in: int, d_emb: int, d_up: int, d_out: int, dtype: str, max_d: int,
+                           n_max: int, ln_eps: float = 1e-5) -> int:
+    dims = l3_dims_t(d_in, d_emb, d_up, d_out, L3_BF16 if dtype == "bf16" else L3_F32, ln_eps)
+    return int(_lib.l3_workspace_size_dims(ctypes.byref(dims), max_d, n_max))
 
 
 def l3_forward(plan, x, token_ids, n, W_K, W_V, W_up, ln_gamma, ln_beta, W_mix, out, workspace,
@@ -305,3 +312,73 @@ class L3Plan:
             self.close()
         except Exception:
             pass
+
+
+class DecodeLayers:
+    """Decode steps through several lookup layers whose tables stay in pinned host
+    memory (the pages' offloaded inference: sciencestack.ai page, Fig. 4 caption;
+    papernotes.org page, section 关键设计 item 3, where the layers sit after several
+    decoder layers so the row copies hide behind them).
+
+    Each layer has its own plan, staging, side stream and ready event.  ``prefetch``
+    is called once when a step's token IDs are known and issues every layer's copy
+    at once, each on its own side stream, so layer i's rows move while the main
+    stream runs everything before layer i.  ``forward(i, x)`` makes the stream wait
+    for layer i's copy and runs its staged forward; layer i + 1 may take layer i's
+    output as its input.  Steps can follow each other without host synchronisation:
+    the library orders each prefetch after the staged forward that last read its
+    staging.  This class only schedules: every step is one C call above.
+
+    layers: list of dicts with keys plan (L3Plan), W_K_host, W_V_host (pinned host
+    tensors), W_up, gamma, beta, W_mix (device tensors); max_tokens: tokens per step.
+    """
+
+    def __init__(self, layers, max_tokens: int):
+        import torch
+        self.max_tokens = max_tokens
+        self.layers = []
+        for spec in layers:
+            plan = spec["plan"]
+            lay = dict(spec)
+            lay["staging"] = l3_staging_create(plan.handle, max_tokens * plan.k, max_tokens)
+            lay["side"] = torch.cuda.Stream()
+            lay["ready"] = torch.cuda.Event()
+            lay["ws"] = torch.empty(l3_workspace_size(plan.handle, max_tokens), dtype=torch.uint8,
+                                    device="cuda")
+            dt = torch.bfloat16 if plan.dtype == "bf16" else torch.float32
+            lay["out"] = torch.empty((max_tokens, plan.d_out), dtype=dt, device="cuda")
+            self.layers.append(lay)
+        self.n = 0
+
+    def set_cache(self, i: int, hot_ids, stream=None) -> None:
+        lay = self.layers[i]
+        l3_staging_set_cache(lay["staging"], hot_ids, lay["W_K_host"], lay["W_V_host"], stream)
+
+    def stats(self, i: int) -> tuple[int, int]:
+        return l3_staging_stats(self.layers[i]["staging"])
+
+    def prefetch(self, token_ids_host) -> None:
+        """Issue every layer's row copy for this step's IDs (host int32 [n])."""
+        ids = np.ascontiguousarray(token_ids_host, dtype=np.int32)
+        self.n = len(ids)
+        for lay in self.layers:
+            l3_prefetch(lay["plan"].handle, ids, self.n, lay["W_K_host"], lay["W_V_host"],
+                        lay["staging"], lay["side"], lay["ready"])
+
+    def forward(self, i: int, x, stream=None):
+        """Layer i's output [n x d_out] for input x [n x d_in] (a view of a buffer the
+        next step overwrites)."""
+        import torch
+        lay = self.layers[i]
+        s = torch.cuda.current_stream() if stream is None else stream
+        s.wait_event(lay["ready"])
+        out = lay["out"][: self.n]
+        l3_forward_staged(lay["staging"], x, self.n, lay["W_up"], lay["gamma"], lay["beta"],
+                          lay["W_mix"], out, lay["ws"], lay["ws"].numel(), s)
+        return out
+
+    def close(self) -> None:
+        for lay in self.layers:
+            if lay.get("staging"):
+                l3_staging_destroy(lay["staging"])
+                lay["staging"] = 0

@@ -31,6 +31,10 @@ struct l3_staging_s {
     int32_t *d_ids = nullptr;
     hipEvent_t small_done = nullptr;  // last copy out of h_meta
     bool small_pending = false;
+    // recorded after each l3_forward_staged on its stream: the next prefetch's side
+    // stream waits for it before it overwrites the staged rows and index block
+    hipEvent_t consumed = nullptr;
+    bool consumed_pending = false;
     int64_t n = 0, m = 0, rows = 0, max_d = 0;
     // device-resident cache of hot IDs' rows (l3_staging_set_cache)
     void *c_K = nullptr, *c_V = nullptr;
@@ -408,6 +412,24 @@ int backward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t
     return L3_OK;
 }
 
+// The largest layout over every batch size 1 .. n_max.  Every region grows with n,
+// except the split-row partials of small bf16 batches: they exist only while
+// n * ceil(max_d / split_rows) stays within kSplitMaxSlots (and n <= kSplitMaxN),
+// so the layout grows with n up to the last size that has them, drops when they
+// switch off, and grows again.  The maximum is therefore at n_max or at that last
+// size.
+template <class Total>
+size_t max_layout_bytes(const Dims &d, int64_t n_max, int32_t max_d, Total total) {
+    size_t need = total(d, n_max, max_d);
+    const int64_t per = (std::max<int32_t>(max_d, 1) + split_rows(d.d_in) - 1) / split_rows(d.d_in);
+    const int64_t n_split = std::min<int64_t>({n_max, kSplitMaxN, kSplitMaxSlots / per});
+    if (n_split >= 1) need = std::max(need, total(d, n_split, max_d));
+    return need;
+}
+
+size_t ws_total(const Dims &d, int64_t n, int32_t max_d) { return ws_layout(d, n, max_d).total; }
+size_t bwd_total(const Dims &d, int64_t n, int32_t max_d) { return bwd_layout(d, n, max_d).total; }
+
 }  // namespace
 
 namespace l3 {
@@ -540,12 +562,15 @@ int l3_worklist_rule(l3_plan_t p, int32_t *min_tokens, int32_t *min_rows) {
     return L3_OK;
 }
 
-// Batches of up to kSplitMaxN tokens take a larger layout per token (the split-row
-// partials), so a workspace sized for n_max must also cover those sizes.
 size_t l3_workspace_size(l3_plan_t p, int64_t n_max) {
     if (!p || n_max < 0) return 0;
-    return std::max(ws_layout(p->dims, n_max, p->max_d).total,
-                    ws_layout(p->dims, std::min<int64_t>(n_max, kSplitMaxN), p->max_d).total);
+    return max_layout_bytes(p->dims, n_max, p->max_d, ws_total);
+}
+
+size_t l3_workspace_size_dims(const l3_dims_t *dims, int32_t max_d, int64_t n_max) {
+    if (validate_dims(dims) != L3_OK || max_d < 1 || n_max < 0) return 0;
+    const Dims d{dims->d_in, dims->d_emb, dims->d_up, dims->d_out, dims->dtype, dims->ln_eps};
+    return max_layout_bytes(d, n_max, max_d, ws_total);
 }
 
 int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
@@ -564,8 +589,7 @@ int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const 
 
 size_t l3_backward_workspace_size(l3_plan_t p, int64_t n_max) {
     if (!p || n_max < 0) return 0;
-    return std::max(bwd_layout(p->dims, n_max, p->max_d).total,
-                    bwd_layout(p->dims, std::min<int64_t>(n_max, kSplitMaxN), p->max_d).total);
+    return max_layout_bytes(p->dims, n_max, p->max_d, bwd_total);
 }
 
 int l3_backward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
@@ -683,7 +707,8 @@ int l3_staging_create(l3_plan_t p, int64_t max_rows, int64_t max_tokens, l3_stag
               hipMalloc(&st->d_V, max_rows * p->dims.d_emb * es) == hipSuccess &&
               hipMalloc(&st->d_meta, meta) == hipSuccess &&
               hipHostMalloc(&st->h_meta, meta, 0) == hipSuccess &&
-              hipEventCreateWithFlags(&st->small_done, hipEventDisableTiming) == hipSuccess;
+              hipEventCreateWithFlags(&st->small_done, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&st->consumed, hipEventDisableTiming) == hipSuccess;
     if (!ok) {
         l3_staging_destroy(st);
         return L3_ERR_HIP;
@@ -702,6 +727,7 @@ int l3_staging_destroy(l3_staging_t st) {
     if (st->c_V) (void)hipFree(st->c_V);
     if (st->h_meta) (void)hipHostFree(st->h_meta);
     if (st->small_done) (void)hipEventDestroy(st->small_done);
+    if (st->consumed) (void)hipEventDestroy(st->consumed);
     delete st;
     return L3_OK;
 }
@@ -756,6 +782,8 @@ int l3_prefetch(l3_plan_t p, const int32_t *ids, int64_t n, const void *WK_host,
     st->d_off = d_coff;
     st->d_ids = reinterpret_cast<int32_t *>(d_coff + (2 * m + 1));
     if (n > 0) {
+        // the previous staged forward may still read the rows and index block
+        if (st->consumed_pending) L3_HIP_TRY(hipStreamWaitEvent(s, st->consumed, 0));
         const size_t bytes = (size_t)(2 * m + 1) * sizeof(int64_t) + (size_t)n * sizeof(int32_t);
         L3_HIP_TRY(hipMemcpyAsync(st->d_meta, st->h_meta, bytes, hipMemcpyHostToDevice, s));
         L3_HIP_TRY(hipEventRecord(st->small_done, s));
@@ -855,8 +883,12 @@ int l3_forward_staged(l3_staging_t st, const void *x, int64_t n, const void *W_u
     view.dims = st->plan->dims;
     view.d_off = st->d_off;
     view.owns_off = false;
-    return forward_impl(view, x, st->d_ids, n, st->d_K, st->d_V, W_up, gamma, beta, W_mix, out, ws,
-                        ws_bytes, (hipStream_t)stream);
+    const int rc = forward_impl(view, x, st->d_ids, n, st->d_K, st->d_V, W_up, gamma, beta, W_mix,
+                                out, ws, ws_bytes, (hipStream_t)stream);
+    if (rc != L3_OK) return rc;
+    L3_HIP_TRY(hipEventRecord(st->consumed, (hipStream_t)stream));
+    st->consumed_pending = true;
+    return L3_OK;
 }
 
 // ---------------------------------------------------------------- stage timing

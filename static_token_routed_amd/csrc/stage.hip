@@ -17,18 +17,21 @@ namespace l3 {
 namespace {
 
 constexpr int kStageWaves = 4;  // wavefronts per workgroup
-constexpr int kStageBatch = 4;  // 16-byte chunks each lane has in flight per round
+constexpr int kStageBatch = 4;  // chunks each lane has in flight per round
 
 // Wavefront w copies destination rows w, w + W, ...: it finds the row's ID by a
 // binary search over the compact offsets, then its lanes move the row's K part
-// (rk chunks of 16 bytes) and V part (rv chunks) in rounds of kStageBatch loads
-// followed by kStageBatch stores.
+// (rk chunks of sizeof(T) bytes) and V part (rv chunks) in rounds of kStageBatch
+// loads followed by kStageBatch stores.  T is uint4 (16-byte chunks) when both row
+// lengths are multiples of 16 bytes (every bf16 plan), else uint32_t (fp32 plans
+// whose d_in or d_emb is not a multiple of 4).
 // src[i] >= 0: the ID's first row in the host tables; src[i] < 0: its first row in
 // the device-resident cache of hot rows is -1 - src[i] (cK, cV).
+template <typename T>
 __global__ __launch_bounds__(64 * kStageWaves) void k_stage_rows(
     const int64_t *__restrict__ coff, const int64_t *__restrict__ src, int64_t m, int64_t rows,
-    const uint4 *__restrict__ WK, const uint4 *__restrict__ WV, const uint4 *__restrict__ cK,
-    const uint4 *__restrict__ cV, uint4 *__restrict__ dK, uint4 *__restrict__ dV, int rk, int rv) {
+    const T *__restrict__ WK, const T *__restrict__ WV, const T *__restrict__ cK,
+    const T *__restrict__ cV, T *__restrict__ dK, T *__restrict__ dV, int rk, int rv) {
     const int lane = threadIdx.x & 63;
     const int64_t nw = (int64_t)gridDim.x * kStageWaves;
     const int rt = rk + rv;
@@ -42,10 +45,10 @@ __global__ __launch_bounds__(64 * kStageWaves) void k_stage_rows(
         const int64_t s0 = src[lo];
         const bool cached = s0 < 0;
         const int64_t s = (cached ? -1 - s0 : s0) + (r - coff[lo]);
-        const uint4 *sk = (cached ? cK : WK) + s * rk, *sv = (cached ? cV : WV) + s * rv;
-        uint4 *tk = dK + r * rk, *tv = dV + r * rv;
+        const T *sk = (cached ? cK : WK) + s * rk, *sv = (cached ? cV : WV) + s * rv;
+        T *tk = dK + r * rk, *tv = dV + r * rv;
         for (int c0 = 0; c0 < rt; c0 += 64 * kStageBatch) {
-            uint4 buf[kStageBatch];
+            T buf[kStageBatch];
 #pragma unroll
             for (int j = 0; j < kStageBatch; ++j) {
                 const int c = c0 + j * 64 + lane;
@@ -73,10 +76,19 @@ hipError_t launch_stage_rows(const int64_t *coff, const int64_t *src, int64_t m,
     // one per destination row
     const int64_t want = (rows + kStageWaves - 1) / kStageWaves;
     const int grid = (int)std::min<int64_t>(want, 1024);
-    hipLaunchKernelGGL(k_stage_rows, dim3(grid), dim3(64 * kStageWaves), 0, s, coff, src, m, rows,
-                       (const uint4 *)WK_dev, (const uint4 *)WV_dev, (const uint4 *)cK,
-                       (const uint4 *)cV, (uint4 *)dK, (uint4 *)dV,
-                       (int)(row_k_bytes / 16), (int)(row_v_bytes / 16));
+    if (row_k_bytes % 16 == 0 && row_v_bytes % 16 == 0) {
+        hipLaunchKernelGGL(k_stage_rows<uint4>, dim3(grid), dim3(64 * kStageWaves), 0, s, coff, src,
+                           m, rows, (const uint4 *)WK_dev, (const uint4 *)WV_dev, (const uint4 *)cK,
+                           (const uint4 *)cV, (uint4 *)dK, (uint4 *)dV, (int)(row_k_bytes / 16),
+                           (int)(row_v_bytes / 16));
+    } else {
+        // row lengths are whole elements of 4 bytes (fp32) or 2 bytes (bf16, whose
+        // dims are multiples of 64 and so never take this branch)
+        hipLaunchKernelGGL(k_stage_rows<uint32_t>, dim3(grid), dim3(64 * kStageWaves), 0, s, coff,
+                           src, m, rows, (const uint32_t *)WK_dev, (const uint32_t *)WV_dev,
+                           (const uint32_t *)cK, (const uint32_t *)cV, (uint32_t *)dK,
+                           (uint32_t *)dV, (int)(row_k_bytes / 4), (int)(row_v_bytes / 4));
+    }
     return hipGetLastError();
 }
 

@@ -95,3 +95,33 @@ def test_gemm_shape_and_alignment_checks():
     assert l3.l3_gemm_workspace_size(513, 1024, 4096) == 0   # large M: no workspace
     assert g(a, b, c, 64, 8192, 2048, None, 0, None) == l3.L3_ERR_CAPACITY
     assert g(a, b, c, 64, 8192, 2048, w, need - 1, None) == l3.L3_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("dims,dtype,max_d", [
+    ((2048, 512, 2048, 2048), "bf16", 512),   # the paper's widths at the k = 512 cap
+    ((4096, 512, 4096, 4096), "bf16", 512),
+    ((1024, 256, 1024, 1024), "bf16", 128),
+    ((192, 64, 128, 64), "bf16", 90),
+    ((100, 37, 72, 52), "f32", 96),
+])
+def test_workspace_size_covers_every_smaller_batch(dims, dtype, max_d):
+    """A workspace sized for n_max serves every batch of 1 .. n_max tokens.  Small bf16
+    batches carry split-row partials whose size grows with n * max_d until they switch
+    off, so the per-token need is largest just below that point: the size function
+    must be non-decreasing in n across it."""
+    size = lambda n: l3.l3_workspace_size_dims(*dims, dtype, max_d, n)
+    sizes = np.array([size(n) for n in range(0, 1300)])
+    assert np.all(sizes[1:] > 0)
+    assert np.all(np.diff(sizes) >= 0), int(np.argmax(np.diff(sizes) < 0))
+    for n_max in (512, 1024, 4096):
+        assert size(n_max) >= sizes[1:min(n_max, 1299) + 1].max()
+    if dtype == "bf16" and dims[0] == 2048:
+        # the split-row partials: 256 tokens x 128 chunks of 4 rows x d_emb fp32 alone
+        assert size(256) >= 256 * 128 * 512 * 4
+        assert size(512) >= size(256)
+
+
+def test_workspace_size_dims_rejects():
+    assert l3.l3_workspace_size_dims(100, 64, 64, 64, "bf16", 8, 10) == 0   # unsupported dims
+    assert l3.l3_workspace_size_dims(64, 64, 64, 64, "bf16", 0, 10) == 0    # max_d < 1
+    assert l3.l3_workspace_size_dims(64, 64, 64, 64, "bf16", 8, -1) == 0
