@@ -57,7 +57,7 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.l3o_backward.restype = ctypes.c_int
     lib.l3o_backward.argtypes = [I64, I64, I64, ctypes.c_int32, P, I64, I64, I64, I64,
                                  P, P, P, P, P, P, P, ctypes.c_double, P, P,
-                                 P, P, P, P, P, P, P]
+                                 P, P, P, P, P, P, P, P, P]
     lib.l3o_check_offsets.restype = ctypes.c_int
     lib.l3o_check_offsets.argtypes = [P, I64, I64, ctypes.c_int32]
     _libs[path] = lib
@@ -112,9 +112,13 @@ def forward(off, k: int, x, ids, W_K, W_V, W_up, gamma, beta, W_mix, eps: float 
 
 
 def backward(off, k: int, x, ids, W_K, W_V, W_up, gamma, beta, W_mix, dout, eps: float = 1e-5,
-             v: int | None = None, lib: ctypes.CDLL | None = None) -> dict:
+             v: int | None = None, lib: ctypes.CDLL | None = None, magnitudes: bool = False) -> dict:
     """Gradients of sum(dout * forward(...)) (fp64): dict with dx, dW_K, dW_V, dW_up,
-    dgamma, dbeta, dW_mix."""
+    dgamma, dbeta, dW_mix.  With ``magnitudes`` also kmag and vmag [v]: per table row,
+    the size of the products its gradient is formed from (key rows: sum over tokens of
+    p_j (||V_j * do||_2 + ||o * do||_2) max|x|, the root sums of squares of the two inner
+    products whose difference is dS_j; value rows: sum over tokens of p_j max|do|;
+    do = dL/do), zero for rows of absent IDs.  ||dW_V[j]||_inf <= vmag[j]."""
     lib = lib or load()
     off = np.ascontiguousarray(off, dtype=np.int64)
     vocab = len(off) - 1
@@ -134,7 +138,9 @@ def backward(off, k: int, x, ids, W_K, W_V, W_up, gamma, beta, W_mix, dout, eps:
                           _p(x), _p(ids), _p(W_K), _p(W_V), _p(W_up), _p(gamma), _p(beta),
                           float(eps), _p(W_mix), _p(dout),
                           *[_p(g[key]) for key in ("dx", "dW_K", "dW_V", "dW_up", "dgamma",
-                                                   "dbeta", "dW_mix")])
+                                                   "dbeta", "dW_mix")],
+                          *((_p(g.setdefault("kmag", np.zeros(v))), _p(g.setdefault("vmag", np.zeros(v))))
+                            if magnitudes else (ctypes.c_void_p(0), ctypes.c_void_p(0))))
     if rc:
         raise OracleError(rc)
     return g

@@ -39,7 +39,10 @@
  * (papernotes.org page, section 训练策略; kimjy99.github.io page, section
  * "2. Efficient Training and Inference": sort, block-diagonal attention,
  * inverse sort), but print no gradient formulas; these are the plain
- * derivatives of the forward equations.
+ * derivatives of the forward equations.  On request it also returns, per table
+ * row, the size of the products that row's gradient is formed from (kmag, vmag):
+ * the scale of the rounding error a finite-precision gradient carries in that
+ * row, however much the products cancel.
  */
 #include <math.h>
 #include <stdint.h>
@@ -193,7 +196,8 @@ int l3o_backward(int64_t n, int64_t vocab, int64_t v, int32_t k, const int64_t *
                  const double *gamma, const double *beta, double eps,
                  const double *Wmix, const double *dout,
                  double *dx, double *dWK, double *dWV, double *dWup,
-                 double *dgamma, double *dbeta, double *dWmix)
+                 double *dgamma, double *dbeta, double *dWmix,
+                 double *kmag, double *vmag)
 {
     int rc = l3o_check_offsets(off, vocab, v, k);
     if (rc) return rc;
@@ -205,6 +209,8 @@ int l3o_backward(int64_t n, int64_t vocab, int64_t v, int32_t k, const int64_t *
     for (int64_t e = 0; e < d_up * d_emb; ++e) dWup[e] = 0.0;
     for (int64_t e = 0; e < d_up; ++e) dgamma[e] = dbeta[e] = 0.0;
     for (int64_t e = 0; e < d_out * dz; ++e) dWmix[e] = 0.0;
+    if (kmag) for (int64_t e = 0; e < v; ++e) kmag[e] = 0.0;
+    if (vmag) for (int64_t e = 0; e < v; ++e) vmag[e] = 0.0;
     /* scratch: p (k), dp (k), o (d_emb), do (d_emb), h, yhat, y, dy, dh (d_up), out (d_out) */
     double *p = (double *)malloc(sizeof(double) * (size_t)(2 * k + 2 * d_emb + 5 * d_up + d_out));
     if (!p) return L3O_NOMEM;
@@ -271,6 +277,27 @@ int l3o_backward(int64_t n, int64_t vocab, int64_t v, int32_t k, const int64_t *
             }
             dp[j] = acc;
             pdp += p[j] * acc;
+        }
+        /* magnitudes of the products behind each row's gradient.  dS_j is the
+         * difference of two inner products, <V_j, do> and <o, do>; key row j gets
+         * p_j (||V_j * do||_2 + ||o * do||_2) max_c |x_c| per token (the root sum of
+         * squares of those products: the scale a rounding error in them takes, however
+         * much the two cancel), value row j gets p_j max_c |do_c|. */
+        if (kmag || vmag) {
+            double od = 0.0, dmax = 0.0, xmax = 0.0;
+            for (int64_t c = 0; c < d_emb; ++c) {
+                od += (o[c] * dov[c]) * (o[c] * dov[c]);
+                if (fabs(dov[c]) > dmax) dmax = fabs(dov[c]);
+            }
+            od = sqrt(od);
+            for (int64_t c = 0; c < d_in; ++c) if (fabs(xi[c]) > xmax) xmax = fabs(xi[c]);
+            for (int64_t j = 0; j < d; ++j) {
+                const double *vrow = WV + (a + j) * d_emb;
+                double vd = 0.0;
+                for (int64_t c = 0; c < d_emb; ++c) vd += (vrow[c] * dov[c]) * (vrow[c] * dov[c]);
+                if (kmag) kmag[a + j] += p[j] * (sqrt(vd) + od) * xmax;
+                if (vmag) vmag[a + j] += p[j] * dmax;
+            }
         }
         /* p = softmax(s), s_j = <K_t[j], x> */
         for (int64_t j = 0; j < d; ++j) {

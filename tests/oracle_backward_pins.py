@@ -88,4 +88,57 @@ def pin_bwd_linear_in_dout(lib):
         assert np.array_equal(2.0 * g1[key], g2[key]), key
 
 
+def _bwd_mag(lib, c, dout):
+    return oracle.backward(c["off"], c["k"], c["x"], c["ids"], c["W_K"], c["W_V"], c["W_up"],
+                           c["gamma"], c["beta"], c["W_mix"], dout, eps=c["eps"], lib=lib,
+                           magnitudes=True)
+
+
+def pin_bwd_magnitudes_rows(lib):
+    # rows of absent IDs have zero magnitude, touched rows a positive one; a value row's
+    # gradient sum_i p_j do_i is at most sum_i p_j max|do_i| (triangle inequality); both
+    # magnitudes are linear in dout
+    c = _case(seed=26, vocab=6, k=4, n=9, d=[3, 1, 4, 2, 2, 4])
+    c["ids"] = np.array([0, 2, 2, 5, 0, 1, 2, 5, 0], np.int32)
+    dout = np.random.default_rng(6).standard_normal((9, c["W_mix"].shape[0]))
+    g = _bwd_mag(lib, c, dout)
+    g3 = _bwd_mag(lib, c, 3.0 * dout)
+    off = c["off"]
+    for t in range(6):
+        rows = slice(off[t], off[t + 1])
+        present = t in (0, 1, 2, 5)
+        for mag in ("kmag", "vmag"):
+            m = g[mag][rows]
+            assert np.all(m > 0) == present and (present or np.all(m == 0)), (mag, t)
+            np.testing.assert_allclose(g3[mag][rows], 3.0 * m, rtol=1e-12)
+        assert np.all(np.max(np.abs(g["dW_V"][rows]), axis=1) <= g["vmag"][rows] * (1 + 1e-12))
+
+
+def pin_bwd_magnitudes_closed_form(lib):
+    # one token whose ID owns three rows: its value-row gradients are p_j * do, so
+    # do = dW_V[j] / p_j; with p = softmax(K_t x) and o = V_t^T p (three numbers, worked
+    # here in numpy) the magnitudes are p_j (||V_j * do||_2 + ||o * do||_2) max|x| and
+    # p_j max|do|.  A one-row ID (p = 1, o = V) gives 2 ||V * do||_2 max|x|.
+    for d, tok in (([3, 1], 0), ([3, 1], 1)):
+        c = _case(seed=27, vocab=2, k=3, n=1, d=d)
+        c["ids"] = np.array([tok], np.int32)
+        g = _bwd_mag(lib, c, np.random.default_rng(7).standard_normal((1, c["W_mix"].shape[0])))
+        a, b = c["off"][tok], c["off"][tok + 1]
+        s = c["W_K"][a:b] @ c["x"][0]
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        do = g["dW_V"][a] / p[0]
+        V = c["W_V"][a:b]
+        o = p @ V
+        xmax = np.max(np.abs(c["x"][0]))
+        for j in range(b - a):
+            want_k = p[j] * (np.linalg.norm(V[j] * do) + np.linalg.norm(o * do)) * xmax
+            want_v = p[j] * np.max(np.abs(do))
+            np.testing.assert_allclose(g["kmag"][a + j], want_k, rtol=1e-12)
+            np.testing.assert_allclose(g["vmag"][a + j], want_v, rtol=1e-12)
+        if b - a == 1:
+            np.testing.assert_allclose(g["kmag"][a], 2 * np.linalg.norm(V[0] * do) * xmax,
+                                       rtol=1e-12)
+
+
 BACKWARD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_bwd_")]

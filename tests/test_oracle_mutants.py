@@ -62,6 +62,13 @@ BACKWARD_MUTANTS = [
     ("bwd_dx_no_attention_term", "dx[i * d_in + c] += ds * kr[c];", "(void)kr;"),
     ("bwd_dv_first_row_only", "double *gv = dWV + (a + j) * d_emb;", "double *gv = dWV + a * d_emb;"),
     ("bwd_dk_uses_dp", "gk[c] += ds * xi[c];", "gk[c] += dp[j] * xi[c];"),
+    # the per-row magnitudes the GPU backward's tolerance is built from
+    ("bwd_kmag_no_output_term", "if (kmag) kmag[a + j] += p[j] * (sqrt(vd) + od) * xmax;",
+     "if (kmag) kmag[a + j] += p[j] * sqrt(vd) * xmax;"),
+    ("bwd_kmag_no_p", "if (kmag) kmag[a + j] += p[j] * (sqrt(vd) + od) * xmax;",
+     "if (kmag) kmag[a + j] += (sqrt(vd) + od) * xmax;"),
+    ("bwd_kmag_l1", "od = sqrt(od);", "od = sqrt(od) * 2.0;"),
+    ("bwd_vmag_first_row", "if (vmag) vmag[a + j] += p[j] * dmax;", "if (vmag) vmag[a] += p[j] * dmax;"),
 ]
 
 
