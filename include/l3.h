@@ -158,6 +158,28 @@ int l3_forward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t 
                void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * l3_forward_noalloc -- l3_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result bits as l3_forward, with the workspace
+ * in a device array the library holds (64 MiB on every GPU it runs on, kept until
+ * the process ends) instead of a caller buffer.  Nothing is allocated per call
+ * (with stage timing, l3_profile_enable, off).  Arguments as for l3_forward, minus
+ * the workspace.  Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (this batch's
+ * workspace would exceed 64 MiB; nothing is enqueued), HIP.  A batch of n tokens
+ * always fits when l3_workspace_size(plan, n) <= 64 MiB: up to 146 tokens at d_in
+ * 2048, d_emb 512, d_up = d_out = 2048 with d_t up to 512, 31 at d_in = d_up =
+ * d_out = 4096, and batches of thousands at d_in 1024, d_emb 256, d_t up to 128.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.  The
+ * out-of-range flag lands in that array, where l3_status cannot read it: callers
+ * that need it use l3_forward.
+ */
+int l3_forward_noalloc(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t n,
+                       const void *W_K, const void *W_V, const void *W_up,
+                       const float *ln_gamma, const float *ln_beta, const void *W_mix,
+                       void *out, void *stream);
+
+/*
  * Backward pass (training).  The pages train the layer end to end, the batch
  * sorted by token ID so attention is block diagonal and the sort undone after
  * (sciencestack.ai page, Fig. 3 caption; kimjy99.github.io page, section "2.

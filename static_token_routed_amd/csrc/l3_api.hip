@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -584,6 +585,70 @@ int l3_forward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const 
     if (!aligned16({x, WK, WV, W_up, gamma, beta, W_mix, out, ws})) return L3_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(ids) & 3) return L3_ERR_INVALID_ARG;
     return forward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, out, ws, ws_bytes,
+                        (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free forward
+//
+// l3_forward_noalloc runs l3_forward with its workspace in this file-scope device
+// array instead of caller memory, for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code must not
+// pass the array's name to a kernel or a copy (on the host it is only a stand-in):
+// its device address is taken once per device with hipGetSymbolAddress, with that
+// device current, and only that address is used.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+int scratch_address(void **out) {
+    int dev = -1;
+    L3_HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kScratchDevices) return L3_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return L3_ERR_HIP;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return L3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int l3_forward_noalloc(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const void *WK,
+                       const void *WV, const void *W_up, const float *gamma, const float *beta,
+                       const void *W_mix, void *out, void *stream) {
+    if (!p || n < 0) return L3_ERR_INVALID_ARG;
+    if (n == 0) return L3_OK;
+    if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
+    if (!x || !ids || !WK || !WV || !W_up || !gamma || !beta || !W_mix || !out)
+        return L3_ERR_INVALID_ARG;
+    if (!aligned16({x, WK, WV, W_up, gamma, beta, W_mix, out})) return L3_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(ids) & 3) return L3_ERR_INVALID_ARG;
+    // the layout this batch uses must fit the array (checked before anything is enqueued)
+    if (ws_layout(p->dims, n, p->max_d).total > kScratchBytes) return L3_ERR_CAPACITY;
+    void *ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != L3_OK) return rc;
+    return forward_impl(*p, x, ids, n, WK, WV, W_up, gamma, beta, W_mix, out, ws, kScratchBytes,
                         (hipStream_t)stream);
 }
 
