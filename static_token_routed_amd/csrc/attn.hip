@@ -104,13 +104,57 @@ struct LightArgs {
     int64_t d_in, d_emb;
     int32_t vocab;
     uint16_t *o;
+    const int4 *items_long;  // the same for blocks of >= kLightMidRows rows (taken first)
+    int cap;                 // entries of items_long (the batch's tokens)
 };
 
-// One item with exactly NT tokens.
-template <int NCI, int VE, int NT>
-__device__ __forceinline__ void light_item(const LightArgs &a, const int (&tok)[8], int64_t r0,
-                                           int64_t d, int lane) {
-    const int64_t d_in = a.d_in;
+template <int NCI>
+constexpr int light_tokens_for() { return NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3); }
+
+// Light items: one wavefront per item.  The item's K / V rows stream through a
+// ring of LR rows of this wavefront's LDS, filled by asynchronous global->LDS
+// copies LR - 1 rows ahead, so a wavefront keeps several rows in flight without
+// holding them in registers (the kernel is bound by the bytes each CU has in
+// flight: a light item's rows are few and their latency is what it waits on).
+// A ring slot is NCI 1 KB pieces of the K row (lane l copies bytes [16l, 16l + 16)
+// of piece c, which are exactly the columns c*512 + 8l .. + 8 it multiplies) and
+// one 1 KB piece of the V row (lanes past the row copy its first bytes again).
+constexpr int kLightWaveLds = 20480;  // LDS bytes per wavefront (two workgroups per CU)
+template <int NCI>
+constexpr int light_ring_rows() {
+    return kLightWaveLds / ((NCI + 1) * 1024) < 8 ? kLightWaveLds / ((NCI + 1) * 1024) : 8;
+}
+
+// s_waitcnt vmcnt(N * later) for a runtime later in [0, MAXL]
+template <int N, int MAXL>
+__device__ inline void wait_rows(int later) {
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) { wait_vmcnt<N * MAXL>(); return; }
+        wait_rows<N, MAXL - 1>(later);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// One light item with exactly NT tokens.  SPLIT = 1: one wavefront takes all its
+// rows.  SPLIT = 4: the four wavefronts of the workgroup take rows w, w + 4, ...
+// each with its own online softmax, then wavefronts 1..3 leave their partials
+// (unnormalised row, running max and sum per token) in their own ring and
+// wavefront 0 merges them: M = max_w m_w, o = sum_w e^(m_w - M) acc_w / sum_w
+// e^(m_w - M) l_w.  Long items thus run four times as many rows in parallel.
+template <int NCI, int VE, int NT, int SPLIT>
+__device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r0, int d, int w,
+                                           int lane, unsigned char *lds_all) {
+    int tok[NT];  // the item's tokens: sorted positions p0 .. p0 + NT - 1
+#pragma unroll
+    for (int q = 0; q < NT; ++q) tok[q] = a.perm[p0 + q];
+    constexpr int LR = light_ring_rows<NCI>();
+    constexpr int SLOT = (NCI + 1) * 1024;
+    unsigned char *const ring = lds_all + w * kLightWaveLds;
+    const uint32_t ring0 = lds_addr(ring);
+    const int64_t d_in = a.d_in, d_emb = a.d_emb;
+    const int wr = SPLIT == 1 ? 0 : w;                      // this wavefront's first row
+    const int nr = wr < d ? (d - wr + SPLIT - 1) / SPLIT : 0;  // and its number of rows
     uint4 xv[NT][NCI];
 #pragma unroll
     for (int q = 0; q < NT; ++q)
@@ -121,6 +165,26 @@ __device__ __forceinline__ void light_item(const LightArgs &a, const int (&tok)[
                            ? *reinterpret_cast<const uint4 *>(a.x + (int64_t)tok[q] * d_in + col)
                            : make_uint4(0, 0, 0, 0);
         }
+    // Take delivery of x before any copy is in flight: the compiler's own wait for
+    // these loads would otherwise also wait for every copy (it does not count them).
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int c = 0; c < NCI; ++c)
+            __asm__ volatile("" ::"v"(xv[q][c].x), "v"(xv[q][c].y), "v"(xv[q][c].z), "v"(xv[q][c].w));
+    const int kcol = lane * 8;
+    const int vcol = lane * 8 < d_emb ? lane * 8 : 0;
+    // local row j of this wavefront is row wr + SPLIT j of the item
+    auto issue = [&](int j) {
+        const uint32_t slot = ring0 + (uint32_t)((j % LR) * SLOT);
+        const int64_t row = r0 + wr + (int64_t)SPLIT * j;
+        const uint16_t *krow = a.WK + row * d_in;
+        static_for<NCI>([&](auto c) {
+            const int64_t col = c * 512 + kcol;
+            async_ld16_o<c * 1024>(krow + (col < d_in ? col : 0), slot);
+        });
+        async_ld16_o<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
+    };
     float m[NT], l[NT], acc[NT][VE];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
@@ -129,26 +193,22 @@ __device__ __forceinline__ void light_item(const LightArgs &a, const int (&tok)[
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[q][e] = 0.f;
     }
-    const uint16_t *kp = a.WK + r0 * d_in + lane * 8;
-    const uint16_t *vp = a.WV + r0 * a.d_emb + lane * VE;
-    uint4 kv[NCI];
-    float vv[VE];
+    for (int j = 0; j < LR && j < nr; ++j) issue(j);
+    for (int j = 0; j < nr; ++j) {
+        // rows issued after row j: min(nr, j + LR) - j - 1
+        wait_rows<NCI + 1, LR - 1>(min(nr, j + LR) - j - 1);
+        __asm__ volatile("" ::: "memory");
+        const unsigned char *sl = ring + (j % LR) * SLOT;
+        uint4 kv[NCI];
 #pragma unroll
-    for (int c = 0; c < NCI; ++c)
-        kv[c] = (c * 512 + lane * 8 < d_in) ? *reinterpret_cast<const uint4 *>(kp + c * 512)
-                                            : make_uint4(0, 0, 0, 0);
-    load_v<VE>(vp, vv);
-    for (int64_t r = 0; r < d; ++r) {
-        // prefetch the next row while this one is reduced
-        uint4 kn[NCI];
-        float vn[VE];
-        if (r + 1 < d) {
-            const uint16_t *kq = kp + (r + 1) * d_in;
-#pragma unroll
-            for (int c = 0; c < NCI; ++c)
-                kn[c] = (c * 512 + lane * 8 < d_in) ? *reinterpret_cast<const uint4 *>(kq + c * 512)
-                                                    : make_uint4(0, 0, 0, 0);
-            load_v<VE>(vp + (r + 1) * a.d_emb, vn);
+        for (int c = 0; c < NCI; ++c) kv[c] = *reinterpret_cast<const uint4 *>(sl + c * 1024 + lane * 16);
+        float vv[VE];
+        load_v<VE>(reinterpret_cast<const uint16_t *>(sl + NCI * 1024) + lane * VE, vv);
+        if (j + LR < nr) {
+            // the slot is refilled only after this wavefront's reads of it are done
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __asm__ volatile("" ::: "memory");
+            issue(j + LR);
         }
         float s[NT];
 #pragma unroll
@@ -175,61 +235,134 @@ __device__ __forceinline__ void light_item(const LightArgs &a, const int (&tok)[
             for (int e = 0; e < VE; ++e) acc[q][e] = fmaf(p, vv[e], acc[q][e] * al);
             m[q] = mn;
         }
-        if (r + 1 < d) {
-#pragma unroll
-            for (int c = 0; c < NCI; ++c) kv[c] = kn[c];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) vv[e] = vn[e];
-        }
     }
+    if constexpr (SPLIT == 1) {
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {
-        const float inv = 1.f / l[q];
-        float r[VE];
+        for (int q = 0; q < NT; ++q) {
+            const float inv = 1.f / l[q];
+            float r[VE];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) r[e] = acc[q][e] * inv;
-        store_o<VE>(a.o + (int64_t)tok[q] * a.d_emb + lane * VE, r);
+            for (int e = 0; e < VE; ++e) r[e] = acc[q][e] * inv;
+            store_o<VE>(a.o + (int64_t)tok[q] * d_emb + lane * VE, r);
+        }
+        // the ring is reused by the next item's copies only after these reads: every
+        // read above was waited for (lgkmcnt) before its value was used
+    } else {
+        // partials in the wavefront's own ring (every copy into it has been consumed):
+        // token q's row at float 64 VE q, then (m, l) pairs after the last row
+        constexpr int ML = NT * 64 * VE;
+        static_assert((ML + 2 * NT) * 4 <= kLightWaveLds, "merge area");
+        if (w > 0) {
+            float *pa = reinterpret_cast<float *>(ring);
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) pa[q * 64 * VE + lane * VE + e] = acc[q][e];
+                if (lane == 0) {
+                    pa[ML + 2 * q] = m[q];
+                    pa[ML + 2 * q + 1] = l[q];
+                }
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // wavefront 0 always holds row 0, so M is finite; a wavefront without rows
+            // left m = -inf, l = 0, acc = 0, which weigh nothing
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+                float M = m[q];
+#pragma unroll
+                for (int v = 1; v < 4; ++v)
+                    M = fmaxf(M, reinterpret_cast<const float *>(lds_all + v * kLightWaveLds)[ML + 2 * q]);
+                const float a0 = __expf(m[q] - M);
+                float L = l[q] * a0, r[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) r[e] = acc[q][e] * a0;
+#pragma unroll
+                for (int v = 1; v < 4; ++v) {
+                    const float *pv = reinterpret_cast<const float *>(lds_all + v * kLightWaveLds);
+                    const float wv = __expf(pv[ML + 2 * q] - M);
+                    L = fmaf(pv[ML + 2 * q + 1], wv, L);
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) r[e] = fmaf(wv, pv[q * 64 * VE + lane * VE + e], r[e]);
+                }
+                const float inv = 1.f / L;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) r[e] *= inv;
+                store_o<VE>(a.o + (int64_t)tok[q] * d_emb + lane * VE, r);
+            }
+        }
+        __syncthreads();  // the rings are refilled only after wavefront 0 has read them
     }
 }
 
-template <int NCI>
-constexpr int light_tokens_for() { return NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3); }
-
-template <int NCI, int VE>
-__global__ __launch_bounds__(256) void k_attn_light_bf16(LightArgs a) {
+template <int NCI, int VE, int SPLIT>
+__device__ __forceinline__ void light_item_nt(const LightArgs &a, int p0, int64_t r0, int d, int nt,
+                                              int w, int lane, unsigned char *lds) {
     constexpr int TL = light_tokens_for<NCI>();
+    switch (nt) {
+        case 1: light_item<NCI, VE, 1, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 3: if constexpr (TL >= 3) light_item<NCI, VE, 3, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 4: if constexpr (TL >= 4) light_item<NCI, VE, 4, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 5: if constexpr (TL >= 5) light_item<NCI, VE, 5, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 6: if constexpr (TL >= 6) light_item<NCI, VE, 6, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 7: if constexpr (TL >= 7) light_item<NCI, VE, 7, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 8: if constexpr (TL >= 8) light_item<NCI, VE, 8, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        default: break;
+    }
+}
+
+// Light items, persistent workgroups (the ones that fit on the chip at once) in two
+// phases.  The work list gives the items of blocks with >= kLightLongRows rows, then
+// those with >= kLightMidRows (both in items_long), then the rest (items).  Phase 1:
+// a workgroup per long item, its four wavefronts splitting the rows.  Phase 2: a
+// wavefront per item, each walking its own items without waiting for the others.
+// Both hand items out in snake order (index g in even rounds, count - 1 - g in odd
+// ones), so the longest start first and each share mixes long and short ones.
+// (Handing items out through per-XCD atomic counters measured 2.6 times slower: the
+// counters serialise thousands of short items.)
+template <int NCI, int VE>
+__global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kLightWaveLds];
     const int lane = threadIdx.x & 63;
-    const int nw = gridDim.x * 4;
-    const int nitems = a.hdr[HDR_NLIGHT];
-    for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < nitems; it += nw) {
-        const int4 item = a.items[it];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nlong = a.items_long ? a.hdr[HDR_NLIGHT_LONG] : 0;
+    const int nmid = a.items_long ? a.hdr[HDR_NLIGHT_MID] : 0;
+    const int ncoop = nlong + nmid, nitems = ncoop + a.hdr[HDR_NLIGHT];
+    auto item_at = [&](int it) {
+        return it < nlong ? a.items_long[it]
+                          : (it < ncoop ? a.items_long[a.cap - 1 - (it - nlong)] : a.items[it - ncoop]);
+    };
+    const int nb = gridDim.x;
+    for (int k = 0;; ++k) {
+        const int it = k * nb + ((k & 1) ? nb - 1 - blockIdx.x : blockIdx.x);
+        if (it >= ncoop) break;
+        const int4 item = item_at(it);  // a valid ID with >= kLightMidRows rows
+        const int p0 = __builtin_amdgcn_readfirstlane(item.x);
+        const int nt = __builtin_amdgcn_readfirstlane(item.y);
+        light_item_nt<NCI, VE, 4>(a, p0, __builtin_amdgcn_readfirstlane(item.z),
+                                  __builtin_amdgcn_readfirstlane(item.w), nt, w, lane, lds);
+    }
+    const int nw = gridDim.x * 4, g = blockIdx.x * 4 + w;
+    for (int k = 0;; ++k) {
+        const int it = ncoop + k * nw + ((k & 1) ? nw - 1 - g : g);
+        if (it >= nitems) break;
+        const int4 item = item_at(it);
         const int p0 = __builtin_amdgcn_readfirstlane(item.x);
         const int nt = __builtin_amdgcn_readfirstlane(item.y);
         const int64_t r0 = __builtin_amdgcn_readfirstlane(item.z);
         const int d = __builtin_amdgcn_readfirstlane(item.w);
-        int tok[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) tok[q] = q < nt ? a.perm[p0 + q] : 0;
-        if (d < 0) {  // ID out of range: the flag is set, the row is zeroed
+        if (d < 0) {  // ID out of range: the flag is set, the rows are zeroed
             for (int q = 0; q < nt; ++q) {
                 float z[VE];
 #pragma unroll
                 for (int e = 0; e < VE; ++e) z[e] = 0.f;
-                store_o<VE>(a.o + (int64_t)tok[q] * a.d_emb + lane * VE, z);
+                store_o<VE>(a.o + (int64_t)a.perm[p0 + q] * a.d_emb + lane * VE, z);
             }
             continue;
         }
-        switch (nt) {
-            case 1: light_item<NCI, VE, 1>(a, tok, r0, d, lane); break;
-            case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2>(a, tok, r0, d, lane); break;
-            case 3: if constexpr (TL >= 3) light_item<NCI, VE, 3>(a, tok, r0, d, lane); break;
-            case 4: if constexpr (TL >= 4) light_item<NCI, VE, 4>(a, tok, r0, d, lane); break;
-            case 5: if constexpr (TL >= 5) light_item<NCI, VE, 5>(a, tok, r0, d, lane); break;
-            case 6: if constexpr (TL >= 6) light_item<NCI, VE, 6>(a, tok, r0, d, lane); break;
-            case 7: if constexpr (TL >= 7) light_item<NCI, VE, 7>(a, tok, r0, d, lane); break;
-            case 8: if constexpr (TL >= 8) light_item<NCI, VE, 8>(a, tok, r0, d, lane); break;
-            default: break;
-        }
+        light_item_nt<NCI, VE, 1>(a, p0, r0, d, nt, w, lane, lds);
     }
 }
 
@@ -875,15 +1008,18 @@ hipError_t launch_heavy(const HeavyArgs &ha, int64_t d_emb, hipStream_t s) {
     }
 }
 
-constexpr int kAttnBlocks = 4096;  // enough wavefronts for one light item each at 32768 tokens
+constexpr int kAttnBlocks = 4096;  // fp32 path: enough wavefronts for one token each at 32768 tokens
+// Light kernel: persistent, the workgroups that fit on the chip at once (two per CU:
+// 80 KB of LDS rings each)
+constexpr int kLightBlocks = 512;
 
 template <int NCI>
 hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
     switch (d_emb / 64) {
-        case 1: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 1>), dim3(kAttnBlocks), dim3(256), 0, s, la); break;
-        case 2: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 2>), dim3(kAttnBlocks), dim3(256), 0, s, la); break;
-        case 4: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 4>), dim3(kAttnBlocks), dim3(256), 0, s, la); break;
-        case 8: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 8>), dim3(kAttnBlocks), dim3(256), 0, s, la); break;
+        case 1: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 1>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+        case 2: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 2>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+        case 4: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 4>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+        case 8: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 8>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1137,7 +1273,7 @@ hipError_t launch_attn_light(const AttnArgs &a, int dtype, hipStream_t s) {
     }
     LightArgs la{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
                  a.uniq, a.seg_start, a.perm, a.hdr, a.light, a.d_in, a.d_emb, (int32_t)a.vocab,
-                 (uint16_t *)a.o};
+                 (uint16_t *)a.o, a.light_long, (int)a.n};
     const int64_t nci = (a.d_in + 511) / 512;
     if (nci <= 1) return launch_light_nci<1>(la, a.d_emb, s);
     if (nci <= 2) return launch_light_nci<2>(la, a.d_emb, s);

@@ -140,6 +140,7 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     b.counts = ws_ptr<int32_t>(ws, L.counts);
     b.seg_start = ws_ptr<int32_t>(ws, L.seg_start);
     int4 *light = ws_ptr<int4>(ws, L.light);
+    int4 *light_long = ws_ptr<int4>(ws, L.light_long);
     int2 *heavy = ws_ptr<int2>(ws, L.heavy);
     int2 *dense = ws_ptr<int2>(ws, L.dense);
     void *o = ws_ptr<char>(ws, L.o);
@@ -174,7 +175,7 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         } else {
             L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));  // clears the header too
             L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
-                                       heavy, dense, s));
+                                       heavy, dense, s, D.dtype == L3_BF16 ? light_long : nullptr));
         }
     }
     {
@@ -182,7 +183,7 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         a.x = x; a.WK = WK; a.WV = WV; a.off = P.d_off;
         a.uniq = b.uniq; a.seg_start = b.seg_start; a.perm = b.perm; a.hdr = b.hdr;
         a.queue = b.hdr + HDR_QUEUE;
-        a.light = light; a.heavy = heavy; a.dense = dense;
+        a.light = light; a.light_long = light_long; a.heavy = heavy; a.dense = dense;
         a.n = n; a.d_in = D.d_in; a.d_emb = D.d_emb; a.vocab = P.vocab;
         a.o = o; a.scores = ws_ptr<float>(ws, L.scores); a.max_d = P.max_d;
         if (heavy_min != INT32_MAX) {
@@ -458,6 +459,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.counts = take(n * 4);
     L.seg_start = take((n + 1) * 4);
     L.light = take(n * 16);
+    L.light_long = take(d.dtype == L3_BF16 ? n * 16 : 0);
     L.heavy = take(n * 8);
     L.dense = take(n * 8);
     L.scores = take(d.dtype == L3_F32 ? (size_t)n * std::max(max_d, 1) * 4 : 0);

@@ -35,8 +35,15 @@ constexpr int kDenseMinD = 64;     // ... and at least this many (a dense item's
 
 // Workspace header (int32 words), zeroed at the start of every call.
 enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4, HDR_NKV = 5,
-       HDR_NSPLIT = 6,
-       HDR_QUEUE = 8, HDR_WORDS = 64 };
+       HDR_NSPLIT = 6, HDR_NLIGHT_LONG = 7,
+       HDR_QUEUE = 8,           // 8 per-XCD counters of the matrix-core gather, then its dense counter
+       HDR_NLIGHT_MID = 17,
+       HDR_WORDS = 64 };
+// Light items of blocks with at least kLightLongRows rows, then those with at least
+// kLightMidRows, are listed apart and taken first, so the longest start first: the
+// former from the front of the light_long region, the latter from its back.
+constexpr int kLightLongRows = 32;
+constexpr int kLightMidRows = 16;
 
 struct Dims {
     int64_t d_in, d_emb, d_up, d_out;
@@ -47,7 +54,7 @@ struct Dims {
 // Byte offsets of the workspace regions for n_max tokens.
 struct WsLayout {
     size_t hdr, keys_a, vals_a, keys_b, vals_b, rank, hist, tile_cnt;
-    size_t inv_perm, uniq, counts, seg_start, light, heavy, dense;
+    size_t inv_perm, uniq, counts, seg_start, light, light_long, heavy, dense;
     size_t scores;  // fp32 path only: n x max_d
     size_t o, h, lnp;
     size_t stats;  // LayerNorm row statistics (mean, rstd)
@@ -86,10 +93,14 @@ hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs 
 // Blocks go to the dense list (>= dense_min_tokens tokens, kDenseMinD <= d_t <= kDenseMaxD, items of
 // kDenseTile tokens), else the heavy list (>= heavy_min_tokens tokens or >= kHeavyMinRows
 // rows, items of kHeavyTile tokens), else the light list (items of light_tokens tokens,
-// written out as {first sorted position, tokens, first row, d_t (-1: ID out of range)}).
+// written out as {first sorted position, tokens, first row, d_t (-1: ID out of range)});
+// with light_long non-null (n entries), light items of blocks with >= kLightLongRows rows
+// go to light_long from the front (count in HDR_NLIGHT_LONG) and those with >=
+// kLightMidRows from its back, entry n - 1 first (count in HDR_NLIGHT_MID).
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
                            int heavy_min_tokens, int dense_min_tokens, int light_tokens,
-                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s);
+                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s,
+                           int4 *light_long = nullptr);
 // The header zeroing, the route and the work lists of a batch of 1 .. kRouteSmallMax
 // tokens in one single-workgroup launch (same outputs; sorted keys and permutation
 // in keys_a / vals_a).
@@ -133,7 +144,7 @@ struct AttnArgs {
     const int64_t *off;
     const int32_t *uniq, *seg_start, *perm, *hdr;
     int32_t *queue;  // per-XCD work counters of the MFMA path (in the header)
-    const int4 *light;
+    const int4 *light, *light_long;  // light items (short blocks), then those of long blocks
     const int2 *heavy, *dense;
     int64_t n, d_in, d_emb, vocab;
     void *o;

@@ -292,7 +292,8 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
                                                   int4 *__restrict__ light,
                                                   int2 *__restrict__ heavy,
                                                   int2 *__restrict__ dense,
-                                                  int32_t *__restrict__ hdr) {
+                                                  int32_t *__restrict__ hdr,
+                                                  int4 *__restrict__ light_long, int nmax) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int m = hdr[HDR_NSEG];
     const int lane = threadIdx.x & 63;
@@ -305,24 +306,42 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
         t = uniq[j];
         bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
     }
-    const int nl = bi.nl, nh = bi.nh, nd = bi.nd;
-    // wave-inclusive scans of nl, nh and nd
-    int sl = nl, sh = nh, sd = nd;
+    // light items of long blocks go to their own lists (when there are any): the longest
+    // to the front of light_long, the next longest to its back
+    const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
+    const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
+    const int nl = (lng || mid) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0;
+    const int nh = bi.nh, nd = bi.nd;
+    // wave-inclusive scans of nl, nq, nm, nh and nd
+    int sl = nl, sq = nq, sm = nm, sh = nh, sd = nd;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(sl, o), b = __shfl_up(sh, o), c = __shfl_up(sd, o);
-        if (lane >= o) { sl += a; sh += b; sd += c; }
+        const int a = __shfl_up(sl, o), e = __shfl_up(sq, o), f = __shfl_up(sm, o),
+                  b = __shfl_up(sh, o), c = __shfl_up(sd, o);
+        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; sd += c; }
     }
-    int bl = 0, bh = 0, bd = 0;
+    int bl = 0, bq = 0, bm = 0, bh = 0, bd = 0;
     if (lane == 63) {
         if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
+        if (sq) bq = atomicAdd(&hdr[HDR_NLIGHT_LONG], sq);
+        if (sm) bm = atomicAdd(&hdr[HDR_NLIGHT_MID], sm);
         if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
         if (sd) bd = atomicAdd(&hdr[HDR_NDENSE], sd);
     }
     bl = __shfl(bl, 63) + sl - nl;
+    bq = __shfl(bq, 63) + sq - nq;
+    bm = __shfl(bm, 63) + sm - nm;
     bh = __shfl(bh, 63) + sh - nh;
     bd = __shfl(bd, 63) + sd - nd;
-    write_items(bi, j, sb, S, t < vocab, light_tok, bl, bh, bd, light, heavy, dense);
+    if (mid) {
+        // from the back of light_long: entries n - 1 - bm, n - 2 - bm, ...
+        for (int q = 0; q < bi.nl; ++q)
+            light_long[nmax - 1 - (bm + q)] =
+                make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), bi.r0, bi.d);
+        bi.nl = 0;
+    }
+    write_items(bi, j, sb, S, t < vocab, light_tok, lng ? bq : bl, bh, bd, lng ? light_long : light,
+                heavy, dense);
 }
 
 // Block-wide exclusive scan over kSmallThreads threads (one int32 each); the total
@@ -518,10 +537,10 @@ hipError_t launch_route_small_split(const int32_t *ids, int64_t n, int64_t vocab
 
 hipError_t launch_worklist(const RouteBufs &b, int64_t n, const int64_t *off, int64_t vocab,
                            int heavy_min_tokens, int dense_min_tokens, int light_tokens,
-                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s) {
+                           int4 *light, int2 *heavy, int2 *dense, hipStream_t s, int4 *light_long) {
     hipLaunchKernelGGL(k_worklist, dim3(blocks_for(n, 256)), dim3(256), 0, s, b.uniq, b.seg_start,
                        b.counts, off, (int)vocab, heavy_min_tokens, dense_min_tokens, light_tokens,
-                       light, heavy, dense, b.hdr);
+                       light, heavy, dense, b.hdr, light_long, (int)n);
     return hipGetLastError();
 }
 
