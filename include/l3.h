@@ -82,7 +82,9 @@ typedef struct {
 const char *l3_strerror(int status);
 
 /*
- * l3_plan -- validate an allocation and upload its CSR offsets.
+ * l3_plan -- validate an allocation and upload its CSR offsets (the allocation D
+ * is fixed, each token ID owning between 1 and k embeddings and v in all:
+ * papernotes.org page, section 关键设计 item 2).
  * offsets: host, vocab + 1 int64 entries; off[0] = 0, 1 <= off[t+1]-off[t] <= k,
  *          off[vocab] = v (the allocation bounds of the pages: every token gets
  *          at least one and at most k embeddings, budget v = sum d_t).
@@ -213,7 +215,9 @@ int l3_backward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t
                 float *dW_mix, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * l3_route -- the batch sort alone (what l3_forward does first).
+ * l3_route -- the batch sort alone (what l3_forward does first): the batch sorted
+ * by token ID so that each ID's tokens form one block and the attention pattern is
+ * block diagonal (sciencestack.ai page, Fig. 3 caption).
  * Sorting is stable: tokens with equal IDs keep their batch order.  IDs outside
  * [0, vocab) sort as the key `vocab` after every valid ID and set the flag.
  * Outputs (dev int32, caller-allocated; any may be NULL to skip):

@@ -43,5 +43,32 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+# Host-side checking build: the sources whose host code handles caller input (plan and
+# argument validation, workspace sizing, the prefetch's distinct-ID remap, the LZW
+# allocation trie) are compiled again with AddressSanitizer and UndefinedBehaviorSanitizer
+# on their host code only, and linked with the regular objects of the other sources.
+# The result is loaded by a process with the clang ASan runtime preloaded.
+SANITIZED = ["l3_api.hip", "alloc.hip"]
+HOST_SAN_LIB = os.path.join(BUILD, "libl3_hostsan.so")
+HOST_SAN_FLAGS = ["-g", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(jobs: int = 4) -> str:
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        build(jobs)
+    san = {s: os.path.join(BUILD, "hostsan_" + s.replace(".hip", ".o")) for s in SANITIZED}
+    cmds = [[HIPCC, *FLAGS, *HOST_SAN_FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in san.items()]
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(_run, cmds))
+    link = [san.get(s, o) for s, o in zip(SOURCES, objs)]
+    tmp = HOST_SAN_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, "-o", tmp])
+    os.replace(tmp, HOST_SAN_LIB)
+    return HOST_SAN_LIB
+
+
 if __name__ == "__main__":
     print(build())
