@@ -62,6 +62,9 @@ def parse():
                          "benchmark and of --copy-probe) into profiles/<stage>_<workload>_"
                          "counters.json, then exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size the copy probe ran with")
+    ap.add_argument("--ingest-mfma", metavar="MFMA_CSV",
+                    help="turn a rocprofv3 --pmc CSV of the MFMA counters into "
+                         "profiles/<stage>_<workload>_mfma.json, then exit")
     args = ap.parse_args()
     args.steps_given = args.steps is not None
     if args.steps is None:
@@ -119,6 +122,63 @@ def read_counter_csv(path: str, counter: str):
             name = name.split("(")[0]
             per.setdefault(name, []).append(float(r["Counter_Value"]))
     return per
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def ingest_mfma(args):
+    """MFMA utilisation of the two GEMM stages from one rocprofv3 --pmc run of
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: per
+    dispatch, bf16 MFMA FLOP = MOPS x 512, busy fraction = busy cycles summed over the
+    SIMDs / (GUI-active cycles per XCD x SIMDs), clock = GUI-active cycles per XCD /
+    dispatch duration.  Means over the dispatches go to profiles/<stage>_<workload>_mfma.json."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(args.ingest_mfma)):
+        name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "")
+        name = (name[5:] if name.startswith("void ") else name).split("(")[0]
+        key = (name, r["Dispatch_Id"])
+        d = per.setdefault(key, {"dur_ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    stages = {}
+    for (name, _), d in per.items():
+        st = next((s_ for p_, s_ in STAGE_OF_KERNEL if name.startswith(p_)), None)
+        if st not in ("w_up_gemm", "w_mix_gemm") or not all(c in d for c in MFMA_COUNTERS):
+            continue
+        gui = d["GRBM_GUI_ACTIVE"] / XCDS
+        stages.setdefault(st, []).append({
+            "flop": d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+            "busy": d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS),
+            "clock_ghz": gui / d["dur_ns"], "dur_us": d["dur_ns"] / 1e3, "kernel": name})
+    for st, rows in stages.items():
+        out = {"stage": st, "workload": args.workload,
+               "source_sha256_16": src_hash(KERNEL_SOURCES[st]), "kernel": rows[0]["kernel"],
+               "dispatches": len(rows),
+               "mfma_flop_per_launch": float(np.mean([r["flop"] for r in rows])),
+               "mfma_busy_fraction": float(np.mean([r["busy"] for r in rows])),
+               "clock_ghz": float(np.median([r["clock_ghz"] for r in rows])),
+               "duration_us_mean": float(np.mean([r["dur_us"] for r in rows])),
+               "commands": [" ".join(sys.argv)]}
+        path = os.path.join(ROOT, "profiles", f"{st}_{args.workload}_mfma.json")
+        json.dump(out, open(path, "w"), indent=1)
+        print(f"{path}: busy {out['mfma_busy_fraction']:.3f}, {out['mfma_flop_per_launch'] / 1e9:.2f} "
+              f"GFLOP, clock {out['clock_ghz']:.2f} GHz")
+
+
+def mfma_from_profiles(stage: str, workload: str):
+    """The counter-based MFMA figures of a GEMM stage, if taken on the current source."""
+    p = os.path.join(ROOT, "profiles", f"{stage}_{workload}_mfma.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != src_hash(KERNEL_SOURCES[stage]):
+        return None
+    return {"busy_fraction": d["mfma_busy_fraction"], "flop_per_launch": d["mfma_flop_per_launch"],
+            "clock_ghz": d["clock_ghz"],
+            "source": f"profiles/{stage}_{workload}_mfma.json (rocprofv3 counters)"}
 
 
 def ingest_counters(args):
@@ -182,6 +242,9 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(args)
+        return
+    if args.ingest_mfma:
+        ingest_mfma(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -306,6 +369,8 @@ def main():
         v_["frac"] = v_["achieved"] / v_["peak"]
         v_["ms"] = avg[k_]
         v_["traffic"] = traffic_from_profiles(k_, cfg.name)
+    for k_ in ("w_up_gemm", "w_mix_gemm"):
+        kernels[k_]["mfma_counters"] = mfma_from_profiles(k_, cfg.name)
     # the dominant single kernel (longest average launch)
     dominant = max(("gather_mfma", "gather_light", "w_up_gemm", "w_mix_gemm"), key=lambda s_: avg[s_])
     roof = {k_: kernels[dominant][k_] for k_ in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
@@ -701,9 +766,33 @@ def cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, seconds):
         spent += time.perf_counter() - t
         done += len(rows)
         chunk = min(chunk * 2, 1024)
+    # one thread, a seeded 512-token sample (the first tokens of the same permutation)
+    rows = order[:512]
+    u, inv = np.unique(ids[rows], return_inverse=True)
+    dd = off[u + 1] - off[u]
+    coff = np.concatenate([[0], np.cumsum(dd)]).astype(np.int64)
+    sel = np.concatenate([np.arange(off[t], off[t + 1]) for t in u])
+    xs, wk, wv = f32(x[rows]), f32(WK[sel]), f32(WV[sel])
+    t = time.perf_counter()
+    oracle.forward(coff, cfg.k, xs, inv.astype(np.int32), wk, wv, Wup64, g, b, Wmix64,
+                   eps=cfg.ln_eps, nthreads=1)
+    one = len(rows) / (time.perf_counter() - t)
     return {"value": done / spent, "unit": "tokens/s", "cores": nt, "kind": "oracle",
             "sample": f"{done} tokens drawn (seeded) from the {cfg.name} batch, tables cut to "
-                      f"their rows; {spent:.1f}s of oracle time on {nt} threads"}
+                      f"their rows; {spent:.1f}s of oracle time on {nt} threads",
+            "single_thread": {"value": one, "unit": "tokens/s",
+                              "sample": "512 tokens of the same seeded draw, 1 thread"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def synth_f32(a):
