@@ -345,11 +345,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
                     pk[j & (LN_OUT ? NJ - 1 : 0)][0] = pack2(acc[i][j][0], acc[i][j][1]);
                     pk[j & (LN_OUT ? NJ - 1 : 0)][1] = pack2(acc[i][j][2], acc[i][j][3]);
                 }
-                if (FULL || (m < p.M && n < p.N)) {
+                if (OUT != 3 && (FULL || (m < p.M && n < p.N))) {
                     if constexpr (OUT == 0) {
                         *reinterpret_cast<uint2 *>(p.C + m * p.N + n) =
                             make_uint2(pk[j & (LN_OUT ? NJ - 1 : 0)][0], pk[j & (LN_OUT ? NJ - 1 : 0)][1]);
-                    } else {
+                    } else if constexpr (OUT != 3) {
                         float4 *dst = reinterpret_cast<float4 *>(p.Cf + m * p.N + n);
                         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
                         if constexpr (OUT == 2) {
@@ -360,12 +360,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
                     }
                 }
             }
-            if constexpr (LN_OUT && OUT == 0) {
-                // partial statistics of this row's stored (bf16) values over each 64
-                // columns (4 blocks of 16)
+            if constexpr (LN_OUT && (OUT == 0 || OUT == 3)) {
+                // partial statistics over each 64 columns (4 blocks of 16) of this row's
+                // stored (bf16) values, or with no output (OUT 3) of the fp32 values
                 auto stored = [&](int j, int e) {
-                    const uint32_t w2 = pk[j][e >> 1];
-                    const float v = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                    float v;
+                    if constexpr (OUT == 3) {
+                        v = acc[i][j][e];
+                    } else {
+                        const uint32_t w2 = pk[j][e >> 1];
+                        v = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                    }
                     if constexpr (FULL) return v;
                     const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
                     return n < p.N ? v : 0.f;
@@ -599,6 +604,116 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
     } else {
         hipLaunchKernelGGL((k_gemm_bf16<false, false>), grid, dim3(256), 0, s, p);
     }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- factored W_mix
+//
+// With h = W_up o, LayerNorm's centred row is h - mean(h) 1 = W_c o, where W_c is W_up
+// with each column's mean over the rows taken away (mean(h) = wbar . o, wbar the
+// column means), and W_mix [LN(h) ; x] = W1 diag(gamma) (h - mean) rstd + W1 beta + W2 x
+//   = rstd * (F o) + c2 + W2 x,   F = W1 diag(gamma) W_c  (d_out x d_emb),  c2 = W1 beta.
+// So the W_mix GEMM runs over [o | x] (K = d_emb + d_in) instead of [h | x]
+// (K = d_up + d_in), and h itself is needed only for its row statistics: the W_up
+// GEMM computes them from its fp32 accumulators and stores nothing.  F is formed
+// per call from the weights: W_c^T (d_emb x d_up, bf16: W_up transposed, each row
+// less its mean), then F^T = W_c^T W1'^T on the small-M GEMM (W1' = W1 diag(gamma)
+// from k_mix_fold), then its transpose.  Centring first means no mean * (row sum) term is subtracted
+// later, so a large mean cancels nothing in bf16.
+
+// W_up^T [d_emb x d_up] (bf16, from the transpose) centred in place: one wavefront
+// per row c subtracts the row's mean (the mean of W_up's column c) and rounds to bf16;
+// lanes take 8 consecutive elements at a time (cols is a multiple of 64).  The first
+// workgroup also zeroes `zero` [nz] (the factored GEMM's mean coefficients).
+__global__ __launch_bounds__(256) void k_center_rows(uint16_t *__restrict__ WT, int64_t rows, int64_t cols,
+                                                     float *__restrict__ zero, int64_t nz) {
+    if (blockIdx.x == 0)
+        for (int64_t i = threadIdx.x; i < nz; i += 256) zero[i] = 0.f;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    uint4 *row = reinterpret_cast<uint4 *>(WT + r * cols);
+    const int64_t nv = cols / 8;
+    float sum = 0.f;
+    for (int64_t c = lane; c < nv; c += 64) {
+        const uint4 u = row[c];
+        sum += ((bf_lo(u.x) + bf_hi(u.x)) + (bf_lo(u.y) + bf_hi(u.y))) +
+               ((bf_lo(u.z) + bf_hi(u.z)) + (bf_lo(u.w) + bf_hi(u.w)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    const float mean = sum / (float)cols;
+    for (int64_t c = lane; c < nv; c += 64) {
+        const uint4 u = row[c];
+        row[c] = make_uint4(pack2(bf_lo(u.x) - mean, bf_hi(u.x) - mean), pack2(bf_lo(u.y) - mean, bf_hi(u.y) - mean),
+                            pack2(bf_lo(u.z) - mean, bf_hi(u.z) - mean), pack2(bf_lo(u.w) - mean, bf_hi(u.w) - mean));
+    }
+}
+
+hipError_t launch_gemm_stats_bf16(const uint16_t *A, const uint16_t *B, int64_t M, int64_t N, int64_t K,
+                                  float *ln_out, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    GemmP p = make_plain(A, B, nullptr, M, N, K);
+    p.ln_out = ln_out;
+    p.npart_out = (int)((N + kLnPart - 1) / kLnPart);
+    hipLaunchKernelGGL((k_gemm_bf16<false, true, 3, 8>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+    return hipGetLastError();
+}
+
+size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    return al((size_t)d_emb * 4) + al((size_t)d_emb * d_up * 2) + 2 * al((size_t)d_emb * d_out * 2) +
+           al((size_t)d_out * 4);
+}
+
+hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
+                             const float *beta, void *fold_ws, void *factor_ws, float *part,
+                             int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    char *f = static_cast<char *>(factor_ws);
+    uint16_t *wct = reinterpret_cast<uint16_t *>(f + al((size_t)d_emb * 4));
+    uint16_t *ft = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(wct) + al((size_t)d_emb * d_up * 2));
+    uint16_t *fm = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(ft) + al((size_t)d_emb * d_out * 2));
+    int32_t *zero = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(fm) + al((size_t)d_emb * d_out * 2));
+    // W_c^T: W_up transposed, then each row less its mean
+    hipError_t e = launch_transpose(W_up, d_emb, d_up, d_emb, wct, d_up, d_up, L3_BF16, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_center_rows, dim3((unsigned)((d_emb + 3) / 4)), dim3(256), 0, s, wct, d_emb, d_up,
+                       reinterpret_cast<float *>(zero), d_out);
+    e = launch_mix_fold(W_mix, gamma, beta, fold_ws, d_up, d_in, d_out, s);
+    if (e != hipSuccess) return e;
+    // F^T [d_emb x d_out] = W_c^T W1'^T (W1' is the fold's first region, d_out x d_up)
+    e = launch_gemm_skinny_bf16(wct, static_cast<const uint16_t *>(fold_ws), ft, d_emb, d_out, d_up, nullptr,
+                                part, s);
+    if (e != hipSuccess) return e;
+    return launch_transpose(ft, d_out, d_emb, d_out, fm, d_emb, d_emb, L3_BF16, s);
+}
+
+hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
+                                         const uint16_t *W_mix, uint16_t *out, const void *fold_ws,
+                                         const void *factor_ws, int64_t M, int64_t d_emb, int64_t d_up,
+                                         int64_t d_in, int64_t d_out, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const char *f = static_cast<const char *>(factor_ws);
+    const uint16_t *fm = reinterpret_cast<const uint16_t *>(
+        f + al((size_t)d_emb * 4) + al((size_t)d_emb * d_up * 2) + al((size_t)d_emb * d_out * 2));
+    const float *zero = reinterpret_cast<const float *>(reinterpret_cast<const char *>(fm) +
+                                                        al((size_t)d_emb * d_out * 2));
+    const float *c2 = reinterpret_cast<const float *>(static_cast<const char *>(fold_ws) +
+                                                      mix_fold_w1p_bytes(d_up, d_out)) + d_out;
+    GemmP p = make_plain(o, fm, out, M, d_out, d_emb + d_in);
+    p.lda = d_emb;
+    p.ldb = d_emb;
+    p.A2 = x;
+    p.lda2 = d_in;
+    p.B2 = W_mix + d_up;
+    p.ldb2 = d_up + d_in;
+    p.K1 = d_emb;
+    p.row_stats = stats;
+    p.c1 = zero;  // F acts on the centred row: no mean term
+    p.c2 = c2;
+    hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -226,24 +226,27 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
                                                    n, D.d_up, D.d_in, D.d_out, part, s));
         }
     } else if (D.dtype == L3_BF16) {
+        // W_mix factored through W_up (gemm.hip): h is formed only for its row statistics
         float *stats = ws_ptr<float>(ws, L.stats);
         void *fold = ws_ptr<char>(ws, L.fold);
+        void *factor = ws_ptr<char>(ws, L.factor);
         {
             StageTimer tm(3, s);
-            L3_HIP_TRY(launch_gemm_bf16((const uint16_t *)o, (const uint16_t *)W_up, (uint16_t *)h, n,
-                                        D.d_up, D.d_emb, lnp, s));
+            L3_HIP_TRY(launch_gemm_stats_bf16((const uint16_t *)o, (const uint16_t *)W_up, n, D.d_up, D.d_emb,
+                                              lnp, s));
         }
         {
             StageTimer tm(4, s);
             L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
-            L3_HIP_TRY(launch_mix_fold((const uint16_t *)W_mix, gamma, beta, fold, D.d_up, D.d_in,
-                                       D.d_out, s));
+            L3_HIP_TRY(launch_mix_factor((const uint16_t *)W_up, (const uint16_t *)W_mix, gamma, beta, fold,
+                                         factor, ws_ptr<float>(ws, L.part), D.d_emb, D.d_up, D.d_in,
+                                         D.d_out, s));
         }
         {
             StageTimer tm(5, s);
-            L3_HIP_TRY(launch_gemm_mix_bf16((const uint16_t *)h, (const uint16_t *)x, stats,
-                                            (const uint16_t *)W_mix, (uint16_t *)out, fold, n, D.d_up,
-                                            D.d_in, D.d_out, s));
+            L3_HIP_TRY(launch_gemm_mix_factored_bf16((const uint16_t *)o, (const uint16_t *)x, stats,
+                                                     (const uint16_t *)W_mix, (uint16_t *)out, fold, factor,
+                                                     n, D.d_emb, D.d_up, D.d_in, D.d_out, s));
         }
     } else {
         {
@@ -470,6 +473,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
     L.stats = take((size_t)n * 2 * 4);
     L.fold = take(d.dtype == L3_BF16 ? mix_fold_bytes(d.d_up, d.d_out) : 0);
+    L.factor = take(d.dtype == L3_BF16 && n > kSkinnyMaxM ? mix_factor_bytes(d.d_emb, d.d_up, d.d_out) : 0);
     const int64_t ns = std::min<int64_t>(n, kSkinnyMaxM);
     L.part = take(d.dtype == L3_BF16 ? std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
                                                  skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in))

@@ -59,6 +59,7 @@ struct WsLayout {
     size_t o, h, lnp;
     size_t stats;  // LayerNorm row statistics (mean, rstd)
     size_t fold;   // LayerNorm fold of W_mix (bf16 path)
+    size_t factor; // the factored W_mix's F and its temporaries (bf16, n > kSkinnyMaxM)
     size_t part;   // split-K partial slabs of the small-M path (bf16 path, n <= kSkinnyMaxM)
     // split-row gather-attention of small batches (split_slots() > 0): row-chunk
     // items, per-block {slot base, chunks, tokens, first sorted position}, each sorted
@@ -176,6 +177,21 @@ hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const floa
 hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const float *beta,
                            void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
+// Factored W_mix (batches of more than kSkinnyMaxM tokens): the W_up GEMM only for its
+// row statistics (ln_out partials from fp32 accumulators, no output), the factor
+// F = W1 diag(gamma) W_c of the centred W_up into factor_ws (mix_factor_bytes; the fold
+// terms into fold_ws; `part` holds the small-M GEMM's slabs, skinny_part_bytes(d_emb,
+// d_out, d_up)), and out = rstd * (F o) + c2 + W2 x.
+hipError_t launch_gemm_stats_bf16(const uint16_t *A, const uint16_t *B, int64_t M, int64_t N, int64_t K,
+                                  float *ln_out, hipStream_t s);
+size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out);
+hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
+                             const float *beta, void *fold_ws, void *factor_ws, float *part,
+                             int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
+hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
+                                         const uint16_t *W_mix, uint16_t *out, const void *fold_ws,
+                                         const void *factor_ws, int64_t M, int64_t d_emb, int64_t d_up,
+                                         int64_t d_in, int64_t d_out, hipStream_t s);
 // Decode staging: destination row r of the compact tables belongs to compact ID i
 // with coff[i] <= r < coff[i+1] and comes from table row src[i] + (r - coff[i]) of
 // the pinned host tables (device mappings WK_dev / WV_dev), or, for src[i] < 0, from
