@@ -29,11 +29,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16 MFMA
-# the library's timed stages (one kernel each, except route and mix_prep)
-STAGES = ["route", "gather_mfma", "gather_light", "w_up_gemm", "mix_prep", "w_mix_gemm"]
-KERNEL_SOURCES = {"gather_attention": "attn.hip", "gather_mfma": "attn.hip",
-                  "gather_light": "attn.hip", "w_up_gemm": "gemm.hip", "mix_prep": "gemm.hip",
-                  "w_mix_gemm": "gemm.hip", "route": "route.hip"}
+# the library's timed stages.  ln_stats_gemm: LayerNorm's row statistics, from the
+# quadratic form o^T G o (a GEMM against G = W_c^T W_c and a finalize) above 512 tokens,
+# from the W_up GEMM at or below; mix_prep: the weight-only factors F and G (above 512
+# tokens) or the split-K W_up (at or below).
+STAGES = ["route", "gather_mfma", "gather_light", "ln_stats_gemm", "mix_prep", "w_mix_gemm"]
+# the source files a stage's kernels come from (a counter summary holds while they hash
+# to the value recorded with it)
+KERNEL_SOURCES = {"gather_attention": ("attn.hip",), "gather_mfma": ("attn.hip",),
+                  "gather_light": ("attn.hip",), "ln_stats_gemm": ("gemm.hip",),
+                  "mix_prep": ("gemm.hip", "gemm_skinny.hip", "backward.hip"),
+                  "w_mix_gemm": ("gemm.hip",), "route": ("route.hip",)}
 
 
 def parse():
@@ -72,9 +78,12 @@ def parse():
     return args
 
 
-def src_hash(name: str) -> str:
-    p = os.path.join(ROOT, "static_token_routed_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def src_hash(names) -> str:
+    """sha256 (first 16 hex digits) of the named sources' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "static_token_routed_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(stage: str, workload: str):
@@ -102,8 +111,10 @@ def copy_probe(mib: int):
 
 # kernel name prefix -> stage of one forward
 STAGE_OF_KERNEL = [("k_attn_mfma", "gather_mfma"), ("k_attn_light", "gather_light"),
-                   ("k_gemm_bf16<false, true, 0,", "w_up_gemm"), ("k_gemm_bf16<true, false, 0,", "w_mix_gemm"),
-                   ("k_ln_finalize", "mix_prep"), ("k_mix_fold", "mix_prep"),
+                   ("k_gemm_bf16<false, false, 3,", "ln_stats_gemm"), ("k_ln_quad_finalize", "ln_stats_gemm"),
+                   ("k_gemm_bf16<true, false, 0,", "w_mix_gemm"),
+                   ("k_transpose", "mix_prep"), ("k_center_rows", "mix_prep"), ("k_mix_fold", "mix_prep"),
+                   ("k_gemm_skinny", "mix_prep"), ("k_skinny_reduce", "mix_prep"),
                    ("k_sort", "route"), ("k_scan", "route"), ("k_seg", "route"),
                    ("k_worklist", "route"), ("k_zero_i32", "route"), ("k_route_small", "route")]
 COMPOSITE = {"gather_attention": ("gather_mfma", "gather_light")}
@@ -146,7 +157,7 @@ def ingest_mfma(args):
     stages = {}
     for (name, _), d in per.items():
         st = next((s_ for p_, s_ in STAGE_OF_KERNEL if name.startswith(p_)), None)
-        if st not in ("w_up_gemm", "w_mix_gemm") or not all(c in d for c in MFMA_COUNTERS):
+        if st not in ("ln_stats_gemm", "w_mix_gemm") or not all(c in d for c in MFMA_COUNTERS):
             continue
         gui = d["GRBM_GUI_ACTIVE"] / XCDS
         stages.setdefault(st, []).append({
@@ -348,11 +359,13 @@ def main():
     R = int(d.sum())
     kv = {"gather_attention": R * row_b, "gather_mfma": int(d[heavy].sum()) * row_b,
           "gather_light": int(d[~heavy].sum()) * row_b}
-    up_flops = 2.0 * n * cfg.d_up * cfg.d_emb
     # batches of more than 512 tokens run W_mix factored through W_up: one GEMM over
-    # [o | x] (K = d_emb + d_in) against [F | W2], F = W1 diag(gamma) W_c formed per call
-    # in the preparation stage (W_up itself runs for LayerNorm's row statistics)
-    mix_k = (cfg.d_emb + cfg.d_in) if n > 512 else (cfg.d_up + cfg.d_in)
+    # [o | x] (K = d_emb + d_in) against [F | W2], F = W1 diag(gamma) W_c, and
+    # LayerNorm's variance from o^T G o (GEMM o G, N = K = d_emb), F and G formed per
+    # call in the preparation stage; smaller batches run W_up and W_mix over [LN(h) | x]
+    factored = n > 512
+    up_flops = 2.0 * n * cfg.d_emb * (cfg.d_emb if factored else cfg.d_up)
+    mix_k = (cfg.d_emb + cfg.d_in) if factored else (cfg.d_up + cfg.d_in)
     mix_flops = 2.0 * n * cfg.d_out * mix_k
     avg = {s_: stage_ms[i] / max(1, launches[i]) for i, s_ in enumerate(STAGES)}
     avg["gather_attention"] = avg["gather_mfma"] + avg["gather_light"]
@@ -363,9 +376,11 @@ def main():
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "work_per_launch": f"{kv[k_]} B of distinct K/V rows ({rows} rows x {row_b} B)"}
     kernels["gather_attention"]["kernels"] = "gather_mfma + gather_light"
-    kernels["w_up_gemm"] = {"bound": "mfma", "achieved": up_flops / (avg["w_up_gemm"] * 1e-3) / 1e12,
-                            "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
-                            "work_per_launch": f"{up_flops:.4g} FLOP"}
+    kernels["ln_stats_gemm"] = {"bound": "mfma",
+                                "achieved": up_flops / (avg["ln_stats_gemm"] * 1e-3) / 1e12,
+                                "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                                "work_per_launch": f"{up_flops:.4g} FLOP ("
+                                + ("o G, K = N = d_emb" if factored else "W_up, K = d_emb") + ")"}
     kernels["w_mix_gemm"] = {"bound": "mfma", "achieved": mix_flops / (avg["w_mix_gemm"] * 1e-3) / 1e12,
                              "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
                              "work_per_launch": f"{mix_flops:.4g} FLOP (K = {mix_k})"}
@@ -373,10 +388,10 @@ def main():
         v_["frac"] = v_["achieved"] / v_["peak"]
         v_["ms"] = avg[k_]
         v_["traffic"] = traffic_from_profiles(k_, cfg.name)
-    for k_ in ("w_up_gemm", "w_mix_gemm"):
+    for k_ in ("ln_stats_gemm", "w_mix_gemm"):
         kernels[k_]["mfma_counters"] = mfma_from_profiles(k_, cfg.name)
     # the dominant single kernel (longest average launch)
-    dominant = max(("gather_mfma", "gather_light", "w_up_gemm", "w_mix_gemm"), key=lambda s_: avg[s_])
+    dominant = max(("gather_mfma", "gather_light", "ln_stats_gemm", "w_mix_gemm"), key=lambda s_: avg[s_])
     roof = {k_: kernels[dominant][k_] for k_ in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
 

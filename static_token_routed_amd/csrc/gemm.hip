@@ -327,6 +327,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
     const int64_t nbase = n0 + wn * WN;
     auto epilogue = [&](auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
+        // OUT 3: the A values at this lane's output positions (A is M x K with K = N),
+        // all loads issued before the first use
+        uint2 av[OUT == 3 ? 8 : 1][OUT == 3 ? NJ : 1];
+        if constexpr (OUT == 3) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int64_t n = nbase + 16 * j + 4 * (lane >> 4);
+                    av[i][j] = (FULL || (m < p.M && n < p.N))
+                                   ? *reinterpret_cast<const uint2 *>(p.A + m * p.lda + n)
+                                   : make_uint2(0u, 0u);
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t m = m0 + wm * 128 + 16 * i + (lane & 15);
@@ -360,17 +376,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
                     }
                 }
             }
-            if constexpr (LN_OUT && (OUT == 0 || OUT == 3)) {
+            if constexpr (OUT == 3) {
+                // the wavefront's share of row m's quadratic form sum_n C[m][n] A[m][n]
+                // (its WN columns; zero-filled A past the edges)
+                float q = 0.f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    q = fmaf(acc[i][j][0], bf_lo(av[i][j].x), q);
+                    q = fmaf(acc[i][j][1], bf_hi(av[i][j].x), q);
+                    q = fmaf(acc[i][j][2], bf_lo(av[i][j].y), q);
+                    q = fmaf(acc[i][j][3], bf_hi(av[i][j].y), q);
+                }
+                q += __shfl_xor(q, 16);
+                q += __shfl_xor(q, 32);
+                if (lane < 16 && (FULL || (m < p.M && nbase < p.N)))
+                    p.ln_out[m * p.npart_out + nbase / WN] = q;
+            }
+            if constexpr (LN_OUT && OUT == 0) {
                 // partial statistics over each 64 columns (4 blocks of 16) of this row's
-                // stored (bf16) values, or with no output (OUT 3) of the fp32 values
+                // stored (bf16) values
                 auto stored = [&](int j, int e) {
-                    float v;
-                    if constexpr (OUT == 3) {
-                        v = acc[i][j][e];
-                    } else {
-                        const uint32_t w2 = pk[j][e >> 1];
-                        v = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
-                    }
+                    const uint32_t w2 = pk[j][e >> 1];
+                    const float v = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
                     if constexpr (FULL) return v;
                     const int64_t n = nbase + 16 * j + 4 * (lane >> 4) + e;
                     return n < p.N ? v : 0.f;
@@ -413,9 +440,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
             }
         }
     };
-    // (only the W_up GEMM, whose statistics double the per-element work, gets the
-    // unchecked copy; the others keep one copy of the code)
-    if (LN_OUT && m0 + BM <= p.M && n0 + BN <= p.N) epilogue(std::true_type{});
+    // (only the GEMMs that reduce their rows in the epilogue, whose per-element work
+    // that doubles, get the unchecked copy; the others keep one copy of the code)
+    if ((LN_OUT || OUT == 3) && m0 + BM <= p.M && n0 + BN <= p.N) epilogue(std::true_type{});
     else epilogue(std::false_type{});
 }
 
@@ -614,12 +641,16 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
 // column means), and W_mix [LN(h) ; x] = W1 diag(gamma) (h - mean) rstd + W1 beta + W2 x
 //   = rstd * (F o) + c2 + W2 x,   F = W1 diag(gamma) W_c  (d_out x d_emb),  c2 = W1 beta.
 // So the W_mix GEMM runs over [o | x] (K = d_emb + d_in) instead of [h | x]
-// (K = d_up + d_in), and h itself is needed only for its row statistics: the W_up
-// GEMM computes them from its fp32 accumulators and stores nothing.  F is formed
-// per call from the weights: W_c^T (d_emb x d_up, bf16: W_up transposed, each row
-// less its mean), then F^T = W_c^T W1'^T on the small-M GEMM (W1' = W1 diag(gamma)
-// from k_mix_fold), then its transpose.  Centring first means no mean * (row sum) term is subtracted
-// later, so a large mean cancels nothing in bf16.
+// (K = d_up + d_in).  h itself is never formed: LayerNorm needs only its variance,
+// var = |W_c o|^2 / d_up = o^T G o / d_up with the Gram matrix G = W_c^T W_c
+// (d_emb x d_emb), and the GEMM o G^T with a quadratic-form epilogue gives
+// o^T G o per row at a quarter of W_up's work when d_up = 4 d_emb.  F and G are
+// formed per call from the weights: W_c^T (W_up transposed, each row less its
+// mean, bf16) is written right after W1' = W1 diag(gamma) (from k_mix_fold), so
+// the rows [W1' ; W_c^T] are one (d_out + d_emb) x d_up matrix, and one small-K-
+// split GEMM of it against W_c^T gives [F ; G] in the layouts the two GEMMs read.
+// Centring first means no mean * (row sum) term is subtracted later, so a large
+// mean cancels nothing in bf16.
 
 // W_up^T [d_emb x d_up] (bf16, from the transpose) centred in place: one wavefront
 // per row c subtracts the row's mean (the mean of W_up's column c) and rounds to bf16;
@@ -650,20 +681,54 @@ __global__ __launch_bounds__(256) void k_center_rows(uint16_t *__restrict__ WT, 
     }
 }
 
-hipError_t launch_gemm_stats_bf16(const uint16_t *A, const uint16_t *B, int64_t M, int64_t N, int64_t K,
-                                  float *ln_out, hipStream_t s) {
-    if (M <= 0 || N <= 0) return hipSuccess;
-    GemmP p = make_plain(A, B, nullptr, M, N, K);
-    p.ln_out = ln_out;
-    p.npart_out = (int)((N + kLnPart - 1) / kLnPart);
-    hipLaunchKernelGGL((k_gemm_bf16<false, true, 3, 8>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+// (mean, rstd) per row from the quadratic-form partials: var = (sum of the row's
+// npart partials) / width, clamped at zero (G's rounding can leave a tiny negative
+// value for a row whose variance is zero).  The mean is not needed (the factored
+// GEMM's mean coefficients are zero) and is written as 0.
+__global__ __launch_bounds__(256) void k_ln_quad_finalize(const float *__restrict__ qp, int64_t M, int npart,
+                                                          int64_t width, float eps, float *__restrict__ stats) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= M) return;
+    float q = 0.f;
+    for (int i = 0; i < npart; ++i) q += qp[row * npart + i];
+    stats[2 * row] = 0.f;
+    stats[2 * row + 1] = 1.f / sqrtf(fmaxf(q / (float)width, 0.f) + eps);
+}
+
+constexpr int kQuadWN = 64;  // output columns per wavefront of k_gemm_bf16<.., 3, 8>
+
+int ln_quad_parts(int64_t d_emb) { return (int)((d_emb + kQuadWN - 1) / kQuadWN); }
+
+hipError_t launch_ln_quad_stats_bf16(const uint16_t *o, const void *factor_ws, int64_t M, int64_t d_emb,
+                                     int64_t d_up, int64_t d_out, float eps, float *qp, float *stats,
+                                     hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const uint16_t *G = reinterpret_cast<const uint16_t *>(
+                            static_cast<const char *>(factor_ws) + al((size_t)(d_out + d_emb) * d_up * 2)) +
+                        d_out * d_emb;
+    GemmP p = make_plain(o, G, nullptr, M, d_emb, d_emb);
+    p.ln_out = qp;
+    p.npart_out = ln_quad_parts(d_emb);
+    // 8 wavefronts in 2 x 4, each kQuadWN columns wide
+    hipLaunchKernelGGL((k_gemm_bf16<false, false, 3, 8>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ln_quad_finalize, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, qp, M,
+                       p.npart_out, d_up, eps, stats);
     return hipGetLastError();
 }
 
+// factor_ws: [W1' ; W_c^T] ((d_out + d_emb) x d_up bf16), [F ; G] ((d_out + d_emb) x
+// d_emb bf16), the d_out zeros; each region 256-byte aligned.
 size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    return al((size_t)d_emb * 4) + al((size_t)d_emb * d_up * 2) + 2 * al((size_t)d_emb * d_out * 2) +
+    return al((size_t)(d_out + d_emb) * d_up * 2) + al((size_t)(d_out + d_emb) * d_emb * 2) +
            al((size_t)d_out * 4);
+}
+
+size_t mix_factor_part_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
+    return skinny_part_bytes(d_out + d_emb, d_emb, d_up);
 }
 
 hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
@@ -671,22 +736,23 @@ hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const 
                              int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *f = static_cast<char *>(factor_ws);
-    uint16_t *wct = reinterpret_cast<uint16_t *>(f + al((size_t)d_emb * 4));
-    uint16_t *ft = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(wct) + al((size_t)d_emb * d_up * 2));
-    uint16_t *fm = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(ft) + al((size_t)d_emb * d_out * 2));
-    int32_t *zero = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(fm) + al((size_t)d_emb * d_out * 2));
+    uint16_t *stack = reinterpret_cast<uint16_t *>(f);  // W1' rows, then W_c^T rows
+    uint16_t *wct = stack + d_out * d_up;
+    uint16_t *fg = reinterpret_cast<uint16_t *>(f + al((size_t)(d_out + d_emb) * d_up * 2));
+    float *zero = reinterpret_cast<float *>(reinterpret_cast<char *>(fg) + al((size_t)(d_out + d_emb) * d_emb * 2));
     // W_c^T: W_up transposed, then each row less its mean
     hipError_t e = launch_transpose(W_up, d_emb, d_up, d_emb, wct, d_up, d_up, L3_BF16, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_center_rows, dim3((unsigned)((d_emb + 3) / 4)), dim3(256), 0, s, wct, d_emb, d_up,
-                       reinterpret_cast<float *>(zero), d_out);
-    e = launch_mix_fold(W_mix, gamma, beta, fold_ws, d_up, d_in, d_out, s);
+                       zero, d_out);
+    // W1' into the stack's first d_out rows; c1, c2 into fold_ws
+    float *c1 = reinterpret_cast<float *>(static_cast<char *>(fold_ws) + mix_fold_w1p_bytes(d_up, d_out));
+    hipLaunchKernelGGL(k_mix_fold, dim3((unsigned)d_out), dim3(256), 0, s, W_mix, gamma, beta, d_up,
+                       d_up + d_in, stack, c1, c1 + d_out);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // F^T [d_emb x d_out] = W_c^T W1'^T (W1' is the fold's first region, d_out x d_up)
-    e = launch_gemm_skinny_bf16(wct, static_cast<const uint16_t *>(fold_ws), ft, d_emb, d_out, d_up, nullptr,
-                                part, s);
-    if (e != hipSuccess) return e;
-    return launch_transpose(ft, d_out, d_emb, d_out, fm, d_emb, d_emb, L3_BF16, s);
+    // [F ; G] = [W1' ; W_c^T] W_c  (row i of the product: stack row i against each W_c^T row)
+    return launch_gemm_skinny_bf16(stack, wct, fg, d_out + d_emb, d_emb, d_up, nullptr, part, s);
 }
 
 hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
@@ -696,10 +762,9 @@ hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, c
     if (M <= 0) return hipSuccess;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const char *f = static_cast<const char *>(factor_ws);
-    const uint16_t *fm = reinterpret_cast<const uint16_t *>(
-        f + al((size_t)d_emb * 4) + al((size_t)d_emb * d_up * 2) + al((size_t)d_emb * d_out * 2));
+    const uint16_t *fm = reinterpret_cast<const uint16_t *>(f + al((size_t)(d_out + d_emb) * d_up * 2));
     const float *zero = reinterpret_cast<const float *>(reinterpret_cast<const char *>(fm) +
-                                                        al((size_t)d_emb * d_out * 2));
+                                                        al((size_t)(d_out + d_emb) * d_emb * 2));
     const float *c2 = reinterpret_cast<const float *>(static_cast<const char *>(fold_ws) +
                                                       mix_fold_w1p_bytes(d_up, d_out)) + d_out;
     GemmP p = make_plain(o, fm, out, M, d_out, d_emb + d_in);

@@ -226,21 +226,21 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
                                                    n, D.d_up, D.d_in, D.d_out, part, s));
         }
     } else if (D.dtype == L3_BF16) {
-        // W_mix factored through W_up (gemm.hip): h is formed only for its row statistics
+        // W_mix factored through W_up (gemm.hip): h is never formed; LayerNorm's variance
+        // comes from o^T G o
         float *stats = ws_ptr<float>(ws, L.stats);
         void *fold = ws_ptr<char>(ws, L.fold);
         void *factor = ws_ptr<char>(ws, L.factor);
         {
-            StageTimer tm(3, s);
-            L3_HIP_TRY(launch_gemm_stats_bf16((const uint16_t *)o, (const uint16_t *)W_up, n, D.d_up, D.d_emb,
-                                              lnp, s));
-        }
-        {
             StageTimer tm(4, s);
-            L3_HIP_TRY(launch_ln_finalize(lnp, n, D.d_up, D.eps, stats, s));
             L3_HIP_TRY(launch_mix_factor((const uint16_t *)W_up, (const uint16_t *)W_mix, gamma, beta, fold,
                                          factor, ws_ptr<float>(ws, L.part), D.d_emb, D.d_up, D.d_in,
                                          D.d_out, s));
+        }
+        {
+            StageTimer tm(3, s);
+            L3_HIP_TRY(launch_ln_quad_stats_bf16((const uint16_t *)o, factor, n, D.d_emb, D.d_up, D.d_out,
+                                                 D.eps, lnp, stats, s));
         }
         {
             StageTimer tm(5, s);
@@ -470,14 +470,18 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.o = take((size_t)n * d.d_emb * es);
     L.h = take((size_t)n * d.d_up * es);
     const int64_t np = (d.d_up + kLnPart - 1) / kLnPart;
-    L.lnp = take((size_t)n * std::max<int64_t>(np, 1) * 2 * 4);
+    L.lnp = take((size_t)n * std::max<int64_t>(std::max<int64_t>(np, 1) * 2, ln_quad_parts(d.d_emb)) * 4);
     L.stats = take((size_t)n * 2 * 4);
     L.fold = take(d.dtype == L3_BF16 ? mix_fold_bytes(d.d_up, d.d_out) : 0);
     L.factor = take(d.dtype == L3_BF16 && n > kSkinnyMaxM ? mix_factor_bytes(d.d_emb, d.d_up, d.d_out) : 0);
     const int64_t ns = std::min<int64_t>(n, kSkinnyMaxM);
-    L.part = take(d.dtype == L3_BF16 ? std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
-                                                 skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in))
-                                     : 0);
+    // (the factor's slabs join the maximum above kSkinnyMaxM tokens, so the size never
+    // falls as n grows)
+    const size_t skinny = std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
+                                   skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in));
+    L.part = take(d.dtype != L3_BF16 ? 0
+                  : n <= kSkinnyMaxM ? skinny
+                                     : std::max(skinny, mix_factor_part_bytes(d.d_emb, d.d_up, d.d_out)));
     L.slots = split_slots(d, n, max_d);
     L.sitems = take((size_t)L.slots * 16);
     L.blkinfo = take(L.slots ? (size_t)n * 16 : 0);

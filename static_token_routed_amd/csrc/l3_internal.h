@@ -177,17 +177,20 @@ hipError_t launch_gemm_mix_bf16(const uint16_t *h, const uint16_t *x, const floa
 hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const float *beta,
                            void *fold_ws, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
-// Factored W_mix (batches of more than kSkinnyMaxM tokens): the W_up GEMM only for its
-// row statistics (ln_out partials from fp32 accumulators, no output), the factor
-// F = W1 diag(gamma) W_c of the centred W_up into factor_ws (mix_factor_bytes; the fold
-// terms into fold_ws; `part` holds the small-M GEMM's slabs, skinny_part_bytes(d_emb,
-// d_out, d_up)), and out = rstd * (F o) + c2 + W2 x.
-hipError_t launch_gemm_stats_bf16(const uint16_t *A, const uint16_t *B, int64_t M, int64_t N, int64_t K,
-                                  float *ln_out, hipStream_t s);
+// Factored W_mix (batches of more than kSkinnyMaxM tokens): F = W1 diag(gamma) W_c and
+// G = W_c^T W_c of the centred W_up into factor_ws (mix_factor_bytes; the fold terms
+// into fold_ws; `part` holds the small-K-split GEMM's slabs, mix_factor_part_bytes),
+// LayerNorm's (0, rstd) per row from o^T G o (qp: [M x ln_quad_parts(d_emb)] fp32
+// partials), and out = rstd * (F o) + c2 + W2 x.
 size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out);
+size_t mix_factor_part_bytes(int64_t d_emb, int64_t d_up, int64_t d_out);
+int ln_quad_parts(int64_t d_emb);
 hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
                              const float *beta, void *fold_ws, void *factor_ws, float *part,
                              int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
+hipError_t launch_ln_quad_stats_bf16(const uint16_t *o, const void *factor_ws, int64_t M, int64_t d_emb,
+                                     int64_t d_up, int64_t d_out, float eps, float *qp, float *stats,
+                                     hipStream_t s);
 hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
                                          const uint16_t *W_mix, uint16_t *out, const void *fold_ws,
                                          const void *factor_ws, int64_t M, int64_t d_emb, int64_t d_up,
