@@ -44,7 +44,10 @@
  *    misaligned pointer is rejected with L3_ERR_INVALID_ARG.
  *  - n = 0 is a no-op returning L3_OK.
  *  - Plans are immutable after creation and may be shared across threads and
- *    streams; a workspace serves one call at a time.
+ *    streams; a workspace serves one call at a time.  A bf16 plan owns one
+ *    stream of its own (default priority) for the weight-only part of large
+ *    forwards (l3_forward): calls on different streams that share the plan
+ *    take turns on it for that part.
  */
 #ifndef L3_H
 #define L3_H
@@ -152,6 +155,13 @@ size_t l3_workspace_size_dims(const l3_dims_t *dims, int32_t max_d, int64_t n_ma
  * caption); the result does not depend on the batch order.  W_V may be the same
  * buffer as W_K when d_emb == d_in (the pages' tied variant, papernotes.org page,
  * ablation table): the second read of each row then mostly hits the caches.
+ * bf16 batches of more than 512 tokens evaluate W_mix [LN(h) ; x] in factored
+ * form (the same function: with W_c the column-centred W_up, h - mean(h) = W_c o,
+ * so W_mix [LN(h) ; x] = rstd (F o) + W1 beta + W2 x with F = W1 diag(gamma) W_c,
+ * and var(h) = o^T G o / d_up with G = W_c^T W_c); F and G depend on the weights
+ * only and are formed on the plan's own stream, forked from `stream` when the
+ * call starts and joined before the first kernel that reads them, so they run
+ * beside the sort and the gather.
  * Errors: INVALID_ARG, CAPACITY (workspace too small), HIP.
  */
 int l3_forward(l3_plan_t plan, const void *x, const int32_t *token_ids, int64_t n,
@@ -332,8 +342,10 @@ int l3_gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, in
  * kernel stages and accumulate their elapsed time; l3_profile_read synchronises
  * those events.  Stages: 0 route (sort + blocks + work lists), 1 gather-attention
  * on the matrix cores (heavy work list), 2 gather-attention, one wavefront per
- * item (light work list), 3 W_up GEMM, 4 W_mix preparation (LayerNorm statistics
- * and the LayerNorm fold of W_mix), 5 W_mix GEMM; backward (which also runs
+ * item (light work list), 3 LayerNorm row statistics (the W_up GEMM for bf16
+ * batches of at most 512 tokens and fp32 plans; o^T G o above), 4 the factors F
+ * and G of larger bf16 batches (recorded on the plan's stream), 5 W_mix GEMM;
+ * backward (which also runs
  * stages 0-2): 6 recompute of h and its LayerNorm statistics, 7 dense products
  * and the LayerNorm backward, 8 attention backward, 9 key / value gradients.
  * bf16 batches of at most 512 tokens run one split-row gather-attention (row

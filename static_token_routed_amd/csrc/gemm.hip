@@ -647,8 +647,8 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
 // o^T G o per row at a quarter of W_up's work when d_up = 4 d_emb.  F and G are
 // formed per call from the weights: W_c^T (W_up transposed, each row less its
 // mean, bf16) is written right after W1' = W1 diag(gamma) (from k_mix_fold), so
-// the rows [W1' ; W_c^T] are one (d_out + d_emb) x d_up matrix, and one small-K-
-// split GEMM of it against W_c^T gives [F ; G] in the layouts the two GEMMs read.
+// the rows [W1' ; W_c^T] are one (d_out + d_emb) x d_up matrix, and one split-K GEMM
+// of it against W_c^T gives [F ; G] in the layouts the two GEMMs read.
 // Centring first means no mean * (row sum) term is subtracted later, so a large
 // mean cancels nothing in bf16.
 
@@ -727,8 +727,32 @@ size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
            al((size_t)d_out * 4);
 }
 
+// [F ; G] = [W1' ; W_c^T] W_c runs on the 256 x 256 tile kernel with K split so that the
+// tiles x splits workgroups about fill the chip (at least 256 K columns each); the fp32
+// slabs are added in slab order and rounded to bf16 by k_slab_sum_bf16.
+int factor_splits(int64_t d_emb, int64_t d_up, int64_t d_out, int64_t *ksplit) {
+    const int64_t tiles = ((d_out + d_emb + BM - 1) / BM) * ((d_emb + BN - 1) / BN);
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(256 / tiles, d_up / 256));
+    const int64_t ks = ((d_up + want - 1) / want + BK - 1) / BK * BK;
+    if (ksplit) *ksplit = ks;
+    return (int)((d_up + ks - 1) / ks);
+}
+
 size_t mix_factor_part_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
-    return skinny_part_bytes(d_out + d_emb, d_emb, d_up);
+    return (size_t)factor_splits(d_emb, d_up, d_out, nullptr) * (size_t)(d_out + d_emb) * d_emb * 4;
+}
+
+// C[i] (bf16, 4 per thread) = sum of the S slabs at i, in slab order
+__global__ __launch_bounds__(256) void k_slab_sum_bf16(const float4 *__restrict__ part, int S, int64_t n4,
+                                                       uint2 *__restrict__ C) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 a = part[i];
+    for (int sp = 1; sp < S; ++sp) {
+        const float4 v = part[(int64_t)sp * n4 + i];
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    C[i] = make_uint2(pack2(a.x, a.y), pack2(a.z, a.w));
 }
 
 hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
@@ -752,7 +776,18 @@ hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // [F ; G] = [W1' ; W_c^T] W_c  (row i of the product: stack row i against each W_c^T row)
-    return launch_gemm_skinny_bf16(stack, wct, fg, d_out + d_emb, d_emb, d_up, nullptr, part, s);
+    const int64_t M = d_out + d_emb;
+    GemmP p = make_plain(stack, wct, nullptr, M, d_emb, d_up);
+    p.Cf = part;
+    p.splits = factor_splits(d_emb, d_up, d_out, &p.ksplit);
+    hipLaunchKernelGGL((k_gemm_bf16<false, false, 1>), dim3(p.tiles_m * p.tiles_n * p.splits), dim3(256), 0, s,
+                       p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = M * d_emb / 4;
+    hipLaunchKernelGGL(k_slab_sum_bf16, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(part), p.splits, n4, reinterpret_cast<uint2 *>(fg));
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,

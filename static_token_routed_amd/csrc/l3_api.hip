@@ -11,6 +11,22 @@
 
 using namespace l3;
 
+// A second stream for work that depends only on the weights (the factored W_mix's
+// F and G): forked from the caller's stream at the start of a forward and joined
+// before the first kernel that reads it, so it runs beside the route.  The mutex
+// keeps one forward's record / wait sequence whole when several host threads share
+// a plan.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+    ~SideStream() {
+        if (join) (void)hipEventDestroy(join);
+        if (fork) (void)hipEventDestroy(fork);
+        if (s) (void)hipStreamDestroy(s);
+    }
+};
+
 struct l3_plan_s {
     int64_t vocab = 0, v = 0;
     int32_t k = 0, max_d = 0;
@@ -18,6 +34,7 @@ struct l3_plan_s {
     int64_t *d_off = nullptr;   // device CSR offsets (vocab + 1)
     std::vector<int64_t> h_off; // host copy, used by the prefetch path
     bool owns_off = true;
+    SideStream *side = nullptr; // bf16 plans (owned unless owns_off is false: a view)
 };
 
 struct l3_staging_s {
@@ -205,9 +222,45 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
     const Dims &D = P.dims;
     const WsLayout L = ws_layout(D, n, P.max_d);
     if (ws_bytes < L.total) return L3_ERR_CAPACITY;
+    const bool factored = D.dtype == L3_BF16 && n > kSkinnyMaxM;
+    void *fold = ws_ptr<char>(ws, L.fold);
+    void *factor = ws_ptr<char>(ws, L.factor);
+    // F and G (weights only) on the side stream, beside the route and gather-attention
+    // (their workspace regions are not touched by those); the caller's stream waits for
+    // them before the first kernel that reads them, or before returning on an error
+    struct Join {
+        SideStream *side = nullptr;
+        hipStream_t s = nullptr;
+        std::unique_lock<std::mutex> lock;
+        hipError_t now() {
+            if (!side) return hipSuccess;
+            SideStream *t = side;
+            side = nullptr;
+            hipError_t e = hipEventRecord(t->join, t->s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(s, t->join, 0);
+            lock.unlock();
+            return e;
+        }
+        ~Join() { (void)now(); }
+    } join;
+    if (factored) {
+        hipStream_t ps = s;
+        if (P.side) {
+            join.lock = std::unique_lock<std::mutex>(P.side->mu);
+            L3_HIP_TRY(hipEventRecord(P.side->fork, s));
+            L3_HIP_TRY(hipStreamWaitEvent(P.side->s, P.side->fork, 0));
+            join.side = P.side;
+            join.s = s;
+            ps = P.side->s;
+        }
+        StageTimer tm(4, ps);
+        L3_HIP_TRY(launch_mix_factor((const uint16_t *)W_up, (const uint16_t *)W_mix, gamma, beta, fold, factor,
+                                     ws_ptr<float>(ws, L.part), D.d_emb, D.d_up, D.d_in, D.d_out, ps));
+    }
     RouteBufs b{};
     const int rc = route_attend(P, x, ids, n, WK, WV, ws, L, b, s);
     if (rc != L3_OK) return rc;
+    L3_HIP_TRY(join.now());
     void *o = ws_ptr<char>(ws, L.o);
     void *h = ws_ptr<char>(ws, L.h);
     float *lnp = ws_ptr<float>(ws, L.lnp);
@@ -229,14 +282,6 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         // W_mix factored through W_up (gemm.hip): h is never formed; LayerNorm's variance
         // comes from o^T G o
         float *stats = ws_ptr<float>(ws, L.stats);
-        void *fold = ws_ptr<char>(ws, L.fold);
-        void *factor = ws_ptr<char>(ws, L.factor);
-        {
-            StageTimer tm(4, s);
-            L3_HIP_TRY(launch_mix_factor((const uint16_t *)W_up, (const uint16_t *)W_mix, gamma, beta, fold,
-                                         factor, ws_ptr<float>(ws, L.part), D.d_emb, D.d_up, D.d_in,
-                                         D.d_out, s));
-        }
         {
             StageTimer tm(3, s);
             L3_HIP_TRY(launch_ln_quad_stats_bf16((const uint16_t *)o, factor, n, D.d_emb, D.d_up, D.d_out,
@@ -545,6 +590,19 @@ int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k, const l
         delete p;
         return L3_ERR_HIP;
     }
+    if (p->dims.dtype == L3_BF16) {
+        // the side stream of the factored W_mix (default priority, not blocking on the
+        // legacy null stream: every dependency is an explicit event wait)
+        p->side = new (std::nothrow) SideStream();
+        if (!p->side || hipStreamCreateWithFlags(&p->side->s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&p->side->fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&p->side->join, hipEventDisableTiming) != hipSuccess) {
+            delete p->side;
+            (void)hipFree(p->d_off);
+            delete p;
+            return L3_ERR_HIP;
+        }
+    }
     *plan = p;
     return L3_OK;
 }
@@ -552,6 +610,7 @@ int l3_plan(const int64_t *offsets, int64_t vocab, int64_t v, int32_t k, const l
 int l3_plan_destroy(l3_plan_t p) {
     if (!p) return L3_OK;
     if (p->owns_off && p->d_off) (void)hipFree(p->d_off);
+    if (p->owns_off) delete p->side;
     delete p;
     return L3_OK;
 }
@@ -957,6 +1016,7 @@ int l3_forward_staged(l3_staging_t st, const void *x, int64_t n, const void *W_u
     view.max_d = st->plan->max_d;
     view.dims = st->plan->dims;
     view.d_off = st->d_off;
+    view.side = st->plan->side;
     view.owns_off = false;
     const int rc = forward_impl(view, x, st->d_ids, n, st->d_K, st->d_V, W_up, gamma, beta, W_mix,
                                 out, ws, ws_bytes, (hipStream_t)stream);

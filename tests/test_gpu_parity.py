@@ -447,3 +447,46 @@ def test_workspace_for_larger_batch_serves_smaller():
         print(f"n={n} on the 512-token workspace ({need} B): err {err:.2e}", flush=True)
         assert err <= case.tol
     g.close()
+
+
+def test_factored_back_to_back_weight_sets():
+    """Batches of more than 512 tokens form the weight-only factors F and G on the
+    plan's own stream, beside the sort and the gather.  Two forwards on one
+    workspace and one non-default stream, with different W_up, gamma, beta and W_mix,
+    are issued with no host synchronisation between them, twice over: the second
+    call's factors must not overwrite the first call's before its W_mix GEMM has
+    read them, nor run before the weights written just before the call.  Each output
+    must equal, bit for bit, the same call run alone, and match the oracle."""
+    cfg = synth.small("b2b", vocab=400, k=24, d_in=256, d_emb=128, d_up=512, d_out=256, n=900,
+                      v=4000, dtype="bf16", seed=41)
+    a = make_case(cfg, ln_random=True)
+    other = make_case(dataclasses.replace(cfg, seed=cfg.seed + 7), ln_random=True)
+    b = dataclasses.replace(a, Wup=other.Wup, Wmix=other.Wmix, gamma=other.gamma, beta=other.beta)
+    g = Gpu(a)
+    wb = {"Wup": dev(b.Wup, "bf16"), "Wmix": dev(b.Wmix, "bf16"),
+          "gamma": torch.from_numpy(b.gamma).cuda(), "beta": torch.from_numpy(b.beta).cuda()}
+    wa = {"Wup": g.Wup, "Wmix": g.Wmix, "gamma": g.gamma, "beta": g.beta}
+
+    def run(w, stream=None):
+        return g.plan.forward(g.x, g.ids, g.WK, g.WV, w["Wup"], w["gamma"], w["beta"], w["Wmix"],
+                              stream=stream)
+
+    alone_a = run(wa)
+    torch.cuda.synchronize()
+    alone_b = run(wb)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        # weights written on this stream just before the calls that read them
+        wb2 = {k_: torch.empty_like(v_) for k_, v_ in wb.items()}
+        for k_ in wb:
+            wb2[k_].copy_(wb[k_])
+        outs = [run(wa, side), run(wb2, side), run(wa, side), run(wb2, side)]
+    side.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, alone_a if i % 2 == 0 else alone_b), f"call {i} differs from the call run alone"
+    for case, got in ((a, alone_a), (b, alone_b)):
+        err = rowwise_err(to_np(got), oracle_out(case))
+        print(f"weight set {'ab'[case is b]}: err {err:.2e}", flush=True)
+        assert err <= case.tol
+    g.close()
