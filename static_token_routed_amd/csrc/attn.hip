@@ -454,9 +454,10 @@ struct HeavyArgs {
     const int32_t *uniq, *seg_start, *perm, *hdr;
     int32_t *queue;  // 8 per-XCD work counters, then the dense items' counter (zeroed with the header)
     const int2 *items;   // streaming items (ID block, first token), 32 tokens
-    const int2 *dense;   // dense items, 128 tokens, d_t <= 512; taken before the others
+    const int2 *dense;   // dense items, 64 tokens, d_t <= 512; taken before the others
     int64_t d_in;
     uint16_t *o;
+    int64_t nmax;        // entries of the items array (its back holds the short blocks' items)
 };
 
 constexpr int kSlot = 16384;       // bytes per ring stage
@@ -478,43 +479,84 @@ __device__ inline void wait_stages(int later) {
     }
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform runtime n in [0, 20] (a larger n waits for
+// vmcnt(20), which is always safe: it only waits for more)
+__device__ inline void wait_vmcnt_rt(int n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        case 16: wait_vmcnt<16>(); break;
+        case 17: wait_vmcnt<17>(); break;
+        case 18: wait_vmcnt<18>(); break;
+        case 19: wait_vmcnt<19>(); break;
+        default: wait_vmcnt<20>(); break;
+    }
+}
+
 // Dense work item: one ID with up to 64 tokens (kDenseTile) and d_t <= 512 rows, so
 // that the rows of the IDs that fill most of a batch are read once per 64 tokens
-// (instead of once per 32).  Wavefront w owns tokens [16w, 16w + 16) and all rows.
-// Scores: the d_in columns stream in 64-column stages (the K rows' chunk, 512 x 64,
-// and the gathered x rows' chunk, 64 x 64: 72 KB, double-buffered) into 32
-// accumulators of v_mfma_f32_16x16x32_bf16 per wavefront, so the softmax is exact.
-// Values: V rows stream in 64-row stages, read transposed, into DE/16 accumulators.
+// (instead of once per 32).  Wavefront w owns tokens [16w, 16w + 16) and all rows;
+// all d_t scores of a token stay in 32 accumulators of v_mfma_f32_16x16x32_bf16, so
+// the softmax is exact.
+// The item is one sequence of stages through a ring of 4 slots of 40 KB, the copies
+// running 3 stages ahead (up to about 100 KB in flight per CU), each stage a barrier:
+//  * scores stages: for each 64-column chunk of d_in, the K rows [0, 256) and, when
+//    d_t > 256, [256, 512) as two stages (32 KB each, 128-byte row pieces); the
+//    first of them also brings the 64 tokens' x chunk (8 KB), whose fragments the
+//    wavefront keeps in registers for the second;
+//  * values stages: V rows in blocks of 32 (d_emb 512) or 64, read transposed.
+// K row groups wholly past d_t are not copied (their stale scores are masked); the
+// waits count the copies each stage actually issues.
 template <int XQ, int DE>
 __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *lds, uint32_t lds0,
                                            int sb, int tq, int ntok, int64_t r0, int d, int w) {
     constexpr int64_t d_in = 64 * XQ;
-    constexpr int NKC = XQ;                  // 64-column stages over d_in
-    constexpr int KT = 512 * 128;            // K chunk: 512 rows x 128 bytes
-    constexpr int SST = KT + 64 * 128;       // + x chunk: 64 tokens x 128 bytes (72 KB)
-    constexpr int VROWS = 64;                // V rows per values stage
-    constexpr int VST = VROWS * DE * 2;      // <= 64 KB
+    constexpr int NKC = XQ;                  // 64-column chunks of d_in
+    constexpr int KH = 256 * 128;            // K stage: 256 rows x 128 bytes
+    constexpr int SLOT = KH + 64 * 128;      // + the x chunk: 64 tokens x 128 bytes (40 KB)
+    constexpr int NSLOT = 4;                 // ring slots: copies run NSLOT - 1 stages ahead
+    constexpr int VROWS = DE == 512 ? 32 : 64;  // V rows per values stage
+    constexpr int VST = VROWS * DE * 2;      // <= 32 KB
     constexpr int VCP = VST / 1024 / 4;      // V copies per wavefront and stage
+    constexpr int VKB = VROWS / 32;          // 32-row blocks per values stage
     constexpr int RPC = 512 / DE;            // V rows per 1 KB copy
     constexpr int CPR = DE / 8;              // 16-byte chunks per V row
     constexpr int OE = DE / 16;              // 16-column output blocks
-    static_assert(VCP >= 1 && CPR >= 8 && VST <= SST && 2 * SST <= kSlots * kSlot + kXchg, "stages");
+    static_assert(VCP >= 1 && CPR >= 8 && VST <= SLOT && NSLOT * SLOT <= kSlots * kSlot + kXchg, "stages");
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, kg = lane >> 4;
+    const int nh = d > 256 ? 2 : 1;          // K row halves holding rows below d_t
+    const int NK = NKC * nh;                 // scores stages
     const int nvs = (d + VROWS - 1) / VROWS; // values stages
+    const int total = NK + nvs;
 
     // every wavefront has read the item index before the LDS is overwritten
     lds_barrier();
 
-    // Copies of a scores stage: K rows [8q, 8q + 8) for q = 16w + i (rows past d_t
-    // repeat row d_t - 1), x rows of tokens [8q, 8q + 8) for q = 2w + i; lane l fills
-    // chunk l % 8 of row 8q + l / 8 with global chunk (l % 8) ^ (l / 8).
+    // Copies of a scores stage of half r: K rows 256r + 64w + [8i, 8i + 8) for i < 8
+    // (rows past d_t repeat row d_t - 1; groups wholly past it are skipped), and for
+    // r = 0 the x rows of tokens [8q, 8q + 8) for q = 2w + i; lane l fills chunk l % 8
+    // of row 8q + l / 8 of the stage with global chunk (l % 8) ^ (l / 8).
     const int gch = (lane & 7) ^ (lane >> 3);
-    uint32_t koff[16];
+    uint32_t koff[16];  // [8r + i]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (16 * w + i) + (lane >> 3);
-        koff[i] = (uint32_t)(min(row, d - 1) * d_in * 2 + gch * 16);
+    for (int j = 0; j < 16; ++j) {
+        const int row = 256 * (j >> 3) + 64 * w + 8 * (j & 7) + (lane >> 3);
+        koff[j] = (uint32_t)(min(row, d - 1) * d_in * 2 + gch * 16);
     }
     const uint16_t *xsrc[2];
 #pragma unroll
@@ -523,29 +565,53 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
         xsrc[i] = a.x + (int64_t)a.perm[sb + tq + min(tk, ntok - 1)] * d_in + gch * 8;
     }
     const uint16_t *kbase = a.WK + r0 * d_in;
-    auto issue_qk = [&](int c) {
-        const uint32_t base = lds0 + (uint32_t)((c & 1) * SST);
-        const int64_t col = (int64_t)c * 64;
-        const uint32_t kb = base + 16 * w * 1024, xb = base + KT + 2 * w * 1024;
-        // K row groups wholly past d_t are not copied: their (stale) scores are masked,
-        // and this path waits for all of its copies (vmcnt 0), whatever their number
-        static_for<16>([&](auto i) {
-            if (8 * (16 * w + i) < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
-        });
-        static_for<2>([&](auto i) { async_ld16_o<i * 1024>(xsrc[i] + col, xb); });
+    // copies this wavefront issues for stage t (0 past the end)
+    auto copies = [&](int t) -> int {
+        if (t >= total) return 0;
+        if (t >= NK) return VCP;
+        const int r = nh == 2 ? (t & 1) : 0;
+        return max(0, min(8, (d - 256 * r - 64 * w + 7) / 8)) + (r == 0 ? 2 : 0);
     };
-    // Copies of values stage g into slot (NKC + g) & 1: rows [64g, 64g + 64) (past d_t
-    // repeat row d_t - 1); copy q = VCP w + i holds rows [RPC q, +RPC); chunk c of
-    // row r holds global chunk c ^ 2 (r & 3).
-    auto issue_v = [&](int g) {
-        const uint32_t base = lds0 + (uint32_t)(((NKC + g) & 1) * SST) + VCP * w * 1024;
-        static_for<VCP>([&](auto i) {
-            const int q = VCP * w + i;
-            const int row = RPC * q + lane / CPR;
-            const int64_t grow = r0 + min(VROWS * g + row, d - 1);
-            const int cc = (lane % CPR) ^ (2 * (row & 3));
-            async_ld16_o<i * 1024>(a.WV + grow * DE + 8 * cc, base);
-        });
+    auto issue = [&](int t) {
+        if (t >= total) return;
+        const uint32_t base = lds0 + (uint32_t)((t % NSLOT) * SLOT);
+        if (t < NK) {
+            const int c = nh == 2 ? (t >> 1) : t, r = nh == 2 ? (t & 1) : 0;
+            const int64_t col = (int64_t)c * 64;
+            const uint32_t kb = base + 8 * w * 1024;
+            if (r == 0) {
+                static_for<8>([&](auto i) {
+                    if (64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
+                });
+                const uint32_t xb = base + KH + 2 * w * 1024;
+                static_for<2>([&](auto i) { async_ld16_o<i * 1024>(xsrc[i] + col, xb); });
+            } else {
+                static_for<8>([&](auto i) {
+                    if (256 + 64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[8 + i], kb);
+                });
+            }
+        } else {
+            // values stage g: rows [VROWS g, +VROWS) (past d_t repeat row d_t - 1); copy
+            // q = VCP w + i holds rows [RPC q, +RPC); chunk c of row r holds global chunk
+            // c ^ 2 (r & 3)
+            const int g = t - NK;
+            const uint32_t vb = base + VCP * w * 1024;
+            static_for<VCP>([&](auto i) {
+                const int q = VCP * w + i;
+                const int row = RPC * q + lane / CPR;
+                const int64_t grow = r0 + min(VROWS * g + row, d - 1);
+                const int cc = (lane % CPR) ^ (2 * (row & 3));
+                async_ld16_o<i * 1024>(a.WV + grow * DE + 8 * cc, vb);
+            });
+        }
+    };
+    // a stage starts once its own copies have landed (those of the next two may still
+    // be in flight) and every wavefront is past the previous stage, whose slot the
+    // copies issued now overwrite
+    auto enter = [&](int t) {
+        wait_vmcnt_rt(copies(t + 1) + copies(t + 2));
+        lds_barrier();
+        issue(t + NSLOT - 1);
     };
 
     // fragment addresses: row (or token) 16b + (l & 15), chunk (4ks + l/16) ^ (l & 7)
@@ -556,22 +622,56 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
     f32x4_t S[32];
 #pragma unroll
     for (int rb = 0; rb < 32; ++rb) S[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    issue_qk(0);
-    for (int c = 0; c < NKC; ++c) {
-        wait_vmcnt<0>();
-        lds_barrier();
-        if (c + 1 < NKC) issue_qk(c + 1);
-        else issue_v(0);  // the first values stage overlaps the last scores stage and the softmax
-        const unsigned char *st = lds + (c & 1) * SST;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8_t xb = *reinterpret_cast<const bf16x8_t *>(st + KT + (16 * w) * 128 + fofs[ks]);
-            // all 32 row blocks: rows past d_t are copies of row d_t - 1, masked below
+    for (int t = 0; t < NSLOT - 1; ++t) issue(t);
+    // one scores stage: the 16 row blocks of half H against the wavefront's 16 tokens
+    // (rows past d_t are copies of row d_t - 1 or stale, masked below).  The
+    // scheduler is told to keep LA fragment reads ahead of the MFMAs (one read issued
+    // after each MFMA), so the LDS latency hides behind them: by itself it waits for
+    // each read right before its MFMA.
+    constexpr int LA = 6;
+    bf16x8_t xr[2];
+    auto kstage = [&](const unsigned char *st, auto half) {
+        constexpr int H = decltype(half)::value;
+        bf16x8_t Af[32];
 #pragma unroll
-            for (int rb = 0; rb < 32; ++rb) {
-                const bf16x8_t A = *reinterpret_cast<const bf16x8_t *>(st + rb * 2048 + fofs[ks]);
-                S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xb, S[rb], 0, 0, 0);
-            }
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 16; ++rb)
+                Af[16 * ks + rb] = *reinterpret_cast<const bf16x8_t *>(st + rb * 2048 + fofs[ks]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 16; ++rb)
+                S[16 * H + rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[16 * ks + rb], xr[ks], S[16 * H + rb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);       // LA LDS reads
+        static_for<32 - LA>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);       // the last LA MFMAs
+    };
+    auto xload = [&](const unsigned char *st) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            xr[ks] = *reinterpret_cast<const bf16x8_t *>(st + KH + (16 * w) * 128 + fofs[ks]);
+    };
+    if (nh == 2) {
+        // both halves of a column chunk in one iteration, so each accumulator has one home
+        for (int c = 0; c < NKC; ++c) {
+            enter(2 * c);
+            const unsigned char *st0 = lds + ((2 * c) % NSLOT) * SLOT;
+            xload(st0);
+            kstage(st0, std::integral_constant<int, 0>{});
+            enter(2 * c + 1);
+            kstage(lds + ((2 * c + 1) % NSLOT) * SLOT, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (int c = 0; c < NKC; ++c) {
+            enter(c);
+            const unsigned char *st0 = lds + (c % NSLOT) * SLOT;
+            xload(st0);
+            kstage(st0, std::integral_constant<int, 0>{});
         }
     }
 
@@ -614,29 +714,40 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
 #pragma unroll
     for (int e = 0; e < OE; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < nvs; ++g) {
-        wait_vmcnt<0>();
-        lds_barrier();
-        if (g + 1 < nvs) issue_v(g + 1);
-        const unsigned char *vt = lds + ((NKC + g) & 1) * SST;
+        const int t = NK + g;
+        enter(t);
+        const unsigned char *vt = lds + (t % NSLOT) * SLOT;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            // P of rows [64g + 32kb, +32): block p = 2g + kb
+        for (int kb = 0; kb < VKB; ++kb) {
+            // P of rows [32 (VKB g + kb), +32): block VKB g + kb
             uint4 pk = Pk[kb];
 #pragma unroll
-            for (int gg = 1; gg < 8; ++gg)
-                if (g == gg) pk = Pk[2 * gg + kb];
+            for (int gg = 1; gg < 16 / VKB; ++gg)
+                if (g == gg) pk = Pk[VKB * gg + kb];
             const bf16x8_t P = __builtin_bit_cast(bf16x8_t, pk);
+            // the transposed reads run LV MFMAs ahead (2 reads per MFMA)
+            constexpr int LV = OE < 4 ? OE : 4;
+            i16x4_t va[OE], vb[OE];
 #pragma unroll
             for (int e = 0; e < OE; ++e) {
                 const uint32_t pa = vbase[e & 3] + 128 * (e >> 2) + 64 * DE * kb;
-                const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                va[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4_t *)(vt + pa));
-                const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                vb[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4_t *)(vt + pa + 32 * DE));
-                const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+            }
+#pragma unroll
+            for (int e = 0; e < OE; ++e) {
+                const uint2 ua = __builtin_bit_cast(uint2, va[e]), ub = __builtin_bit_cast(uint2, vb[e]);
                 const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
                 O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, P, O[e], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LV, 0);
+            static_for<OE - LV>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            });
+            __builtin_amdgcn_sched_group_barrier(0x008, LV, 0);
         }
     }
     const int qi = 16 * w + l16;
@@ -691,7 +802,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     const int tg = QU ? 0 : (w & 1), ch = QU ? w : (w >> 1);
     const int l16 = lane & 15, kg = lane >> 4;
     const int ndense = a.hdr[HDR_NDENSE];
-    const int nitems = a.hdr[HDR_NHEAVY];
+    // streaming items: those of long blocks from the list's front, then the others from
+    // its back (entry nmax - 1 first)
+    const int nlong = a.hdr[HDR_NHEAVY];
+    const int nitems = nlong + a.hdr[HDR_NHEAVY_SHORT];
     // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
     // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
     // items from its own counter, in order, and once it is empty take the other
@@ -756,7 +870,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         lds_barrier();
         const int it = *s_item;
         if (it < 0) break;
-        const int2 item = a.items[it];
+        const int2 item = a.items[it < nlong ? it : a.nmax - 1 - (it - nlong)];
         const int j = item.x, tq = item.y;
         const int sb = a.seg_start[j];
         const int ntok = min(kHeavyTile, a.seg_start[j + 1] - sb - tq);
@@ -867,6 +981,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                             S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], xr[q * HWW + i], S0, 0, 0, 0);
                             S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i + 1], xr[q * HWW + i + 1], S1, 0, 0, 0);
                         }
+                        // keep LK fragment reads ahead of the MFMAs (by itself the
+                        // scheduler waits for each read right before its MFMA)
+                        constexpr int LK = HWW < 4 ? HWW : 4;
+                        __builtin_amdgcn_sched_group_barrier(0x100, LK, 0);
+                        static_for<HWW - LK>([&](auto) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        });
+                        __builtin_amdgcn_sched_group_barrier(0x008, LK, 0);
                     }
                 }
                 xw[rb * 64] = S0 + S1;
@@ -942,18 +1065,30 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                                     if (vr == p) pk = Pk[p * (RV / 32) + kb];
                             }
                             const bf16x8_t P = __builtin_bit_cast(bf16x8_t, pk);
+                            // rows 32kb + 4kg + l16/4 (first read) and 16 rows further
+                            // (second); the reads run LV MFMAs ahead
+                            constexpr int LV = OBW < 3 ? OBW : 3;
+                            i16x4_t va[OBW], vb[OBW];
 #pragma unroll
                             for (int e = 0; e < OBW; ++e) {
-                                // rows 32kb + 4kg + l16/4 (first read) and 16 rows further (second)
                                 const uint32_t pa = vt + vbase[e & 3] + 128 * (e >> 2) + 64 * DEV * kb;
-                                const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                va[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                     (__attribute__((address_space(3))) i16x4_t *)(ring + pa));
-                                const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                vb[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                     (__attribute__((address_space(3))) i16x4_t *)(ring + pa + 32 * DEV));
-                                const uint2 ua = __builtin_bit_cast(uint2, va), ub = __builtin_bit_cast(uint2, vb);
+                            }
+#pragma unroll
+                            for (int e = 0; e < OBW; ++e) {
+                                const uint2 ua = __builtin_bit_cast(uint2, va[e]), ub = __builtin_bit_cast(uint2, vb[e]);
                                 const bf16x8_t Av = __builtin_bit_cast(bf16x8_t, make_uint4(ua.x, ua.y, ub.x, ub.y));
                                 O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, P, O[e], 0, 0, 0);
                             }
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LV, 0);
+                            static_for<OBW - LV>([&](auto) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                            });
+                            __builtin_amdgcn_sched_group_barrier(0x008, LV, 0);
                         }
                     }
                 }
@@ -1224,7 +1359,7 @@ int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
 hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {
     HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
                  a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.dense, a.d_in,
-                 (uint16_t *)a.o};
+                 (uint16_t *)a.o, a.n};
     return launch_heavy(ha, a.d_emb, s);
 }
 

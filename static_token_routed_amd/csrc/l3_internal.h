@@ -26,6 +26,9 @@ constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 feat
 constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
+// streaming items of blocks with at least this many rows head their list (the others are
+// written from its back), so the longest start first
+constexpr int kHeavyLongRows = 256;
 constexpr int kHeavyMinTokensWide = 64;  // the token threshold at d_in 4096
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
 constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...
@@ -38,6 +41,7 @@ enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4
        HDR_NSPLIT = 6, HDR_NLIGHT_LONG = 7,
        HDR_QUEUE = 8,           // 8 per-XCD counters of the matrix-core gather, then its dense counter
        HDR_NLIGHT_MID = 17,
+       HDR_NHEAVY_SHORT = 18,   // streaming items of blocks under kHeavyLongRows rows (list's back)
        HDR_WORDS = 64 };
 // Light items of blocks with at least kLightLongRows rows, then those with at least
 // kLightMidRows, are listed apart and taken first, so the longest start first: the

@@ -311,28 +311,37 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
     const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
     const int nl = (lng || mid) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0;
-    const int nh = bi.nh, nd = bi.nd;
-    // wave-inclusive scans of nl, nq, nm, nh and nd
-    int sl = nl, sq = nq, sm = nm, sh = nh, sd = nd;
+    // streaming items of long blocks to the front of the heavy list, the rest to its back
+    const bool hlong = bi.d >= kHeavyLongRows;
+    const int nh = hlong ? bi.nh : 0, ns = hlong ? 0 : bi.nh, nd = bi.nd;
+    // wave-inclusive scans of nl, nq, nm, nh, ns and nd
+    int sl = nl, sq = nq, sm = nm, sh = nh, ss = ns, sd = nd;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int a = __shfl_up(sl, o), e = __shfl_up(sq, o), f = __shfl_up(sm, o),
-                  b = __shfl_up(sh, o), c = __shfl_up(sd, o);
-        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; sd += c; }
+                  b = __shfl_up(sh, o), g = __shfl_up(ss, o), c = __shfl_up(sd, o);
+        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; ss += g; sd += c; }
     }
-    int bl = 0, bq = 0, bm = 0, bh = 0, bd = 0;
+    int bl = 0, bq = 0, bm = 0, bh = 0, bs = 0, bd = 0;
     if (lane == 63) {
         if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
         if (sq) bq = atomicAdd(&hdr[HDR_NLIGHT_LONG], sq);
         if (sm) bm = atomicAdd(&hdr[HDR_NLIGHT_MID], sm);
         if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
+        if (ss) bs = atomicAdd(&hdr[HDR_NHEAVY_SHORT], ss);
         if (sd) bd = atomicAdd(&hdr[HDR_NDENSE], sd);
     }
     bl = __shfl(bl, 63) + sl - nl;
     bq = __shfl(bq, 63) + sq - nq;
     bm = __shfl(bm, 63) + sm - nm;
     bh = __shfl(bh, 63) + sh - nh;
+    bs = __shfl(bs, 63) + ss - ns;
     bd = __shfl(bd, 63) + sd - nd;
+    if (!hlong) {
+        // from the back of the heavy list: entries nmax - 1 - bs, nmax - 2 - bs, ...
+        for (int q = 0; q < bi.nh; ++q) heavy[nmax - 1 - (bs + q)] = make_int2(j, q * kHeavyTile);
+        bi.nh = 0;
+    }
     if (mid) {
         // from the back of light_long: entries n - 1 - bm, n - 2 - bm, ...
         for (int q = 0; q < bi.nl; ++q)
