@@ -181,9 +181,9 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
         const uint16_t *krow = a.WK + row * d_in;
         static_for<NCI>([&](auto c) {
             const int64_t col = c * 512 + kcol;
-            async_ld16_o<c * 1024>(krow + (col < d_in ? col : 0), slot);
+            async_ld16_o_nt<c * 1024>(krow + (col < d_in ? col : 0), slot);
         });
-        async_ld16_o<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
+        async_ld16_o_nt<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
     };
     float m[NT], l[NT], acc[NT][VE];
 #pragma unroll
@@ -479,8 +479,8 @@ __device__ inline void wait_stages(int later) {
     }
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform runtime n in [0, 20] (a larger n waits for
-// vmcnt(20), which is always safe: it only waits for more)
+// s_waitcnt vmcnt(n) for a wave-uniform runtime n in [0, 24] (a larger n waits for
+// vmcnt(24), which is always safe: it only waits for more)
 __device__ inline void wait_vmcnt_rt(int n) {
     switch (n) {
         case 0: wait_vmcnt<0>(); break;
@@ -503,7 +503,11 @@ __device__ inline void wait_vmcnt_rt(int n) {
         case 17: wait_vmcnt<17>(); break;
         case 18: wait_vmcnt<18>(); break;
         case 19: wait_vmcnt<19>(); break;
-        default: wait_vmcnt<20>(); break;
+        case 20: wait_vmcnt<20>(); break;
+        case 21: wait_vmcnt<21>(); break;
+        case 22: wait_vmcnt<22>(); break;
+        case 23: wait_vmcnt<23>(); break;
+        default: wait_vmcnt<24>(); break;
     }
 }
 
@@ -512,23 +516,27 @@ __device__ inline void wait_vmcnt_rt(int n) {
 // (instead of once per 32).  Wavefront w owns tokens [16w, 16w + 16) and all rows;
 // all d_t scores of a token stay in 32 accumulators of v_mfma_f32_16x16x32_bf16, so
 // the softmax is exact.
-// The item is one sequence of stages through a ring of 4 slots of 40 KB, the copies
-// running 3 stages ahead (up to about 100 KB in flight per CU), each stage a barrier:
+// The K and V rows go through a ring of 4 slots of 32 KB, the copies running 3
+// stages ahead, each stage a barrier:
 //  * scores stages: for each 64-column chunk of d_in, the K rows [0, 256) and, when
-//    d_t > 256, [256, 512) as two stages (32 KB each, 128-byte row pieces); the
-//    first of them also brings the 64 tokens' x chunk (8 KB), whose fragments the
-//    wavefront keeps in registers for the second;
+//    d_t > 256, [256, 512) as two stages (128-byte row pieces);
 //  * values stages: V rows in blocks of 32 (d_emb 512) or 64, read transposed.
-// K row groups wholly past d_t are not copied (their stale scores are masked); the
-// waits count the copies each stage actually issues.
+// The tokens' x chunks (8 KB; x rows are read once per item, from HBM, while the K
+// rows mostly hit the caches) have 4 slots of their own and are copied 3 column
+// chunks ahead; the wavefront reads its x fragments at a chunk's first stage and
+// keeps them in registers for the second.  K row groups wholly past d_t are not
+// copied (their stale scores are masked); the waits count the copies each stage
+// actually issued.
 template <int XQ, int DE>
 __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *lds, uint32_t lds0,
                                            int sb, int tq, int ntok, int64_t r0, int d, int w) {
     constexpr int64_t d_in = 64 * XQ;
     constexpr int NKC = XQ;                  // 64-column chunks of d_in
-    constexpr int KH = 256 * 128;            // K stage: 256 rows x 128 bytes
-    constexpr int SLOT = KH + 64 * 128;      // + the x chunk: 64 tokens x 128 bytes (40 KB)
+    constexpr int SLOT = 256 * 128;          // K stage: 256 rows x 128 bytes (32 KB)
     constexpr int NSLOT = 4;                 // ring slots: copies run NSLOT - 1 stages ahead
+    constexpr int XS = 64 * 128;             // x chunk: 64 tokens x 128 bytes
+    constexpr int NXS = 4;                   // x slots: chunks run NXS - 1 column chunks ahead
+    constexpr int XBASE = NSLOT * SLOT;
     constexpr int VROWS = DE == 512 ? 32 : 64;  // V rows per values stage
     constexpr int VST = VROWS * DE * 2;      // <= 32 KB
     constexpr int VCP = VST / 1024 / 4;      // V copies per wavefront and stage
@@ -536,7 +544,8 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
     constexpr int RPC = 512 / DE;            // V rows per 1 KB copy
     constexpr int CPR = DE / 8;              // 16-byte chunks per V row
     constexpr int OE = DE / 16;              // 16-column output blocks
-    static_assert(VCP >= 1 && CPR >= 8 && VST <= SLOT && NSLOT * SLOT <= kSlots * kSlot + kXchg, "stages");
+    static_assert(VCP >= 1 && CPR >= 8 && VST <= SLOT && XBASE + NXS * XS <= kSlots * kSlot + kXchg,
+                  "stages");
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, kg = lane >> 4;
     const int nh = d > 256 ? 2 : 1;          // K row halves holding rows below d_t
@@ -548,9 +557,9 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
     lds_barrier();
 
     // Copies of a scores stage of half r: K rows 256r + 64w + [8i, 8i + 8) for i < 8
-    // (rows past d_t repeat row d_t - 1; groups wholly past it are skipped), and for
-    // r = 0 the x rows of tokens [8q, 8q + 8) for q = 2w + i; lane l fills chunk l % 8
-    // of row 8q + l / 8 of the stage with global chunk (l % 8) ^ (l / 8).
+    // (rows past d_t repeat row d_t - 1; groups wholly past it are skipped); of an x
+    // chunk: the x rows of tokens [8q, 8q + 8) for q = 2w + i.  Lane l fills chunk
+    // l % 8 of row 8q + l / 8 with global chunk (l % 8) ^ (l / 8).
     const int gch = (lane & 7) ^ (lane >> 3);
     uint32_t koff[16];  // [8r + i]
 #pragma unroll
@@ -565,12 +574,22 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
         xsrc[i] = a.x + (int64_t)a.perm[sb + tq + min(tk, ntok - 1)] * d_in + gch * 8;
     }
     const uint16_t *kbase = a.WK + r0 * d_in;
-    // copies this wavefront issues for stage t (0 past the end)
-    auto copies = [&](int t) -> int {
+    // copies of stage t's K or V rows this wavefront issues (0 past the end)
+    auto kv_copies = [&](int t) -> int {
         if (t >= total) return 0;
         if (t >= NK) return VCP;
         const int r = nh == 2 ? (t & 1) : 0;
-        return max(0, min(8, (d - 256 * r - 64 * w + 7) / 8)) + (r == 0 ? 2 : 0);
+        return max(0, min(8, (d - 256 * r - 64 * w + 7) / 8));
+    };
+    // x chunk copies issued when stage s starts: chunk c(s) + NXS - 1, at the first
+    // stage of chunk c(s) (its slot's previous chunk, c(s) - 1, is done by then)
+    auto x_copies = [&](int s) -> int {
+        if (s < 0 || s >= NK || (nh == 2 && (s & 1))) return 0;
+        return (nh == 2 ? s >> 1 : s) + NXS - 1 < NKC ? 2 : 0;
+    };
+    auto issue_x = [&](int c) {
+        const uint32_t xb = lds0 + (uint32_t)(XBASE + (c % NXS) * XS) + 2 * w * 1024;
+        static_for<2>([&](auto i) { async_ld16_o_nt<i * 1024>(xsrc[i] + (int64_t)c * 64, xb); });
     };
     auto issue = [&](int t) {
         if (t >= total) return;
@@ -583,8 +602,6 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
                 static_for<8>([&](auto i) {
                     if (64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
                 });
-                const uint32_t xb = base + KH + 2 * w * 1024;
-                static_for<2>([&](auto i) { async_ld16_o<i * 1024>(xsrc[i] + col, xb); });
             } else {
                 static_for<8>([&](auto i) {
                     if (256 + 64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[8 + i], kb);
@@ -605,13 +622,18 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
             });
         }
     };
-    // a stage starts once its own copies have landed (those of the next two may still
-    // be in flight) and every wavefront is past the previous stage, whose slot the
-    // copies issued now overwrite
+    // Issue order: x chunks 0 .. NXS - 2, stages 0 .. NSLOT - 2, then when stage s
+    // starts the rows of stage s + NSLOT - 1 and (at a chunk's first stage) an x chunk.
+    // Stage t needs its rows (issued when stage t - 3 started) and, at a chunk's first
+    // stage, its x chunk: with two stages per chunk issued earlier still, with one
+    // right after those rows.  Copies complete in order, so what may still be in
+    // flight is everything issued after the later of the two.
     auto enter = [&](int t) {
-        wait_vmcnt_rt(copies(t + 1) + copies(t + 2));
+        wait_vmcnt_rt((nh == 2 ? x_copies(t - 3) : 0) + kv_copies(t + 1) + x_copies(t - 2) +
+                      kv_copies(t + 2) + x_copies(t - 1));
         lds_barrier();
         issue(t + NSLOT - 1);
+        if (x_copies(t)) issue_x((nh == 2 ? t >> 1 : t) + NXS - 1);
     };
 
     // fragment addresses: row (or token) 16b + (l & 15), chunk (4ks + l/16) ^ (l & 7)
@@ -622,6 +644,7 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
     f32x4_t S[32];
 #pragma unroll
     for (int rb = 0; rb < 32; ++rb) S[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NXS - 1 && c < NKC; ++c) issue_x(c);
 #pragma unroll
     for (int t = 0; t < NSLOT - 1; ++t) issue(t);
     // one scores stage: the 16 row blocks of half H against the wavefront's 16 tokens
@@ -651,27 +674,26 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
         });
         __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);       // the last LA MFMAs
     };
-    auto xload = [&](const unsigned char *st) {
+    auto xload = [&](int c) {
+        const unsigned char *xs = lds + XBASE + (c % NXS) * XS;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            xr[ks] = *reinterpret_cast<const bf16x8_t *>(st + KH + (16 * w) * 128 + fofs[ks]);
+            xr[ks] = *reinterpret_cast<const bf16x8_t *>(xs + (16 * w) * 128 + fofs[ks]);
     };
     if (nh == 2) {
         // both halves of a column chunk in one iteration, so each accumulator has one home
         for (int c = 0; c < NKC; ++c) {
             enter(2 * c);
-            const unsigned char *st0 = lds + ((2 * c) % NSLOT) * SLOT;
-            xload(st0);
-            kstage(st0, std::integral_constant<int, 0>{});
+            xload(c);
+            kstage(lds + ((2 * c) % NSLOT) * SLOT, std::integral_constant<int, 0>{});
             enter(2 * c + 1);
             kstage(lds + ((2 * c + 1) % NSLOT) * SLOT, std::integral_constant<int, 1>{});
         }
     } else {
         for (int c = 0; c < NKC; ++c) {
             enter(c);
-            const unsigned char *st0 = lds + (c % NSLOT) * SLOT;
-            xload(st0);
-            kstage(st0, std::integral_constant<int, 0>{});
+            xload(c);
+            kstage(lds + (c % NSLOT) * SLOT, std::integral_constant<int, 0>{});
         }
     }
 
@@ -890,7 +912,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
             const uint16_t *xp = a.x + (int64_t)tok * d_in + 32 * HWW * ch + 8 * kg;
 #pragma unroll
             for (int f = 0; f < NXR; ++f)
-                xr[f] = *reinterpret_cast<const bf16x8_t *>(xp + 32 * (16 * (f / HWW) + f % HWW));
+                xr[f] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t *>(xp + 32 * (16 * (f / HWW) + f % HWW)));
             // Take delivery of x here, before any copy of this item is in flight: the
             // compiler's own wait for these loads would otherwise be repeated in every
             // group and drain the copy ring (it does not count the asynchronous copies).
@@ -917,7 +939,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                     const int64_t grow = r0 + min(c_gr + 16 * c_b + row, d - 1);
                     int64_t col = (int64_t)kKCols * c_p + 8 * (lane ^ (row & 7));
                     if (col >= d_in) col = 0;  // past d_in: filler, never read
-                    async_ld16_o<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
+                    async_ld16_o_nt<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
                 });
                 if (++c_p == nq) {
                     c_p = 0;
@@ -931,7 +953,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                     const int row = cp * RPC + lane / CPR;
                     const int64_t grow = r0 + min(c_gr + RV * c_b + row, d - 1);
                     const int cc = (lane % CPR) ^ (2 * (row & 3));
-                    async_ld16_o<c * 1024>(a.WV + grow * DE + DEV * c_p + 8 * cc, base + 4 * w * 1024);
+                    async_ld16_o_nt<c * 1024>(a.WV + grow * DE + DEV * c_p + 8 * cc, base + 4 * w * 1024);
                 });
                 if (++c_p == NVH) {
                     c_p = 0;

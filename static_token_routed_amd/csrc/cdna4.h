@@ -100,6 +100,18 @@ __device__ inline void async_ld16_o(const void *gptr, uint32_t lds_base) {
                      : "memory", "scc");
 }
 
+// async_ld16_o with the non-temporal hint (nt): for rows read once per call (cold
+// table rows, the tokens' x rows), so they do not push out of L2 the rows that other
+// workgroups are about to read again.
+template <uint32_t OFF>
+__device__ inline void async_ld16_o_nt(const void *gptr, uint32_t lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    __asm__ volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                     :
+                     : "s"(m0v), "v"(gptr), "i"(OFF)
+                     : "memory", "scc");
+}
+
 template <uint32_t OFF>
 __device__ inline void async_ld16_sbo(const void *sbase, uint32_t voff, uint32_t lds_base) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
