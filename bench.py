@@ -46,8 +46,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; a decode workload's own step count)")
-    ap.add_argument("--warmup", type=int, default=5)
+                    help="timed steps (default 50; a decode workload's own step count)")
+    # the first 20 or so forwards of a process run about 5 % slower than the rest (the
+    # GPU settling after start-up), so the default warm-up covers them
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="paper_bf16")
     ap.add_argument("--cache-rows", type=int, default=0,
                     help="decode: keep the rows of the most frequent IDs (up to this many rows) in a "
@@ -74,7 +76,7 @@ def parse():
     args = ap.parse_args()
     args.steps_given = args.steps is not None
     if args.steps is None:
-        args.steps = 20
+        args.steps = 50
     return args
 
 
