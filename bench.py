@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TF = 157.3   # MI355X fp32 vector FMA
 # the library's timed stages.  ln_stats_gemm: LayerNorm's row statistics, from the
 # quadratic form o^T G o (a GEMM against G = W_c^T W_c and a finalize) above 512 tokens,
 # from the W_up GEMM at or below; mix_prep: the weight-only factors F and G (above 512
@@ -288,7 +289,11 @@ def main():
     Wup, Wmix = synth.dense(cfg, "W_up"), synth.dense(cfg, "W_mix")
     g, b = synth.ln_params(cfg)
 
+    is32 = cfg.dtype == "f32"
+
     def dev(a):
+        if is32:
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
     dx, dWK, dWup, dWmix = dev(x), dev(WK), dev(Wup), dev(Wmix)
@@ -299,9 +304,9 @@ def main():
     print(f"[bench] {cfg.name}: inputs generated and uploaded in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
 
-    plan = l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, "bf16", cfg.ln_eps)
+    plan = l3.L3Plan(off, cfg.k, cfg.d_in, cfg.d_emb, cfg.d_up, cfg.d_out, cfg.dtype, cfg.ln_eps)
     n = cfg.n
-    out = torch.empty((n, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((n, cfg.d_out), dtype=torch.float32 if is32 else torch.bfloat16, device="cuda")
     ws = plan.workspace(n)
 
     def step():
@@ -357,7 +362,7 @@ def main():
     min_tok, min_rows = l3.l3_worklist_rule(plan.handle)
     heavy = (cnt >= min_tok) | (d >= min_rows)
     # a tied configuration's row serves both roles: its algorithmic bytes are one row
-    row_b = (cfg.d_in + (0 if cfg.tied else cfg.d_emb)) * 2
+    row_b = (cfg.d_in + (0 if cfg.tied else cfg.d_emb)) * (4 if is32 else 2)
     R = int(d.sum())
     kv = {"gather_attention": R * row_b, "gather_mfma": int(d[heavy].sum()) * row_b,
           "gather_light": int(d[~heavy].sum()) * row_b}
@@ -365,7 +370,7 @@ def main():
     # [o | x] (K = d_emb + d_in) against [F | W2], F = W1 diag(gamma) W_c, and
     # LayerNorm's variance from o^T G o (GEMM o G, N = K = d_emb), F and G formed per
     # call in the preparation stage; smaller batches run W_up and W_mix over [LN(h) | x]
-    factored = n > 512
+    factored = n > 512 and not is32
     up_flops = 2.0 * n * cfg.d_emb * (cfg.d_emb if factored else cfg.d_up)
     mix_k = (cfg.d_emb + cfg.d_in) if factored else (cfg.d_up + cfg.d_in)
     mix_flops = 2.0 * n * cfg.d_out * mix_k
@@ -378,13 +383,15 @@ def main():
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "work_per_launch": f"{kv[k_]} B of distinct K/V rows ({rows} rows x {row_b} B)"}
     kernels["gather_attention"]["kernels"] = "gather_mfma + gather_light"
-    kernels["ln_stats_gemm"] = {"bound": "mfma",
+    # fp32 plans run their GEMMs on the vector ALUs (fp32 FMA peak 157.3 TFLOP/s)
+    gemm_bound, gemm_peak = ("alu", FP32_VALU_PEAK_TF) if is32 else ("mfma", MFMA_BF16_PEAK_TF)
+    kernels["ln_stats_gemm"] = {"bound": gemm_bound,
                                 "achieved": up_flops / (avg["ln_stats_gemm"] * 1e-3) / 1e12,
-                                "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                                "peak": gemm_peak, "unit": "TFLOP/s",
                                 "work_per_launch": f"{up_flops:.4g} FLOP ("
                                 + ("o G, K = N = d_emb" if factored else "W_up, K = d_emb") + ")"}
-    kernels["w_mix_gemm"] = {"bound": "mfma", "achieved": mix_flops / (avg["w_mix_gemm"] * 1e-3) / 1e12,
-                             "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+    kernels["w_mix_gemm"] = {"bound": gemm_bound, "achieved": mix_flops / (avg["w_mix_gemm"] * 1e-3) / 1e12,
+                             "peak": gemm_peak, "unit": "TFLOP/s",
                              "work_per_launch": f"{mix_flops:.4g} FLOP (K = {mix_k})"}
     for k_, v_ in kernels.items():
         v_["frac"] = v_["achieved"] / v_["peak"]
@@ -413,7 +420,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded Zipf token IDs, Zipf-shaped allocation, N(0, 1/sqrt(fan_in)) weights)",
         "config": {"workload": f"{cfg.name}: vocab {cfg.vocab}, v {cfg.v}, k {cfg.k}, d_in {cfg.d_in}, "
                                f"d_emb {cfg.d_emb}, d_up {cfg.d_up}, d_out {cfg.d_out}, "
@@ -768,7 +775,7 @@ def cpu_baseline(cfg, off, ids, x, WK, WV, Wup, Wmix, g, b, seconds):
     grown until about `seconds` of wall time; tokens/s over the timed chunks."""
     import oracle
 
-    f32 = lambda a: synth_f32(a)
+    f32 = lambda a: synth_f32(a, cfg.dtype)
     nt = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(123)
     order = rng.permutation(len(ids))
@@ -816,9 +823,9 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def synth_f32(a):
+def synth_f32(a, dtype):
     import synth
-    return synth.as_f32(a, "bf16")
+    return synth.as_f32(a, dtype)
 
 
 if __name__ == "__main__":

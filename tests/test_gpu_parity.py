@@ -174,15 +174,19 @@ def small_cfg_gpu():
     g.close()
 
 
-def test_small_bf16_config_sampled(small_cfg_gpu):
+def test_small_bf16_config_full(small_cfg_gpu):
+    """Every one of the small bf16 workload's 16384 output rows against the oracle."""
     g = small_cfg_gpu
     case = g.case
     got = to_np(g.forward())
-    rows = sample_rows(case.ids, 512)
-    err = rowwise_err(got[rows], oracle_out(case, rows=rows))
-    print(f"small_bf16 config: {len(rows)} sampled tokens, err {err:.2e}", flush=True)
-    assert err <= case.tol
     assert np.all(np.isfinite(got))
+    errs = []
+    for c0 in range(0, len(case.ids), 8192):
+        r = np.arange(c0, min(c0 + 8192, len(case.ids)))
+        errs.append(rowwise_err(got[r], oracle_out(case, rows=r)))
+    err = max(errs)
+    print(f"small_bf16 config: all {len(case.ids)} tokens, max row-normwise err {err:.2e}", flush=True)
+    assert err <= case.tol
 
 
 def _close(a, b, tol):
