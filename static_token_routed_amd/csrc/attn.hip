@@ -119,6 +119,9 @@ constexpr int light_tokens_for() { return NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3); }
 // A ring slot is NCI 1 KB pieces of the K row (lane l copies bytes [16l, 16l + 16)
 // of piece c, which are exactly the columns c*512 + 8l .. + 8 it multiplies) and
 // one 1 KB piece of the V row (lanes past the row copy its first bytes again).
+// With tied tables (W_V the same buffer as W_K, d_emb = d_in <= 512: the pages' tied
+// variant) the V row is the K row, whose single piece already holds its d_emb values
+// in order, so no V piece is copied and each row enters the CU once.
 constexpr int kLightWaveLds = 20480;  // LDS bytes per wavefront (two workgroups per CU)
 template <int NCI>
 constexpr int light_ring_rows() {
@@ -142,14 +145,16 @@ __device__ inline void wait_rows(int later) {
 // (unnormalised row, running max and sum per token) in their own ring and
 // wavefront 0 merges them: M = max_w m_w, o = sum_w e^(m_w - M) acc_w / sum_w
 // e^(m_w - M) l_w.  Long items thus run four times as many rows in parallel.
-template <int NCI, int VE, int NT, int SPLIT>
+template <int NCI, int VE, int NT, int SPLIT, bool TIED>
 __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r0, int d, int w,
                                            int lane, unsigned char *lds_all) {
+    static_assert(!TIED || NCI == 1, "tied rows fit one piece");
+    constexpr int NP = NCI + (TIED ? 0 : 1);  // 1 KB copies per row
     int tok[NT];  // the item's tokens: sorted positions p0 .. p0 + NT - 1
 #pragma unroll
     for (int q = 0; q < NT; ++q) tok[q] = a.perm[p0 + q];
     constexpr int LR = light_ring_rows<NCI>();
-    constexpr int SLOT = (NCI + 1) * 1024;
+    constexpr int SLOT = NP * 1024;
     unsigned char *const ring = lds_all + w * kLightWaveLds;
     const uint32_t ring0 = lds_addr(ring);
     const int64_t d_in = a.d_in, d_emb = a.d_emb;
@@ -183,7 +188,7 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
             const int64_t col = c * 512 + kcol;
             async_ld16_o_nt<c * 1024>(krow + (col < d_in ? col : 0), slot);
         });
-        async_ld16_o_nt<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
+        if constexpr (!TIED) async_ld16_o_nt<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
     };
     float m[NT], l[NT], acc[NT][VE];
 #pragma unroll
@@ -196,14 +201,14 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
     for (int j = 0; j < LR && j < nr; ++j) issue(j);
     for (int j = 0; j < nr; ++j) {
         // rows issued after row j: min(nr, j + LR) - j - 1
-        wait_rows<NCI + 1, LR - 1>(min(nr, j + LR) - j - 1);
+        wait_rows<NP, LR - 1>(min(nr, j + LR) - j - 1);
         __asm__ volatile("" ::: "memory");
         const unsigned char *sl = ring + (j % LR) * SLOT;
         uint4 kv[NCI];
 #pragma unroll
         for (int c = 0; c < NCI; ++c) kv[c] = *reinterpret_cast<const uint4 *>(sl + c * 1024 + lane * 16);
         float vv[VE];
-        load_v<VE>(reinterpret_cast<const uint16_t *>(sl + NCI * 1024) + lane * VE, vv);
+        load_v<VE>(reinterpret_cast<const uint16_t *>(sl + (TIED ? 0 : NCI * 1024)) + lane * VE, vv);
         if (j + LR < nr) {
             // the slot is refilled only after this wavefront's reads of it are done
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -296,19 +301,19 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
     }
 }
 
-template <int NCI, int VE, int SPLIT>
+template <int NCI, int VE, int SPLIT, bool TIED>
 __device__ __forceinline__ void light_item_nt(const LightArgs &a, int p0, int64_t r0, int d, int nt,
                                               int w, int lane, unsigned char *lds) {
     constexpr int TL = light_tokens_for<NCI>();
     switch (nt) {
-        case 1: light_item<NCI, VE, 1, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 3: if constexpr (TL >= 3) light_item<NCI, VE, 3, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 4: if constexpr (TL >= 4) light_item<NCI, VE, 4, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 5: if constexpr (TL >= 5) light_item<NCI, VE, 5, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 6: if constexpr (TL >= 6) light_item<NCI, VE, 6, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 7: if constexpr (TL >= 7) light_item<NCI, VE, 7, SPLIT>(a, p0, r0, d, w, lane, lds); break;
-        case 8: if constexpr (TL >= 8) light_item<NCI, VE, 8, SPLIT>(a, p0, r0, d, w, lane, lds); break;
+        case 1: light_item<NCI, VE, 1, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 3: if constexpr (TL >= 3) light_item<NCI, VE, 3, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 4: if constexpr (TL >= 4) light_item<NCI, VE, 4, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 5: if constexpr (TL >= 5) light_item<NCI, VE, 5, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 6: if constexpr (TL >= 6) light_item<NCI, VE, 6, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 7: if constexpr (TL >= 7) light_item<NCI, VE, 7, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
+        case 8: if constexpr (TL >= 8) light_item<NCI, VE, 8, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
         default: break;
     }
 }
@@ -322,7 +327,7 @@ __device__ __forceinline__ void light_item_nt(const LightArgs &a, int p0, int64_
 // ones), so the longest start first and each share mixes long and short ones.
 // (Handing items out through per-XCD atomic counters measured 2.6 times slower: the
 // counters serialise thousands of short items.)
-template <int NCI, int VE>
+template <int NCI, int VE, bool TIED = false>
 __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kLightWaveLds];
     const int lane = threadIdx.x & 63;
@@ -341,8 +346,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
         const int4 item = item_at(it);  // a valid ID with >= kLightMidRows rows
         const int p0 = __builtin_amdgcn_readfirstlane(item.x);
         const int nt = __builtin_amdgcn_readfirstlane(item.y);
-        light_item_nt<NCI, VE, 4>(a, p0, __builtin_amdgcn_readfirstlane(item.z),
-                                  __builtin_amdgcn_readfirstlane(item.w), nt, w, lane, lds);
+        light_item_nt<NCI, VE, 4, TIED>(a, p0, __builtin_amdgcn_readfirstlane(item.z),
+                                        __builtin_amdgcn_readfirstlane(item.w), nt, w, lane, lds);
     }
     const int nw = gridDim.x * 4, g = blockIdx.x * 4 + w;
     for (int k = 0;; ++k) {
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
             }
             continue;
         }
-        light_item_nt<NCI, VE, 1>(a, p0, r0, d, nt, w, lane, lds);
+        light_item_nt<NCI, VE, 1, TIED>(a, p0, r0, d, nt, w, lane, lds);
     }
 }
 
@@ -458,6 +463,7 @@ struct HeavyArgs {
     int64_t d_in;
     uint16_t *o;
     int64_t nmax;        // entries of the items array (its back holds the short blocks' items)
+    int tied;            // W_V is W_K (d_emb = d_in): a K row is read again as a V row
 };
 
 constexpr int kSlot = 16384;       // bytes per ring stage
@@ -939,7 +945,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
                     const int64_t grow = r0 + min(c_gr + 16 * c_b + row, d - 1);
                     int64_t col = (int64_t)kKCols * c_p + 8 * (lane ^ (row & 7));
                     if (col >= d_in) col = 0;  // past d_in: filler, never read
-                    async_ld16_o_nt<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
+                    // (read once, unless the same row comes back as a V row)
+                    if (a.tied) async_ld16_o<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
+                    else async_ld16_o_nt<c * 1024>(a.WK + grow * d_in + col, base + 4 * w * 1024);
                 });
                 if (++c_p == nq) {
                     c_p = 0;
@@ -1172,6 +1180,19 @@ constexpr int kLightBlocks = 512;
 
 template <int NCI>
 hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
+    if constexpr (NCI == 1) {
+        // tied tables: one copy per row serves both roles
+        if (la.WK == la.WV && la.d_in == d_emb) {
+            switch (d_emb / 64) {
+                case 1: hipLaunchKernelGGL((k_attn_light_bf16<1, 1, true>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+                case 2: hipLaunchKernelGGL((k_attn_light_bf16<1, 2, true>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+                case 4: hipLaunchKernelGGL((k_attn_light_bf16<1, 4, true>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+                case 8: hipLaunchKernelGGL((k_attn_light_bf16<1, 8, true>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (d_emb / 64) {
         case 1: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 1>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
         case 2: hipLaunchKernelGGL((k_attn_light_bf16<NCI, 2>), dim3(kLightBlocks), dim3(256), 0, s, la); break;
@@ -1381,7 +1402,7 @@ int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
 hipError_t launch_attn_heavy(const AttnArgs &a, hipStream_t s) {
     HeavyArgs ha{(const uint16_t *)a.x, (const uint16_t *)a.WK, (const uint16_t *)a.WV, a.off,
                  a.uniq, a.seg_start, a.perm, a.hdr, a.queue, a.heavy, a.dense, a.d_in,
-                 (uint16_t *)a.o, a.n};
+                 (uint16_t *)a.o, a.n, a.WK == a.WV && a.d_in == a.d_emb};
     return launch_heavy(ha, a.d_emb, s);
 }
 

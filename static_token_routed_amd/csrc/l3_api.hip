@@ -500,7 +500,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.keys_b = take(n * 4);
     L.vals_b = take(n * 4);
     L.rank = take(n * 4);
-    L.hist = take((size_t)kRadix * L.ntiles * 4);
+    L.hist = take((size_t)kRadix * (L.ntiles + 1) * 4);  // + the digit totals (k_hist_scan)
     L.tile_cnt = take(L.ntiles * 4);
     L.inv_perm = take(n * 4);
     L.uniq = take(n * 4);

@@ -29,6 +29,9 @@ constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this ma
 // streaming items of blocks with at least this many rows head their list (the others are
 // written from its back), so the longest start first
 constexpr int kHeavyLongRows = 256;
+// Radix scatter: up to this many 512-key tiles each workgroup forms its own digit
+// offsets from the whole histogram; past it one workgroup forms them all first
+constexpr int kScatterDirectTiles = 64;
 constexpr int kHeavyMinTokensWide = 64;  // the token threshold at d_in 4096
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
 constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...

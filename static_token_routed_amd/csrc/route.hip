@@ -14,7 +14,10 @@
 //                  stable; writes the tile's digit histogram (digit-major).
 //   k_sort_scatter each workgroup forms its tile's digit offsets from the whole
 //                  digit-major histogram (an exclusive prefix), then writes each
-//                  key to offset + rank.
+//                  key to offset + rank.  Past kScatterDirectTiles tiles, where
+//                  every workgroup summing the whole histogram would cost
+//                  O(tiles^2), a wavefront per digit (k_hist_scan) first replaces
+//                  each digit's row by its prefix over the tiles.
 // Blocks: head flags of the sorted keys, counted per tile, then written at the
 // tile's offset (the sum of the earlier tiles' counts).
 // Nothing is read back to the host: counts stay on the device.
@@ -113,6 +116,29 @@ __device__ inline int32_t block_scan_256(int32_t v, int32_t *wsum, int32_t *tota
     return pre + x - v;
 }
 
+// Past kScatterDirectTiles tiles: a wavefront per digit replaces the digit's row of
+// the histogram by its exclusive prefix over the tiles and writes the digit's total
+// after the last row (the histogram region holds kRadix x (ntiles + 1) words).
+__global__ __launch_bounds__(256) void k_hist_scan(int32_t *__restrict__ hist, int ntiles) {
+    const int lane = threadIdx.x & 63;
+    const int d = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int32_t *row = hist + (int64_t)d * ntiles;
+    int32_t carry = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += 64) {
+        const int t = t0 + lane;
+        const int32_t v = t < ntiles ? row[t] : 0;
+        int32_t x = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t u = __shfl_up(x, o);
+            if (lane >= o) x += u;
+        }
+        if (t < ntiles) row[t] = carry + x - v;
+        carry += __shfl(x, 63);
+    }
+    if (lane == 0) hist[(int64_t)kRadix * ntiles + d] = carry;
+}
+
 // One workgroup per kSortTile-key tile.  The destination of digit d's keys in tile t
 // is the exclusive prefix of the digit-major histogram at (d, t): the keys of all
 // smaller digits, plus those of digit d in earlier tiles.  Each workgroup forms the
@@ -122,6 +148,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict_
                                                       const int32_t *__restrict__ vals_in, int n,
                                                       int shift, int from_ids, int vocab,
                                                       const int32_t *__restrict__ hist, int ntiles,
+                                                      int offsets_ready,
                                                       const int32_t *__restrict__ rank,
                                                       int32_t *__restrict__ keys_out,
                                                       int32_t *__restrict__ vals_out) {
@@ -133,6 +160,12 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict_
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int32_t *h = hist + (int64_t)(2 * threadIdx.x + e) * ntiles;
+        if (offsets_ready) {
+            // k_hist_scan has left each row's prefix over the tiles and the totals
+            tot[e] = hist[(int64_t)kRadix * ntiles + 2 * threadIdx.x + e];
+            pre[e] = h[t];
+            continue;
+        }
         int32_t a = 0, b = 0;
 #pragma unroll 8
         for (int u = 0; u < ntiles; ++u) {
@@ -501,8 +534,10 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
         const int from_ids = p == 0;
         hipLaunchKernelGGL(k_sort_rank, dim3((unsigned)ntiles), dim3(256), 0, s, kin, n, shift,
                            from_ids, (int)vocab, b.rank, b.hist, (int)ntiles, b.hdr);
+        const int ready = ntiles > kScatterDirectTiles;
+        if (ready) hipLaunchKernelGGL(k_hist_scan, dim3(kRadix / 4), dim3(256), 0, s, b.hist, (int)ntiles);
         hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)ntiles), dim3(256), 0, s, kin,
-                           vin ? vin : kin, n, shift, from_ids, (int)vocab, b.hist, (int)ntiles,
+                           vin ? vin : kin, n, shift, from_ids, (int)vocab, b.hist, (int)ntiles, ready,
                            b.rank, kout, vout);
         kin = kout;
         vin = vout;

@@ -45,6 +45,12 @@ def _route_case(name):
         ids[:4] = [vocab, -(2 ** 31), 2 ** 31 - 1, vocab + 7]
     elif name in ("n1024", "n1025"):
         ids = rng.integers(0, 300, size=int(name[1:])).astype(np.int32)
+    # more than 64 tiles of 512 keys: the scatter offsets come from one pass over the
+    # histogram first
+    elif name == "tiles_2048":
+        ids = rng.integers(0, vocab, size=1 << 20).astype(np.int32)
+    elif name == "tiles_65":
+        ids = rng.integers(0, 700, size=64 * 512 + 1).astype(np.int32)
     else:
         raise KeyError(name)
     return off, ids
@@ -52,7 +58,7 @@ def _route_case(name):
 
 ROUTE_CASES = ["tiny_f32", "small_bf16", "paper_bf16", "skew_bf16", "all_equal", "all_distinct",
                "single", "ragged", "max_id", "out_of_range", "small_zipf", "small_out_of_range",
-               "n1024", "n1025"]
+               "n1024", "n1025", "tiles_65", "tiles_2048"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -384,19 +390,20 @@ def test_full_size(name):
     g.close()
 
 
-@pytest.mark.parametrize("n", [300, 1200])
-def test_tied_tables(n):
+@pytest.mark.parametrize("d,n", [(256, 300), (256, 1200), (512, 1500), (64, 900)])
+def test_tied_tables(d, n):
     """W_V = W_K (one device table passed for both; d_emb = d_in): the forward equals
-    the oracle's with equal tables (the pages' tied variant)."""
+    the oracle's with equal tables (the pages' tied variant).  Above 512 tokens the
+    wavefront kernel's items read each row once for both roles (d_in <= 512)."""
     cfg = dataclasses.replace(
-        synth.small("tied", vocab=500, k=48, d_in=256, d_emb=256, d_up=256, d_out=192, n=n,
+        synth.small("tied", vocab=500, k=48, d_in=d, d_emb=d, d_up=256, d_out=192, n=n,
                     v=6000, dtype="bf16", seed=11), ids_s=1.05, tied=True)
     case = make_case(cfg)
     assert np.array_equal(case.WK, case.WV)
     g = Gpu(case)
     got = to_np(g.plan.forward(g.x, g.ids, g.WK, g.WK, g.Wup, g.gamma, g.beta, g.Wmix))
     err = rowwise_err(got, oracle_out(case))
-    print(f"tied n={n}: err {err:.2e}", flush=True)
+    print(f"tied d={d} n={n}: err {err:.2e}", flush=True)
     assert err <= case.tol
     g.close()
 
