@@ -513,26 +513,39 @@ __device__ inline void wait_vmcnt_rt(int n) {
         case 21: wait_vmcnt<21>(); break;
         case 22: wait_vmcnt<22>(); break;
         case 23: wait_vmcnt<23>(); break;
-        default: wait_vmcnt<24>(); break;
+        case 24: wait_vmcnt<24>(); break;
+        case 25: wait_vmcnt<25>(); break;
+        case 26: wait_vmcnt<26>(); break;
+        case 27: wait_vmcnt<27>(); break;
+        case 28: wait_vmcnt<28>(); break;
+        case 29: wait_vmcnt<29>(); break;
+        case 30: wait_vmcnt<30>(); break;
+        case 31: wait_vmcnt<31>(); break;
+        default: wait_vmcnt<32>(); break;
     }
 }
 
 // Dense work item: one ID with up to 64 tokens (kDenseTile) and d_t <= 512 rows, so
 // that the rows of the IDs that fill most of a batch are read once per 64 tokens
-// (instead of once per 32).  Wavefront w owns tokens [16w, 16w + 16) and all rows;
-// all d_t scores of a token stay in 32 accumulators of v_mfma_f32_16x16x32_bf16, so
-// the softmax is exact.
-// The K and V rows go through a ring of 4 slots of 32 KB, the copies running 3
-// stages ahead, each stage a barrier:
-//  * scores stages: for each 64-column chunk of d_in, the K rows [0, 256) and, when
-//    d_t > 256, [256, 512) as two stages (128-byte row pieces);
-//  * values stages: V rows in blocks of 32 (d_emb 512) or 64, read transposed.
-// The tokens' x chunks (8 KB; x rows are read once per item, from HBM, while the K
-// rows mostly hit the caches) have 4 slots of their own and are copied 3 column
-// chunks ahead; the wavefront reads its x fragments at a chunk's first stage and
-// keeps them in registers for the second.  K row groups wholly past d_t are not
-// copied (their stale scores are masked); the waits count the copies each stage
-// actually issued.
+// (instead of once per 32).  All d_t scores of a token stay in MFMA accumulators,
+// so the softmax is exact.
+// Scores: the K rows go through a ring of 4 slots of 32 KB, the copies running 3
+// stages ahead, each stage a barrier: for each 64-column chunk of d_in, the rows
+// [0, 256) and, when d_t > 256, [256, 512) (128-byte row pieces).  Wavefront w takes
+// rows 64w + [0, 64) of each half for all 64 tokens (32 accumulators of
+// v_mfma_f32_16x16x32_bf16), so every K fragment is read from LDS once per item (a
+// split by tokens would have each wavefront read all of them: LDS reads, not copies
+// or MFMAs, bounded that form).  The tokens' x chunks (8 KB; read once per item,
+// from HBM) have 4 slots of their own and are copied 3 chunks ahead; the wavefront
+// keeps a chunk's x fragments in registers for both halves.
+// Softmax: per-token maxima and sums of the four row quarters meet in LDS, and the
+// probabilities (bf16, in the MFMA register layout) go through LDS to the wavefront
+// that owns the token (tokens 16w + [0, 16)) for the values.
+// Values: V rows in blocks of 32 (d_emb 512) or 64 through the same 4-slot ring, read
+// transposed; the ring runs on from the scores, so the first two values stages are
+// copied during the last scores stages and the exchange uses the two slots the last
+// scores stages free.  K row groups wholly past d_t are not copied (their stale scores
+// are masked); the waits count the copies each stage actually issued.
 template <int XQ, int DE>
 __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *lds, uint32_t lds0,
                                            int sb, int tq, int ntok, int64_t r0, int d, int w) {
@@ -552,12 +565,12 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
     constexpr int OE = DE / 16;              // 16-column output blocks
     static_assert(VCP >= 1 && CPR >= 8 && VST <= SLOT && XBASE + NXS * XS <= kSlots * kSlot + kXchg,
                   "stages");
+    static_assert(2 * SLOT == 4 * 16 * 64 * 16, "probability exchange: two ring slots");
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, kg = lane >> 4;
     const int nh = d > 256 ? 2 : 1;          // K row halves holding rows below d_t
     const int NK = NKC * nh;                 // scores stages
     const int nvs = (d + VROWS - 1) / VROWS; // values stages
-    const int total = NK + nvs;
 
     // every wavefront has read the item index before the LDS is overwritten
     lds_barrier();
@@ -580,65 +593,79 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
         xsrc[i] = a.x + (int64_t)a.perm[sb + tq + min(tk, ntok - 1)] * d_in + gch * 8;
     }
     const uint16_t *kbase = a.WK + r0 * d_in;
-    // copies of stage t's K or V rows this wavefront issues (0 past the end)
-    auto kv_copies = [&](int t) -> int {
-        if (t >= total) return 0;
-        if (t >= NK) return VCP;
+    // The items of one ID walk the column chunks from different starting chunks
+    // (item q of the block from chunk 5q mod NKC, NKC a power of two), so items of the
+    // same ID running at once ask for different pieces.  The scores are sums over all
+    // chunks in any order.
+    const int c0 = (5 * (tq / kDenseTile)) & (NKC - 1);
+    auto colof = [&](int c) { return (int64_t)((c + c0) & (NKC - 1)) * 64; };
+    static_assert((NKC & (NKC - 1)) == 0, "column chunks: a power of two");
+    // K copies this wavefront issues for scores stage t (0 past the last)
+    auto k_copies = [&](int t) -> int {
+        if (t >= NK) return 0;
         const int r = nh == 2 ? (t & 1) : 0;
         return max(0, min(8, (d - 256 * r - 64 * w + 7) / 8));
     };
-    // x chunk copies issued when stage s starts: chunk c(s) + NXS - 1, at the first
-    // stage of chunk c(s) (its slot's previous chunk, c(s) - 1, is done by then)
+    // copies of ring stage s: scores stages, then the values stages copied early
+    constexpr int VEARLY = NSLOT - 2;
+    auto stage_copies = [&](int s) -> int {
+        return s < NK ? k_copies(s) : (s - NK < VEARLY && s - NK < nvs ? VCP : 0);
+    };
+    // x chunk copies issued when scores stage s starts: chunk c(s) + NXS - 1, at the
+    // first stage of chunk c(s) (its slot's previous chunk, c(s) - 1, is done by then)
     auto x_copies = [&](int s) -> int {
         if (s < 0 || s >= NK || (nh == 2 && (s & 1))) return 0;
         return (nh == 2 ? s >> 1 : s) + NXS - 1 < NKC ? 2 : 0;
     };
     auto issue_x = [&](int c) {
         const uint32_t xb = lds0 + (uint32_t)(XBASE + (c % NXS) * XS) + 2 * w * 1024;
-        static_for<2>([&](auto i) { async_ld16_o_nt<i * 1024>(xsrc[i] + (int64_t)c * 64, xb); });
+        static_for<2>([&](auto i) { async_ld16_o_nt<i * 1024>(xsrc[i] + colof(c), xb); });
     };
-    auto issue = [&](int t) {
-        if (t >= total) return;
-        const uint32_t base = lds0 + (uint32_t)((t % NSLOT) * SLOT);
-        if (t < NK) {
-            const int c = nh == 2 ? (t >> 1) : t, r = nh == 2 ? (t & 1) : 0;
-            const int64_t col = (int64_t)c * 64;
-            const uint32_t kb = base + 8 * w * 1024;
-            if (r == 0) {
-                static_for<8>([&](auto i) {
-                    if (64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
-                });
-            } else {
-                static_for<8>([&](auto i) {
-                    if (256 + 64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[8 + i], kb);
-                });
-            }
+    auto issue_k = [&](int t) {
+        if (t >= NK) return;
+        const uint32_t kb = lds0 + (uint32_t)((t % NSLOT) * SLOT) + 8 * w * 1024;
+        const int c = nh == 2 ? (t >> 1) : t, r = nh == 2 ? (t & 1) : 0;
+        const int64_t col = colof(c);
+        if (r == 0) {
+            static_for<8>([&](auto i) {
+                if (64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[i], kb);
+            });
         } else {
-            // values stage g: rows [VROWS g, +VROWS) (past d_t repeat row d_t - 1); copy
-            // q = VCP w + i holds rows [RPC q, +RPC); chunk c of row r holds global chunk
-            // c ^ 2 (r & 3)
-            const int g = t - NK;
-            const uint32_t vb = base + VCP * w * 1024;
-            static_for<VCP>([&](auto i) {
-                const int q = VCP * w + i;
-                const int row = RPC * q + lane / CPR;
-                const int64_t grow = r0 + min(VROWS * g + row, d - 1);
-                const int cc = (lane % CPR) ^ (2 * (row & 3));
-                async_ld16_o<i * 1024>(a.WV + grow * DE + 8 * cc, vb);
+            static_for<8>([&](auto i) {
+                if (256 + 64 * w + 8 * i < d) async_ld16_sbo<i * 1024>(kbase + col, koff[8 + i], kb);
             });
         }
     };
+    // values stage g: rows [VROWS g, +VROWS) (past d_t repeat row d_t - 1) into ring
+    // slot (NK + g) mod NSLOT; copy q = VCP w + i holds rows [RPC q, +RPC); chunk c of
+    // row r holds global chunk c ^ 2 (r & 3)
+    auto issue_v = [&](int g) {
+        if (g >= nvs) return;
+        const uint32_t vb = lds0 + (uint32_t)(((NK + g) % NSLOT) * SLOT) + VCP * w * 1024;
+        static_for<VCP>([&](auto i) {
+            const int q = VCP * w + i;
+            const int row = RPC * q + lane / CPR;
+            const int64_t grow = r0 + min(VROWS * g + row, d - 1);
+            const int cc = (lane % CPR) ^ (2 * (row & 3));
+            async_ld16_o<i * 1024>(a.WV + grow * DE + 8 * cc, vb);
+        });
+    };
+    auto issue_s = [&](int s) {
+        if (s < NK) issue_k(s);
+        else if (s - NK < VEARLY) issue_v(s - NK);
+    };
     // Issue order: x chunks 0 .. NXS - 2, stages 0 .. NSLOT - 2, then when stage s
-    // starts the rows of stage s + NSLOT - 1 and (at a chunk's first stage) an x chunk.
-    // Stage t needs its rows (issued when stage t - 3 started) and, at a chunk's first
-    // stage, its x chunk: with two stages per chunk issued earlier still, with one
-    // right after those rows.  Copies complete in order, so what may still be in
-    // flight is everything issued after the later of the two.
-    auto enter = [&](int t) {
-        wait_vmcnt_rt((nh == 2 ? x_copies(t - 3) : 0) + kv_copies(t + 1) + x_copies(t - 2) +
-                      kv_copies(t + 2) + x_copies(t - 1));
+    // starts the copies of ring stage s + NSLOT - 1 and (at a chunk's first stage) an x
+    // chunk (none once the ring stage is a values one).  Stage t needs its rows (issued
+    // when stage t - 3 started) and, at a chunk's first stage, its x chunk: with two
+    // stages per chunk issued earlier still, with one right after those rows.  Copies
+    // complete in order, so what may still be in flight is everything issued after the
+    // later of the two.
+    auto enter_k = [&](int t) {
+        wait_vmcnt_rt((nh == 2 ? x_copies(t - 3) : 0) + stage_copies(t + 1) + x_copies(t - 2) +
+                      stage_copies(t + 2) + x_copies(t - 1));
         lds_barrier();
-        issue(t + NSLOT - 1);
+        issue_s(t + NSLOT - 1);
         if (x_copies(t)) issue_x((nh == 2 ? t >> 1 : t) + NXS - 1);
     };
 
@@ -647,90 +674,133 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) fofs[ks] = (uint32_t)l16 * 128 + 16 * ((4 * ks + kg) ^ (lane & 7));
 
-    f32x4_t S[32];
+    // S[4r + j][tb]: lane (l16, kg) holds rows 256r + 64w + 16j + 4kg + i of token 16tb + l16
+    f32x4_t S[8][4];
 #pragma unroll
-    for (int rb = 0; rb < 32; ++rb) S[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) S[rb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < NXS - 1 && c < NKC; ++c) issue_x(c);
 #pragma unroll
-    for (int t = 0; t < NSLOT - 1; ++t) issue(t);
-    // one scores stage: the 16 row blocks of half H against the wavefront's 16 tokens
-    // (rows past d_t are copies of row d_t - 1 or stale, masked below).  The
-    // scheduler is told to keep LA fragment reads ahead of the MFMAs (one read issued
-    // after each MFMA), so the LDS latency hides behind them: by itself it waits for
-    // each read right before its MFMA.
-    constexpr int LA = 6;
-    bf16x8_t xr[2];
+    for (int t = 0; t < NSLOT - 1; ++t) issue_s(t);
+    // One scores stage: the wavefront's 4 row blocks of half H against the 4 token
+    // blocks.  The scheduler is told to keep the fragment reads ahead of the MFMAs (by
+    // itself it waits for each read right before its MFMA).
+    bf16x8_t xr[4][2];
     auto kstage = [&](const unsigned char *st, auto half) {
         constexpr int H = decltype(half)::value;
-        bf16x8_t Af[32];
+        bf16x8_t Af[8];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int rb = 0; rb < 16; ++rb)
-                Af[16 * ks + rb] = *reinterpret_cast<const bf16x8_t *>(st + rb * 2048 + fofs[ks]);
+            for (int j = 0; j < 4; ++j)
+                Af[4 * ks + j] = *reinterpret_cast<const bf16x8_t *>(st + (64 * w + 16 * j) * 128 + fofs[ks]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int rb = 0; rb < 16; ++rb)
-                S[16 * H + rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[16 * ks + rb], xr[ks], S[16 * H + rb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);       // LA LDS reads
-        static_for<32 - LA>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    S[4 * H + j][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[4 * ks + j], xr[tb][ks],
+                                                                              S[4 * H + j][tb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 4 LDS reads
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         });
-        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);       // the last LA MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);    // the last 16 MFMAs
     };
     auto xload = [&](int c) {
         const unsigned char *xs = lds + XBASE + (c % NXS) * XS;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            xr[ks] = *reinterpret_cast<const bf16x8_t *>(xs + (16 * w) * 128 + fofs[ks]);
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                xr[tb][ks] = *reinterpret_cast<const bf16x8_t *>(xs + (16 * tb) * 128 + fofs[ks]);
     };
     if (nh == 2) {
         // both halves of a column chunk in one iteration, so each accumulator has one home
         for (int c = 0; c < NKC; ++c) {
-            enter(2 * c);
+            enter_k(2 * c);
             xload(c);
             kstage(lds + ((2 * c) % NSLOT) * SLOT, std::integral_constant<int, 0>{});
-            enter(2 * c + 1);
+            enter_k(2 * c + 1);
             kstage(lds + ((2 * c + 1) % NSLOT) * SLOT, std::integral_constant<int, 1>{});
         }
     } else {
         for (int c = 0; c < NKC; ++c) {
-            enter(c);
+            enter_k(c);
             xload(c);
             kstage(lds + (c % NSLOT) * SLOT, std::integral_constant<int, 0>{});
         }
     }
 
-    // exact softmax per token over its d_t rows: lane holds rows 16rb + 4kg + i of
-    // token 16w + l16 (scores are only read, never rewritten)
-    float mx = -INFINITY;
+    // Exact softmax per token over its d_t rows.  Every scores copy has landed (only
+    // the early values stages may be in flight), and after this barrier no wavefront
+    // reads a K slot or an x slot again: the slots of the last two scores stages and
+    // the x slots hold the exchange until the values loop starts.
+    lds_barrier();
+    auto rowof = [&](int rb, int i) { return 256 * (rb >> 2) + 64 * w + 16 * (rb & 3) + 4 * kg + i; };
+    float *const xm = reinterpret_cast<float *>(lds + XBASE);         // [wavefront][tb][16] maxima
+    float *const xs = reinterpret_cast<float *>(lds + XBASE + 1024);  // [wavefront][tb][16] sums
+    // probabilities of token block tb: [32-row block][lane], 16 KB
+    auto pbt = [&](int tb) {
+        return reinterpret_cast<uint4 *>(lds + ((NK + VEARLY + (tb >> 1)) % NSLOT) * SLOT + (tb & 1) * 16384);
+    };
+    float M[4];
 #pragma unroll
-    for (int rb = 0; rb < 32; ++rb)
+    for (int tb = 0; tb < 4; ++tb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (16 * rb + 4 * kg + i < d) mx = fmaxf(mx, S[rb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    uint4 Pk[16];
-    float ls = 0.f;
+        for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        float pr[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = (32 * p + 4 * kg + i < d) ? __expf(S[2 * p][i] - mx) : 0.f;
-            pr[4 + i] = (32 * p + 16 + 4 * kg + i < d) ? __expf(S[2 * p + 1][i] - mx) : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ls += pr[i];
-        Pk[p] = make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]),
-                           pack2(pr[6], pr[7]));
+            for (int i = 0; i < 4; ++i)
+                if (rowof(rb, i) < d) mx = fmaxf(mx, S[rb][tb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (kg == 0) xm[(4 * w + tb) * 16 + l16] = mx;
     }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    const float inv = 1.f / ls;
+    lds_barrier();
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+        M[tb] = fmaxf(fmaxf(xm[tb * 16 + l16], xm[(4 + tb) * 16 + l16]),
+                      fmaxf(xm[(8 + tb) * 16 + l16], xm[(12 + tb) * 16 + l16]));
+    // probabilities (bf16, packed as the values' MFMAs take them) of this wavefront's
+    // 32-row blocks p = 8r + 2w + q, and their partial sums per token
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        float ls = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int rb = 4 * h + 2 * q;
+                float pr[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = rowof(rb, i) < d ? __expf(S[rb][tb][i] - M[tb]) : 0.f;
+                    pr[4 + i] = rowof(rb + 1, i) < d ? __expf(S[rb + 1][tb][i] - M[tb]) : 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ls += pr[i];
+                pbt(tb)[(8 * h + 2 * w + q) * 64 + lane] =
+                    make_uint4(pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]), pack2(pr[6], pr[7]));
+            }
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        if (kg == 0) xs[(4 * w + tb) * 16 + l16] = ls;
+    }
+    lds_barrier();
+    // this wavefront's tokens 16w + l16: all their 32-row blocks, and the total sum
+    uint4 Pk[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) Pk[p] = pbt(w)[p * 64 + lane];
+    const float inv = 1.f / ((xs[w * 16 + l16] + xs[(4 + w) * 16 + l16]) +
+                             (xs[(8 + w) * 16 + l16] + xs[(12 + w) * 16 + l16]));
+    lds_barrier();  // the values' copies overwrite the exchange
+    // values stages 0 .. VEARLY - 1 are issued; the ring is filled up to NSLOT - 2 ahead
+#pragma unroll
+    for (int g = VEARLY; g < NSLOT - 1; ++g) issue_v(g);
 
     // values: O^T (DE x 16 tokens) += V^T P^T per 32-row block kb of each stage
     const int r3 = (l16 >> 2) & 3;
@@ -742,9 +812,10 @@ __device__ __forceinline__ void dense_item(const HeavyArgs &a, unsigned char *ld
 #pragma unroll
     for (int e = 0; e < OE; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < nvs; ++g) {
-        const int t = NK + g;
-        enter(t);
-        const unsigned char *vt = lds + (t % NSLOT) * SLOT;
+        wait_vmcnt_rt(VCP * (min(nvs - 1 - g, NSLOT - 2)));
+        lds_barrier();
+        issue_v(g + NSLOT - 1);
+        const unsigned char *vt = lds + ((NK + g) % NSLOT) * SLOT;
 #pragma unroll
         for (int kb = 0; kb < VKB; ++kb) {
             // P of rows [32 (VKB g + kb), +32): block VKB g + kb
