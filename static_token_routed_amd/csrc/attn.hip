@@ -462,7 +462,8 @@ struct HeavyArgs {
     const int2 *dense;   // dense items, 64 tokens, d_t <= 512; taken before the others
     int64_t d_in;
     uint16_t *o;
-    int64_t nmax;        // entries of the items array (its back holds the short blocks' items)
+    int64_t nmax;        // entries of the items and dense arrays (their backs hold streaming
+                         // items of the mid-length and of the short blocks)
     int tied;            // W_V is W_K (d_emb = d_in): a K row is read again as a V row
 };
 
@@ -901,10 +902,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
     const int tg = QU ? 0 : (w & 1), ch = QU ? w : (w >> 1);
     const int l16 = lane & 15, kg = lane >> 4;
     const int ndense = a.hdr[HDR_NDENSE];
-    // streaming items: those of long blocks from the list's front, then the others from
-    // its back (entry nmax - 1 first)
+    // streaming items, longest blocks first: those of long blocks from the list's front,
+    // then those of mid-length blocks from its back (entry nmax - 1 first), then the
+    // others from the back of the dense array
     const int nlong = a.hdr[HDR_NHEAVY];
-    const int nitems = nlong + a.hdr[HDR_NHEAVY_SHORT];
+    const int nmid = nlong + a.hdr[HDR_NHEAVY_SHORT];
+    const int nitems = nmid + a.hdr[HDR_NHEAVY_TAIL];
     // The list is cut into chunks of QCHUNK consecutive items dealt round-robin to
     // the 8 XCDs (workgroup id mod 8); the workgroups of one XCD take that XCD's
     // items from its own counter, in order, and once it is empty take the other
@@ -969,7 +972,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(HeavyArgs a) {
         lds_barrier();
         const int it = *s_item;
         if (it < 0) break;
-        const int2 item = a.items[it < nlong ? it : a.nmax - 1 - (it - nlong)];
+        const int2 item = it < nlong  ? a.items[it]
+                          : it < nmid ? a.items[a.nmax - 1 - (it - nlong)]
+                                      : a.dense[a.nmax - 1 - (it - nmid)];
         const int j = item.x, tq = item.y;
         const int sb = a.seg_start[j];
         const int ntok = min(kHeavyTile, a.seg_start[j + 1] - sb - tq);

@@ -26,9 +26,12 @@ constexpr int kLnPart = 64;        // LayerNorm partial statistics cover 64 feat
 constexpr int kHeavyTile = 32;     // tokens per MFMA gather-attention work item
 constexpr int kHeavyMinTokens = 8; // blocks with at least this many tokens use the MFMA path
 constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this many rows
-// streaming items of blocks with at least this many rows head their list (the others are
-// written from its back), so the longest start first
+// Streaming items are taken longest first, in three classes by the block's rows: at least
+// kHeavyLongRows (the heavy list's front), at least kHeavyMidRows (its back), the rest
+// (the back of the dense list, whose front holds the dense items: the two never meet, as
+// every item holds at least one token of the batch)
 constexpr int kHeavyLongRows = 256;
+constexpr int kHeavyMidRows = 128;
 // Radix scatter: up to this many 512-key tiles each workgroup forms its own digit
 // offsets from the whole histogram; past it one workgroup forms them all first
 constexpr int kScatterDirectTiles = 64;
@@ -44,7 +47,8 @@ enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4
        HDR_NSPLIT = 6, HDR_NLIGHT_LONG = 7,
        HDR_QUEUE = 8,           // 8 per-XCD counters of the matrix-core gather, then its dense counter
        HDR_NLIGHT_MID = 17,
-       HDR_NHEAVY_SHORT = 18,   // streaming items of blocks under kHeavyLongRows rows (list's back)
+       HDR_NHEAVY_SHORT = 18,   // streaming items of blocks in [kHeavyMidRows, kHeavyLongRows) rows
+       HDR_NHEAVY_TAIL = 19,    // streaming items of blocks under kHeavyMidRows rows
        HDR_WORDS = 64 };
 // Light items of blocks with at least kLightLongRows rows, then those with at least
 // kLightMidRows, are listed apart and taken first, so the longest start first: the

@@ -344,24 +344,27 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
     const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
     const int nl = (lng || mid) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0;
-    // streaming items of long blocks to the front of the heavy list, the rest to its back
-    const bool hlong = bi.d >= kHeavyLongRows;
-    const int nh = hlong ? bi.nh : 0, ns = hlong ? 0 : bi.nh, nd = bi.nd;
-    // wave-inclusive scans of nl, nq, nm, nh, ns and nd
-    int sl = nl, sq = nq, sm = nm, sh = nh, ss = ns, sd = nd;
+    // streaming items of long blocks to the front of the heavy list, of mid-length ones
+    // to its back, of the others to the back of the dense list
+    const bool hlong = bi.d >= kHeavyLongRows, hmid = !hlong && bi.d >= kHeavyMidRows;
+    const int nh = hlong ? bi.nh : 0, ns = hmid ? bi.nh : 0, nt = (hlong || hmid) ? 0 : bi.nh,
+              nd = bi.nd;
+    // wave-inclusive scans of nl, nq, nm, nh, ns, nt and nd
+    int sl = nl, sq = nq, sm = nm, sh = nh, ss = ns, st = nt, sd = nd;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int a = __shfl_up(sl, o), e = __shfl_up(sq, o), f = __shfl_up(sm, o),
-                  b = __shfl_up(sh, o), g = __shfl_up(ss, o), c = __shfl_up(sd, o);
-        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; ss += g; sd += c; }
+                  b = __shfl_up(sh, o), g = __shfl_up(ss, o), u = __shfl_up(st, o), c = __shfl_up(sd, o);
+        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; ss += g; st += u; sd += c; }
     }
-    int bl = 0, bq = 0, bm = 0, bh = 0, bs = 0, bd = 0;
+    int bl = 0, bq = 0, bm = 0, bh = 0, bs = 0, bt = 0, bd = 0;
     if (lane == 63) {
         if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
         if (sq) bq = atomicAdd(&hdr[HDR_NLIGHT_LONG], sq);
         if (sm) bm = atomicAdd(&hdr[HDR_NLIGHT_MID], sm);
         if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
         if (ss) bs = atomicAdd(&hdr[HDR_NHEAVY_SHORT], ss);
+        if (st) bt = atomicAdd(&hdr[HDR_NHEAVY_TAIL], st);
         if (sd) bd = atomicAdd(&hdr[HDR_NDENSE], sd);
     }
     bl = __shfl(bl, 63) + sl - nl;
@@ -369,10 +372,14 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     bm = __shfl(bm, 63) + sm - nm;
     bh = __shfl(bh, 63) + sh - nh;
     bs = __shfl(bs, 63) + ss - ns;
+    bt = __shfl(bt, 63) + st - nt;
     bd = __shfl(bd, 63) + sd - nd;
     if (!hlong) {
-        // from the back of the heavy list: entries nmax - 1 - bs, nmax - 2 - bs, ...
-        for (int q = 0; q < bi.nh; ++q) heavy[nmax - 1 - (bs + q)] = make_int2(j, q * kHeavyTile);
+        // from the back of the heavy list (mid-length blocks) or of the dense list (the
+        // others): entries nmax - 1 - b, nmax - 2 - b, ...
+        int2 *const back = hmid ? heavy : dense;
+        const int b0 = hmid ? bs : bt;
+        for (int q = 0; q < bi.nh; ++q) back[nmax - 1 - (b0 + q)] = make_int2(j, q * kHeavyTile);
         bi.nh = 0;
     }
     if (mid) {
