@@ -150,9 +150,6 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
                                            int lane, unsigned char *lds_all) {
     static_assert(!TIED || NCI == 1, "tied rows fit one piece");
     constexpr int NP = NCI + (TIED ? 0 : 1);  // 1 KB copies per row
-    int tok[NT];  // the item's tokens: sorted positions p0 .. p0 + NT - 1
-#pragma unroll
-    for (int q = 0; q < NT; ++q) tok[q] = a.perm[p0 + q];
     constexpr int LR = light_ring_rows<NCI>();
     constexpr int SLOT = NP * 1024;
     unsigned char *const ring = lds_all + w * kLightWaveLds;
@@ -160,23 +157,6 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
     const int64_t d_in = a.d_in, d_emb = a.d_emb;
     const int wr = SPLIT == 1 ? 0 : w;                      // this wavefront's first row
     const int nr = wr < d ? (d - wr + SPLIT - 1) / SPLIT : 0;  // and its number of rows
-    uint4 xv[NT][NCI];
-#pragma unroll
-    for (int q = 0; q < NT; ++q)
-#pragma unroll
-        for (int c = 0; c < NCI; ++c) {
-            const int64_t col = c * 512 + lane * 8;
-            xv[q][c] = col < d_in
-                           ? *reinterpret_cast<const uint4 *>(a.x + (int64_t)tok[q] * d_in + col)
-                           : make_uint4(0, 0, 0, 0);
-        }
-    // Take delivery of x before any copy is in flight: the compiler's own wait for
-    // these loads would otherwise also wait for every copy (it does not count them).
-#pragma unroll
-    for (int q = 0; q < NT; ++q)
-#pragma unroll
-        for (int c = 0; c < NCI; ++c)
-            __asm__ volatile("" ::"v"(xv[q][c].x), "v"(xv[q][c].y), "v"(xv[q][c].z), "v"(xv[q][c].w));
     const int kcol = lane * 8;
     const int vcol = lane * 8 < d_emb ? lane * 8 : 0;
     // local row j of this wavefront is row wr + SPLIT j of the item
@@ -190,6 +170,30 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
         });
         if constexpr (!TIED) async_ld16_o_nt<NCI * 1024>(a.WV + row * d_emb + vcol, slot);
     };
+    // The first rows' copies go out before the tokens' x rows are looked up, so their
+    // latency overlaps that of the two dependent reads (positions, then x).
+    for (int j = 0; j < LR && j < nr; ++j) issue(j);
+    int tok[NT];  // the item's tokens: sorted positions p0 .. p0 + NT - 1
+#pragma unroll
+    for (int q = 0; q < NT; ++q) tok[q] = a.perm[p0 + q];
+    uint4 xv[NT][NCI];
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int c = 0; c < NCI; ++c) {
+            const int64_t col = c * 512 + lane * 8;
+            xv[q][c] = col < d_in
+                           ? *reinterpret_cast<const uint4 *>(a.x + (int64_t)tok[q] * d_in + col)
+                           : make_uint4(0, 0, 0, 0);
+        }
+    // Take delivery of x here: the wait also covers the copies issued before it
+    // (completions come in issue order; the compiler does not count the copies), which
+    // the first row needs anyway, and leaves no x read pending under the waits below.
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int c = 0; c < NCI; ++c)
+            __asm__ volatile("" ::"v"(xv[q][c].x), "v"(xv[q][c].y), "v"(xv[q][c].z), "v"(xv[q][c].w));
     float m[NT], l[NT], acc[NT][VE];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
@@ -198,7 +202,6 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[q][e] = 0.f;
     }
-    for (int j = 0; j < LR && j < nr; ++j) issue(j);
     for (int j = 0; j < nr; ++j) {
         // rows issued after row j: min(nr, j + LR) - j - 1
         wait_rows<NP, LR - 1>(min(nr, j + LR) - j - 1);
@@ -339,21 +342,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
         return it < nlong ? a.items_long[it]
                           : (it < ncoop ? a.items_long[a.cap - 1 - (it - nlong)] : a.items[it - ncoop]);
     };
+    // Each round reads the next round's entry before running its own item, so the
+    // entry's latency hides behind the item.
     const int nb = gridDim.x;
-    for (int k = 0;; ++k) {
-        const int it = k * nb + ((k & 1) ? nb - 1 - blockIdx.x : blockIdx.x);
-        if (it >= ncoop) break;
-        const int4 item = item_at(it);  // a valid ID with >= kLightMidRows rows
+    auto coop_at = [&](int k) { return k * nb + ((k & 1) ? nb - 1 - blockIdx.x : blockIdx.x); };
+    int it = coop_at(0);
+    int4 item = it < ncoop ? item_at(it) : make_int4(0, 0, 0, 0);
+    for (int k = 1; it < ncoop; ++k) {
+        const int itn = coop_at(k);
+        const int4 next = itn < ncoop ? item_at(itn) : item;
+        // a valid ID with >= kLightMidRows rows
         const int p0 = __builtin_amdgcn_readfirstlane(item.x);
         const int nt = __builtin_amdgcn_readfirstlane(item.y);
         light_item_nt<NCI, VE, 4, TIED>(a, p0, __builtin_amdgcn_readfirstlane(item.z),
                                         __builtin_amdgcn_readfirstlane(item.w), nt, w, lane, lds);
+        it = itn;
+        item = next;
     }
     const int nw = gridDim.x * 4, g = blockIdx.x * 4 + w;
-    for (int k = 0;; ++k) {
-        const int it = ncoop + k * nw + ((k & 1) ? nw - 1 - g : g);
-        if (it >= nitems) break;
-        const int4 item = item_at(it);
+    auto wave_at = [&](int k) { return ncoop + k * nw + ((k & 1) ? nw - 1 - g : g); };
+    it = wave_at(0);
+    item = it < nitems ? item_at(it) : make_int4(0, 0, 0, 0);
+    for (int k = 1; it < nitems; ++k) {
+        const int itn = wave_at(k);
+        const int4 next = itn < nitems ? item_at(itn) : item;
         const int p0 = __builtin_amdgcn_readfirstlane(item.x);
         const int nt = __builtin_amdgcn_readfirstlane(item.y);
         const int64_t r0 = __builtin_amdgcn_readfirstlane(item.z);
@@ -365,9 +377,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
                 for (int e = 0; e < VE; ++e) z[e] = 0.f;
                 store_o<VE>(a.o + (int64_t)a.perm[p0 + q] * a.d_emb + lane * VE, z);
             }
-            continue;
+        } else {
+            light_item_nt<NCI, VE, 1, TIED>(a, p0, r0, d, nt, w, lane, lds);
         }
-        light_item_nt<NCI, VE, 1, TIED>(a, p0, r0, d, nt, w, lane, lds);
+        it = itn;
+        item = next;
     }
 }
 
