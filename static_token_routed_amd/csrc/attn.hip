@@ -337,10 +337,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_light_bf16(LightArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nlong = a.items_long ? a.hdr[HDR_NLIGHT_LONG] : 0;
     const int nmid = a.items_long ? a.hdr[HDR_NLIGHT_MID] : 0;
-    const int ncoop = nlong + nmid, nitems = ncoop + a.hdr[HDR_NLIGHT];
+    const int ncoop = nlong + nmid, nfront = ncoop + a.hdr[HDR_NLIGHT];
+    const int nitems = nfront + (a.items_long ? a.hdr[HDR_NLIGHT_SHORT] : 0);
     auto item_at = [&](int it) {
-        return it < nlong ? a.items_long[it]
-                          : (it < ncoop ? a.items_long[a.cap - 1 - (it - nlong)] : a.items[it - ncoop]);
+        return it < nlong    ? a.items_long[it]
+               : it < ncoop  ? a.items_long[a.cap - 1 - (it - nlong)]
+               : it < nfront ? a.items[it - ncoop]
+                             : a.items[a.cap - 1 - (it - nfront)];
     };
     // Each round reads the next round's entry before running its own item, so the
     // entry's latency hides behind the item.

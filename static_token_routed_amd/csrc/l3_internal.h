@@ -49,12 +49,17 @@ enum { HDR_ERR = 0, HDR_NSEG = 1, HDR_NLIGHT = 2, HDR_NHEAVY = 3, HDR_NDENSE = 4
        HDR_NLIGHT_MID = 17,
        HDR_NHEAVY_SHORT = 18,   // streaming items of blocks in [kHeavyMidRows, kHeavyLongRows) rows
        HDR_NHEAVY_TAIL = 19,    // streaming items of blocks under kHeavyMidRows rows
+       HDR_NLIGHT_SHORT = 20,   // light items of blocks under kLightShortRows rows (light's back)
        HDR_WORDS = 64 };
 // Light items of blocks with at least kLightLongRows rows, then those with at least
 // kLightMidRows, are listed apart and taken first, so the longest start first: the
 // former from the front of the light_long region, the latter from its back.
 constexpr int kLightLongRows = 32;
 constexpr int kLightMidRows = 16;
+// The other light items: those of blocks with at least kLightShortRows rows from the
+// front of the light list, the rest from its back, so the wavefronts' shares (dealt in
+// snake order) start with the longer ones and even out.
+constexpr int kLightShortRows = 8;
 
 struct Dims {
     int64_t d_in, d_emb, d_up, d_out;

@@ -343,25 +343,28 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     // to the front of light_long, the next longest to its back
     const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
     const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
-    const int nl = (lng || mid) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0;
+    const bool lsh = light_long != nullptr && bi.d < kLightShortRows;  // to the light list's back
+    const int nl = (lng || mid || lsh) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0,
+              nk = lsh ? bi.nl : 0;
     // streaming items of long blocks to the front of the heavy list, of mid-length ones
     // to its back, of the others to the back of the dense list
     const bool hlong = bi.d >= kHeavyLongRows, hmid = !hlong && bi.d >= kHeavyMidRows;
     const int nh = hlong ? bi.nh : 0, ns = hmid ? bi.nh : 0, nt = (hlong || hmid) ? 0 : bi.nh,
               nd = bi.nd;
-    // wave-inclusive scans of nl, nq, nm, nh, ns, nt and nd
-    int sl = nl, sq = nq, sm = nm, sh = nh, ss = ns, st = nt, sd = nd;
+    // wave-inclusive scans of nl, nq, nm, nk, nh, ns, nt and nd
+    int sl = nl, sq = nq, sm = nm, sk = nk, sh = nh, ss = ns, st = nt, sd = nd;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(sl, o), e = __shfl_up(sq, o), f = __shfl_up(sm, o),
+        const int a = __shfl_up(sl, o), e = __shfl_up(sq, o), f = __shfl_up(sm, o), k = __shfl_up(sk, o),
                   b = __shfl_up(sh, o), g = __shfl_up(ss, o), u = __shfl_up(st, o), c = __shfl_up(sd, o);
-        if (lane >= o) { sl += a; sq += e; sm += f; sh += b; ss += g; st += u; sd += c; }
+        if (lane >= o) { sl += a; sq += e; sm += f; sk += k; sh += b; ss += g; st += u; sd += c; }
     }
-    int bl = 0, bq = 0, bm = 0, bh = 0, bs = 0, bt = 0, bd = 0;
+    int bl = 0, bq = 0, bm = 0, bk = 0, bh = 0, bs = 0, bt = 0, bd = 0;
     if (lane == 63) {
         if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
         if (sq) bq = atomicAdd(&hdr[HDR_NLIGHT_LONG], sq);
         if (sm) bm = atomicAdd(&hdr[HDR_NLIGHT_MID], sm);
+        if (sk) bk = atomicAdd(&hdr[HDR_NLIGHT_SHORT], sk);
         if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
         if (ss) bs = atomicAdd(&hdr[HDR_NHEAVY_SHORT], ss);
         if (st) bt = atomicAdd(&hdr[HDR_NHEAVY_TAIL], st);
@@ -370,6 +373,7 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     bl = __shfl(bl, 63) + sl - nl;
     bq = __shfl(bq, 63) + sq - nq;
     bm = __shfl(bm, 63) + sm - nm;
+    bk = __shfl(bk, 63) + sk - nk;
     bh = __shfl(bh, 63) + sh - nh;
     bs = __shfl(bs, 63) + ss - ns;
     bt = __shfl(bt, 63) + st - nt;
@@ -382,11 +386,14 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
         for (int q = 0; q < bi.nh; ++q) back[nmax - 1 - (b0 + q)] = make_int2(j, q * kHeavyTile);
         bi.nh = 0;
     }
-    if (mid) {
-        // from the back of light_long: entries n - 1 - bm, n - 2 - bm, ...
+    if (mid || lsh) {
+        // from the back of light_long (mid) or of light (short): entries n - 1 - b, ...
+        int4 *const back = mid ? light_long : light;
+        const int b0 = mid ? bm : bk;
         for (int q = 0; q < bi.nl; ++q)
-            light_long[nmax - 1 - (bm + q)] =
-                make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), bi.r0, bi.d);
+            back[nmax - 1 - (b0 + q)] =
+                make_int4(sb + q * light_tok, min(light_tok, S - q * light_tok), bi.r0,
+                          t < vocab ? bi.d : -1);
         bi.nl = 0;
     }
     write_items(bi, j, sb, S, t < vocab, light_tok, lng ? bq : bl, bh, bd, lng ? light_long : light,
