@@ -63,6 +63,11 @@ struct GemmP {
     int64_t lda, lda2, ldb, ldb2, K1;
     int64_t M, N, K;
     const float *row_stats;  // [M x 2] (mean, rstd) of the A rows in [0, K1)  (LN_IN)
+    // (LN_IN, instead of row_stats) per-row shares of o^T G o, [M x quad_npart]: the row's
+    // mean is 0 and rstd = 1 / sqrt(max(sum / quad_width, 0) + quad_eps), shares added in order
+    const float *quad_parts;
+    int quad_npart;
+    float quad_width, quad_eps;
     const float *c1, *c2;    // [N] LayerNorm fold terms                         (LN_IN)
     float *ln_out;           // [M x npart_out x 2] partial statistics of the stored rows
     int npart_out;
@@ -213,16 +218,36 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (LN_IN) {
-        // written before any copy is in flight; the first barrier publishes them
+    // LN_IN: the tile's row statistics and column terms, loaded while the first stage's
+    // copies are in flight (the wait for these loads also covers the copies, which were
+    // issued first); the first stage's barrier publishes them
+    auto load_ln = [&]() {
+        if constexpr (LN_IN) {
         const int t = threadIdx.x;
         if (t < 256) {
             const int64_t m = min<int64_t>(m0 + t, p.M - 1), n = min<int64_t>(n0 + t, p.N - 1);
-            rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
-            c1s[t] = p.c1[n];
-            c2s[t] = p.c2[n];
+            const float c1v = p.c1[n], c2v = p.c2[n];
+            if (p.quad_parts) {
+                // the shares in groups of 8 loads, added in order
+                const float *qp = p.quad_parts + m * p.quad_npart;
+                float q = 0.f;
+                for (int i0 = 0; i0 < p.quad_npart; i0 += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[i] = i0 + i < p.quad_npart ? qp[i0 + i] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (i0 + i < p.quad_npart) q += v[i];
+                }
+                rowst[t] = make_float2(0.f, 1.f / sqrtf(fmaxf(q / p.quad_width, 0.f) + p.quad_eps));
+            } else {
+                rowst[t] = make_float2(p.row_stats[2 * m], p.row_stats[2 * m + 1]);
+            }
+            c1s[t] = c1v;
+            c2s[t] = c2v;
         }
-    }
+        }
+    };
     // the accumulators pinned to AGPRs around the rescale, so the stage loops on either
     // side keep them in place instead of shuffling them between registers
     auto pin_acc = [&]() {
@@ -312,6 +337,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_bf16(GemmP p) {
 #pragma unroll
             for (int c = 0; c < 2 * CPW; ++c) issue_one(KFirst{}, 0, c, o);
         }
+        load_ln();
         for (int st = 0; st < nst1; ++st) stage(KSel{}, st);
         pin_acc();
         fold();
@@ -647,8 +673,8 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, i
 // o^T G o per row at a quarter of W_up's work when d_up = 4 d_emb.  F and G are
 // formed per call from the weights: W_c^T (W_up transposed, each row less its
 // mean, bf16) is written right after W1' = W1 diag(gamma) (from k_mix_fold), so
-// the rows [W1' ; W_c^T] are one (d_out + d_emb) x d_up matrix, and one split-K GEMM
-// of it against W_c^T gives [F ; G] in the layouts the two GEMMs read.
+// the rows [W1' ; W_c^T] are one (d_out + d_emb) x d_up matrix, and one GEMM of it
+// against W_c^T gives [F ; G] in the layouts the two GEMMs read.
 // Centring first means no mean * (row sum) term is subtracted later, so a large
 // mean cancels nothing in bf16.
 
@@ -685,23 +711,12 @@ __global__ __launch_bounds__(256) void k_center_rows(uint16_t *__restrict__ WT, 
 // npart partials) / width, clamped at zero (G's rounding can leave a tiny negative
 // value for a row whose variance is zero).  The mean is not needed (the factored
 // GEMM's mean coefficients are zero) and is written as 0.
-__global__ __launch_bounds__(256) void k_ln_quad_finalize(const float *__restrict__ qp, int64_t M, int npart,
-                                                          int64_t width, float eps, float *__restrict__ stats) {
-    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= M) return;
-    float q = 0.f;
-    for (int i = 0; i < npart; ++i) q += qp[row * npart + i];
-    stats[2 * row] = 0.f;
-    stats[2 * row + 1] = 1.f / sqrtf(fmaxf(q / (float)width, 0.f) + eps);
-}
-
 constexpr int kQuadWN = 64;  // output columns per wavefront of k_gemm_bf16<.., 3, 8>
 
 int ln_quad_parts(int64_t d_emb) { return (int)((d_emb + kQuadWN - 1) / kQuadWN); }
 
 hipError_t launch_ln_quad_stats_bf16(const uint16_t *o, const void *factor_ws, int64_t M, int64_t d_emb,
-                                     int64_t d_up, int64_t d_out, float eps, float *qp, float *stats,
-                                     hipStream_t s) {
+                                     int64_t d_up, int64_t d_out, float *qp, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const uint16_t *G = reinterpret_cast<const uint16_t *>(
@@ -712,10 +727,6 @@ hipError_t launch_ln_quad_stats_bf16(const uint16_t *o, const void *factor_ws, i
     p.npart_out = ln_quad_parts(d_emb);
     // 8 wavefronts in 2 x 4, each kQuadWN columns wide
     hipLaunchKernelGGL((k_gemm_bf16<false, false, 3, 8>), dim3(p.tiles_m * p.tiles_n), dim3(512), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ln_quad_finalize, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, qp, M,
-                       p.npart_out, d_up, eps, stats);
     return hipGetLastError();
 }
 
@@ -727,37 +738,12 @@ size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
            al((size_t)d_out * 4);
 }
 
-// [F ; G] = [W1' ; W_c^T] W_c runs on the 256 x 256 tile kernel with K split so that the
-// tiles x splits workgroups about fill the chip (at least 256 K columns each); the fp32
-// slabs are added in slab order and rounded to bf16 by k_slab_sum_bf16.
-int factor_splits(int64_t d_emb, int64_t d_up, int64_t d_out, int64_t *ksplit) {
-    const int64_t tiles = ((d_out + d_emb + BM - 1) / BM) * ((d_emb + BN - 1) / BN);
-    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(256 / tiles, d_up / 256));
-    const int64_t ks = ((d_up + want - 1) / want + BK - 1) / BK * BK;
-    if (ksplit) *ksplit = ks;
-    return (int)((d_up + ks - 1) / ks);
-}
-
-size_t mix_factor_part_bytes(int64_t d_emb, int64_t d_up, int64_t d_out) {
-    return (size_t)factor_splits(d_emb, d_up, d_out, nullptr) * (size_t)(d_out + d_emb) * d_emb * 4;
-}
-
-// C[i] (bf16, 4 per thread) = sum of the S slabs at i, in slab order
-__global__ __launch_bounds__(256) void k_slab_sum_bf16(const float4 *__restrict__ part, int S, int64_t n4,
-                                                       uint2 *__restrict__ C) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;
-    float4 a = part[i];
-    for (int sp = 1; sp < S; ++sp) {
-        const float4 v = part[(int64_t)sp * n4 + i];
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-    }
-    C[i] = make_uint2(pack2(a.x, a.y), pack2(a.z, a.w));
-}
-
+// [F ; G] = [W1' ; W_c^T] W_c runs on the 256 x 256 tile kernel over the whole K = d_up
+// (bf16 output): few workgroups and no partial sums in memory, so it leaves the chip
+// and its memory to the route it runs beside; it is needed only after the gather.
 hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
-                             const float *beta, void *fold_ws, void *factor_ws, float *part,
-                             int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
+                             const float *beta, void *fold_ws, void *factor_ws, int64_t d_emb,
+                             int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s) {
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *f = static_cast<char *>(factor_ws);
     uint16_t *stack = reinterpret_cast<uint16_t *>(f);  // W1' rows, then W_c^T rows
@@ -776,21 +762,10 @@ hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // [F ; G] = [W1' ; W_c^T] W_c  (row i of the product: stack row i against each W_c^T row)
-    const int64_t M = d_out + d_emb;
-    GemmP p = make_plain(stack, wct, nullptr, M, d_emb, d_up);
-    p.Cf = part;
-    p.splits = factor_splits(d_emb, d_up, d_out, &p.ksplit);
-    hipLaunchKernelGGL((k_gemm_bf16<false, false, 1>), dim3(p.tiles_m * p.tiles_n * p.splits), dim3(256), 0, s,
-                       p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t n4 = M * d_emb / 4;
-    hipLaunchKernelGGL(k_slab_sum_bf16, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float4 *>(part), p.splits, n4, reinterpret_cast<uint2 *>(fg));
-    return hipGetLastError();
+    return launch_gemm_bf16(stack, wct, fg, d_out + d_emb, d_emb, d_up, nullptr, s);
 }
 
-hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
+hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *qp, float eps,
                                          const uint16_t *W_mix, uint16_t *out, const void *fold_ws,
                                          const void *factor_ws, int64_t M, int64_t d_emb, int64_t d_up,
                                          int64_t d_in, int64_t d_out, hipStream_t s) {
@@ -810,7 +785,10 @@ hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, c
     p.B2 = W_mix + d_up;
     p.ldb2 = d_up + d_in;
     p.K1 = d_emb;
-    p.row_stats = stats;
+    p.quad_parts = qp;  // rstd per row from the statistics GEMM's shares, in the prologue
+    p.quad_npart = ln_quad_parts(d_emb);
+    p.quad_width = (float)d_up;
+    p.quad_eps = eps;
     p.c1 = zero;  // F acts on the centred row: no mean term
     p.c2 = c2;
     hipLaunchKernelGGL((k_gemm_bf16<true, false>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);

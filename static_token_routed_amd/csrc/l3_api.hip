@@ -190,9 +190,9 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
             L3_HIP_TRY(launch_route_small(ids, n, P.vocab, P.d_off, heavy_min, dense_min, light_tok, b,
                                           light, heavy, dense, s));
         } else {
-            L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, s));  // clears the header too
-            L3_HIP_TRY(launch_worklist(b, n, P.d_off, P.vocab, heavy_min, dense_min, light_tok, light,
-                                       heavy, dense, s, D.dtype == L3_BF16 ? light_long : nullptr));
+            // (clears the header too)
+            L3_HIP_TRY(launch_route(ids, n, P.vocab, b, L.ntiles, P.d_off, heavy_min, dense_min, light_tok,
+                                    light, heavy, dense, D.dtype == L3_BF16 ? light_long : nullptr, s));
         }
     }
     {
@@ -255,7 +255,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         }
         StageTimer tm(4, ps);
         L3_HIP_TRY(launch_mix_factor((const uint16_t *)W_up, (const uint16_t *)W_mix, gamma, beta, fold, factor,
-                                     ws_ptr<float>(ws, L.part), D.d_emb, D.d_up, D.d_in, D.d_out, ps));
+                                     D.d_emb, D.d_up, D.d_in, D.d_out, ps));
     }
     RouteBufs b{};
     const int rc = route_attend(P, x, ids, n, WK, WV, ws, L, b, s);
@@ -280,16 +280,15 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         }
     } else if (D.dtype == L3_BF16) {
         // W_mix factored through W_up (gemm.hip): h is never formed; LayerNorm's variance
-        // comes from o^T G o
-        float *stats = ws_ptr<float>(ws, L.stats);
+        // comes from o^T G o (its per-row shares in lnp, turned into rstd by the W_mix GEMM)
         {
             StageTimer tm(3, s);
             L3_HIP_TRY(launch_ln_quad_stats_bf16((const uint16_t *)o, factor, n, D.d_emb, D.d_up, D.d_out,
-                                                 D.eps, lnp, stats, s));
+                                                 lnp, s));
         }
         {
             StageTimer tm(5, s);
-            L3_HIP_TRY(launch_gemm_mix_factored_bf16((const uint16_t *)o, (const uint16_t *)x, stats,
+            L3_HIP_TRY(launch_gemm_mix_factored_bf16((const uint16_t *)o, (const uint16_t *)x, lnp, D.eps,
                                                      (const uint16_t *)W_mix, (uint16_t *)out, fold, factor,
                                                      n, D.d_emb, D.d_up, D.d_in, D.d_out, s));
         }
@@ -501,7 +500,7 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.vals_b = take(n * 4);
     L.rank = take(n * 4);
     L.hist = take((size_t)kRadix * (L.ntiles + 1) * 4);  // + the digit totals (k_hist_scan)
-    L.tile_cnt = take(L.ntiles * 4);
+    L.tile_cnt = take(L.ntiles * 2 * 4);  // head counts, then first head positions
     L.inv_perm = take(n * 4);
     L.uniq = take(n * 4);
     L.counts = take(n * 4);
@@ -520,13 +519,11 @@ WsLayout ws_layout(const Dims &d, int64_t n_max, int32_t max_d) {
     L.fold = take(d.dtype == L3_BF16 ? mix_fold_bytes(d.d_up, d.d_out) : 0);
     L.factor = take(d.dtype == L3_BF16 && n > kSkinnyMaxM ? mix_factor_bytes(d.d_emb, d.d_up, d.d_out) : 0);
     const int64_t ns = std::min<int64_t>(n, kSkinnyMaxM);
-    // (the factor's slabs join the maximum above kSkinnyMaxM tokens, so the size never
-    // falls as n grows)
+    // (sized at min(n, kSkinnyMaxM) above kSkinnyMaxM tokens too, so the size never falls
+    // as n grows)
     const size_t skinny = std::max(skinny_part_bytes(ns, d.d_up, d.d_emb),
                                    skinny_part_bytes(ns, d.d_out, d.d_up + d.d_in));
-    L.part = take(d.dtype != L3_BF16 ? 0
-                  : n <= kSkinnyMaxM ? skinny
-                                     : std::max(skinny, mix_factor_part_bytes(d.d_emb, d.d_up, d.d_out)));
+    L.part = take(d.dtype != L3_BF16 ? 0 : skinny);
     L.slots = split_slots(d, n, max_d);
     L.sitems = take((size_t)L.slots * 16);
     L.blkinfo = take(L.slots ? (size_t)n * 16 : 0);
@@ -773,10 +770,9 @@ int l3_route(l3_plan_t p, const int32_t *ids, int64_t n, void *ws, size_t ws_byt
                                       ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
                                       ws_ptr<int2>(ws, L.dense), s));
     } else {
-        L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, s));  // clears the header too
-        L3_HIP_TRY(launch_worklist(b, n, p->d_off, p->vocab, INT32_MAX, INT32_MAX, 1,
-                                   ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
-                                   ws_ptr<int2>(ws, L.dense), s));
+        L3_HIP_TRY(launch_route(ids, n, p->vocab, b, L.ntiles, p->d_off, INT32_MAX, INT32_MAX, 1,
+                                ws_ptr<int4>(ws, L.light), ws_ptr<int2>(ws, L.heavy),
+                                ws_ptr<int2>(ws, L.dense), nullptr, s));  // clears the header too
     }
     const size_t nb = (size_t)n * 4;
     auto cp = [&](int32_t *dst, const int32_t *src, size_t bytes) -> hipError_t {

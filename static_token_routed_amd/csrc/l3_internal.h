@@ -103,9 +103,12 @@ struct RouteBufs {
 // ---- launchers (all enqueue on `s`; return hipError_t of the last launch)
 hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s);
 // The multi-kernel route; it also clears the header (the first sort pass) and
-// sets the out-of-range flag (the block writer), so no separate clear is needed.
+// sets the out-of-range flag (the block writer), so no separate clear is needed.  Its
+// block writer also forms the blocks' sizes and, with light non-null, their work items
+// (the lists and thresholds of launch_worklist).  tile_cnt holds 2 ntiles words.
 hipError_t launch_route(const int32_t *ids, int64_t n, int64_t vocab, RouteBufs &b, int64_t ntiles,
-                        hipStream_t s);
+                        const int64_t *off, int heavy_min_tokens, int dense_min_tokens, int light_tokens,
+                        int4 *light, int2 *heavy, int2 *dense, int4 *light_long, hipStream_t s);
 // Work lists for the gather-attention kernels (reads the route outputs).
 // Blocks go to the dense list (>= dense_min_tokens tokens, kDenseMinD <= d_t <= kDenseMaxD, items of
 // kDenseTile tokens), else the heavy list (>= heavy_min_tokens tokens or >= kHeavyMinRows
@@ -195,19 +198,18 @@ hipError_t launch_mix_fold(const uint16_t *W_mix, const float *gamma, const floa
 size_t mix_fold_bytes(int64_t d_up, int64_t d_out);
 // Factored W_mix (batches of more than kSkinnyMaxM tokens): F = W1 diag(gamma) W_c and
 // G = W_c^T W_c of the centred W_up into factor_ws (mix_factor_bytes; the fold terms
-// into fold_ws; `part` holds the small-K-split GEMM's slabs, mix_factor_part_bytes),
-// LayerNorm's (0, rstd) per row from o^T G o (qp: [M x ln_quad_parts(d_emb)] fp32
-// partials), and out = rstd * (F o) + c2 + W2 x.
+// into fold_ws),
+// the per-row shares of o^T G o (qp: [M x ln_quad_parts(d_emb)] fp32), and out = rstd *
+// (F o) + c2 + W2 x, the W_mix GEMM forming each row's rstd = 1 / sqrt(o^T G o / d_up +
+// eps) from the shares.
 size_t mix_factor_bytes(int64_t d_emb, int64_t d_up, int64_t d_out);
-size_t mix_factor_part_bytes(int64_t d_emb, int64_t d_up, int64_t d_out);
 int ln_quad_parts(int64_t d_emb);
 hipError_t launch_mix_factor(const uint16_t *W_up, const uint16_t *W_mix, const float *gamma,
-                             const float *beta, void *fold_ws, void *factor_ws, float *part,
-                             int64_t d_emb, int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
+                             const float *beta, void *fold_ws, void *factor_ws, int64_t d_emb,
+                             int64_t d_up, int64_t d_in, int64_t d_out, hipStream_t s);
 hipError_t launch_ln_quad_stats_bf16(const uint16_t *o, const void *factor_ws, int64_t M, int64_t d_emb,
-                                     int64_t d_up, int64_t d_out, float eps, float *qp, float *stats,
-                                     hipStream_t s);
-hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *stats,
+                                     int64_t d_up, int64_t d_out, float *qp, hipStream_t s);
+hipError_t launch_gemm_mix_factored_bf16(const uint16_t *o, const uint16_t *x, const float *qp, float eps,
                                          const uint16_t *W_mix, uint16_t *out, const void *fold_ws,
                                          const void *factor_ws, int64_t M, int64_t d_emb, int64_t d_up,
                                          int64_t d_in, int64_t d_out, hipStream_t s);

@@ -195,86 +195,39 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict_
     }
 }
 
-// Per kSortTile-key tile: number of block heads; also the inverse permutation.
+// Per kSortTile-key tile: number of block heads and the position of its first head (n
+// if it has none; tile_cnt[ntiles + tile]); also the inverse permutation.
 __global__ __launch_bounds__(256) void k_seg_heads(const int32_t *__restrict__ sk,
-                                                   const int32_t *__restrict__ perm, int n,
+                                                   const int32_t *__restrict__ perm, int n, int ntiles,
                                                    int32_t *__restrict__ tile_cnt,
                                                    int32_t *__restrict__ inv_perm) {
-    __shared__ int32_t wsum[4];
+    __shared__ int32_t wsum[4], wfirst[4];
     const int base = blockIdx.x * kSortTile;
-    int c = 0;
+    int c = 0, first = n;
 #pragma unroll
     for (int r = 0; r < kSortPer; ++r) {
         const int s = base + r * 256 + threadIdx.x;
         if (s < n) {
-            c += (s == 0 || sk[s] != sk[s - 1]);
+            const bool h = s == 0 || sk[s] != sk[s - 1];
+            c += h;
+            if (h) first = min(first, s);
             const int i = perm[s];
             if ((unsigned)i < (unsigned)n) inv_perm[i] = s;
         }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = c;
-    __syncthreads();
-    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-}
-
-// Writes uniq[] and seg_start[] of the heads in one tile (kSortPer consecutive keys per
-// thread); the tile's first block index is the sum of the head counts of the tiles
-// before it (summed here, no separate scan pass).  The number of blocks m goes to
-// *nseg and seg_start[m] = n.
-__global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ sk, int n,
-                                                   const int32_t *__restrict__ tile_cnt, int ntiles,
-                                                   int32_t *__restrict__ hdr, int vocab,
-                                                   int32_t *__restrict__ uniq,
-                                                   int32_t *__restrict__ seg_start) {
-    __shared__ int32_t wsum[4];
-    __shared__ int32_t tile_sums[2];
-    int32_t before = 0, total = 0;
-    for (int u = threadIdx.x; u < ntiles; u += 256) {
-        const int32_t c = tile_cnt[u];
-        total += c;
-        before += u < (int)blockIdx.x ? c : 0;
-    }
-#pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        before += __shfl_xor(before, o);
-        total += __shfl_xor(total, o);
+        c += __shfl_xor(c, o);
+        first = min(first, __shfl_xor(first, o));
     }
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = before;
-    __syncthreads();
-    if (threadIdx.x == 0) tile_sums[0] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = total;
-    __syncthreads();
-    if (threadIdx.x == 0) tile_sums[1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    const int32_t tile_off = tile_sums[0], m = tile_sums[1];
-
-    const int base = blockIdx.x * kSortTile + threadIdx.x * kSortPer;
-    int flags = 0, c = 0;
-#pragma unroll
-    for (int i = 0; i < kSortPer; ++i) {
-        const int s = base + i;
-        const int f = (s < n) && (s == 0 || sk[s] != sk[s - 1]);
-        flags |= f << i;
-        c += f;
+    if ((threadIdx.x & 63) == 0) {
+        wsum[threadIdx.x >> 6] = c;
+        wfirst[threadIdx.x >> 6] = first;
     }
-    int32_t all;
-    int j = tile_off + block_scan_256(c, wsum, &all);
-#pragma unroll
-    for (int i = 0; i < kSortPer; ++i) {
-        if ((flags & (1 << i)) && j < n) {
-            uniq[j] = sk[base + i];
-            seg_start[j] = base + i;
-            ++j;
-        }
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        hdr[HDR_NSEG] = m;
-        seg_start[min(m, n)] = n;
-        // IDs outside [0, vocab) have the key vocab, the largest, so they sort last
-        hdr[HDR_ERR] = n > 0 && sk[n - 1] == vocab;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        tile_cnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        tile_cnt[ntiles + blockIdx.x] = min(min(wfirst[0], wfirst[1]), min(wfirst[2], wfirst[3]));
     }
 }
 
@@ -314,40 +267,32 @@ __device__ inline void write_items(const BlockItems &b, int j, int sb, int S, bo
     for (int q = 0; q < b.nd; ++q) dense[bd + q] = make_int2(j, q * kDenseTile);
 }
 
-// One thread per block (segment): its size, and its work items appended to the light
-// or heavy list (one wave-aggregated atomic per list; item order does not affect
-// results, only scheduling).
-__global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ uniq,
-                                                  const int32_t *__restrict__ seg_start,
-                                                  int32_t *__restrict__ counts,
-                                                  const int64_t *__restrict__ off, int vocab,
-                                                  int heavy_min, int dense_min, int light_tok,
-                                                  int4 *__restrict__ light,
-                                                  int2 *__restrict__ heavy,
-                                                  int2 *__restrict__ dense,
-                                                  int32_t *__restrict__ hdr,
-                                                  int4 *__restrict__ light_long, int nmax) {
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    const int m = hdr[HDR_NSEG];
+// Work items of one block per lane (act: the lane holds block j of S tokens from sorted
+// position sb, ID t), appended to the light or heavy lists with one wave-aggregated
+// reservation per list: reserve(k, c) adds c to list counter k (the header words of
+// list_hdr(k)) and returns the old value.  Item order does not affect
+// results, only scheduling.  Light items of long blocks go to their own lists (when
+// there are any): the longest to the front of light_long, the next longest to its
+// back; streaming items of long blocks to the front of the heavy list, of mid-length
+// ones to its back, of the others to the back of the dense list.
+__device__ constexpr int list_hdr(int k) {
+    return k == 0 ? HDR_NLIGHT : k == 1 ? HDR_NLIGHT_LONG : k == 2 ? HDR_NLIGHT_MID
+         : k == 3 ? HDR_NLIGHT_SHORT : k == 4 ? HDR_NHEAVY : k == 5 ? HDR_NHEAVY_SHORT
+         : k == 6 ? HDR_NHEAVY_TAIL : HDR_NDENSE;
+}
+template <class Reserve>
+__device__ inline void block_worklist(bool act, int j, int sb, int S, int t, const int64_t *off, int vocab,
+                                      int heavy_min, int dense_min, int light_tok, int4 *light,
+                                      int2 *heavy, int2 *dense, int4 *light_long, int nmax,
+                                      Reserve reserve) {
     const int lane = threadIdx.x & 63;
-    int S = 0, sb = 0, t = vocab;
     BlockItems bi;
-    if (j < m) {
-        sb = seg_start[j];
-        S = seg_start[j + 1] - sb;
-        counts[j] = S;
-        t = uniq[j];
-        bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
-    }
-    // light items of long blocks go to their own lists (when there are any): the longest
-    // to the front of light_long, the next longest to its back
+    if (act) bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
     const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
     const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
     const bool lsh = light_long != nullptr && bi.d < kLightShortRows;  // to the light list's back
     const int nl = (lng || mid || lsh) ? 0 : bi.nl, nq = lng ? bi.nl : 0, nm = mid ? bi.nl : 0,
               nk = lsh ? bi.nl : 0;
-    // streaming items of long blocks to the front of the heavy list, of mid-length ones
-    // to its back, of the others to the back of the dense list
     const bool hlong = bi.d >= kHeavyLongRows, hmid = !hlong && bi.d >= kHeavyMidRows;
     const int nh = hlong ? bi.nh : 0, ns = hmid ? bi.nh : 0, nt = (hlong || hmid) ? 0 : bi.nh,
               nd = bi.nd;
@@ -361,14 +306,14 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     }
     int bl = 0, bq = 0, bm = 0, bk = 0, bh = 0, bs = 0, bt = 0, bd = 0;
     if (lane == 63) {
-        if (sl) bl = atomicAdd(&hdr[HDR_NLIGHT], sl);
-        if (sq) bq = atomicAdd(&hdr[HDR_NLIGHT_LONG], sq);
-        if (sm) bm = atomicAdd(&hdr[HDR_NLIGHT_MID], sm);
-        if (sk) bk = atomicAdd(&hdr[HDR_NLIGHT_SHORT], sk);
-        if (sh) bh = atomicAdd(&hdr[HDR_NHEAVY], sh);
-        if (ss) bs = atomicAdd(&hdr[HDR_NHEAVY_SHORT], ss);
-        if (st) bt = atomicAdd(&hdr[HDR_NHEAVY_TAIL], st);
-        if (sd) bd = atomicAdd(&hdr[HDR_NDENSE], sd);
+        if (sl) bl = reserve(0, sl);
+        if (sq) bq = reserve(1, sq);
+        if (sm) bm = reserve(2, sm);
+        if (sk) bk = reserve(3, sk);
+        if (sh) bh = reserve(4, sh);
+        if (ss) bs = reserve(5, ss);
+        if (st) bt = reserve(6, st);
+        if (sd) bd = reserve(7, sd);
     }
     bl = __shfl(bl, 63) + sl - nl;
     bq = __shfl(bq, 63) + sq - nq;
@@ -398,6 +343,136 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
     }
     write_items(bi, j, sb, S, t < vocab, light_tok, lng ? bq : bl, bh, bd, lng ? light_long : light,
                 heavy, dense);
+}
+
+// One thread per block (segment): its size, and its work items (block_worklist).
+__global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ uniq,
+                                                  const int32_t *__restrict__ seg_start,
+                                                  int32_t *__restrict__ counts,
+                                                  const int64_t *__restrict__ off, int vocab,
+                                                  int heavy_min, int dense_min, int light_tok,
+                                                  int4 *__restrict__ light,
+                                                  int2 *__restrict__ heavy,
+                                                  int2 *__restrict__ dense,
+                                                  int32_t *__restrict__ hdr,
+                                                  int4 *__restrict__ light_long, int nmax) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int m = hdr[HDR_NSEG];
+    int S = 0, sb = 0, t = vocab;
+    if (j < m) {
+        sb = seg_start[j];
+        S = seg_start[j + 1] - sb;
+        counts[j] = S;
+        t = uniq[j];
+    }
+    block_worklist(j < m, j, sb, S, t, off, vocab, heavy_min, dense_min, light_tok, light, heavy, dense,
+                   light_long, nmax, [&](int k, int c) { return atomicAdd(&hdr[list_hdr(k)], c); });
+}
+
+// Writes uniq[], seg_start[] and counts[] of the blocks whose heads lie in one tile
+// (kSortPer consecutive keys per thread), and with light non-null their work items
+// (block_worklist).  The tile's first block index is the sum of the earlier tiles' head
+// counts; a block ends at the next head: in the tile (a suffix minimum over the threads'
+// first heads), else the first head of a later tile (tile_cnt[ntiles + u]), else n.  The
+// number of blocks m goes to *nseg and seg_start[m] = n.
+__global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ sk, int n,
+                                                   const int32_t *__restrict__ tile_cnt, int ntiles,
+                                                   int32_t *__restrict__ hdr, int vocab,
+                                                   int32_t *__restrict__ uniq,
+                                                   int32_t *__restrict__ seg_start,
+                                                   int32_t *__restrict__ counts,
+                                                   const int64_t *__restrict__ off, int heavy_min,
+                                                   int dense_min, int light_tok,
+                                                   int4 *__restrict__ light, int2 *__restrict__ heavy,
+                                                   int2 *__restrict__ dense,
+                                                   int4 *__restrict__ light_long) {
+    __shared__ int32_t wsum[4], wmin[4];
+    __shared__ int32_t tile_sums[3];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // heads before this tile, all heads, and the first head after it
+    int32_t before = 0, total = 0, after = n;
+    for (int u = threadIdx.x; u < ntiles; u += 256) {
+        const int32_t c = tile_cnt[u];
+        total += c;
+        before += u < (int)blockIdx.x ? c : 0;
+        if (u > (int)blockIdx.x) after = min(after, tile_cnt[ntiles + u]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        before += __shfl_xor(before, o);
+        total += __shfl_xor(total, o);
+        after = min(after, __shfl_xor(after, o));
+    }
+    if (lane == 0) {
+        wsum[w] = before;
+        wmin[w] = after;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        tile_sums[0] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        tile_sums[2] = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+    }
+    __syncthreads();
+    if (lane == 0) wsum[w] = total;
+    __syncthreads();
+    if (threadIdx.x == 0) tile_sums[1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    const int32_t tile_off = tile_sums[0], m = tile_sums[1], next_tile_head = tile_sums[2];
+
+    const int base = blockIdx.x * kSortTile + threadIdx.x * kSortPer;
+    int flags = 0, c = 0, mine = n;  // mine: this thread's first head
+    int key[kSortPer];
+#pragma unroll
+    for (int i = kSortPer - 1; i >= 0; --i) {
+        const int s = base + i;
+        key[i] = s < n ? sk[s] : vocab;
+        const int f = (s < n) && (s == 0 || key[i] != sk[s - 1]);
+        flags |= f << i;
+        c += f;
+        if (f) mine = s;
+    }
+    // the first head after this thread's positions: a suffix minimum over the later
+    // lanes, then the later wavefronts of the tile, then the later tiles
+    int suf = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_down(suf, o);
+        if (lane + o < 64) suf = min(suf, u);
+    }
+    int later = __shfl_down(suf, 1);
+    if (lane == 63) later = n;
+    if (lane == 0) wmin[w] = suf;
+    int32_t all;
+    int j = tile_off + block_scan_256(c, wsum, &all);  // (its barriers publish wmin)
+    for (int ww = w + 1; ww < 4; ++ww) later = min(later, wmin[ww]);
+    later = min(later, next_tile_head);
+#pragma unroll
+    for (int i = 0; i < kSortPer; ++i) {
+        const bool h = (flags >> i) & 1;
+        int S = 0;
+        if (h) {
+            const int s = base + i;
+            int e = later;
+#pragma unroll
+            for (int q = kSortPer - 1; q > i; --q)
+                if ((flags >> q) & 1) e = base + q;
+            S = e - s;
+            uniq[j] = key[i];
+            seg_start[j] = s;
+            counts[j] = S;
+        }
+        if (light)
+            block_worklist(h, j, base + i, S, key[i], off, vocab, heavy_min, dense_min, light_tok, light,
+                           heavy, dense, light_long, n,
+                           [&](int k, int v) { return atomicAdd(&hdr[list_hdr(k)], v); });
+        j += h;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[HDR_NSEG] = m;
+        seg_start[min(m, n)] = n;
+        // IDs outside [0, vocab) have the key vocab, the largest, so they sort last
+        hdr[HDR_ERR] = n > 0 && sk[n - 1] == vocab;
+    }
 }
 
 // Block-wide exclusive scan over kSmallThreads threads (one int32 each); the total
@@ -535,7 +610,8 @@ hipError_t launch_zero_i32(int32_t *p, int64_t count, hipStream_t s) {
 }
 
 hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBufs &b, int64_t ntiles,
-                        hipStream_t s) {
+                        const int64_t *off, int heavy_min_tokens, int dense_min_tokens, int light_tokens,
+                        int4 *light, int2 *heavy, int2 *dense, int4 *light_long, hipStream_t s) {
     const int n = (int)n64;
     int bits = 1;
     while ((1ll << bits) <= vocab) ++bits;  // keys lie in [0, vocab]
@@ -561,9 +637,10 @@ hipError_t launch_route(const int32_t *ids, int64_t n64, int64_t vocab, RouteBuf
     b.sorted_ids = const_cast<int32_t *>(kin);
     b.perm = const_cast<int32_t *>(vin);
     hipLaunchKernelGGL(k_seg_heads, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, b.perm,
-                       n, b.tile_cnt, b.inv_perm);
+                       n, (int)ntiles, b.tile_cnt, b.inv_perm);
     hipLaunchKernelGGL(k_seg_write, dim3((unsigned)ntiles), dim3(256), 0, s, b.sorted_ids, n,
-                       b.tile_cnt, (int)ntiles, b.hdr, (int)vocab, b.uniq, b.seg_start);
+                       b.tile_cnt, (int)ntiles, b.hdr, (int)vocab, b.uniq, b.seg_start, b.counts, off,
+                       heavy_min_tokens, dense_min_tokens, light_tokens, light, heavy, dense, light_long);
     return hipGetLastError();
 }
 
