@@ -114,9 +114,10 @@ def copy_probe(mib: int):
 
 # kernel name prefix -> stage of one forward
 STAGE_OF_KERNEL = [("k_attn_mfma", "gather_mfma"), ("k_attn_light", "gather_light"),
-                   ("k_gemm_bf16<false, false, 3,", "ln_stats_gemm"), ("k_ln_quad_finalize", "ln_stats_gemm"),
+                   ("k_gemm_bf16<false, false, 3,", "ln_stats_gemm"),
                    ("k_gemm_bf16<true, false, 0,", "w_mix_gemm"),
                    ("k_transpose", "mix_prep"), ("k_center_rows", "mix_prep"), ("k_mix_fold", "mix_prep"),
+                   ("k_gemm_bf16<false, false, 0,", "mix_prep"),  # [F ; G] (the only plain GEMM)
                    ("k_gemm_skinny", "mix_prep"), ("k_skinny_reduce", "mix_prep"),
                    ("k_sort", "route"), ("k_scan", "route"), ("k_seg", "route"),
                    ("k_worklist", "route"), ("k_zero_i32", "route"), ("k_route_small", "route")]
@@ -131,7 +132,7 @@ def read_counter_csv(path: str, counter: str):
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "")
+            name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "").replace("l3::", "")
             name = name[5:] if name.startswith("void ") else name
             name = name.split("(")[0]
             per.setdefault(name, []).append(float(r["Counter_Value"]))
@@ -152,7 +153,7 @@ def ingest_mfma(args):
     import csv
     per = {}
     for r in csv.DictReader(open(args.ingest_mfma)):
-        name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "")
+        name = r["Kernel_Name"].replace("l3::(anonymous namespace)::", "").replace("l3::", "")
         name = (name[5:] if name.startswith("void ") else name).split("(")[0]
         key = (name, r["Dispatch_Id"])
         d = per.setdefault(key, {"dur_ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
