@@ -93,7 +93,10 @@ const char *l3_strerror(int status);
  *          at least one and at most k embeddings, budget v = sum d_t).
  *          v and vocab must be below 2^31 (UNSUPPORTED otherwise).
  * dims:    host; bf16 needs d_in, d_up, d_out multiples of 64, d_in <= 4096
- *          and d_emb one of 64, 128, 256, 512; fp32 takes any positive dims.
+ *          and d_emb one of 64, 128, 256, 512, or d_emb = d_in = 1024 or 2048 for
+ *          tied tables only (l3_forward then needs W_V to be the W_K buffer;
+ *          l3_backward and the decode stagings refuse such plans with
+ *          UNSUPPORTED); fp32 takes any positive dims.
  * plan:    out; the handle owns a device copy of the offsets (allocated on the
  *          current HIP device).  Errors: INVALID_ARG, BAD_OFFSETS, UNSUPPORTED,
  *          NOMEM, HIP.
@@ -154,7 +157,10 @@ size_t l3_workspace_size_dims(const l3_dims_t *dims, int32_t max_d, int64_t n_ma
  * read once per call (the pages' batch sort: sciencestack.ai page, Fig. 3
  * caption); the result does not depend on the batch order.  W_V may be the same
  * buffer as W_K when d_emb == d_in (the pages' tied variant, papernotes.org page,
- * ablation table): the second read of each row then mostly hits the caches.
+ * ablation table): the wavefront gather kernel then copies each row once for both
+ * roles, and the matrix-core one finds the second read mostly in the caches.  bf16
+ * plans with d_emb 1024 or 2048 take tied tables only (UNSUPPORTED when W_V is not
+ * the W_K buffer) and gather every block in the wavefront kernel.
  * bf16 batches of more than 512 tokens evaluate W_mix [LN(h) ; x] in factored
  * form (the same function: with W_c the column-centred W_up, h - mean(h) = W_c o,
  * so W_mix [LN(h) ; x] = rstd (F o) + W1 beta + W2 x with F = W1 diag(gamma) W_c,
@@ -213,7 +219,8 @@ int l3_forward_noalloc(l3_plan_t plan, const void *x, const int32_t *token_ids, 
  * The forward is recomputed inside (nothing is saved from l3_forward).  Every sum
  * over tokens runs in a fixed order (no atomics): results are bit-for-bit
  * reproducible.  Operands of the dense products are bf16 for bf16 plans
- * (fp32 accumulation), fp32 otherwise.  Supports d_in <= 4096, d_emb <= 1024.
+ * (fp32 accumulation), fp32 otherwise.  Supports d_in <= 4096, d_emb <= 1024
+ * (bf16: d_emb <= 512; plans of the tied-only widths return UNSUPPORTED).
  * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, HIP.  IDs outside [0, vocab) set
  * the status flag (l3_status) and contribute no attention gradient.
  */
@@ -262,6 +269,8 @@ int l3_status(void *workspace, void *stream);
  * l3_staging_create -- device staging for up to max_rows table rows and
  * max_tokens tokens per step (rows: K and V of the distinct IDs of one step).
  * Allocates device memory (owned by the staging object) on the current device.
+ * Errors: INVALID_ARG, NOMEM, HIP; UNSUPPORTED for the tied-only bf16 plans
+ * (d_emb 1024, 2048), whose K and V rows a staging would hold apart.
  */
 int l3_staging_create(l3_plan_t plan, int64_t max_rows, int64_t max_tokens,
                       l3_staging_t *staging);

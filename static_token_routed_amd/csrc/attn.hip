@@ -36,7 +36,16 @@ __device__ inline float wave_sum(float v) {
 // VE consecutive bf16 of a d_emb row as fp32 (VE = d_emb / 64).
 template <int VE>
 __device__ inline void load_v(const uint16_t *p, float (&v)[VE]) {
-    if constexpr (VE == 8) {
+    if constexpr (VE > 8) {
+        // VE / 8 consecutive 16-byte pieces (d_emb 1024, 2048)
+#pragma unroll
+        for (int k = 0; k < VE / 8; ++k) {
+            const uint4 u = reinterpret_cast<const uint4 *>(p)[k];
+            v[8 * k + 0] = bf_lo(u.x); v[8 * k + 1] = bf_hi(u.x); v[8 * k + 2] = bf_lo(u.y);
+            v[8 * k + 3] = bf_hi(u.y); v[8 * k + 4] = bf_lo(u.z); v[8 * k + 5] = bf_hi(u.z);
+            v[8 * k + 6] = bf_lo(u.w); v[8 * k + 7] = bf_hi(u.w);
+        }
+    } else if constexpr (VE == 8) {
         const uint4 u = *reinterpret_cast<const uint4 *>(p);
         v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
         v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
@@ -53,7 +62,15 @@ __device__ inline void load_v(const uint16_t *p, float (&v)[VE]) {
 
 template <int VE>
 __device__ inline void store_o(uint16_t *p, const float (&v)[VE]) {
-    if constexpr (VE == 8) {
+    if constexpr (VE > 8) {
+#pragma unroll
+        for (int k = 0; k < VE / 8; ++k) {
+            uint4 u;
+            u.x = pack2(v[8 * k + 0], v[8 * k + 1]); u.y = pack2(v[8 * k + 2], v[8 * k + 3]);
+            u.z = pack2(v[8 * k + 4], v[8 * k + 5]); u.w = pack2(v[8 * k + 6], v[8 * k + 7]);
+            reinterpret_cast<uint4 *>(p)[k] = u;
+        }
+    } else if constexpr (VE == 8) {
         uint4 u;
         u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
         u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
@@ -108,8 +125,12 @@ struct LightArgs {
     int cap;                 // entries of items_long (the batch's tokens)
 };
 
-template <int NCI>
-constexpr int light_tokens_for() { return NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3); }
+// tokens per light item: as many x rows and output rows as the registers hold (an output
+// row takes VE fp32 per lane, 16 or 32 for the tied d_emb 1024 / 2048 tables)
+template <int NCI, int VE = 8>
+constexpr int light_tokens_for() {
+    return VE >= 32 ? 2 : VE >= 16 ? 4 : (NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3));
+}
 
 // Light items: one wavefront per item.  The item's K / V rows stream through a
 // ring of LR rows of this wavefront's LDS, filled by asynchronous global->LDS
@@ -119,9 +140,10 @@ constexpr int light_tokens_for() { return NCI <= 2 ? 8 : (NCI == 4 ? 6 : 3); }
 // A ring slot is NCI 1 KB pieces of the K row (lane l copies bytes [16l, 16l + 16)
 // of piece c, which are exactly the columns c*512 + 8l .. + 8 it multiplies) and
 // one 1 KB piece of the V row (lanes past the row copy its first bytes again).
-// With tied tables (W_V the same buffer as W_K, d_emb = d_in <= 512: the pages' tied
-// variant) the V row is the K row, whose single piece already holds its d_emb values
-// in order, so no V piece is copied and each row enters the CU once.
+// With tied tables (W_V the same buffer as W_K, d_emb = d_in: the pages' tied variant)
+// the V row is the K row, whose NCI pieces already hold its d_emb values in order, so no
+// V piece is copied and each row enters the CU once (d_emb 1024 and 2048, beyond the
+// matrix-core kernel's widths, are tied-only and take this kernel for every block).
 constexpr int kLightWaveLds = 20480;  // LDS bytes per wavefront (two workgroups per CU)
 template <int NCI>
 constexpr int light_ring_rows() {
@@ -148,7 +170,9 @@ __device__ inline void wait_rows(int later) {
 template <int NCI, int VE, int NT, int SPLIT, bool TIED>
 __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r0, int d, int w,
                                            int lane, unsigned char *lds_all) {
-    static_assert(!TIED || NCI == 1, "tied rows fit one piece");
+    // tied tables: d_emb = d_in, and the row's NCI pieces lie in order in the slot, so
+    // the lane's VE values of the V row are read from the K pieces
+    static_assert(!TIED || NCI == 1 || VE == 8 * NCI, "tied: d_emb = d_in");
     constexpr int NP = NCI + (TIED ? 0 : 1);  // 1 KB copies per row
     constexpr int LR = light_ring_rows<NCI>();
     constexpr int SLOT = NP * 1024;
@@ -307,7 +331,7 @@ __device__ __forceinline__ void light_item(const LightArgs &a, int p0, int64_t r
 template <int NCI, int VE, int SPLIT, bool TIED>
 __device__ __forceinline__ void light_item_nt(const LightArgs &a, int p0, int64_t r0, int d, int nt,
                                               int w, int lane, unsigned char *lds) {
-    constexpr int TL = light_tokens_for<NCI>();
+    constexpr int TL = light_tokens_for<NCI, VE>();
     switch (nt) {
         case 1: light_item<NCI, VE, 1, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
         case 2: if constexpr (TL >= 2) light_item<NCI, VE, 2, SPLIT, TIED>(a, p0, r0, d, w, lane, lds); break;
@@ -1271,6 +1295,15 @@ constexpr int kLightBlocks = 512;
 
 template <int NCI>
 hipError_t launch_light_nci(const LightArgs &la, int64_t d_emb, hipStream_t s) {
+    // tied tables of d_emb = d_in = 1024, 2048 (only tied: the wavefront kernel is the one
+    // gather path for them)
+    if constexpr (NCI == 2 || NCI == 4) {
+        if (la.WK == la.WV && la.d_in == d_emb && d_emb == 512 * NCI) {
+            hipLaunchKernelGGL((k_attn_light_bf16<NCI, 8 * NCI, true>), dim3(kLightBlocks), dim3(256), 0, s,
+                               la);
+            return hipGetLastError();
+        }
+    }
     if constexpr (NCI == 1) {
         // tied tables: one copy per row serves both roles
         if (la.WK == la.WV && la.d_in == d_emb) {
@@ -1470,22 +1503,26 @@ hipError_t launch_split_nci(const SplitArgs &sa, int64_t d_emb, int nblocks, hip
 
 }  // namespace
 
-int attn_light_tokens(int64_t d_in, int dtype) {
+int attn_light_tokens(int64_t d_in, int64_t d_emb, int dtype) {
     if (dtype != L3_BF16) return 1;
+    if (d_emb == 2048) return light_tokens_for<4, 32>();  // tied d_in = d_emb tables
+    if (d_emb == 1024) return light_tokens_for<2, 16>();
     if (d_in <= 1024) return light_tokens_for<2>();
     if (d_in <= 2048) return light_tokens_for<4>();
     return light_tokens_for<8>();
 }
 
-int attn_dense_min_tokens(int64_t d_in, int64_t, int dtype) {
-    return dtype == L3_BF16 && (heavy_d_in(d_in) || d_in == 4096) ? kDenseMinTokens : INT32_MAX;
+int attn_dense_min_tokens(int64_t d_in, int64_t d_emb, int dtype) {
+    return dtype == L3_BF16 && d_emb <= 512 && (heavy_d_in(d_in) || d_in == 4096) ? kDenseMinTokens
+                                                                                  : INT32_MAX;
 }
 
-int attn_heavy_min_tokens(int64_t d_in, int64_t, int dtype, int32_t) {
+int attn_heavy_min_tokens(int64_t d_in, int64_t d_emb, int dtype, int32_t) {
     // Streaming items also at d_in 4096 (the quarter layout).  There an item's two
     // 16-token groups run one after the other, so blocks of few rows stay with the
-    // wavefront kernel unless they have many tokens.
-    if (dtype != L3_BF16) return INT32_MAX;
+    // wavefront kernel unless they have many tokens.  The matrix-core kernel holds
+    // d_emb up to 512 (wider tied tables take the wavefront kernel only).
+    if (dtype != L3_BF16 || d_emb > 512) return INT32_MAX;
     if (heavy_d_in(d_in)) return kHeavyMinTokens;
     return d_in == 4096 ? kHeavyMinTokensWide : INT32_MAX;
 }

@@ -113,7 +113,10 @@ int validate_dims(const l3_dims_t *d) {
     if (d->dtype == L3_BF16) {
         if (d->d_in % 64 || d->d_up % 64 || d->d_out % 64) return L3_ERR_UNSUPPORTED;
         if (d->d_in > 4096) return L3_ERR_UNSUPPORTED;
-        if (d->d_emb != 64 && d->d_emb != 128 && d->d_emb != 256 && d->d_emb != 512)
+        // d_emb 1024 and 2048 for tied tables only (d_in = d_emb; the forward then
+        // requires W_V to be the W_K buffer)
+        const bool tied_wide = (d->d_emb == 1024 || d->d_emb == 2048) && d->d_in == d->d_emb;
+        if (d->d_emb != 64 && d->d_emb != 128 && d->d_emb != 256 && d->d_emb != 512 && !tied_wide)
             return L3_ERR_UNSUPPORTED;
     }
     return L3_OK;
@@ -181,7 +184,7 @@ int route_attend(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
         L3_HIP_TRY(launch_attn_split(sa, s));
         return L3_OK;
     }
-    const int light_tok = attn_light_tokens(D.d_in, D.dtype);
+    const int light_tok = attn_light_tokens(D.d_in, D.d_emb, D.dtype);
     const int heavy_min = attn_heavy_min_tokens(D.d_in, D.d_emb, D.dtype, P.max_d);
     const int dense_min = attn_dense_min_tokens(D.d_in, D.d_emb, D.dtype);
     {
@@ -220,6 +223,7 @@ int forward_impl(const l3_plan_s &P, const void *x, const int32_t *ids, int64_t 
                  const void *WV, const void *W_up, const float *gamma, const float *beta,
                  const void *W_mix, void *out, void *ws, size_t ws_bytes, hipStream_t s) {
     const Dims &D = P.dims;
+    if (tied_only(D) && WV != WK) return L3_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(D, n, P.max_d);
     if (ws_bytes < L.total) return L3_ERR_CAPACITY;
     const bool factored = D.dtype == L3_BF16 && n > kSkinnyMaxM;
@@ -729,7 +733,7 @@ int l3_backward(l3_plan_t p, const void *x, const int32_t *ids, int64_t n, const
                 float *dgamma, float *dbeta, float *dWmix, void *ws, size_t ws_bytes, void *stream) {
     if (!p || n < 0) return L3_ERR_INVALID_ARG;
     if (n == 0) return L3_OK;
-    if (n >= (1ll << 30)) return L3_ERR_UNSUPPORTED;
+    if (n >= (1ll << 30) || tied_only(p->dims)) return L3_ERR_UNSUPPORTED;
     if (!x || !ids || !WK || !WV || !W_up || !gamma || !beta || !W_mix || !dout || !dx || !dWK ||
         !dWV || !dWup || !dgamma || !dbeta || !dWmix || !ws)
         return L3_ERR_INVALID_ARG;
@@ -826,6 +830,7 @@ static size_t staging_meta_bytes(int64_t max_tokens) {
 int l3_staging_create(l3_plan_t p, int64_t max_rows, int64_t max_tokens, l3_staging_t *out) {
     if (!p || !out || max_rows <= 0 || max_tokens <= 0) return L3_ERR_INVALID_ARG;
     *out = nullptr;
+    if (tied_only(p->dims)) return L3_ERR_UNSUPPORTED;  // stagings hold K and V rows apart
     l3_staging_s *st = new (std::nothrow) l3_staging_s();
     if (!st) return L3_ERR_NOMEM;
     st->plan = p;

@@ -66,6 +66,10 @@ struct Dims {
     int dtype;
     float eps;
 };
+// bf16 plans with d_emb above 512 (1024, 2048; d_in = d_emb) serve tied tables only: the
+// forward requires W_V to be the W_K buffer, and the wavefront gather kernel takes
+// every block
+inline bool tied_only(const Dims &d) { return d.dtype == L3_BF16 && d.d_emb > 512; }
 
 // Byte offsets of the workspace regions for n_max tokens.
 struct WsLayout {
@@ -171,7 +175,7 @@ struct AttnArgs {
     float *scores;  // fp32 path scratch
     int32_t max_d;
 };
-int attn_light_tokens(int64_t d_in, int dtype);   // tokens per light work item
+int attn_light_tokens(int64_t d_in, int64_t d_emb, int dtype);   // tokens per light work item
 int attn_heavy_min_tokens(int64_t d_in, int64_t d_emb, int dtype, int32_t max_d);  // INT32_MAX = none
 int attn_dense_min_tokens(int64_t d_in, int64_t d_emb, int dtype);                  // INT32_MAX = none
 // the MFMA kernel over the heavy work list (bf16, when attn_heavy_min_tokens allows it),

@@ -60,6 +60,8 @@ def test_plan_rejects_bad_offsets(off, v, k, code):
     ((100, 64, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),   # d_in not a multiple of 64
     ((64, 96, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),    # d_emb not a supported width
     ((8192, 64, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),  # d_in above 4096
+    ((512, 1024, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED),  # d_emb 1024 only with d_in = d_emb (tied)
+    ((2048, 1536, 64, 64), "bf16", l3.L3_ERR_UNSUPPORTED), # d_emb not a supported width
     ((64, 64, 64, -1), "bf16", l3.L3_ERR_INVALID_ARG),
 ])
 def test_plan_rejects_bad_dims(dims, dtype, code):

@@ -390,11 +390,14 @@ def test_full_size(name):
     g.close()
 
 
-@pytest.mark.parametrize("d,n", [(256, 300), (256, 1200), (512, 1500), (64, 900)])
+@pytest.mark.parametrize("d,n", [(256, 300), (256, 1200), (512, 1500), (64, 900),
+                                 (1024, 1300), (1024, 300), (2048, 700), (2048, 200)])
 def test_tied_tables(d, n):
     """W_V = W_K (one device table passed for both; d_emb = d_in): the forward equals
-    the oracle's with equal tables (the pages' tied variant).  Above 512 tokens the
-    wavefront kernel's items read each row once for both roles (d_in <= 512)."""
+    the oracle's with equal tables (the pages' tied variant).  The wavefront kernel's
+    items read each row once for both roles; at d 1024 and 2048 (the tied-only widths)
+    that kernel takes every block, above 512 tokens with the factored W_mix and at or
+    below with the small-batch GEMMs."""
     cfg = dataclasses.replace(
         synth.small("tied", vocab=500, k=48, d_in=d, d_emb=d, d_up=256, d_out=192, n=n,
                     v=6000, dtype="bf16", seed=11), ids_s=1.05, tied=True)
@@ -405,6 +408,41 @@ def test_tied_tables(d, n):
     err = rowwise_err(got, oracle_out(case))
     print(f"tied d={d} n={n}: err {err:.2e}", flush=True)
     assert err <= case.tol
+    g.close()
+
+
+def test_tied_only_widths_refuse_separate_tables():
+    """bf16 plans with d_emb = d_in = 1024 serve tied tables only: a forward with a
+    separate W_V, a decode staging and the backward are refused with UNSUPPORTED
+    before anything is enqueued."""
+    cfg = dataclasses.replace(
+        synth.small("tied_only", vocab=200, k=16, d_in=1024, d_emb=1024, d_up=128, d_out=128,
+                    n=600, v=2000, dtype="bf16", seed=5), ids_s=1.05, tied=True)
+    case = make_case(cfg)
+    g = Gpu(case)
+    WV = g.WK.clone()
+    with pytest.raises(l3.L3Error) as e:
+        g.plan.forward(g.x, g.ids, g.WK, WV, g.Wup, g.gamma, g.beta, g.Wmix)
+    assert e.value.code == l3.L3_ERR_UNSUPPORTED
+    with pytest.raises(l3.L3Error) as e:
+        l3.l3_staging_create(g.plan.handle, 1024, 64)
+    assert e.value.code == l3.L3_ERR_UNSUPPORTED
+    n = len(case.ids)
+    f32 = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(l3.l3_backward_workspace_size(g.plan.handle, n), 256), dtype=torch.uint8,
+                     device="cuda")
+    dout = torch.zeros(n, cfg.d_out, dtype=torch.bfloat16, device="cuda")
+    rc = l3._lib.l3_backward(g.plan.handle, g.x.data_ptr(), g.ids.data_ptr(), n, g.WK.data_ptr(),
+                             g.WK.data_ptr(), g.Wup.data_ptr(), g.gamma.data_ptr(), g.beta.data_ptr(),
+                             g.Wmix.data_ptr(), dout.data_ptr(), f32(n, cfg.d_in).data_ptr(),
+                             f32(cfg.v, cfg.d_in).data_ptr(), f32(cfg.v, cfg.d_emb).data_ptr(),
+                             f32(cfg.d_up, cfg.d_emb).data_ptr(), f32(cfg.d_up).data_ptr(),
+                             f32(cfg.d_up).data_ptr(), f32(cfg.d_out, cfg.d_up + cfg.d_in).data_ptr(),
+                             ws.data_ptr(), ws.numel(), None)
+    assert rc == l3.L3_ERR_UNSUPPORTED
+    # the tied forward itself runs
+    got = to_np(g.plan.forward(g.x, g.ids, g.WK, g.WK, g.Wup, g.gamma, g.beta, g.Wmix))
+    assert rowwise_err(got, oracle_out(case)) <= case.tol
     g.close()
 
 
