@@ -27,10 +27,29 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// v shuffled within each 16-lane row by a DPP control (every source lane is in the row)
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+// Sum over the wavefront (every lane active), the same value in every lane: within each
+// 16-lane row by DPP (lane pairs, pairs of pairs, then the half-row and row mirrors;
+// each step adds two equal-order partials, so a row's lanes agree bit for bit), then the
+// four row sums read from lanes 0, 16, 32, 48 and added in that fixed order.  (Six
+// ds_bpermute shuffles per sum kept the wavefront kernel's rows waiting on LDS.)
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+    v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    v += dpp_f32<0x141>(v);  // row_half_mirror: lane i <-> 7 - i within 8
+    v += dpp_f32<0x140>(v);  // row_mirror: lane i <-> 15 - i within 16
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // VE consecutive bf16 of a d_emb row as fp32 (VE = d_emb / 64).
