@@ -37,10 +37,11 @@ FP32_VALU_PEAK_TF = 157.3   # MI355X fp32 vector FMA
 STAGES = ["route", "gather_mfma", "gather_light", "ln_stats_gemm", "mix_prep", "w_mix_gemm"]
 # the source files a stage's kernels come from (a counter summary holds while they hash
 # to the value recorded with it)
-KERNEL_SOURCES = {"gather_attention": ("attn.hip",), "gather_mfma": ("attn.hip",),
-                  "gather_light": ("attn.hip",), "ln_stats_gemm": ("gemm.hip",),
-                  "mix_prep": ("gemm.hip", "gemm_skinny.hip", "backward.hip"),
-                  "w_mix_gemm": ("gemm.hip",), "route": ("route.hip",)}
+_HDRS = ("l3_internal.h", "cdna4.h")  # constants and helpers every kernel source includes
+KERNEL_SOURCES = {"gather_attention": ("attn.hip",) + _HDRS, "gather_mfma": ("attn.hip",) + _HDRS,
+                  "gather_light": ("attn.hip",) + _HDRS, "ln_stats_gemm": ("gemm.hip",) + _HDRS,
+                  "mix_prep": ("gemm.hip", "gemm_skinny.hip", "backward.hip") + _HDRS,
+                  "w_mix_gemm": ("gemm.hip",) + _HDRS, "route": ("route.hip",) + _HDRS}
 
 
 def parse():
@@ -119,7 +120,7 @@ STAGE_OF_KERNEL = [("k_attn_mfma", "gather_mfma"), ("k_attn_light", "gather_ligh
                    ("k_transpose", "mix_prep"), ("k_center_rows", "mix_prep"), ("k_mix_fold", "mix_prep"),
                    ("k_gemm_bf16<false, false, 0,", "mix_prep"),  # [F ; G] (the only plain GEMM)
                    ("k_gemm_skinny", "mix_prep"), ("k_skinny_reduce", "mix_prep"),
-                   ("k_sort", "route"), ("k_scan", "route"), ("k_seg", "route"),
+                   ("k_sort", "route"), ("k_hist_scan", "route"), ("k_seg", "route"),
                    ("k_worklist", "route"), ("k_zero_i32", "route"), ("k_route_small", "route")]
 COMPOSITE = {"gather_attention": ("gather_mfma", "gather_light")}
 

@@ -33,8 +33,9 @@ constexpr int kHeavyMinRows = 64;  // ... and so do blocks with at least this ma
 constexpr int kHeavyLongRows = 256;
 constexpr int kHeavyMidRows = 128;
 // Radix scatter: up to this many 512-key tiles each workgroup forms its own digit
-// offsets from the whole histogram; past it one workgroup forms them all first
-constexpr int kScatterDirectTiles = 64;
+// offsets from the whole histogram; past it a scan launch forms them all first (from
+// 32 tiles on, the extra launch costs less than every workgroup reading the histogram)
+constexpr int kScatterDirectTiles = 16;
 constexpr int kHeavyMinTokensWide = 64;  // the token threshold at d_in 4096
 constexpr int kDenseTile = 64;     // tokens per dense work item (long blocks of the Zipf head)
 constexpr int kDenseMinTokens = 33;  // blocks with at least this many tokens ...
