@@ -239,11 +239,12 @@ struct BlockItems {
     int nl = 0, nh = 0, nd = 0, r0 = 0, d = 0;
 };
 
-__device__ inline BlockItems block_items(int S, int t, const int64_t *off, int vocab, int heavy_min,
+// (r0, d: the block's first table row and row count, 0 for IDs out of range)
+__device__ inline BlockItems block_items(int S, int t, int r0, int d, int vocab, int heavy_min,
                                          int dense_min, int light_tok) {
     BlockItems b;
-    b.d = t < vocab ? (int)(off[t + 1] - off[t]) : 0;
-    b.r0 = t < vocab ? (int)off[t] : 0;
+    b.d = d;
+    b.r0 = r0;
     if (heavy_min != INT32_MAX && t < vocab && (S >= heavy_min || b.d >= kHeavyMinRows)) {
         if (S >= dense_min && b.d >= kDenseMinD && b.d <= kDenseMaxD)
             b.nd = (S + kDenseTile - 1) / kDenseTile;
@@ -281,13 +282,13 @@ __device__ constexpr int list_hdr(int k) {
          : k == 6 ? HDR_NHEAVY_TAIL : HDR_NDENSE;
 }
 template <class Reserve>
-__device__ inline void block_worklist(bool act, int j, int sb, int S, int t, const int64_t *off, int vocab,
+__device__ inline void block_worklist(bool act, int j, int sb, int S, int t, int r0, int d, int vocab,
                                       int heavy_min, int dense_min, int light_tok, int4 *light,
                                       int2 *heavy, int2 *dense, int4 *light_long, int nmax,
                                       Reserve reserve) {
     const int lane = threadIdx.x & 63;
     BlockItems bi;
-    if (act) bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
+    if (act) bi = block_items(S, t, r0, d, vocab, heavy_min, dense_min, light_tok);
     const bool lng = light_long != nullptr && bi.d >= kLightLongRows;
     const bool mid = light_long != nullptr && !lng && bi.d >= kLightMidRows;
     const bool lsh = light_long != nullptr && bi.d < kLightShortRows;  // to the light list's back
@@ -358,15 +359,20 @@ __global__ __launch_bounds__(256) void k_worklist(const int32_t *__restrict__ un
                                                   int4 *__restrict__ light_long, int nmax) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int m = hdr[HDR_NSEG];
-    int S = 0, sb = 0, t = vocab;
+    int S = 0, sb = 0, t = vocab, r0 = 0, d = 0;
     if (j < m) {
         sb = seg_start[j];
         S = seg_start[j + 1] - sb;
         counts[j] = S;
         t = uniq[j];
+        if (t < vocab) {
+            r0 = (int)off[t];
+            d = (int)(off[t + 1] - off[t]);
+        }
     }
-    block_worklist(j < m, j, sb, S, t, off, vocab, heavy_min, dense_min, light_tok, light, heavy, dense,
-                   light_long, nmax, [&](int k, int c) { return atomicAdd(&hdr[list_hdr(k)], c); });
+    block_worklist(j < m, j, sb, S, t, r0, d, vocab, heavy_min, dense_min, light_tok, light, heavy,
+                   dense, light_long, nmax,
+                   [&](int k, int c) { return atomicAdd(&hdr[list_hdr(k)], c); });
 }
 
 // Writes uniq[], seg_start[] and counts[] of the blocks whose heads lie in one tile
@@ -389,12 +395,37 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
     __shared__ int32_t wsum[4], wmin[4];
     __shared__ int32_t tile_sums[3];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the thread's sorted keys, its heads and their blocks' CSR offsets come first, so
+    // these dependent reads overlap the tile sums below
+    const int base = blockIdx.x * kSortTile + threadIdx.x * kSortPer;
+    int flags = 0, c = 0, mine = n;  // mine: this thread's first head
+    int key[kSortPer], r0[kSortPer], drows[kSortPer];
+    {
+        const int prev = base > 0 && base - 1 < n ? sk[base - 1] : -1;
+#pragma unroll
+        for (int i = 0; i < kSortPer; ++i) key[i] = base + i < n ? sk[base + i] : vocab;
+#pragma unroll
+        for (int i = kSortPer - 1; i >= 0; --i) {
+            const int s = base + i;
+            const int f = (s < n) && (s == 0 || key[i] != (i ? key[i - 1] : prev));
+            flags |= f << i;
+            c += f;
+            if (f) mine = s;
+        }
+#pragma unroll
+        for (int i = 0; i < kSortPer; ++i) {
+            const bool h = ((flags >> i) & 1) && key[i] < vocab;
+            const int64_t a = h ? off[key[i]] : 0, b = h ? off[key[i] + 1] : 0;
+            r0[i] = (int)a;
+            drows[i] = (int)(b - a);
+        }
+    }
     // heads before this tile, all heads, and the first head after it
     int32_t before = 0, total = 0, after = n;
     for (int u = threadIdx.x; u < ntiles; u += 256) {
-        const int32_t c = tile_cnt[u];
-        total += c;
-        before += u < (int)blockIdx.x ? c : 0;
+        const int32_t cu = tile_cnt[u];
+        total += cu;
+        before += u < (int)blockIdx.x ? cu : 0;
         if (u > (int)blockIdx.x) after = min(after, tile_cnt[ntiles + u]);
     }
 #pragma unroll
@@ -418,19 +449,6 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
     if (threadIdx.x == 0) tile_sums[1] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
     const int32_t tile_off = tile_sums[0], m = tile_sums[1], next_tile_head = tile_sums[2];
-
-    const int base = blockIdx.x * kSortTile + threadIdx.x * kSortPer;
-    int flags = 0, c = 0, mine = n;  // mine: this thread's first head
-    int key[kSortPer];
-#pragma unroll
-    for (int i = kSortPer - 1; i >= 0; --i) {
-        const int s = base + i;
-        key[i] = s < n ? sk[s] : vocab;
-        const int f = (s < n) && (s == 0 || key[i] != sk[s - 1]);
-        flags |= f << i;
-        c += f;
-        if (f) mine = s;
-    }
     // the first head after this thread's positions: a suffix minimum over the later
     // lanes, then the later wavefronts of the tile, then the later tiles
     int suf = mine;
@@ -462,8 +480,8 @@ __global__ __launch_bounds__(256) void k_seg_write(const int32_t *__restrict__ s
             counts[j] = S;
         }
         if (light)
-            block_worklist(h, j, base + i, S, key[i], off, vocab, heavy_min, dense_min, light_tok, light,
-                           heavy, dense, light_long, n,
+            block_worklist(h, j, base + i, S, key[i], r0[i], drows[i], vocab, heavy_min, dense_min,
+                           light_tok, light, heavy, dense, light_long, n,
                            [&](int k, int v) { return atomicAdd(&hdr[list_hdr(k)], v); });
         j += h;
     }
@@ -586,7 +604,11 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(
         return;
     }
     BlockItems bi;
-    if (i < m) bi = block_items(S, t, off, vocab, heavy_min, dense_min, light_tok);
+    if (i < m) {
+        const bool in = t < vocab;
+        bi = block_items(S, t, in ? (int)off[t] : 0, in ? (int)(off[t + 1] - off[t]) : 0, vocab, heavy_min,
+                         dense_min, light_tok);
+    }
     int32_t tl, th, td;
     const int bl = block_scan_small(bi.nl, wsum, &tl);
     const int bh = block_scan_small(bi.nh, wsum, &th);
