@@ -51,6 +51,11 @@ def _route_case(name):
         ids = rng.integers(0, vocab, size=1 << 20).astype(np.int32)
     elif name == "tiles_65":
         ids = rng.integers(0, 700, size=64 * 512 + 1).astype(np.int32)
+    # the last batch whose scatter reads the whole histogram (16 tiles) and the first that
+    # takes the digit scan (17)
+    elif name in ("tiles_16", "tiles_17"):
+        n = 16 * 512 + (name == "tiles_17")
+        ids = rng.integers(0, 900, size=n).astype(np.int32)
     else:
         raise KeyError(name)
     return off, ids
@@ -58,7 +63,7 @@ def _route_case(name):
 
 ROUTE_CASES = ["tiny_f32", "small_bf16", "paper_bf16", "skew_bf16", "all_equal", "all_distinct",
                "single", "ragged", "max_id", "out_of_range", "small_zipf", "small_out_of_range",
-               "n1024", "n1025", "tiles_65", "tiles_2048"]
+               "n1024", "n1025", "tiles_16", "tiles_17", "tiles_65", "tiles_2048"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -117,6 +122,8 @@ SMALL_BF16 = [
     # 512-column slice (masked lanes, 16-row chunks) at the largest such batch, the
     # widest d_in (2-row chunks, one token per group), and one token past the limit
     # (the single-workgroup route with the per-block gather kernels)
+    # 17 route tiles: the digit-scan scatter, then the factored W_mix
+    ("d1024_n8193", 2000, 96, 1024, 256, 256, 256, 8193, 40000),
     ("split_d192_n512", 300, 90, 192, 64, 128, 64, 512, 9000),
     ("split_d4096_e128", 200, 40, 4096, 128, 128, 128, 100, 4000),
     ("nosplit_d192_n513", 300, 90, 192, 64, 128, 64, 513, 9000),
