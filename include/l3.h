@@ -67,7 +67,7 @@ enum {
     L3_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum        */
     L3_ERR_BAD_OFFSETS = -2, /* off[0] != 0, d_t < 1, d_t > k, off[vocab]!=v */
     L3_ERR_TOKEN_RANGE = -3, /* a token ID outside [0, vocab)                */
-    L3_ERR_UNSUPPORTED = -4, /* dims this build does not handle              */
+    L3_ERR_UNSUPPORTED = -4, /* dims the library does not handle            */
     L3_ERR_CAPACITY = -5,    /* n or rows above what a buffer was sized for  */
     L3_ERR_NOMEM = -6,       /* host or device allocation failed             */
     L3_ERR_HIP = -7          /* a HIP runtime call failed                    */
